@@ -1,0 +1,11 @@
+"""Block-scaled FP4 routed-expert MoE layer and 4/6 quantizer for MI355X (gfx950).
+
+The computation lives in hand-written HIP kernels behind the C ABI of
+include/fp4moe.h (libfp4moe.so, built by `python -m
+block_scaled_fp4_nvfp4_amd.build`).  This package is its thin Python binding.
+"""
+from ._lib import (FMT, RULE, Fp4Error, MoELayer, dequantize, lib, moe_forward,
+                   quantize, status_string, workspace_layout, workspace_size)
+
+__all__ = ["FMT", "RULE", "Fp4Error", "MoELayer", "dequantize", "lib", "moe_forward",
+           "quantize", "status_string", "workspace_layout", "workspace_size"]

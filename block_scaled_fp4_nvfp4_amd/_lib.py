@@ -1,0 +1,226 @@
+"""ctypes binding of libfp4moe.so (the C ABI in include/fp4moe.h).
+
+Argument marshalling only: every computation runs in the HIP kernels of the
+library.  torch provides device memory and the current HIP stream.  There is
+no fallback: if the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp4moe.so")
+
+FMT = {"nvfp4": 0, "mxfp4": 1, "mxfp8": 2, "fp8_block": 3, "fp8_row": 4, "none": 5}
+RULE = {"rtn": 0, "4over6": 1}
+TS_DYNAMIC, TS_STATIC = 0, 1
+DT_BF16, DT_F32 = 0, 1
+STATUS = {0: "FP4_OK", -1: "FP4_ERR_INVALID_ARG", -2: "FP4_ERR_SHAPE",
+          -3: "FP4_ERR_UNSUPPORTED", -4: "FP4_ERR_WORKSPACE", -5: "FP4_ERR_HIP"}
+
+EXPORTED = ["fp4_quantize", "fp4_dequantize", "moe_fp4_workspace_layout",
+            "moe_fp4_workspace_size", "moe_fp4_forward", "fp4_status_string",
+            "fp4_last_error"]
+
+
+class Fp4Error(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+class LayerStruct(ctypes.Structure):
+    _fields_ = [
+        ("w_fmt", ctypes.c_int32), ("a_fmt", ctypes.c_int32),
+        ("num_experts", ctypes.c_int32), ("hidden", ctypes.c_int32),
+        ("inter", ctypes.c_int32), ("top_k", ctypes.c_int32),
+        ("w13", ctypes.c_void_p), ("w13_scale", ctypes.c_void_p), ("w13_scale_2", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p), ("w2_scale", ctypes.c_void_p), ("w2_scale_2", ctypes.c_void_p),
+        ("input_scale", ctypes.c_void_p), ("inter_scale", ctypes.c_void_p),
+        ("shared_inter", ctypes.c_int32),
+        ("ws13", ctypes.c_void_p), ("ws13_scale", ctypes.c_void_p),
+        ("ws2", ctypes.c_void_p), ("ws2_scale", ctypes.c_void_p),
+        ("shared_gate", ctypes.c_void_p),
+    ]
+
+
+class WsLayoutStruct(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "total", "error_flag", "counts", "offsets", "pair_of_row", "row_of_pair",
+        "x_tensor_scale", "h_tensor_scale", "h", "hq_codes", "hq_scales", "o")]
+
+
+_lib = None
+
+
+def lib():
+    """Load libfp4moe.so; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"{_LIB_PATH} is missing: run "
+                              "`python -m block_scaled_fp4_nvfp4_amd.build` first")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        L.fp4_quantize.argtypes = [i32, i32, i32, vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.fp4_quantize.restype = i32
+        L.fp4_dequantize.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp, i32, vp]
+        L.fp4_dequantize.restype = i32
+        L.moe_fp4_workspace_layout.argtypes = [ctypes.POINTER(LayerStruct), i64, ctypes.POINTER(WsLayoutStruct)]
+        L.moe_fp4_workspace_layout.restype = i32
+        L.moe_fp4_workspace_size.argtypes = [ctypes.POINTER(LayerStruct), i64, ctypes.POINTER(sz)]
+        L.moe_fp4_workspace_size.restype = i32
+        L.moe_fp4_forward.argtypes = [ctypes.POINTER(LayerStruct), vp, i64, vp, vp, vp, vp, sz, vp]
+        L.moe_fp4_forward.restype = i32
+        L.fp4_status_string.argtypes = [i32]
+        L.fp4_status_string.restype = ctypes.c_char_p
+        L.fp4_last_error.argtypes = []
+        L.fp4_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise Fp4Error(status, lib().fp4_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    if t.dtype == torch.float32:
+        return DT_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dims(x: torch.Tensor):
+    if x.dim() == 2:
+        return 1, x.shape[0], x.shape[1]
+    if x.dim() == 3:
+        return x.shape
+    raise ValueError("expected [rows, cols] or [batch, rows, cols]")
+
+
+def quantize(x: torch.Tensor, fmt: str, rule: str = "4over6",
+             tensor_scale: Optional[torch.Tensor] = None, want_m4: bool = False):
+    """fp4_quantize.  x: contiguous bf16/f32 device tensor [rows, cols] or
+    [batch, rows, cols].  Returns dict(codes, scales, tensor_scale, m4)."""
+    assert x.is_cuda and x.is_contiguous()
+    b, r, c = (int(v) for v in _dims(x))
+    dev = x.device
+    f = FMT[fmt]
+    lead = x.shape[:-1]
+    if fmt in ("nvfp4", "mxfp4"):
+        codes = torch.empty(*lead, c // 2, dtype=torch.uint8, device=dev)
+    else:
+        codes = torch.empty(*lead, c, dtype=torch.uint8, device=dev)
+    bs = {"nvfp4": 16, "mxfp4": 32, "mxfp8": 32}.get(fmt)
+    if bs is not None:
+        scales = torch.empty(*lead, max(c // bs, 0), dtype=torch.uint8, device=dev)
+    elif fmt == "fp8_row":
+        scales = torch.empty(*lead, c // 128, dtype=torch.float32, device=dev)
+    else:
+        scales = torch.empty(*x.shape[:-2], r // 128, c // 128, dtype=torch.float32, device=dev)
+    ts_mode = TS_DYNAMIC
+    ts = None
+    if fmt == "nvfp4":
+        if tensor_scale is None:
+            ts = torch.empty(b, dtype=torch.float32, device=dev)
+        else:
+            ts = tensor_scale.to(device=dev, dtype=torch.float32).reshape(b).contiguous()
+            ts_mode = TS_STATIC
+    m4 = None
+    if want_m4 and bs is not None and fmt != "mxfp8":
+        m4 = torch.empty(*lead, c // bs, dtype=torch.uint8, device=dev)
+    _check(lib().fp4_quantize(f, RULE[rule], ts_mode, _ptr(x), _dtype_code(x), b, r, c,
+                              _ptr(codes), _ptr(scales), _ptr(ts), _ptr(m4), _stream()))
+    return {"codes": codes, "scales": scales, "tensor_scale": ts, "m4": m4}
+
+
+def dequantize(q: dict, fmt: str, shape, out_dtype=torch.float32) -> torch.Tensor:
+    """fp4_dequantize of a record produced by quantize(); shape = x's shape."""
+    codes = q["codes"]
+    out = torch.empty(*shape, dtype=out_dtype, device=codes.device)
+    b, r, c = (int(v) for v in _dims(out))
+    _check(lib().fp4_dequantize(FMT[fmt], _ptr(codes), _ptr(q["scales"]), _ptr(q.get("tensor_scale")),
+                                b, r, c, _ptr(out), _dtype_code(out), _stream()))
+    return out
+
+
+@dataclasses.dataclass
+class MoELayer:
+    """Device tensors of one routed-expert layer (see moe_fp4_layer)."""
+    w_fmt: str
+    a_fmt: str
+    num_experts: int
+    hidden: int
+    inter: int
+    top_k: int
+    w13: torch.Tensor
+    w13_scale: torch.Tensor
+    w2: torch.Tensor
+    w2_scale: torch.Tensor
+    w13_scale_2: Optional[torch.Tensor] = None
+    w2_scale_2: Optional[torch.Tensor] = None
+    input_scale: Optional[torch.Tensor] = None
+    inter_scale: Optional[torch.Tensor] = None
+    shared_inter: int = 0
+    ws13: Optional[torch.Tensor] = None
+    ws13_scale: Optional[torch.Tensor] = None
+    ws2: Optional[torch.Tensor] = None
+    ws2_scale: Optional[torch.Tensor] = None
+    shared_gate: Optional[torch.Tensor] = None
+
+    def struct(self) -> LayerStruct:
+        p = lambda t: None if t is None else t.data_ptr()
+        return LayerStruct(
+            FMT[self.w_fmt], FMT[self.a_fmt], self.num_experts, self.hidden, self.inter, self.top_k,
+            p(self.w13), p(self.w13_scale), p(self.w13_scale_2),
+            p(self.w2), p(self.w2_scale), p(self.w2_scale_2),
+            p(self.input_scale), p(self.inter_scale), self.shared_inter,
+            p(self.ws13), p(self.ws13_scale), p(self.ws2), p(self.ws2_scale), p(self.shared_gate))
+
+
+def workspace_layout(layer: MoELayer, tokens: int) -> dict:
+    s = layer.struct()
+    out = WsLayoutStruct()
+    _check(lib().moe_fp4_workspace_layout(ctypes.byref(s), tokens, ctypes.byref(out)))
+    return {n: getattr(out, n) for n, _ in WsLayoutStruct._fields_}
+
+
+def workspace_size(layer: MoELayer, tokens: int) -> int:
+    s = layer.struct()
+    n = ctypes.c_size_t()
+    _check(lib().moe_fp4_workspace_size(ctypes.byref(s), tokens, ctypes.byref(n)))
+    return n.value
+
+
+def moe_forward(layer: MoELayer, x: torch.Tensor, topk_ids: torch.Tensor,
+                topk_weights: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+                y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_fp4_forward: x bf16 [T, H], topk_ids int32 [T, k], topk_weights f32 [T, k] -> y f32 [T, H]."""
+    T = int(x.shape[0])
+    if y is None:
+        y = torch.empty(T, layer.hidden, dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(workspace_size(layer, T), 1), dtype=torch.uint8, device=x.device)
+    s = layer.struct()
+    _check(lib().moe_fp4_forward(ctypes.byref(s), _ptr(x), T, _ptr(topk_ids), _ptr(topk_weights),
+                                 _ptr(y), _ptr(workspace), workspace.numel(), _stream()))
+    return y
+
+
+def status_string(status: int) -> str:
+    return lib().fp4_status_string(status).decode()

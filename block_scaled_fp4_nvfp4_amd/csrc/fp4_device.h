@@ -1,0 +1,141 @@
+// Device helpers for the E2M1 / E4M3 / UE8M0 formats (gfx950).
+//
+// NVFP4 = E2M1 values, an E4M3 scale per 16 values and an FP32 tensor scale
+// (dabsLabs NVFP4 card, "What makes this build different"; Local-Hessian NVFP4
+// card, opening section); MXFP4 = E2M1 with a UE8M0 scale per 32
+// (MXFP4-FP8-R12 card, "Quantization format"); MXFP8 = E4M3 values with a
+// power-of-two scale per 32 (FP4-Local AZ card, "The shared expert").
+//
+// Every rounding decision here is exact: scales are rounded from float64
+// quotients that cannot sit within float64 rounding error of an E4M3 decision
+// point unless they are exactly on it, and E2M1 codes are decided by comparing
+// |x| with float32 thresholds rounded in the direction that keeps each
+// comparison exact (see e2m1_thresholds).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4 {
+
+constexpr float kE4M3Max = 448.0f;
+constexpr double kNvTensorDivisor = 2688.0;  // E2M1 max 6 times E4M3 max 448
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) {
+  return __uint_as_float(b16 << 16);
+}
+
+// float32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// E4M3 (FN) byte -> float; 0x7F/0xFF never occur in scales written here.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))
+                : (float)m * 0.001953125f;  // m * 2^-9
+  return (c & 0x80u) ? -mag : mag;
+}
+
+// E2M1 magnitude code (0..7) -> float: 0, .5, 1, 1.5, 2, 3, 4, 6
+__device__ __forceinline__ float e2m1_mag_to_f32(uint32_t c) {
+  return c >= 2 ? __uint_as_float((c + 252u) << 22) : 0.5f * (float)c;
+}
+
+// UE8M0 byte -> 2^(c-127) as double (exact for c in 0..254)
+__device__ __forceinline__ double ue8m0_to_f64(uint32_t c) {
+  return ldexp(1.0, (int)c - 127);
+}
+
+// Round a non-negative double to the nearest E4M3 code, ties to even,
+// saturating at 448 (0x7E).  Exact for any double input.
+__device__ __forceinline__ uint32_t e4m3_rne_sat_f64(double q) {
+  if (!(q > 0.0)) return 0u;
+  if (q >= 448.0) return 0x7Eu;
+  int e;
+  (void)frexp(q, &e);           // q in [2^(e-1), 2^e)
+  int E = e - 1;                // unbiased exponent of q
+  if (E < -6) {                 // subnormal range: quantum 2^-9; code = n (n == 8 is 2^-6)
+    double n = rint(ldexp(q, 9));
+    return (uint32_t)n;
+  }
+  double n = rint(ldexp(q, 3 - E));  // in [8, 16]
+  uint32_t code = ((uint32_t)(E + 7) << 3) + ((uint32_t)n - 8u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// Round a non-negative float to the nearest E4M3 code (ties to even,
+// saturating).  Exact: the scalings are by powers of two.
+__device__ __forceinline__ uint32_t e4m3_rne_sat_f32(float v) {
+  if (!(v > 0.0f)) return 0u;
+  if (v >= 448.0f) return 0x7Eu;
+  int E = (int)((__float_as_uint(v) >> 23) & 0xFF) - 127;
+  if (E < -6) return (uint32_t)rintf(ldexpf(v, 9));
+  float n = rintf(ldexpf(v, 3 - E));
+  uint32_t code = ((uint32_t)(E + 7) << 3) + ((uint32_t)n - 8u);
+  return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// Largest float <= T and smallest float >= T, for a non-negative double T.
+__device__ __forceinline__ float f32_round_down(double T) {
+  float f = (float)T;
+  if ((double)f > T) f = __uint_as_float(__float_as_uint(f) - 1u);
+  return f;
+}
+__device__ __forceinline__ float f32_round_up(double T) {
+  float f = (float)T;
+  if ((double)f < T) f = __uint_as_float(__float_as_uint(f) + 1u);
+  return f;
+}
+
+// Thresholds deciding the E2M1 code of |x| / unit.  The E2M1 midpoints are
+// 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; at a tie the even code wins, so the
+// magnitude code is
+//   sum_{j even} [|x| > mid_j*unit] + sum_{j odd} [|x| >= mid_j*unit].
+// mid_j*unit is exact in double (<= 3 + 28 significant bits); for a float
+// |x|, "|x| > T" equals "|x| > round_down(T)" and "|x| >= T" equals
+// "|x| >= round_up(T)", so float comparisons decide exactly.  unit == 0
+// gives thresholds of +inf (all codes 0).
+struct E2M1Thresholds {
+  float t[7];
+};
+
+__device__ __forceinline__ E2M1Thresholds e2m1_thresholds(double unit) {
+  E2M1Thresholds th;
+  const double mids[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    double T = mids[j] * unit;
+    th.t[j] = (unit > 0.0) ? ((j & 1) ? f32_round_up(T) : f32_round_down(T))
+                           : __builtin_inff();
+  }
+  return th;
+}
+
+__device__ __forceinline__ uint32_t e2m1_code(float a, const E2M1Thresholds& th) {
+  uint32_t c = 0;
+  c += a > th.t[0];
+  c += a >= th.t[1];
+  c += a > th.t[2];
+  c += a >= th.t[3];
+  c += a > th.t[4];
+  c += a >= th.t[5];
+  c += a > th.t[6];
+  return c;
+}
+
+// Smallest e with M * 2^e >= a (a > 0 finite), M in {4, 6, 448}, clamped to
+// [-127, 127]; a == 0 gives -127.  Exact integer logic on frexp.
+__device__ __forceinline__ int mx_exponent(float a, float M) {
+  if (!(a > 0.0f)) return -127;
+  int p;
+  float f = frexpf(a, &p);     // a = f * 2^p, f in [0.5, 1)
+  int pm;
+  float fm = frexpf(M, &pm);   // M = fm * 2^pm
+  // M * 2^e >= a  <=>  fm * 2^(pm+e) >= f * 2^p
+  int e = (fm >= f) ? (p - pm) : (p - pm + 1);
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+}  // namespace fp4

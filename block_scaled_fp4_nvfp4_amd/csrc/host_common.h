@@ -1,0 +1,47 @@
+// Host-side helpers of the C ABI: status codes, the thread-local error text,
+// launch checking.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/fp4moe.h"
+
+namespace fp4 {
+
+void set_last_error(const char* fmt, ...);
+
+inline int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  set_last_error("%s: %s", fp4_status_string(status), buf);
+  return status;
+}
+
+inline int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess)
+    return fail(FP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return FP4_OK;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline unsigned grid_1d(int64_t n, int threads) {
+  return (unsigned)((n + threads - 1) / threads);
+}
+
+// number of compute units of the current device (cached per device id)
+int device_cu_count();
+
+}  // namespace fp4
+
+#define FP4_CHECK(expr)                  \
+  do {                                   \
+    int _st = (expr);                    \
+    if (_st != FP4_OK) return _st;       \
+  } while (0)

@@ -1,0 +1,661 @@
+// Routed-expert MoE forward behind moe_fp4_forward (gfx950).
+//
+// Steps (model cards on block_scaled_fp4_nvfp4: stacked [E, out, in] experts
+// with fused gate_up, dabsLabs NVFP4 card; top-k routing width and shared
+// expert width from the configuration, FP4-Local AZ card):
+//   1. permute: stable counting sort of the T*k (token, slot) pairs by expert
+//   2. dynamic activation quantization of x (W4A4 / MX / FP8 modes)
+//   3. gate_up projection of each pair's token, SiLU(gate) * up -> h (f32)
+//   4. quantization of h (same modes)
+//   5. down projection of each pair -> o (f32, unweighted)
+//   6. combine: y[t] = sum_j w[t, j] * o[row(t, j)] in slot order (+ shared expert)
+//
+// This file holds the workspace plan, the permutation, the weight-only
+// (bf16 activation) GEMV path used at decode sizes, the combine and the
+// C entry points; the MFMA grouped GEMMs live in moe_gemm.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+
+#include "fp4_device.h"
+#include "host_common.h"
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace fp4 {
+
+// ------------------------------------------------------------ workspace plan
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int plan_workspace(const moe_fp4_layer* L, int64_t T, WsPlan* w) {
+  const int64_t E = L->num_experts, H = L->hidden, I = L->inter, k = L->top_k;
+  const int64_t P = T * k;
+  const int64_t nb = (P + kPermBlock - 1) / kPermBlock;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + std::max<size_t>(bytes, 1), 256);
+    return at;
+  };
+  WsPlan p{};
+  p.error_flag = take(sizeof(int32_t) * 4);
+  p.counts = take(sizeof(int32_t) * E);
+  p.offsets = take(sizeof(int32_t) * (E + 1));
+  p.pair_of_row = take(sizeof(int32_t) * P);
+  p.row_of_pair = take(sizeof(int32_t) * P);
+  p.active = take(sizeof(int32_t) * (E + 1));
+  p.tile_offsets = take(sizeof(int32_t) * (E + 1));
+  p.block_counts = take(sizeof(int32_t) * nb * E);
+  p.block_invalid = take(sizeof(int32_t) * nb);
+  p.x_tensor_scale = take(sizeof(float) * 2);
+  p.h_tensor_scale = take(sizeof(float) * 2);
+  p.h = take(sizeof(float) * P * I);
+  // quantized activations (layout of the activation format)
+  size_t xq_codes = 0, xq_scales = 0, hq_codes = 0, hq_scales = 0;
+  switch (L->a_fmt) {
+    case FP4_FMT_NVFP4:
+      xq_codes = T * H / 2; xq_scales = T * H / 16;
+      hq_codes = P * I / 2; hq_scales = P * I / 16;
+      break;
+    case FP4_FMT_MXFP8:
+      xq_codes = T * H; xq_scales = T * H / 32;
+      hq_codes = P * I; hq_scales = P * I / 32;
+      break;
+    case FP4_FMT_FP8_ROW:
+      xq_codes = T * H; xq_scales = T * H / 128 * 4;
+      hq_codes = P * I; hq_scales = P * I / 128 * 4;
+      break;
+    default: break;
+  }
+  p.xq_codes = take(xq_codes);
+  p.xq_scales = take(xq_scales);
+  p.hq_codes = take(hq_codes);
+  p.hq_scales = take(hq_scales);
+  p.o = take(sizeof(float) * P * H);
+  if (L->shared_inter > 0) {
+    const int64_t S = L->shared_inter;
+    p.sx_codes = take(T * H);
+    p.sx_scales = take(T * H / 32);
+    p.sh = take(sizeof(float) * T * S);
+    p.sh_codes = take(T * S);
+    p.sh_scales = take(T * S / 32);
+    p.s_out = take(sizeof(float) * T * H);
+  }
+  p.total = off;
+  *w = p;
+  return FP4_OK;
+}
+
+// ----------------------------------------------------------------- permute
+
+// Exclusive scan over 1024 threads of one workgroup; returns the prefix of
+// `v` and writes the total to *total.  `tmp` holds 1024 ints of LDS.
+__device__ int block_scan_1024(int v, int* tmp, int* total) {
+  int tid = threadIdx.x;
+  tmp[tid] = v;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    int add = tid >= d ? tmp[tid - d] : 0;
+    __syncthreads();
+    tmp[tid] += add;
+    __syncthreads();
+  }
+  int incl = tmp[tid];
+  *total = tmp[1023];
+  __syncthreads();
+  return incl - v;
+}
+
+// Counts, offsets, active-expert list and GEMM tile offsets from per-expert
+// counts held in `cnt` (global, E ints).  One workgroup of 1024 threads.
+__device__ void finish_offsets(const int32_t* cnt, int E, int tile_m, int32_t* offsets,
+                               int32_t* active, int32_t* tile_offsets, int* tmp) {
+  int tid = threadIdx.x;
+  int per = (E + 1023) / 1024;
+  int lo = min(E, tid * per), hi = min(E, lo + per);
+  int s_cnt = 0, s_act = 0, s_tile = 0;
+  for (int e = lo; e < hi; ++e) {
+    int c = cnt[e];
+    s_cnt += c;
+    s_act += c > 0;
+    s_tile += (c + tile_m - 1) / tile_m;
+  }
+  int tot_cnt, tot_act, tot_tile;
+  int b_cnt = block_scan_1024(s_cnt, tmp, &tot_cnt);
+  int b_act = block_scan_1024(s_act, tmp, &tot_act);
+  int b_tile = block_scan_1024(s_tile, tmp, &tot_tile);
+  for (int e = lo; e < hi; ++e) {
+    int c = cnt[e];
+    offsets[e] = b_cnt;
+    tile_offsets[e] = b_tile;
+    if (c > 0) active[1 + b_act++] = e;
+    b_cnt += c;
+    b_tile += (c + tile_m - 1) / tile_m;
+  }
+  if (tid == 0) {
+    offsets[E] = tot_cnt;
+    tile_offsets[E] = tot_tile;
+    active[0] = tot_act;
+  }
+}
+
+// Pass 1 (grid = ceil(P/256)): per block of 256 consecutive pairs, the rank of
+// each pair among the earlier pairs of the block with the same expert, and
+// the block's per-expert counts.
+__global__ void __launch_bounds__(kPermBlock) perm_count_kernel(const int32_t* __restrict__ ids, int64_t P,
+                                                                int E, int32_t* __restrict__ rank,
+                                                                int32_t* __restrict__ block_counts,
+                                                                int32_t* __restrict__ block_invalid) {
+  extern __shared__ int smem[];
+  int* s_ids = smem;              // kPermBlock
+  int* s_hist = smem + kPermBlock;  // E
+  int tid = threadIdx.x;
+  int64_t p = (int64_t)blockIdx.x * kPermBlock + tid;
+  for (int e = tid; e < E; e += kPermBlock) s_hist[e] = 0;
+  int my = -1;
+  if (p < P) {
+    int v = ids[p];
+    my = (v >= 0 && v < E) ? v : -2;
+  }
+  s_ids[tid] = my;
+  __syncthreads();
+  if (my >= 0) atomicAdd(&s_hist[my], 1);
+  int r = 0;
+  if (my >= 0)
+    for (int q = 0; q < tid; ++q) r += s_ids[q] == my;
+  __syncthreads();
+  if (p < P) rank[p] = my >= 0 ? r : -1;
+  for (int e = tid; e < E; e += kPermBlock) block_counts[(int64_t)blockIdx.x * E + e] = s_hist[e];
+  if (tid == 0) {
+    int bad = 0;
+    for (int q = 0; q < kPermBlock; ++q) bad += s_ids[q] == -2;
+    block_invalid[blockIdx.x] = bad;
+  }
+}
+
+// Pass 2 (one workgroup of 1024): per-expert running sums over blocks
+// (turning block_counts into block bases), totals, offsets, active list,
+// tile offsets and the error flag.
+__global__ void __launch_bounds__(1024) perm_scan_kernel(int nb, int E, int tile_m,
+                                                         int32_t* __restrict__ block_counts,
+                                                         const int32_t* __restrict__ block_invalid,
+                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ active,
+                                                         int32_t* __restrict__ tile_offsets,
+                                                         int32_t* __restrict__ error_flag) {
+  __shared__ int tmp[1024];
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    int run = 0;
+    for (int b = 0; b < nb; ++b) {
+      int c = block_counts[(int64_t)b * E + e];
+      block_counts[(int64_t)b * E + e] = run;
+      run += c;
+    }
+    counts[e] = run;
+  }
+  int bad = 0;
+  for (int b = threadIdx.x; b < nb; b += 1024) bad += block_invalid[b];
+  int tot_bad;
+  (void)block_scan_1024(bad, tmp, &tot_bad);
+  __threadfence_block();
+  __syncthreads();
+  finish_offsets(counts, E, tile_m, offsets, active, tile_offsets, tmp);
+  if (threadIdx.x == 0) error_flag[0] = tot_bad;
+}
+
+// Pass 3 (grid = ceil(P/256)): sorted row of every pair.
+__global__ void __launch_bounds__(kPermBlock) perm_scatter_kernel(const int32_t* __restrict__ ids, int64_t P,
+                                                                  int E, const int32_t* __restrict__ block_base,
+                                                                  const int32_t* __restrict__ offsets,
+                                                                  int32_t* __restrict__ row_of_pair,
+                                                                  int32_t* __restrict__ pair_of_row) {
+  int64_t p = (int64_t)blockIdx.x * kPermBlock + threadIdx.x;
+  if (p >= P) return;
+  int r = row_of_pair[p];  // rank written by pass 1
+  if (r < 0) {
+    row_of_pair[p] = -1;
+    return;
+  }
+  int e = ids[p];
+  int row = offsets[e] + block_base[(int64_t)blockIdx.x * E + e] + r;
+  row_of_pair[p] = row;
+  pair_of_row[row] = (int32_t)p;
+}
+
+int launch_permute(const int32_t* ids, int64_t P, int E, int tile_m, const WsPtrs& w, hipStream_t st) {
+  int64_t nb = (P + kPermBlock - 1) / kPermBlock;
+  if (nb == 0) nb = 1;  // still writes counts/offsets for P == 0
+  size_t lds = sizeof(int) * (kPermBlock + E);
+  hipLaunchKernelGGL(perm_count_kernel, dim3((unsigned)nb), dim3(kPermBlock), lds, st, ids, P, E,
+                     w.row_of_pair, w.block_counts, w.block_invalid);
+  FP4_CHECK(check_launch("perm_count"));
+  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, (int)nb, E, tile_m, w.block_counts,
+                     w.block_invalid, w.counts, w.offsets, w.active, w.tile_offsets, w.error_flag);
+  FP4_CHECK(check_launch("perm_scan"));
+  if (P > 0) {
+    hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)nb), dim3(kPermBlock), 0, st, ids, P, E,
+                       w.block_counts, w.offsets, w.row_of_pair, w.pair_of_row);
+    FP4_CHECK(check_launch("perm_scatter"));
+  }
+  return FP4_OK;
+}
+
+// --------------------------------------------- weight-only GEMV path (decode)
+
+// Scale of block b (16 values) of a weight row: NVFP4 E4M3 per 16, or MXFP4
+// UE8M0 per 32 (shared by the two 16-value halves).
+template <int WFMT>
+__device__ __forceinline__ float block_scale(const uint8_t* srow, int b) {
+  if (WFMT == FP4_FMT_NVFP4) return e4m3_to_f32(srow[b]);
+  return ldexpf(1.0f, (int)srow[b >> 1] - 127);
+}
+
+template <int WFMT>
+__device__ __forceinline__ int64_t scale_row_stride(int64_t cols) {
+  return WFMT == FP4_FMT_NVFP4 ? cols / 16 : cols / 32;
+}
+
+// gate_up + SiLU*up for the pairs of one expert, bf16 activations.
+// Grid: (I / 32 row tiles, max active experts).  A half-wave (32 lanes) owns
+// one output j at a time: the gate row j and the up row I+j, with K = H split
+// into 16-value blocks, lane l taking blocks l, l+32, ...  The pairs' tokens
+// (TB per pass) are held in registers as bf16 pairs.
+template <int WFMT, int TB, int BPL>
+__global__ void __launch_bounds__(256) gemv_gateup_kernel(
+    const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ pair_of_row, const int32_t* __restrict__ active,
+    const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s, const float* __restrict__ w13s2,
+    int H, int I, int k, float* __restrict__ h) {
+  const int ai = blockIdx.y;
+  if (ai >= active[0]) return;
+  const int e = active[1 + ai];
+  const int r0 = offsets[e], n = offsets[e + 1] - r0;
+  const int hw = threadIdx.x >> 5, l = threadIdx.x & 31;
+  const int NB = H >> 4;
+  const int64_t row_bytes = H >> 1;
+  const int64_t srow = scale_row_stride<WFMT>(H);
+  const uint8_t* wq = w13 + (int64_t)e * 2 * I * row_bytes;
+  const uint8_t* ws = w13s + (int64_t)e * 2 * I * srow;
+  const float S = WFMT == FP4_FMT_NVFP4 ? w13s2[e] : 1.0f;
+  const int j_begin = blockIdx.x * 32;
+
+  for (int t0 = 0; t0 < n; t0 += TB) {
+    const int nt = min(TB, n - t0);
+    uint32_t xr[TB][BPL][8];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      int tok = pair_of_row[r0 + t0 + min(t, nt - 1)] / k;
+      const uint16_t* xrow = x + (int64_t)tok * H;
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        int b = l + 32 * i;
+        if (b < NB) {
+          const uint4* src = reinterpret_cast<const uint4*>(xrow + b * 16);
+          uint4 a0 = src[0], a1 = src[1];
+          uint32_t n0[4] = {a0.x, a0.y, a0.z, a0.w}, n1[4] = {a1.x, a1.y, a1.z, a1.w};
+          uint32_t p0[4], p1[4];
+          permute_pairs_like_e2m1(n0, p0);
+          permute_pairs_like_e2m1(n1, p1);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            xr[t][i][q] = p0[q];
+            xr[t][i][4 + q] = p1[q];
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) xr[t][i][q] = 0u;
+        }
+      }
+    }
+    for (int jj = hw; jj < 32; jj += 8) {
+      const int j = j_begin + jj;
+      if (j >= I) break;
+      float ag[TB], au[TB];
+#pragma unroll
+      for (int t = 0; t < TB; ++t) ag[t] = au[t] = 0.0f;
+      const uint8_t* qg = wq + (int64_t)j * row_bytes;
+      const uint8_t* qu = wq + (int64_t)(I + j) * row_bytes;
+      const uint8_t* sg = ws + (int64_t)j * srow;
+      const uint8_t* su = ws + (int64_t)(I + j) * srow;
+      uint2 cg[BPL], cu[BPL];
+      float fg[BPL], fu[BPL];
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        int b = l + 32 * i;
+        if (b < NB) {
+          cg[i] = reinterpret_cast<const uint2*>(qg)[b];
+          cu[i] = reinterpret_cast<const uint2*>(qu)[b];
+          fg[i] = block_scale<WFMT>(sg, b);
+          fu[i] = block_scale<WFMT>(su, b);
+        } else {
+          cg[i] = cu[i] = make_uint2(0u, 0u);
+          fg[i] = fu[i] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        uint32_t wg[8], wu[8];
+        {
+          uint32_t a[4], b[4];
+          e2m1x8_to_bf16x8(cg[i].x, a);
+          e2m1x8_to_bf16x8(cg[i].y, b);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { wg[q] = a[q]; wg[4 + q] = b[q]; }
+          e2m1x8_to_bf16x8(cu[i].x, a);
+          e2m1x8_to_bf16x8(cu[i].y, b);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) { wu[q] = a[q]; wu[4 + q] = b[q]; }
+        }
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          float dg = 0.0f, du = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            dg = dot2_bf16(wg[q], xr[t][i][q], dg);
+            du = dot2_bf16(wu[q], xr[t][i][q], du);
+          }
+          ag[t] = fmaf(dg, fg[i], ag[t]);
+          au[t] = fmaf(du, fu[i], au[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+#pragma unroll
+        for (int off = 16; off > 0; off >>= 1) {
+          ag[t] += __shfl_xor(ag[t], off, 32);
+          au[t] += __shfl_xor(au[t], off, 32);
+        }
+      }
+      if (l == 0) {
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+          if (t < nt) {
+            float g = ag[t] * S, u = au[t] * S;
+            h[(int64_t)(r0 + t0 + t) * I + j] = silu_f32(g) * u;
+          }
+      }
+    }
+  }
+}
+
+// Down projection o[row] = W2[e] h[row] for the rows of one expert, f32 h.
+// Grid: (ceil(H / 64) row tiles, max active experts).  8 lanes own one output
+// row n (K = I split into 16-value blocks, lane q taking blocks q, q+8, ...);
+// h of TB rows at a time is staged in LDS.
+template <int WFMT, int TB>
+__global__ void __launch_bounds__(256) gemv_down_kernel(
+    const float* __restrict__ h, const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
+    const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s, const float* __restrict__ w2s2,
+    int H, int I, float* __restrict__ o) {
+  extern __shared__ float s_h[];  // [TB][I]
+  const int ai = blockIdx.y;
+  if (ai >= active[0]) return;
+  const int e = active[1 + ai];
+  const int r0 = offsets[e], n = offsets[e + 1] - r0;
+  const int q = threadIdx.x & 7, rg = threadIdx.x >> 3;  // 32 row groups
+  const int NB = I >> 4;
+  const int64_t row_bytes = I >> 1;
+  const int64_t srow = scale_row_stride<WFMT>(I);
+  const uint8_t* wq = w2 + (int64_t)e * H * row_bytes;
+  const uint8_t* ws = w2s + (int64_t)e * H * srow;
+  const float S = WFMT == FP4_FMT_NVFP4 ? w2s2[e] : 1.0f;
+
+  for (int t0 = 0; t0 < n; t0 += TB) {
+    const int nt = min(TB, n - t0);
+    __syncthreads();
+    for (int i = threadIdx.x; i < TB * I; i += 256) {
+      int t = i / I, c = i - t * I;
+      s_h[i] = t < nt ? h[(int64_t)(r0 + t0 + t) * I + c] : 0.0f;
+    }
+    __syncthreads();
+    for (int nn = blockIdx.x * 64 + rg; nn < min(H, (int)blockIdx.x * 64 + 64); nn += 32) {
+      float acc[TB];
+#pragma unroll
+      for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
+      const uint8_t* qr = wq + (int64_t)nn * row_bytes;
+      const uint8_t* sr = ws + (int64_t)nn * srow;
+      for (int b = q; b < NB; b += 8) {
+        uint2 c = reinterpret_cast<const uint2*>(qr)[b];
+        float sb = block_scale<WFMT>(sr, b);
+        float wv[16];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          uint32_t n0 = (c.x >> (4 * m)) & 15u, n1 = (c.y >> (4 * m)) & 15u;
+          float v0 = e2m1_mag_to_f32(n0 & 7u), v1 = e2m1_mag_to_f32(n1 & 7u);
+          wv[m] = (n0 & 8u) ? -v0 : v0;
+          wv[8 + m] = (n1 & 8u) ? -v1 : v1;
+        }
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          const float4* hp = reinterpret_cast<const float4*>(s_h + t * I + b * 16);
+          float d = 0.0f;
+#pragma unroll
+          for (int m4 = 0; m4 < 4; ++m4) {
+            float4 hv = hp[m4];
+            d = fmaf(wv[4 * m4], hv.x, d);
+            d = fmaf(wv[4 * m4 + 1], hv.y, d);
+            d = fmaf(wv[4 * m4 + 2], hv.z, d);
+            d = fmaf(wv[4 * m4 + 3], hv.w, d);
+          }
+          acc[t] = fmaf(d, sb, acc[t]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        acc[t] += __shfl_xor(acc[t], 4, 8);
+        acc[t] += __shfl_xor(acc[t], 2, 8);
+        acc[t] += __shfl_xor(acc[t], 1, 8);
+      }
+      if (q == 0) {
+#pragma unroll
+        for (int t = 0; t < TB; ++t)
+          if (t < nt) o[(int64_t)(r0 + t0 + t) * H + nn] = acc[t] * S;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ combine
+
+// y[t, :] = sum_j w[t, j] * o[row(t, j), :] (+ extra[t, :]), slot order, f32.
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o,
+                                                      const int32_t* __restrict__ row_of_pair,
+                                                      const float* __restrict__ topk_w, int64_t T, int H,
+                                                      int k, const float* __restrict__ extra,
+                                                      float* __restrict__ y) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // one float4 of y
+  int64_t per_row = H / 4;
+  if (i >= T * per_row) return;
+  int64_t t = i / per_row, c4 = i - t * per_row;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    int row = row_of_pair[t * k + j];
+    if (row < 0) continue;
+    float w = topk_w[t * k + j];
+    float4 v = reinterpret_cast<const float4*>(o + (int64_t)row * H)[c4];
+    acc.x = fmaf(w, v.x, acc.x);
+    acc.y = fmaf(w, v.y, acc.y);
+    acc.z = fmaf(w, v.z, acc.z);
+    acc.w = fmaf(w, v.w, acc.w);
+  }
+  if (extra) {
+    float4 v = reinterpret_cast<const float4*>(extra + t * H)[c4];
+    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  }
+  reinterpret_cast<float4*>(y + t * H)[c4] = acc;
+}
+
+// ---------------------------------------------------------- GEMV dispatch
+
+template <int WFMT, int TB>
+static int launch_gemv_gateup_tb(const uint16_t* x, const WsPtrs& w, const moe_fp4_layer* L,
+                                 int max_active, hipStream_t st) {
+  dim3 grid((unsigned)((L->inter + 31) / 32), (unsigned)max_active);
+  const int NB = L->hidden / 16;
+  const int bpl = (NB + 31) / 32;
+#define FP4_GV(B)                                                                                       \
+  case B:                                                                                               \
+    hipLaunchKernelGGL((gemv_gateup_kernel<WFMT, TB, B>), grid, dim3(256), 0, st, x, w.offsets,         \
+                       w.pair_of_row, w.active, L->w13, (const uint8_t*)L->w13_scale, L->w13_scale_2,  \
+                       L->hidden, L->inter, L->top_k, w.h);                                             \
+    break;
+  switch (bpl) {
+    FP4_GV(1) FP4_GV(2) FP4_GV(3) FP4_GV(4) FP4_GV(5) FP4_GV(6) FP4_GV(7) FP4_GV(8)
+    default: return fail(FP4_ERR_UNSUPPORTED, "hidden %d too large for the GEMV path", L->hidden);
+  }
+#undef FP4_GV
+  return check_launch("gemv_gateup");
+}
+
+template <int WFMT>
+static int launch_gemv(const uint16_t* x, const WsPtrs& w, const moe_fp4_layer* L, int64_t P,
+                       int max_active, hipStream_t st) {
+  const bool small = P <= 2 * (int64_t)L->num_experts;
+  if (small) FP4_CHECK((launch_gemv_gateup_tb<WFMT, 2>(x, w, L, max_active, st)));
+  else FP4_CHECK((launch_gemv_gateup_tb<WFMT, 4>(x, w, L, max_active, st)));
+  dim3 grid((unsigned)((L->hidden + 63) / 64), (unsigned)max_active);
+  if (small) {
+    hipLaunchKernelGGL((gemv_down_kernel<WFMT, 2>), grid, dim3(256), sizeof(float) * 2 * L->inter, st,
+                       w.h, w.offsets, w.active, L->w2, (const uint8_t*)L->w2_scale, L->w2_scale_2,
+                       L->hidden, L->inter, w.o);
+  } else {
+    hipLaunchKernelGGL((gemv_down_kernel<WFMT, 4>), grid, dim3(256), sizeof(float) * 4 * L->inter, st,
+                       w.h, w.offsets, w.active, L->w2, (const uint8_t*)L->w2_scale, L->w2_scale_2,
+                       L->hidden, L->inter, w.o);
+  }
+  return check_launch("gemv_down");
+}
+
+WsPtrs ws_pointers(const WsPlan& p, void* base) {
+  char* b = reinterpret_cast<char*>(base);
+  WsPtrs w;
+  w.error_flag = reinterpret_cast<int32_t*>(b + p.error_flag);
+  w.counts = reinterpret_cast<int32_t*>(b + p.counts);
+  w.offsets = reinterpret_cast<int32_t*>(b + p.offsets);
+  w.pair_of_row = reinterpret_cast<int32_t*>(b + p.pair_of_row);
+  w.row_of_pair = reinterpret_cast<int32_t*>(b + p.row_of_pair);
+  w.active = reinterpret_cast<int32_t*>(b + p.active);
+  w.tile_offsets = reinterpret_cast<int32_t*>(b + p.tile_offsets);
+  w.block_counts = reinterpret_cast<int32_t*>(b + p.block_counts);
+  w.block_invalid = reinterpret_cast<int32_t*>(b + p.block_invalid);
+  w.x_ts = reinterpret_cast<float*>(b + p.x_tensor_scale);
+  w.h_ts = reinterpret_cast<float*>(b + p.h_tensor_scale);
+  w.h = reinterpret_cast<float*>(b + p.h);
+  w.xq_codes = reinterpret_cast<uint8_t*>(b + p.xq_codes);
+  w.xq_scales = b + p.xq_scales;
+  w.hq_codes = reinterpret_cast<uint8_t*>(b + p.hq_codes);
+  w.hq_scales = b + p.hq_scales;
+  w.o = reinterpret_cast<float*>(b + p.o);
+  w.sx_codes = reinterpret_cast<uint8_t*>(b + p.sx_codes);
+  w.sx_scales = reinterpret_cast<uint8_t*>(b + p.sx_scales);
+  w.sh = reinterpret_cast<float*>(b + p.sh);
+  w.sh_codes = reinterpret_cast<uint8_t*>(b + p.sh_codes);
+  w.sh_scales = reinterpret_cast<uint8_t*>(b + p.sh_scales);
+  w.s_out = reinterpret_cast<float*>(b + p.s_out);
+  return w;
+}
+
+static int validate_layer(const moe_fp4_layer* L, int64_t T) {
+  if (!L) return fail(FP4_ERR_INVALID_ARG, "null layer");
+  if (T < 0) return fail(FP4_ERR_SHAPE, "negative token count");
+  if (L->num_experts < 1 || L->hidden < 1 || L->inter < 1)
+    return fail(FP4_ERR_SHAPE, "experts, hidden and inter must be positive");
+  if (L->top_k < 1 || L->top_k > L->num_experts)
+    return fail(FP4_ERR_INVALID_ARG, "top_k %d outside [1, %d]", L->top_k, L->num_experts);
+  if (L->num_experts > kMaxExperts) return fail(FP4_ERR_UNSUPPORTED, "more than %d experts", kMaxExperts);
+  const int w = L->w_fmt, a = L->a_fmt;
+  bool ok = (w == FP4_FMT_NVFP4 && (a == FP4_FMT_NONE || a == FP4_FMT_NVFP4)) ||
+            (w == FP4_FMT_MXFP4 && (a == FP4_FMT_NONE || a == FP4_FMT_MXFP8)) ||
+            (w == FP4_FMT_FP8_BLOCK && a == FP4_FMT_FP8_ROW);
+  if (!ok) return fail(FP4_ERR_UNSUPPORTED, "format pair (w=%d, a=%d) not provided", w, a);
+  int blk = 16;
+  if (w == FP4_FMT_MXFP4) blk = 32;
+  if (w == FP4_FMT_FP8_BLOCK) blk = 128;
+  if (a != FP4_FMT_NONE) blk = std::max(blk, 32);
+  if (L->hidden % blk || L->inter % blk)
+    return fail(FP4_ERR_SHAPE, "hidden %d / inter %d not multiples of %d", L->hidden, L->inter, blk);
+  if (a != FP4_FMT_NONE && (L->hidden % 128 || L->inter % 128))
+    return fail(FP4_ERR_SHAPE, "quantized-activation paths need hidden and inter multiples of 128");
+  if (L->shared_inter < 0) return fail(FP4_ERR_SHAPE, "negative shared width");
+  if (L->shared_inter > 0 && (L->shared_inter % 128 || L->hidden % 128))
+    return fail(FP4_ERR_SHAPE, "shared width and hidden must be multiples of 128");
+  return FP4_OK;
+}
+
+}  // namespace fp4
+
+using namespace fp4;
+
+extern "C" {
+
+int moe_fp4_workspace_layout(const moe_fp4_layer* layer, int64_t tokens, moe_fp4_ws_layout* out) {
+  FP4_CHECK(validate_layer(layer, tokens));
+  if (!out) return fail(FP4_ERR_INVALID_ARG, "null layout");
+  WsPlan p;
+  FP4_CHECK(plan_workspace(layer, tokens, &p));
+  out->total = p.total;
+  out->error_flag = p.error_flag;
+  out->counts = p.counts;
+  out->offsets = p.offsets;
+  out->pair_of_row = p.pair_of_row;
+  out->row_of_pair = p.row_of_pair;
+  out->x_tensor_scale = p.x_tensor_scale;
+  out->h_tensor_scale = p.h_tensor_scale;
+  out->h = p.h;
+  out->hq_codes = p.hq_codes;
+  out->hq_scales = p.hq_scales;
+  out->o = p.o;
+  return FP4_OK;
+}
+
+int moe_fp4_workspace_size(const moe_fp4_layer* layer, int64_t tokens, size_t* bytes) {
+  if (!bytes) return fail(FP4_ERR_INVALID_ARG, "null size pointer");
+  FP4_CHECK(validate_layer(layer, tokens));
+  WsPlan p;
+  FP4_CHECK(plan_workspace(layer, tokens, &p));
+  *bytes = p.total;
+  return FP4_OK;
+}
+
+int moe_fp4_forward(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const int32_t* topk_ids,
+                    const float* topk_weights, float* y, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  FP4_CHECK(validate_layer(L, T));
+  if (T == 0) return FP4_OK;
+  if (!x || !topk_ids || !topk_weights || !y) return fail(FP4_ERR_INVALID_ARG, "null tensor pointer");
+  if (!L->w13 || !L->w13_scale || !L->w2 || !L->w2_scale)
+    return fail(FP4_ERR_INVALID_ARG, "null weight pointer");
+  if (L->w_fmt == FP4_FMT_NVFP4 && (!L->w13_scale_2 || !L->w2_scale_2))
+    return fail(FP4_ERR_INVALID_ARG, "NVFP4 weights need weight_scale_2");
+  if (L->shared_inter > 0 && (!L->ws13 || !L->ws13_scale || !L->ws2 || !L->ws2_scale || !L->shared_gate))
+    return fail(FP4_ERR_INVALID_ARG, "null shared-expert pointer");
+  WsPlan p;
+  FP4_CHECK(plan_workspace(L, T, &p));
+  if (!workspace || workspace_bytes < p.total)
+    return fail(FP4_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, p.total);
+  hipStream_t st = as_stream(stream);
+  WsPtrs w = ws_pointers(p, workspace);
+  const int64_t P = T * L->top_k;
+  const int max_active = (int)std::min<int64_t>(L->num_experts, P);
+
+  FP4_CHECK(launch_permute(topk_ids, P, L->num_experts, kGemmTileM, w, st));
+
+  if (L->a_fmt == FP4_FMT_NONE) {
+    if (L->w_fmt == FP4_FMT_NVFP4) FP4_CHECK(launch_gemv<FP4_FMT_NVFP4>(x, w, L, P, max_active, st));
+    else FP4_CHECK(launch_gemv<FP4_FMT_MXFP4>(x, w, L, P, max_active, st));
+  } else {
+    FP4_CHECK(launch_grouped(L, x, T, w, max_active, st));
+  }
+  const float* extra = nullptr;
+  if (L->shared_inter > 0) {
+    FP4_CHECK(launch_shared_expert(L, x, T, w, st));
+    extra = w.s_out;
+  }
+  int64_t n4 = T * L->hidden / 4;
+  hipLaunchKernelGGL(combine_kernel, dim3(grid_1d(n4, 256)), dim3(256), 0, st, w.o, w.row_of_pair,
+                     topk_weights, T, L->hidden, L->top_k, extra, y);
+  return check_launch("combine");
+}
+
+}  // extern "C"

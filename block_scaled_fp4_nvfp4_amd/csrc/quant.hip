@@ -1,0 +1,632 @@
+// Quantizers and dequantizers behind fp4_quantize / fp4_dequantize (gfx950).
+//
+// NVFP4 with the 4/6 block-scale choice (dabsLabs NVFP4 card, "What makes
+// this build different"), tensor scale amax/2688 shared by a fused gate_up
+// (Local-Hessian NVFP4 card, opening section), MXFP4 (MXFP4-FP8-R12 card,
+// "Quantization format"), MXFP8 (FP4-Local AZ card, "The shared expert") and
+// block FP8 (MXFP4-FP8-R12 card, runtime contract table).
+//
+// The 4/6 choice needs, per block and plan M, the exact error
+//   err_M = sum (|x_i| - g_i s_M S)^2 = sum x_i^2 - 2 s_M S GX_M + s_M^2 S^2 G2_M
+// with G2_M = sum g_i^2 and GX_M = sum g_i |x_i| (g the E2M1 magnitudes).  So
+//   err_6 - err_4 = S * (S * A - 2 * B),
+//   A = s6^2 G2_6 - s4^2 G2_4,  B = s6 GX_6 - s4 GX_4,
+// and M=4 wins iff S*A - 2*B > 0.  G2 is a multiple of 1/4 below 2^12; for bf16
+// inputs every g|x| has <= 10 significant bits and the nonzero ones span
+// fewer than 21 bits, so GX is exact in float; A, B and S*A are exact in
+// double and the one rounding of S*A - 2*B cannot change its sign.  For f32
+// inputs GX is accumulated in double (exact for the same reason, 24+2 bits).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <mutex>
+#include <string>
+
+#include "fp4_device.h"
+#include "host_common.h"
+
+#pragma clang fp contract(off)
+
+namespace fp4 {
+
+static thread_local std::string g_last_error;
+
+void set_last_error(const char* fmt, ...) {
+  char buf[768];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// ------------------------------------------------------------ element loads
+
+template <int N>
+__device__ __forceinline__ void load_vals(const uint16_t* p, float (&v)[N]) {
+  static_assert(N % 8 == 0, "");
+  const uint4* q = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+  for (int i = 0; i < N / 8; ++i) {
+    uint4 w = q[i];
+    uint32_t d[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[8 * i + 2 * j] = __uint_as_float(d[j] << 16);
+      v[8 * i + 2 * j + 1] = __uint_as_float(d[j] & 0xFFFF0000u);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void load_vals(const float* p, float (&v)[N]) {
+  static_assert(N % 4 == 0, "");
+  const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    float4 w = q[i];
+    v[4 * i] = w.x;
+    v[4 * i + 1] = w.y;
+    v[4 * i + 2] = w.z;
+    v[4 * i + 3] = w.w;
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+
+// ------------------------------------------------------------------ kernels
+
+__global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// amax of each tensor (batch item) as float bits, combined with atomicMax on
+// the bit pattern (non-negative floats order like their bit patterns).
+template <typename T>
+__global__ void __launch_bounds__(256) tensor_amax_kernel(const T* x, int64_t per_tensor,
+                                                          uint32_t* amax_bits) {
+  const T* base = x + (int64_t)blockIdx.y * per_tensor;
+  float m = 0.0f;
+  int64_t stride = (int64_t)gridDim.x * 256 * 8;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i < per_tensor; i += stride) {
+    float v[8];
+    load_vals<8>(base + i, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0 && m > 0.0f) atomicMax(amax_bits + blockIdx.y, __float_as_uint(m));
+}
+
+// S = fp32(fp64(amax) / 2688), in place over the amax bits.
+__global__ void nv_tensor_scale_kernel(float* s, int64_t n) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) s[i] = (float)((double)s[i] / kNvTensorDivisor);
+}
+
+template <typename T> struct GxAcc { using type = float; };
+template <> struct GxAcc<float> { using type = double; };
+
+// One thread per block of BS values (16: NVFP4, 32: MXFP4).
+template <int BS, bool MX, bool FOUR_SIX, typename T>
+__global__ void __launch_bounds__(256) quant_fp4_kernel(
+    const T* __restrict__ x, int64_t blocks_per_tensor, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale,
+    uint8_t* __restrict__ m4_flags) {
+  using Acc = typename GxAcc<T>::type;
+  int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (blk >= blocks_per_tensor) return;
+  int64_t g = (int64_t)blockIdx.y * blocks_per_tensor + blk;
+  float v[BS];
+  load_vals<BS>(x + g * BS, v);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < BS; ++i) amax = fmaxf(amax, fabsf(v[i]));
+
+  double S = 1.0, s6, s4 = 0.0;
+  uint32_t code6, code4 = 0;
+  if (MX) {
+    int e6 = mx_exponent(amax, 6.0f);
+    code6 = (uint32_t)(e6 + 127);
+    s6 = ldexp(1.0, e6);
+    if (FOUR_SIX) {
+      int e4 = mx_exponent(amax, 4.0f);
+      code4 = (uint32_t)(e4 + 127);
+      s4 = ldexp(1.0, e4);
+    }
+  } else {
+    S = (double)tensor_scale[blockIdx.y];
+    code6 = S > 0.0 ? e4m3_rne_sat_f64((double)amax / (6.0 * S)) : 0u;
+    s6 = (double)e4m3_to_f32(code6);
+    if (FOUR_SIX) {
+      code4 = S > 0.0 ? e4m3_rne_sat_f64((double)amax / (4.0 * S)) : 0u;
+      s4 = (double)e4m3_to_f32(code4);
+    }
+  }
+
+  E2M1Thresholds th6 = e2m1_thresholds(s6 * S);
+  uint32_t c6[BS];
+  float g2_6 = 0.0f;
+  Acc gx_6 = 0;
+#pragma unroll
+  for (int i = 0; i < BS; ++i) {
+    float a = fabsf(v[i]);
+    c6[i] = e2m1_code(a, th6);
+    float gm = e2m1_mag_to_f32(c6[i]);
+    g2_6 += gm * gm;
+    gx_6 += (Acc)gm * (Acc)a;
+  }
+  bool use4 = false;
+  uint32_t c4[BS];
+  if (FOUR_SIX) {
+    E2M1Thresholds th4 = e2m1_thresholds(s4 * S);
+    float g2_4 = 0.0f;
+    Acc gx_4 = 0;
+#pragma unroll
+    for (int i = 0; i < BS; ++i) {
+      float a = fabsf(v[i]);
+      c4[i] = e2m1_code(a, th4);
+      float gm = e2m1_mag_to_f32(c4[i]);
+      g2_4 += gm * gm;
+      gx_4 += (Acc)gm * (Acc)a;
+    }
+    double A = s6 * s6 * (double)g2_6 - s4 * s4 * (double)g2_4;
+    double B = s6 * (double)gx_6 - s4 * (double)gx_4;
+    use4 = (S * A - 2.0 * B) > 0.0;
+  }
+
+  uint32_t packed[BS / 8];
+#pragma unroll
+  for (int w = 0; w < BS / 8; ++w) {
+    uint32_t d = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      int i = 8 * w + j;
+      uint32_t c = (FOUR_SIX && use4) ? c4[i] : c6[i];
+      c |= (__float_as_uint(v[i]) >> 28) & 8u;  // sign bit of x
+      d |= c << (4 * j);
+    }
+    packed[w] = d;
+  }
+  if (BS == 16) {
+    reinterpret_cast<uint2*>(codes)[g] = make_uint2(packed[0], packed[1]);
+  } else {
+    reinterpret_cast<uint4*>(codes)[g] = make_uint4(packed[0], packed[1 % (BS / 8)],
+                                                    packed[2 % (BS / 8)], packed[3 % (BS / 8)]);
+  }
+  scales[g] = (uint8_t)((FOUR_SIX && use4) ? code4 : code6);
+  if (m4_flags) m4_flags[g] = use4 ? 1 : 0;
+}
+
+// MXFP8: one thread per block of 32; e = min{e : 448 * 2^e >= amax}.
+template <typename T>
+__global__ void __launch_bounds__(256) quant_mxfp8_kernel(const T* __restrict__ x, int64_t nblocks,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= nblocks) return;
+  float v[32];
+  load_vals<32>(x + g * 32, v);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  int e = mx_exponent(amax, kE4M3Max);
+  uint32_t out[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t d = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float a = v[4 * w + j];
+      uint32_t c = e4m3_rne_sat_f32(ldexpf(fabsf(a), -e)) | ((__float_as_uint(a) >> 24) & 0x80u);
+      d |= c << (8 * j);
+    }
+    out[w] = d;
+  }
+  uint4* dst = reinterpret_cast<uint4*>(codes + g * 32);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  scales[g] = (uint8_t)(e + 127);
+}
+
+// Exact E4M3 code of a / sigma (a >= 0, sigma > 0 float): a float quotient
+// picks a candidate, which is then corrected against the neighbouring
+// midpoints times sigma, compared exactly in double (5 + 24 bits).
+__device__ __forceinline__ uint32_t e4m3_exact_quotient(float a, float sigma) {
+  uint32_t c = e4m3_rne_sat_f32(a / sigma);
+  double A = (double)a, sg = (double)sigma;
+  if (c > 0) {
+    double mlo = 0.5 * ((double)e4m3_to_f32(c - 1) + (double)e4m3_to_f32(c)) * sg;
+    if (A < mlo || (A == mlo && ((c - 1) & 1u) == 0)) return c - 1;
+  }
+  if (c < 0x7Eu) {
+    double mhi = 0.5 * ((double)e4m3_to_f32(c) + (double)e4m3_to_f32(c + 1)) * sg;
+    if (A > mhi || (A == mhi && ((c + 1) & 1u) == 0)) return c + 1;
+  }
+  return c;
+}
+
+// FP8 with one fp32 scale per (row, 128 columns): 4 lanes per group of 128.
+template <typename T>
+__global__ void __launch_bounds__(256) quant_fp8_row_kernel(const T* __restrict__ x, int64_t ngroups,
+                                                            uint8_t* __restrict__ codes,
+                                                            float* __restrict__ scales) {
+  int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  int64_t g = t >> 2;
+  bool active = g < ngroups;
+  float v[32];
+  if (active) {
+    load_vals<32>(x + t * 32, v);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  if (!active) return;
+  float sigma = (float)((double)amax / 448.0);
+  uint32_t out[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t d = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float a = v[4 * w + j];
+      uint32_t c = sigma > 0.0f ? e4m3_exact_quotient(fabsf(a), sigma) : 0u;
+      c |= (__float_as_uint(a) >> 24) & 0x80u;
+      d |= c << (8 * j);
+    }
+    out[w] = d;
+  }
+  uint4* dst = reinterpret_cast<uint4*>(codes + t * 32);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+  if ((t & 3) == 0) scales[g] = sigma;
+}
+
+// Block FP8 weights: amax of each 128 x 128 tile (one workgroup per tile).
+template <typename T>
+__global__ void __launch_bounds__(256) fp8_tile_amax_kernel(const T* __restrict__ x, int64_t rows,
+                                                            int64_t cols, float* __restrict__ sigma) {
+  int64_t tiles_c = cols / 128, tiles_r = rows / 128;
+  int64_t tile = blockIdx.x;
+  int64_t b = blockIdx.y;
+  int64_t tr = tile / tiles_c, tc = tile % tiles_c;
+  const T* base = x + b * rows * cols + tr * 128 * cols + tc * 128;
+  float m = 0.0f;
+  // 256 threads: 16 threads per row (8 values each), 16 rows per pass
+  int r0 = threadIdx.x >> 4, c0 = (threadIdx.x & 15) * 8;
+  for (int r = r0; r < 128; r += 16) {
+    float v[8];
+    load_vals<8>(base + (int64_t)r * cols + c0, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  }
+  m = wave_max(m);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    sigma[b * tiles_r * tiles_c + tile] = (float)((double)a / 448.0);
+  }
+}
+
+// Block FP8 weights: one thread per 32 consecutive values of a row.
+template <typename T>
+__global__ void __launch_bounds__(256) quant_fp8_tile_kernel(const T* __restrict__ x, int64_t rows,
+                                                             int64_t cols, int64_t nchunks,
+                                                             const float* __restrict__ sigma,
+                                                             uint8_t* __restrict__ codes) {
+  int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= nchunks) return;
+  int64_t e0 = t * 32;
+  int64_t per = rows * cols;
+  int64_t b = e0 / per, rem = e0 % per;
+  int64_t r = rem / cols, c = rem % cols;
+  float sg = sigma[(b * (rows / 128) + r / 128) * (cols / 128) + c / 128];
+  float v[32];
+  load_vals<32>(x + e0, v);
+  uint32_t out[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    uint32_t d = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float a = v[4 * w + j];
+      uint32_t cc = sg > 0.0f ? e4m3_exact_quotient(fabsf(a), sg) : 0u;
+      cc |= (__float_as_uint(a) >> 24) & 0x80u;
+      d |= cc << (8 * j);
+    }
+    out[w] = d;
+  }
+  uint4* dst = reinterpret_cast<uint4*>(codes + e0);
+  dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
+  dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
+}
+
+// ---------------------------------------------------------------- dequantize
+
+template <typename OutT>
+__device__ __forceinline__ void store8(OutT* out, int64_t i, const float (&f)[8]);
+
+template <>
+__device__ __forceinline__ void store8<float>(float* out, int64_t i, const float (&f)[8]) {
+  float4* d = reinterpret_cast<float4*>(out + i);
+  d[0] = make_float4(f[0], f[1], f[2], f[3]);
+  d[1] = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+template <>
+__device__ __forceinline__ void store8<uint16_t>(uint16_t* out, int64_t i, const float (&f)[8]) {
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    w[j] = f32_to_bf16_bits(f[2 * j]) | (f32_to_bf16_bits(f[2 * j + 1]) << 16);
+  *reinterpret_cast<uint4*>(out + i) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// fmt: 0 NVFP4, 1 MXFP4, 2 MXFP8, 3 FP8_BLOCK, 4 FP8_ROW.  One thread per 8 values.
+template <int FMT, typename OutT>
+__global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ codes,
+                                                      const void* __restrict__ scales,
+                                                      const float* __restrict__ tensor_scale,
+                                                      int64_t rows, int64_t cols, int64_t n8,
+                                                      OutT* __restrict__ out) {
+  int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n8) return;
+  int64_t e0 = t * 8;
+  float f[8];
+  if (FMT == 0 || FMT == 1) {
+    uint32_t d = reinterpret_cast<const uint32_t*>(codes)[t];
+    float s;
+    if (FMT == 0) {
+      int64_t b = e0 / (rows * cols);
+      float sb = e4m3_to_f32(reinterpret_cast<const uint8_t*>(scales)[e0 / 16]);
+      float S = tensor_scale[b];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t c = (d >> (4 * j)) & 15u;
+        float gs = e2m1_mag_to_f32(c & 7u) * sb;   // exact (<= 6 significant bits)
+        float val = gs * S;                          // the one rounding
+        f[j] = (c & 8u) ? -val : val;
+      }
+    } else {
+      int e = (int)reinterpret_cast<const uint8_t*>(scales)[e0 / 32] - 127;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        uint32_t c = (d >> (4 * j)) & 15u;
+        float val = ldexpf(e2m1_mag_to_f32(c & 7u), e);
+        f[j] = (c & 8u) ? -val : val;
+      }
+    }
+    (void)s;
+  } else {
+    uint2 d2 = reinterpret_cast<const uint2*>(codes)[t];
+    uint32_t dd[2] = {d2.x, d2.y};
+    if (FMT == 2) {
+      int e = (int)reinterpret_cast<const uint8_t*>(scales)[e0 / 32] - 127;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = ldexpf(e4m3_to_f32((dd[j >> 2] >> (8 * (j & 3))) & 0xFFu), e);
+    } else {
+      float sg;
+      if (FMT == 3) {
+        int64_t per = rows * cols;
+        int64_t b = e0 / per, rem = e0 % per;
+        int64_t r = rem / cols, c = rem % cols;
+        sg = reinterpret_cast<const float*>(scales)[(b * (rows / 128) + r / 128) * (cols / 128) + c / 128];
+      } else {
+        sg = reinterpret_cast<const float*>(scales)[e0 / 128];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] = e4m3_to_f32((dd[j >> 2] >> (8 * (j & 3))) & 0xFFu) * sg;
+    }
+  }
+  store8<OutT>(out, e0, f);
+}
+
+}  // namespace fp4
+
+using namespace fp4;
+
+// ---------------------------------------------------------------- host side
+
+namespace {
+
+int launch_fill(uint32_t* p, uint32_t v, int64_t n, hipStream_t st) {
+  if (n <= 0) return FP4_OK;
+  hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, st, p, v, n);
+  return check_launch("fill");
+}
+
+template <typename T>
+int quantize_typed(int fmt, int rule, int ts_mode, const T* x, int64_t batch, int64_t rows,
+                   int64_t cols, uint8_t* codes, void* scales, float* tensor_scale,
+                   uint8_t* m4, hipStream_t st) {
+  const int64_t per = rows * cols;
+  if (fmt == FP4_FMT_NVFP4 || fmt == FP4_FMT_MXFP4) {
+    const bool mx = fmt == FP4_FMT_MXFP4;
+    const int bs = mx ? 32 : 16;
+    const int64_t bpt = per / bs;
+    if (!mx && ts_mode == FP4_TS_DYNAMIC) {
+      FP4_CHECK(launch_fill(reinterpret_cast<uint32_t*>(tensor_scale), 0u, batch, st));
+      int64_t chunks = (per / 8 + 255) / 256;
+      int64_t target = 4LL * device_cu_count() * 8 / (batch > 0 ? batch : 1);
+      unsigned gx = (unsigned)std::max<int64_t>(1, std::min<int64_t>(chunks, std::max<int64_t>(target, 1)));
+      for (int64_t b0 = 0; b0 < batch; b0 += 65535) {
+        unsigned gy = (unsigned)std::min<int64_t>(65535, batch - b0);
+        hipLaunchKernelGGL(tensor_amax_kernel<T>, dim3(gx, gy), dim3(256), 0, st, x + b0 * per, per,
+                           reinterpret_cast<uint32_t*>(tensor_scale) + b0);
+        FP4_CHECK(check_launch("tensor_amax"));
+      }
+      hipLaunchKernelGGL(nv_tensor_scale_kernel, dim3(grid_1d(batch, 256)), dim3(256), 0, st,
+                         tensor_scale, batch);
+      FP4_CHECK(check_launch("tensor_scale"));
+    }
+    unsigned gx = grid_1d(bpt, 256);
+    for (int64_t b0 = 0; b0 < batch; b0 += 65535) {
+      unsigned gy = (unsigned)std::min<int64_t>(65535, batch - b0);
+      const T* xb = x + b0 * per;
+      uint8_t* cb = codes + b0 * per / 2;
+      uint8_t* sb = reinterpret_cast<uint8_t*>(scales) + b0 * bpt;
+      const float* tb = tensor_scale ? tensor_scale + b0 : nullptr;
+      uint8_t* mb = m4 ? m4 + b0 * bpt : nullptr;
+      dim3 grid(gx, gy);
+      if (!mx && rule == FP4_RULE_4OVER6)
+        hipLaunchKernelGGL((quant_fp4_kernel<16, false, true, T>), grid, dim3(256), 0, st, xb, bpt, cb, sb, tb, mb);
+      else if (!mx)
+        hipLaunchKernelGGL((quant_fp4_kernel<16, false, false, T>), grid, dim3(256), 0, st, xb, bpt, cb, sb, tb, mb);
+      else if (rule == FP4_RULE_4OVER6)
+        hipLaunchKernelGGL((quant_fp4_kernel<32, true, true, T>), grid, dim3(256), 0, st, xb, bpt, cb, sb, tb, mb);
+      else
+        hipLaunchKernelGGL((quant_fp4_kernel<32, true, false, T>), grid, dim3(256), 0, st, xb, bpt, cb, sb, tb, mb);
+      FP4_CHECK(check_launch("quant_fp4"));
+    }
+    return FP4_OK;
+  }
+  if (fmt == FP4_FMT_MXFP8) {
+    int64_t nb = batch * per / 32;
+    hipLaunchKernelGGL(quant_mxfp8_kernel<T>, dim3(grid_1d(nb, 256)), dim3(256), 0, st, x, nb, codes,
+                       reinterpret_cast<uint8_t*>(scales));
+    return check_launch("quant_mxfp8");
+  }
+  if (fmt == FP4_FMT_FP8_ROW) {
+    int64_t ng = batch * per / 128;
+    hipLaunchKernelGGL(quant_fp8_row_kernel<T>, dim3(grid_1d(ng * 4, 256)), dim3(256), 0, st, x, ng,
+                       codes, reinterpret_cast<float*>(scales));
+    return check_launch("quant_fp8_row");
+  }
+  if (fmt == FP4_FMT_FP8_BLOCK) {
+    int64_t tiles = (rows / 128) * (cols / 128);
+    for (int64_t b0 = 0; b0 < batch; b0 += 65535) {
+      unsigned gy = (unsigned)std::min<int64_t>(65535, batch - b0);
+      hipLaunchKernelGGL(fp8_tile_amax_kernel<T>, dim3((unsigned)tiles, gy), dim3(256), 0, st,
+                         x + b0 * per, rows, cols, reinterpret_cast<float*>(scales) + b0 * tiles);
+      FP4_CHECK(check_launch("fp8_tile_amax"));
+    }
+    int64_t nchunks = batch * per / 32;
+    hipLaunchKernelGGL(quant_fp8_tile_kernel<T>, dim3(grid_1d(nchunks, 256)), dim3(256), 0, st, x, rows,
+                       cols, nchunks, reinterpret_cast<const float*>(scales), codes);
+    return check_launch("quant_fp8_tile");
+  }
+  return fail(FP4_ERR_INVALID_ARG, "unknown format %d", fmt);
+}
+
+int block_of(int fmt) {
+  switch (fmt) {
+    case FP4_FMT_NVFP4: return 16;
+    case FP4_FMT_MXFP4:
+    case FP4_FMT_MXFP8: return 32;
+    case FP4_FMT_FP8_BLOCK:
+    case FP4_FMT_FP8_ROW: return 128;
+    default: return 0;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fp4_status_string(int status) {
+  switch (status) {
+    case FP4_OK: return "FP4_OK";
+    case FP4_ERR_INVALID_ARG: return "FP4_ERR_INVALID_ARG";
+    case FP4_ERR_SHAPE: return "FP4_ERR_SHAPE";
+    case FP4_ERR_UNSUPPORTED: return "FP4_ERR_UNSUPPORTED";
+    case FP4_ERR_WORKSPACE: return "FP4_ERR_WORKSPACE";
+    case FP4_ERR_HIP: return "FP4_ERR_HIP";
+    default: return "FP4_ERR_UNKNOWN";
+  }
+}
+
+const char* fp4_last_error(void) { return fp4::g_last_error.c_str(); }
+
+int fp4_quantize(int fmt, int rule, int ts_mode, const void* x, int x_dtype, int64_t batch,
+                 int64_t rows, int64_t cols, uint8_t* codes, void* scales, float* tensor_scale,
+                 uint8_t* m4_flags, void* stream) {
+  int bs = block_of(fmt);
+  if (bs == 0) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: unknown format %d", fmt);
+  if (rule != FP4_RULE_RTN && rule != FP4_RULE_4OVER6)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: unknown rule %d", rule);
+  if (ts_mode != FP4_TS_DYNAMIC && ts_mode != FP4_TS_STATIC)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: unknown tensor-scale mode %d", ts_mode);
+  if (x_dtype != FP4_DT_BF16 && x_dtype != FP4_DT_F32)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: unknown dtype %d", x_dtype);
+  if (batch < 0 || rows < 0 || cols < 0)
+    return fail(FP4_ERR_SHAPE, "fp4_quantize: negative dimension");
+  if (cols % bs) return fail(FP4_ERR_SHAPE, "fp4_quantize: cols %lld not a multiple of %d", (long long)cols, bs);
+  if (fmt == FP4_FMT_FP8_BLOCK && rows % 128)
+    return fail(FP4_ERR_SHAPE, "fp4_quantize: rows %lld not a multiple of 128", (long long)rows);
+  if (batch == 0 || rows == 0 || cols == 0) return FP4_OK;
+  if (!x || !codes || !scales) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: null pointer");
+  if (fmt == FP4_FMT_NVFP4 && !tensor_scale)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: NVFP4 needs tensor_scale");
+  if (fmt != FP4_FMT_NVFP4 && fmt != FP4_FMT_MXFP4) m4_flags = nullptr;
+  hipStream_t st = as_stream(stream);
+  if (x_dtype == FP4_DT_BF16)
+    return quantize_typed<uint16_t>(fmt, rule, ts_mode, reinterpret_cast<const uint16_t*>(x), batch,
+                                    rows, cols, codes, scales, tensor_scale, m4_flags, st);
+  return quantize_typed<float>(fmt, rule, ts_mode, reinterpret_cast<const float*>(x), batch, rows,
+                               cols, codes, scales, tensor_scale, m4_flags, st);
+}
+
+int fp4_dequantize(int fmt, const uint8_t* codes, const void* scales, const float* tensor_scale,
+                   int64_t batch, int64_t rows, int64_t cols, void* out, int out_dtype,
+                   void* stream) {
+  int bs = block_of(fmt);
+  if (bs == 0) return fail(FP4_ERR_INVALID_ARG, "fp4_dequantize: unknown format %d", fmt);
+  if (out_dtype != FP4_DT_BF16 && out_dtype != FP4_DT_F32)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_dequantize: unknown dtype %d", out_dtype);
+  if (batch < 0 || rows < 0 || cols < 0) return fail(FP4_ERR_SHAPE, "fp4_dequantize: negative dimension");
+  if (cols % bs) return fail(FP4_ERR_SHAPE, "fp4_dequantize: cols %lld not a multiple of %d", (long long)cols, bs);
+  if (fmt == FP4_FMT_FP8_BLOCK && rows % 128)
+    return fail(FP4_ERR_SHAPE, "fp4_dequantize: rows %lld not a multiple of 128", (long long)rows);
+  if (batch == 0 || rows == 0 || cols == 0) return FP4_OK;
+  if (!codes || !scales || !out) return fail(FP4_ERR_INVALID_ARG, "fp4_dequantize: null pointer");
+  if (fmt == FP4_FMT_NVFP4 && !tensor_scale)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_dequantize: NVFP4 needs tensor_scale");
+  hipStream_t st = as_stream(stream);
+  int64_t n8 = batch * rows * cols / 8;
+  dim3 grid(grid_1d(n8, 256));
+#define FP4_DQ(F)                                                                                  \
+  if (out_dtype == FP4_DT_F32)                                                                     \
+    hipLaunchKernelGGL((dequant_kernel<F, float>), grid, dim3(256), 0, st, codes, scales,          \
+                       tensor_scale, rows, cols, n8, reinterpret_cast<float*>(out));               \
+  else                                                                                             \
+    hipLaunchKernelGGL((dequant_kernel<F, uint16_t>), grid, dim3(256), 0, st, codes, scales,       \
+                       tensor_scale, rows, cols, n8, reinterpret_cast<uint16_t*>(out));
+  switch (fmt) {
+    case FP4_FMT_NVFP4: FP4_DQ(0) break;
+    case FP4_FMT_MXFP4: FP4_DQ(1) break;
+    case FP4_FMT_MXFP8: FP4_DQ(2) break;
+    case FP4_FMT_FP8_BLOCK: FP4_DQ(3) break;
+    case FP4_FMT_FP8_ROW: FP4_DQ(4) break;
+  }
+#undef FP4_DQ
+  return check_launch("dequant");
+}
+
+}  // extern "C"

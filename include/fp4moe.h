@@ -1,0 +1,192 @@
+/*
+ * fp4moe.h - C ABI of the block-scaled FP4 routed-expert MoE library (gfx950).
+ *
+ * Formats, as the model cards on block_scaled_fp4_nvfp4 state them:
+ *  - NVFP4: E2M1 values packed two per byte, one E4M3 block scale per 16 values
+ *    ("weight_scale"), one FP32 tensor scale per tensor ("weight_scale_2");
+ *    activations use the tensor scale amax/2688 ("Local-Hessian NVFP4
+ *    experts", opening section); gate and up share one tensor scale (same
+ *    passage); one tensor scale per expert (section "What is different about it").
+ *  - The per-block 4/6 choice: the block scale maps the block max to 6 or to 4,
+ *    whichever gives the smaller exact post-rounding squared error ("dabsLabs
+ *    NVFP4 (4/6-optimal scales)", section "What makes this build different").
+ *  - MXFP4: E2M1 values with one UE8M0 scale per 32 ("MXFP4-FP8-R12",
+ *    section "Quantization format").
+ *  - MXFP8: E4M3 values, one power-of-two scale per 32, e = ceil(log2(amax/448))
+ *    ("FP4-Local AZ", section "The shared expert").
+ *  - Block FP8: E4M3 weights with one FP32 scale per 128 x 128 tile, dynamic
+ *    E4M3 activations with one FP32 scale per (row, 128 columns)
+ *    ("MXFP4-FP8-R12", runtime contract table: retained block-FP8 experts on a
+ *    dynamic-FP8 path).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers of the current HIP device; the
+ *    caller owns every buffer.  The library never allocates or frees device
+ *    memory and keeps no state between calls except a thread-local error text.
+ *  - `stream` is a hipStream_t (NULL = default stream).  Calls only enqueue
+ *    work and return; a launch failure returns FP4_ERR_HIP, asynchronous faults
+ *    surface at the caller's next synchronisation.
+ *  - Layouts are row-major; blocks run along the last (reduction) dimension.
+ *    Packed 4-bit codes: element 2i in the low nibble of byte i, element 2i+1 in
+ *    the high nibble; the nibble's bit 3 is the sign.
+ *  - Errors are negative fp4_status values; fp4_last_error() describes the last
+ *    one raised on the calling thread.  A zero-sized problem is a no-op (FP4_OK).
+ */
+#ifndef FP4MOE_H
+#define FP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP4_OK = 0,
+  FP4_ERR_INVALID_ARG = -1, /* null pointer, unknown enum, k out of range   */
+  FP4_ERR_SHAPE = -2,       /* a dimension is not a multiple of its block    */
+  FP4_ERR_UNSUPPORTED = -3, /* combination of formats not provided           */
+  FP4_ERR_WORKSPACE = -4,   /* workspace missing or smaller than required    */
+  FP4_ERR_HIP = -5          /* a HIP launch or runtime call failed           */
+} fp4_status;
+
+typedef enum {
+  FP4_FMT_NVFP4 = 0,     /* E2M1 codes [.., cols/2], E4M3 scales [.., cols/16], f32 tensor scale */
+  FP4_FMT_MXFP4 = 1,     /* E2M1 codes [.., cols/2], UE8M0 scales [.., cols/32]                  */
+  FP4_FMT_MXFP8 = 2,     /* E4M3 codes [.., cols],   UE8M0 scales [.., cols/32]                  */
+  FP4_FMT_FP8_BLOCK = 3, /* E4M3 codes [b, rows, cols], f32 scales [b, rows/128, cols/128]        */
+  FP4_FMT_FP8_ROW = 4,   /* E4M3 codes [.., cols],   f32 scales [.., cols/128] (per row)          */
+  FP4_FMT_NONE = 5       /* 16-bit activations (weight-only quantization)                        */
+} fp4_format;
+
+typedef enum {
+  FP4_RULE_RTN = 0,    /* block max mapped to 6 (the amax/6 plan)                       */
+  FP4_RULE_4OVER6 = 1  /* per block, the amax/6 or the block-max-to-4 plan, whichever has
+                          the strictly smaller exact squared error (ties keep amax/6)      */
+} fp4_rule;
+
+typedef enum { FP4_DT_BF16 = 0, FP4_DT_F32 = 1 } fp4_dtype;
+
+typedef enum {
+  FP4_TS_DYNAMIC = 0, /* NVFP4: compute S = fp32(amax / 2688) per tensor, write it */
+  FP4_TS_STATIC = 1   /* NVFP4: read the caller's tensor scale                     */
+} fp4_ts_mode;
+
+/*
+ * fp4_quantize - quantize `batch` independent tensors x[batch][rows][cols].
+ *
+ *  fmt      NVFP4, MXFP4 (rule applies), MXFP8, FP8_BLOCK or FP8_ROW.
+ *  rule     FP4_RULE_RTN or FP4_RULE_4OVER6 (NVFP4 and MXFP4 only; ignored otherwise).
+ *  x        bf16 or f32 values, `x_dtype`; must be finite.
+ *  codes    out: packed E2M1 [batch, rows, cols/2] (NVFP4, MXFP4) or E4M3 bytes
+ *           [batch, rows, cols] (MXFP8, FP8_*).
+ *  scales   out: E4M3 bytes [batch, rows, cols/16] (NVFP4), UE8M0 bytes
+ *           [batch, rows, cols/32] (MXFP4, MXFP8), f32 [batch, rows/128, cols/128]
+ *           (FP8_BLOCK) or f32 [batch, rows, cols/128] (FP8_ROW).
+ *  tensor_scale  NVFP4 only, f32 [batch]: written (FP4_TS_DYNAMIC) or read
+ *           (FP4_TS_STATIC).  One tensor per batch item, so a fused gate_up
+ *           [2I, H] quantized as one item shares its scale between gate and up.
+ *  m4_flags optional out (may be NULL), one byte per block: 1 where the
+ *           block-max-to-4 plan was chosen.
+ * Shape errors: cols % 16 (NVFP4), % 32 (MX), % 128 (FP8_*), rows % 128 (FP8_BLOCK).
+ */
+int fp4_quantize(int fmt, int rule, int ts_mode, const void* x, int x_dtype,
+                 int64_t batch, int64_t rows, int64_t cols, uint8_t* codes,
+                 void* scales, float* tensor_scale, uint8_t* m4_flags,
+                 void* stream);
+
+/*
+ * fp4_dequantize - decode codes/scales (layouts as fp4_quantize) to
+ * out[batch][rows][cols] in `out_dtype`.  f32 output is the correctly rounded
+ * value g * s * S (NVFP4), g * 2^e (MX) or v * sigma (FP8_*); bf16 output is
+ * that f32 value rounded to nearest-even bf16.
+ */
+int fp4_dequantize(int fmt, const uint8_t* codes, const void* scales,
+                   const float* tensor_scale, int64_t batch, int64_t rows,
+                   int64_t cols, void* out, int out_dtype, void* stream);
+
+/*
+ * One routed-expert MoE layer.  E experts, hidden H, expert intermediate I,
+ * top-k routing.  Expert weights are stacked: fused gate_up W13 [E, 2I, H]
+ * (rows [0, I) gate, [I, 2I) up) and down W2 [E, H, I], in the layouts of
+ * fp4_quantize with batch = E ("dabsLabs NVFP4", section "What makes this
+ * build different": stacked [512, out, in] with fused gate_up).  Widths and k
+ * are runtime values ("FP4-Local AZ": the engine must read the routing width
+ * and the shared-expert width from the configuration).
+ *
+ * Supported (w_fmt, a_fmt) pairs:
+ *   (NVFP4, NONE)      W4A16: bf16 x, f32 intermediate h
+ *   (MXFP4, NONE)      W4A16 with MX weights
+ *   (NVFP4, NVFP4)     W4A4: x and h dynamically quantized with tensor scale
+ *                      amax/2688 over all of x [T, H] and all of h [T*k, I]
+ *                      and amax/6 block scales (unless input_scale /
+ *                      inter_scale give static tensor scales)
+ *   (MXFP4, MXFP8)     MXFP4 weights x dynamic MXFP8 activations
+ *   (FP8_BLOCK, FP8_ROW) block-FP8 weights x dynamic per-(row,128) FP8 activations
+ * Optional shared expert (shared_inter > 0): MXFP8 Ws13 [2*Si, H] and Ws2
+ * [H, Si] with dynamic MXFP8 activations, scaled per token by
+ * sigmoid(x . shared_gate) (bf16 gate [H] on unquantized x) and added to y
+ * ("FP4-Local AZ", section "The shared expert" and its table of differences).
+ */
+typedef struct {
+  int32_t w_fmt, a_fmt;
+  int32_t num_experts, hidden, inter, top_k;
+  const uint8_t* w13;
+  const void* w13_scale;
+  const float* w13_scale_2; /* NVFP4: [E] */
+  const uint8_t* w2;
+  const void* w2_scale;
+  const float* w2_scale_2;  /* NVFP4: [E] */
+  const float* input_scale; /* NVFP4 activations: optional static S_x (device f32[1]) */
+  const float* inter_scale; /* NVFP4 activations: optional static S_h (device f32[1]) */
+  int32_t shared_inter;     /* 0: no shared expert */
+  const uint8_t* ws13;      /* MXFP8 codes [2*Si, H] */
+  const uint8_t* ws13_scale;/* UE8M0 [2*Si, H/32] */
+  const uint8_t* ws2;       /* MXFP8 codes [H, Si] */
+  const uint8_t* ws2_scale; /* UE8M0 [H, Si/32] */
+  const uint16_t* shared_gate; /* bf16 [H] */
+} moe_fp4_layer;
+
+/* Byte offsets of the stage buffers inside the forward's workspace, for
+ * inspection by tests (all buffers are written by moe_fp4_forward). */
+typedef struct {
+  size_t total;          /* required workspace bytes                              */
+  size_t error_flag;     /* int32: nonzero if a topk id was out of range           */
+  size_t counts;         /* int32 [E]   pairs per expert                           */
+  size_t offsets;        /* int32 [E+1] first sorted row of each expert            */
+  size_t pair_of_row;    /* int32 [T*k] pair (t*k + j) held by each sorted row      */
+  size_t row_of_pair;    /* int32 [T*k] sorted row of each pair                     */
+  size_t x_tensor_scale; /* f32: S_x (NVFP4 activations)                            */
+  size_t h_tensor_scale; /* f32: S_h (NVFP4 activations)                            */
+  size_t h;              /* f32 [T*k, I]  SiLU(gate)*up in sorted row order          */
+  size_t hq_codes;       /* quantized h codes (layout of a_fmt), sorted row order    */
+  size_t hq_scales;      /* quantized h scales                                       */
+  size_t o;              /* f32 [T*k, H]  down projection per sorted row (unweighted) */
+} moe_fp4_ws_layout;
+
+int moe_fp4_workspace_layout(const moe_fp4_layer* layer, int64_t tokens,
+                             moe_fp4_ws_layout* out);
+int moe_fp4_workspace_size(const moe_fp4_layer* layer, int64_t tokens,
+                           size_t* bytes);
+
+/*
+ * moe_fp4_forward - y[T, H] (f32) = routed-expert FFN of x[T, H] (bf16).
+ *  topk_ids     int32 [T, k], expert of each (token, slot); 0 <= id < E.  A pair
+ *               with an id out of range is skipped and sets the workspace error
+ *               flag (checked by the caller after synchronising).
+ *  topk_weights f32 [T, k], routing weights, applied after the down projection.
+ *  workspace    >= moe_fp4_workspace_size bytes of device memory.
+ * Routing (softmax / top-k) is done by the caller.
+ */
+int moe_fp4_forward(const moe_fp4_layer* layer, const uint16_t* x, int64_t tokens,
+                    const int32_t* topk_ids, const float* topk_weights, float* y,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+const char* fp4_status_string(int status);
+const char* fp4_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* FP4MOE_H */

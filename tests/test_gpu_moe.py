@@ -1,0 +1,142 @@
+"""GPU MoE forward parity through the C ABI against the float64 oracle.
+
+Bar: relative Frobenius error <= 2e-3 on y; the permutation is compared
+exactly; stage-wise checks read the forward's workspace buffers (offsets
+from moe_fp4_workspace_layout)."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import moe
+
+from gpu_util import (OracleLayer, dev, dev_bf16, gpu_layer, gpu_ok, host, print_case,
+                      rel_fro, torch)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_ok(), reason="needs a GPU")]
+
+TOL = 2e-3
+
+
+def _lib():
+    import block_scaled_fp4_nvfp4_amd as m
+    return m
+
+
+def _run(layer, x_bits, ids, wts):
+    m = _lib()
+    T = x_bits.shape[0]
+    ws = torch.zeros(m.workspace_size(layer, T), dtype=torch.uint8, device="cuda")
+    y = m.moe_forward(layer, dev_bf16(x_bits), dev(ids.astype(np.int32)), dev(wts.astype(np.float32)), ws)
+    torch.cuda.synchronize()
+    return host(y), ws, m.workspace_layout(layer, T)
+
+
+def _ws_i32(ws, off, n):
+    return host(ws[off:off + 4 * n].view(torch.int32))
+
+
+def _ws_f32(ws, off, n):
+    return host(ws[off:off + 4 * n].view(torch.float32))
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    cfg = synth.CONFIGS["tiny"]
+    w13, w2 = synth.layer_weights(cfg)
+    return cfg, w13, w2, synth.activations(cfg), *synth.routing(cfg)
+
+
+@pytest.mark.parametrize("w_fmt", ["nvfp4", "mxfp4"])
+def test_tiny_w4a16_matches_oracle(tiny, w_fmt):
+    print_case(f"tiny W4A16 {w_fmt}")
+    cfg, w13, w2, x, ids, wts = tiny
+    cfg = cfg.replace(w_fmt=w_fmt)
+    y, ws, lay = _run(gpu_layer(cfg, w13, w2), x, ids, wts)
+    ol = OracleLayer(cfg, w13, w2)
+    y_ref, st = moe.moe_forward(ol.as_dict(), x, ids, wts, return_stages=True)
+    assert rel_fro(y, y_ref) <= TOL
+    assert rel_fro(y, y_ref) < 1e-5          # f32 accumulation only
+    # permutation: exact
+    P = cfg.tokens * cfg.top_k
+    off, por, rop = moe.permute(ids, cfg.num_experts)
+    np.testing.assert_array_equal(_ws_i32(ws, lay["offsets"], cfg.num_experts + 1), off)
+    np.testing.assert_array_equal(_ws_i32(ws, lay["pair_of_row"], P), por)
+    np.testing.assert_array_equal(_ws_i32(ws, lay["row_of_pair"], P), rop)
+    assert _ws_i32(ws, lay["error_flag"], 1)[0] == 0
+    # stage: h in sorted row order
+    h = _ws_f32(ws, lay["h"], P * cfg.inter).reshape(P, cfg.inter)
+    assert rel_fro(h, st["h"][por]) < 1e-5
+
+
+def test_tiny_zero_padding_bit_identical(tiny):
+    """640 real + 640 zero rows give bit-identical output (FP4-Local AZ card,
+    "The shared expert": silu(0) * 0 = 0); here 128 -> 160 zero-padded."""
+    print_case("tiny zero padding")
+    cfg, w13, w2, x, ids, wts = tiny
+    I, pad = cfg.inter, 32
+    z = np.zeros((w13.shape[0], pad, w13.shape[2]), np.uint16)
+    w13p = np.concatenate([w13[:, :I], z, w13[:, I:], z], axis=1)
+    w2p = np.concatenate([w2, np.zeros((w2.shape[0], w2.shape[1], pad), np.uint16)], axis=2)
+    y, _, _ = _run(gpu_layer(cfg, w13, w2), x, ids, wts)
+    yp, _, _ = _run(gpu_layer(cfg.replace(inter=I + pad), w13p, w2p), x, ids, wts)
+    np.testing.assert_array_equal(y.view(np.uint32), yp.view(np.uint32))
+
+
+def test_tiny_invalid_ids_flagged_and_skipped(tiny):
+    print_case("tiny invalid ids")
+    cfg, w13, w2, x, ids, wts = tiny
+    bad = ids.copy()
+    bad[5, 1] = cfg.num_experts + 3
+    bad[9, 0] = -1
+    y, ws, lay = _run(gpu_layer(cfg, w13, w2), x, bad, wts)
+    assert _ws_i32(ws, lay["error_flag"], 1)[0] == 2
+    wz = wts.copy()
+    wz[5, 1] = 0.0
+    wz[9, 0] = 0.0
+    fixed = ids.copy()
+    fixed[5, 1] = 0
+    fixed[9, 0] = 0
+    y_ref = moe.moe_forward(OracleLayer(cfg, w13, w2).as_dict(), x, fixed, wz)
+    assert rel_fro(y, y_ref) < 1e-5
+
+
+def test_single_expert_top1_reduces_to_dense(tiny):
+    print_case("tiny E=1 k=1")
+    cfg, w13, w2, x, _, _ = tiny
+    c1 = cfg.replace(num_experts=1, top_k=1)
+    ids = np.zeros((cfg.tokens, 1), np.int32)
+    wts = np.ones((cfg.tokens, 1), np.float32)
+    y, _, _ = _run(gpu_layer(c1, w13[:1], w2[:1]), x, ids, wts)
+    ol = OracleLayer(c1, w13[:1], w2[:1])
+    from oracle.quant import dequantize_nvfp4
+    from oracle.formats import bf16_to_f64
+    a, b = ol.w13(0), ol.w2(0)
+    W13 = dequantize_nvfp4(a["codes"], a["scales"], a["tensor_scale"])
+    W2 = dequantize_nvfp4(b["codes"], b["scales"], b["tensor_scale"])
+    ref = moe.dense_swiglu(bf16_to_f64(x), W13, W2)
+    assert rel_fro(y, ref) < 1e-5
+
+
+@pytest.fixture(scope="module")
+def decode_layer():
+    cfg = synth.CONFIGS["decode"]
+    w13, w2 = synth.layer_weights(cfg)
+    return cfg, w13, w2
+
+
+def test_decode_layer_sampled_tokens(decode_layer):
+    """512 experts, top-10, hidden 2560, inter 640, 16 tokens: the workload
+    and launch configuration the benchmark times; sampled tokens vs oracle."""
+    print_case("decode layer, sampled tokens")
+    cfg, w13, w2 = decode_layer
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    y, ws, lay = _run(gpu_layer(cfg, w13, w2), x, ids, wts)
+    sample = [0, 7, 15]
+    y_ref = moe.moe_forward(OracleLayer(cfg, w13, w2).as_dict(), x, ids, wts, sample_tokens=sample)
+    assert rel_fro(y[sample], y_ref) <= TOL
+    assert rel_fro(y[sample], y_ref) < 1e-5
+    off, por, _ = moe.permute(ids, cfg.num_experts)
+    np.testing.assert_array_equal(_ws_i32(ws, lay["pair_of_row"], cfg.pairs), por)
+    assert np.all(np.isfinite(y)) and np.linalg.norm(y) > 0

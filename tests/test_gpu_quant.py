@@ -1,0 +1,169 @@
+"""GPU quantizer / dequantizer parity through the C ABI: codes and scales are
+bit-exact against the oracle; dequantized values equal the oracle's exact
+values rounded once to f32 (bf16: then rounded to bf16)."""
+import numpy as np
+import pytest
+
+import synth
+from oracle import formats as F
+from oracle import quant as Q
+
+from gpu_util import dev, dev_bf16, gpu_ok, host, print_case, torch
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_ok(), reason="needs a GPU")]
+
+
+def _lib():
+    import block_scaled_fp4_nvfp4_amd as m
+    return m
+
+
+def _oracle_q(fmt, x64, rule):
+    if fmt == "nvfp4":
+        return Q.quantize_nvfp4(x64, rule)
+    if fmt == "mxfp4":
+        return Q.quantize_mxfp4(x64, rule)
+    if fmt == "mxfp8":
+        return Q.quantize_mxfp8(x64)
+    if fmt == "fp8_row":
+        return Q.quantize_fp8_rows(x64)
+    if fmt == "fp8_block":
+        return Q.quantize_fp8_block_weight(x64)
+    raise ValueError(fmt)
+
+
+def _compare(fmt, rule, xt, x64_per_tensor):
+    """Quantize xt ([B, R, C] device) on the GPU and compare every tensor."""
+    m = _lib()
+    q = m.quantize(xt, fmt, rule, want_m4=fmt in ("nvfp4", "mxfp4"))
+    torch.cuda.synchronize()
+    codes, scales = host(q["codes"]), host(q["scales"])
+    for b, x64 in enumerate(x64_per_tensor):
+        o = _oracle_q(fmt, x64, rule)
+        oc = F.pack_nibbles(o["codes"]) if fmt in ("nvfp4", "mxfp4") else o["codes"]
+        np.testing.assert_array_equal(codes[b], oc, err_msg=f"{fmt}/{rule} codes, tensor {b}")
+        if fmt in ("fp8_row", "fp8_block"):
+            np.testing.assert_array_equal(scales[b].view(np.uint32), o["scales"].view(np.uint32))
+        else:
+            np.testing.assert_array_equal(scales[b], o["scales"], err_msg=f"{fmt}/{rule} scales, tensor {b}")
+        if fmt == "nvfp4":
+            assert host(q["tensor_scale"])[b].view(np.uint32) == np.float32(o["tensor_scale"]).view(np.uint32)
+        if q["m4"] is not None:
+            np.testing.assert_array_equal(host(q["m4"])[b].astype(bool), o["m4"])
+    return q
+
+
+@pytest.mark.parametrize("fmt,rule", [("nvfp4", "4over6"), ("nvfp4", "rtn"),
+                                      ("mxfp4", "4over6"), ("mxfp4", "rtn")])
+def test_fp4_weights_bit_exact_tiny_layer(fmt, rule):
+    print_case(f"tiny layer weights {fmt}/{rule}")
+    cfg = synth.CONFIGS["tiny"]
+    w13, w2 = synth.layer_weights(cfg)
+    for w in (w13, w2):
+        _compare(fmt, rule, dev_bf16(w), [F.bf16_to_f64(w[e]) for e in range(w.shape[0])])
+
+
+def test_fp4_adversarial_blocks_bit_exact():
+    print_case("adversarial blocks")
+    rows = [
+        [2688, 112, 336, 560, 784, 1120, 1568, 2240, -224, -0.0, 100, 120, 448, 672, 896, 1344] * 2,
+        [0.0] * 32, [-0.0] * 32,
+        [2688 * 2.0 ** -14] + [0.0] * 31,
+        [2688 * 2.0 ** -20] * 32,
+        [1792.0, -1792.0] * 16,
+        [6.0, 4.0, 3.0, 2.0, 1.5, 1.0, 0.5, 0.0] * 4,
+        [8, 4, 2, 6, 1, 3, 0, -8, -4, -2, -6, -1, -3, -0.0, 8, 4] * 2,
+    ]
+    x = np.array(rows, np.float32)
+    # add E2M1 tie points at many scales
+    rng = np.random.default_rng(0)
+    ties = (np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0] * 4, np.float32)[None, :]
+            * np.exp2(rng.integers(-8, 8, (24, 1))).astype(np.float32))
+    x = np.concatenate([x, ties])
+    bits = F.bf16_bits_from_f32(x)
+    x64 = F.bf16_to_f64(bits)
+    for fmt in ("nvfp4", "mxfp4"):
+        for rule in ("4over6", "rtn"):
+            _compare(fmt, rule, dev_bf16(bits)[None], [x64])
+
+
+def test_fp4_f32_inputs_bit_exact():
+    print_case("f32 inputs")
+    rng = np.random.default_rng(1)
+    x = (rng.standard_t(3, (3, 64, 256)) * 0.03).astype(np.float32)
+    x[0, 0, :16] = np.float32(1e-40)  # subnormal block
+    for fmt in ("nvfp4", "mxfp4"):
+        for rule in ("4over6", "rtn"):
+            _compare(fmt, rule, dev(x), [x[b].astype(np.float64) for b in range(3)])
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "fp8_row", "fp8_block"])
+def test_fp8_formats_bit_exact(fmt):
+    print_case(f"fp8 format {fmt}")
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((2, 256, 512)).astype(np.float32) * np.exp2(
+        rng.integers(-6, 6, (2, 256, 1))).astype(np.float32)
+    x[0, :128, :128] = 0.0
+    bits = F.bf16_bits_from_f32(x)
+    _compare(fmt, "rtn", dev_bf16(bits), [F.bf16_to_f64(bits[b]) for b in range(2)])
+    _compare(fmt, "rtn", dev(x), [x[b].astype(np.float64) for b in range(2)])
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "mxfp8", "fp8_row", "fp8_block"])
+def test_dequantize_is_the_rounded_exact_value(fmt):
+    print_case(f"dequantize {fmt}")
+    m = _lib()
+    rng = np.random.default_rng(3)
+    x = (rng.standard_t(4, (2, 128, 256)) * 0.02).astype(np.float32)
+    bits = F.bf16_bits_from_f32(x)
+    xt = dev_bf16(bits)
+    q = m.quantize(xt, fmt, "4over6")
+    f32 = host(m.dequantize(q, fmt, xt.shape, torch.float32))
+    b16 = host(m.dequantize(q, fmt, xt.shape, torch.bfloat16))
+    codes, scales = host(q["codes"]), host(q["scales"])
+    for b in range(2):
+        if fmt == "nvfp4":
+            exact = Q.dequantize_nvfp4(F.unpack_nibbles(codes[b]), scales[b], host(q["tensor_scale"])[b])
+        elif fmt == "mxfp4":
+            exact = Q.dequantize_mxfp4(F.unpack_nibbles(codes[b]), scales[b])
+        elif fmt == "mxfp8":
+            exact = Q.dequantize_mxfp8(codes[b], scales[b])
+        elif fmt == "fp8_row":
+            exact = Q.dequantize_fp8_rows(codes[b], scales[b])
+        else:
+            exact = Q.dequantize_fp8_block_weight(codes[b], scales[b])
+        want32 = exact.astype(np.float32)
+        np.testing.assert_array_equal(f32[b].view(np.uint32), want32.view(np.uint32))
+        np.testing.assert_array_equal(b16[b], F.bf16_bits_from_f32(want32))
+
+
+def test_decode_layer_sampled_experts_and_determinism():
+    """Two experts of the 512-expert layer at its real shapes, and a repeat run
+    giving identical bytes (two machines building byte-identical trees, QAD5500
+    card, "Verification")."""
+    print_case("decode-shape experts")
+    m = _lib()
+    cfg = synth.CONFIGS["decode"]
+    ids = [0, 311]
+    w13, w2 = synth.layer_weights(cfg, experts=ids)
+    t13 = dev_bf16(w13)
+    q1 = _compare("nvfp4", "4over6", t13, [F.bf16_to_f64(w13[i]) for i in range(2)])
+    q2 = m.quantize(t13, "nvfp4", "4over6")
+    torch.cuda.synchronize()
+    assert torch.equal(q1["codes"], q2["codes"]) and torch.equal(q1["scales"], q2["scales"])
+    _compare("nvfp4", "4over6", dev_bf16(w2), [F.bf16_to_f64(w2[i]) for i in range(2)])
+
+
+def test_static_tensor_scale_and_error_codes():
+    print_case("static tensor scale / errors")
+    m = _lib()
+    rng = np.random.default_rng(4)
+    x = F.bf16_bits_from_f32((rng.standard_normal((1, 32, 64)) * 0.02).astype(np.float32))
+    S = np.float32(0.0001234)
+    q = m.quantize(dev_bf16(x), "nvfp4", "4over6", tensor_scale=torch.tensor([S]))
+    o = Q.quantize_nvfp4(F.bf16_to_f64(x[0]), "4over6", tensor_scale=S)
+    np.testing.assert_array_equal(host(q["codes"])[0], F.pack_nibbles(o["codes"]))
+    np.testing.assert_array_equal(host(q["scales"])[0], o["scales"])
+    with pytest.raises(m.Fp4Error):
+        m.quantize(dev_bf16(x[:, :, :40]).contiguous(), "nvfp4")
