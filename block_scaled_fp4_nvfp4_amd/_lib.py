@@ -23,8 +23,9 @@ STATUS = {0: "FP4_OK", -1: "FP4_ERR_INVALID_ARG", -2: "FP4_ERR_SHAPE",
           -3: "FP4_ERR_UNSUPPORTED", -4: "FP4_ERR_WORKSPACE", -5: "FP4_ERR_HIP"}
 
 EXPORTED = ["fp4_quantize", "fp4_dequantize", "moe_fp4_workspace_layout",
-            "moe_fp4_workspace_size", "moe_fp4_forward", "fp4_status_string",
-            "fp4_last_error"]
+            "moe_fp4_workspace_size", "moe_fp4_forward", "moe_fp4_forward_profiled",
+            "fp4_status_string", "fp4_last_error"]
+STAGES = ["permute", "x_quant", "gate_up", "h_quant", "down", "shared", "combine"]
 
 
 class Fp4Error(RuntimeError):
@@ -76,6 +77,9 @@ def lib():
         L.moe_fp4_workspace_size.restype = i32
         L.moe_fp4_forward.argtypes = [ctypes.POINTER(LayerStruct), vp, i64, vp, vp, vp, vp, sz, vp]
         L.moe_fp4_forward.restype = i32
+        L.moe_fp4_forward_profiled.argtypes = [ctypes.POINTER(LayerStruct), vp, i64, vp, vp, vp, vp, sz, vp,
+                                               ctypes.POINTER(vp), i32]
+        L.moe_fp4_forward_profiled.restype = i32
         L.fp4_status_string.argtypes = [i32]
         L.fp4_status_string.restype = ctypes.c_char_p
         L.fp4_last_error.argtypes = []
@@ -219,6 +223,32 @@ def moe_forward(layer: MoELayer, x: torch.Tensor, topk_ids: torch.Tensor,
     s = layer.struct()
     _check(lib().moe_fp4_forward(ctypes.byref(s), _ptr(x), T, _ptr(topk_ids), _ptr(topk_weights),
                                  _ptr(y), _ptr(workspace), workspace.numel(), _stream()))
+    return y
+
+
+class StageTimer:
+    """Eight HIP events recorded by moe_fp4_forward_profiled at the stage
+    boundaries; durations() gives milliseconds per stage of the last call."""
+
+    def __init__(self):
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+        for e in self.events:  # create the underlying hipEvent_t
+            e.record()
+        torch.cuda.synchronize()
+        self._arr = (ctypes.c_void_p * 8)(*[e.cuda_event for e in self.events])
+
+    def durations(self) -> dict:
+        return {name: self.events[i].elapsed_time(self.events[i + 1]) for i, name in enumerate(STAGES)}
+
+
+def moe_forward_profiled(layer: MoELayer, x: torch.Tensor, topk_ids: torch.Tensor,
+                         topk_weights: torch.Tensor, workspace: torch.Tensor, y: torch.Tensor,
+                         timer: StageTimer) -> torch.Tensor:
+    T = int(x.shape[0])
+    s = layer.struct()
+    _check(lib().moe_fp4_forward_profiled(ctypes.byref(s), _ptr(x), T, _ptr(topk_ids), _ptr(topk_weights),
+                                          _ptr(y), _ptr(workspace), workspace.numel(), _stream(),
+                                          timer._arr, 8))
     return y
 
 

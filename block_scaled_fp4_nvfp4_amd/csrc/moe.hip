@@ -110,7 +110,7 @@ __device__ int block_scan_1024(int v, int* tmp, int* total) {
 // Counts, offsets, active-expert list and GEMM tile offsets from per-expert
 // counts held in `cnt` (global, E ints).  One workgroup of 1024 threads.
 __device__ void finish_offsets(const int32_t* cnt, int E, int tile_m, int32_t* offsets,
-                               int32_t* active, int32_t* tile_offsets, int* tmp) {
+                               int32_t* active, int32_t* tile_offsets, int* tmp, int* s_off = nullptr) {
   int tid = threadIdx.x;
   int per = (E + 1023) / 1024;
   int lo = min(E, tid * per), hi = min(E, lo + per);
@@ -128,6 +128,7 @@ __device__ void finish_offsets(const int32_t* cnt, int E, int tile_m, int32_t* o
   for (int e = lo; e < hi; ++e) {
     int c = cnt[e];
     offsets[e] = b_cnt;
+    if (s_off) s_off[e] = b_cnt;
     tile_offsets[e] = b_tile;
     if (c > 0) active[1 + b_act++] = e;
     b_cnt += c;
@@ -138,6 +139,51 @@ __device__ void finish_offsets(const int32_t* cnt, int E, int tile_m, int32_t* o
     tile_offsets[E] = tot_tile;
     active[0] = tot_act;
   }
+}
+
+// Whole permutation in one workgroup of 1024 threads for P <= 1024 pairs
+// (decode batches): ranks, histogram, scan and scatter all through LDS.
+__global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restrict__ ids, int P, int E,
+                                                         int tile_m, int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ pair_of_row,
+                                                         int32_t* __restrict__ row_of_pair,
+                                                         int32_t* __restrict__ active,
+                                                         int32_t* __restrict__ tile_offsets,
+                                                         int32_t* __restrict__ error_flag) {
+  extern __shared__ int smem[];
+  int* s_ids = smem;            // 1024
+  int* tmp = smem + 1024;       // 1024
+  int* s_hist = smem + 2048;    // E
+  int* s_off = s_hist + E;      // E
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 1024) s_hist[e] = 0;
+  int my = -1;
+  if (tid < P) {
+    int v = ids[tid];
+    my = (v >= 0 && v < E) ? v : -2;
+  }
+  s_ids[tid] = my;
+  __syncthreads();
+  if (my >= 0) atomicAdd(&s_hist[my], 1);
+  int r = 0;
+  if (my >= 0)
+    for (int q = 0; q < tid; ++q) r += s_ids[q] == my;
+  int bad_total;
+  (void)block_scan_1024(my == -2 ? 1 : 0, tmp, &bad_total);  // also orders the histogram updates
+  for (int e = tid; e < E; e += 1024) counts[e] = s_hist[e];
+  finish_offsets(s_hist, E, tile_m, offsets, active, tile_offsets, tmp, s_off);
+  __syncthreads();
+  if (tid < P) {
+    if (my >= 0) {
+      int row = s_off[my] + r;
+      row_of_pair[tid] = row;
+      pair_of_row[row] = tid;
+    } else {
+      row_of_pair[tid] = -1;
+    }
+  }
+  if (tid == 0) error_flag[0] = bad_total;
 }
 
 // Pass 1 (grid = ceil(P/256)): per block of 256 consecutive pairs, the rank of
@@ -224,6 +270,12 @@ __global__ void __launch_bounds__(kPermBlock) perm_scatter_kernel(const int32_t*
 }
 
 int launch_permute(const int32_t* ids, int64_t P, int E, int tile_m, const WsPtrs& w, hipStream_t st) {
+  if (P <= 1024 && E <= 4096) {
+    size_t lds = sizeof(int) * (2048 + 2 * (size_t)E);
+    hipLaunchKernelGGL(perm_small_kernel, dim3(1), dim3(1024), lds, st, ids, (int)P, E, tile_m, w.counts,
+                       w.offsets, w.pair_of_row, w.row_of_pair, w.active, w.tile_offsets, w.error_flag);
+    return check_launch("perm_small");
+  }
   int64_t nb = (P + kPermBlock - 1) / kPermBlock;
   if (nb == 0) nb = 1;  // still writes counts/offsets for P == 0
   size_t lds = sizeof(int) * (kPermBlock + E);
@@ -243,12 +295,15 @@ int launch_permute(const int32_t* ids, int64_t P, int E, int tile_m, const WsPtr
 
 // --------------------------------------------- weight-only GEMV path (decode)
 
-// Scale of block b (16 values) of a weight row: NVFP4 E4M3 per 16, or MXFP4
-// UE8M0 per 32 (shared by the two 16-value halves).
+// Scale of 16-value block b of a weight row: NVFP4 E4M3 per 16 (hardware
+// E4M3 -> f32 convert, exact), or MXFP4 UE8M0 per 32 shared by the block's two
+// 16-value halves (2^(c-127) built from its exponent bits; c = 0 is not a
+// normal float and is decoded separately).
 template <int WFMT>
 __device__ __forceinline__ float block_scale(const uint8_t* srow, int b) {
-  if (WFMT == FP4_FMT_NVFP4) return e4m3_to_f32(srow[b]);
-  return ldexpf(1.0f, (int)srow[b >> 1] - 127);
+  if (WFMT == FP4_FMT_NVFP4) return __builtin_amdgcn_cvt_f32_fp8((int)srow[b], 0);
+  uint32_t c = srow[b >> 1];
+  return c ? __uint_as_float(c << 23) : 5.877471754111438e-39f;  // 2^-127
 }
 
 template <int WFMT>
@@ -256,12 +311,28 @@ __device__ __forceinline__ int64_t scale_row_stride(int64_t cols) {
   return WFMT == FP4_FMT_NVFP4 ? cols / 16 : cols / 32;
 }
 
+// acc += s_b * sum over the 16 values of block b of w * x (one token row)
+__device__ __forceinline__ float block_dot(uint2 c, float sb, const uint32_t (&x)[8], float acc) {
+  uint32_t a[4], b[4];
+  e2m1x8_to_bf16x8(c.x, a);
+  e2m1x8_to_bf16x8(c.y, b);
+  float d = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d = dot2_bf16(a[q], x[q], d);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d = dot2_bf16(b[q], x[4 + q], d);
+  return fmaf(d, sb, acc);
+}
+
+constexpr int kGvJTile = 32;  // outputs j per workgroup: 8 half-waves x 4 steps
+
 // gate_up + SiLU*up for the pairs of one expert, bf16 activations.
-// Grid: (I / 32 row tiles, max active experts).  A half-wave (32 lanes) owns
-// one output j at a time: the gate row j and the up row I+j, with K = H split
-// into 16-value blocks, lane l taking blocks l, l+32, ...  The pairs' tokens
-// (TB per pass) are held in registers as bf16 pairs.
-template <int WFMT, int TB, int BPL>
+// Grid: (I / 32 output tiles, max active experts).  A half-wave (32 lanes)
+// owns one output j per step: gate row j and up row I+j, K = H split into
+// 16-value blocks, lane l taking blocks l, l+32, ...  The two rows' codes and
+// scales are loaded once per step and reused for every token of the expert;
+// the token's activations come through L1 (they are shared by all rows).
+template <int WFMT, int BPL>
 __global__ void __launch_bounds__(256) gemv_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ pair_of_row, const int32_t* __restrict__ active,
@@ -270,7 +341,6 @@ __global__ void __launch_bounds__(256) gemv_gateup_kernel(
   const int ai = blockIdx.y;
   if (ai >= active[0]) return;
   const int e = active[1 + ai];
-  const int r0 = offsets[e], n = offsets[e + 1] - r0;
   const int hw = threadIdx.x >> 5, l = threadIdx.x & 31;
   const int NB = H >> 4;
   const int64_t row_bytes = H >> 1;
@@ -278,179 +348,142 @@ __global__ void __launch_bounds__(256) gemv_gateup_kernel(
   const uint8_t* wq = w13 + (int64_t)e * 2 * I * row_bytes;
   const uint8_t* ws = w13s + (int64_t)e * 2 * I * srow;
   const float S = WFMT == FP4_FMT_NVFP4 ? w13s2[e] : 1.0f;
-  const int j_begin = blockIdx.x * 32;
-
-  for (int t0 = 0; t0 < n; t0 += TB) {
-    const int nt = min(TB, n - t0);
-    uint32_t xr[TB][BPL][8];
+  const int r0 = offsets[e], n = offsets[e + 1] - r0;
+  for (int j = blockIdx.x * kGvJTile + hw; j < min(I, (int)(blockIdx.x + 1) * kGvJTile); j += 8) {
+    uint2 cg[BPL], cu[BPL];
+    float fg[BPL], fu[BPL];
+    const uint2* qg = reinterpret_cast<const uint2*>(wq + (int64_t)j * row_bytes);
+    const uint2* qu = reinterpret_cast<const uint2*>(wq + (int64_t)(I + j) * row_bytes);
+    const uint8_t* sg = ws + (int64_t)j * srow;
+    const uint8_t* su = ws + (int64_t)(I + j) * srow;
 #pragma unroll
-    for (int t = 0; t < TB; ++t) {
-      int tok = pair_of_row[r0 + t0 + min(t, nt - 1)] / k;
-      const uint16_t* xrow = x + (int64_t)tok * H;
+    for (int i = 0; i < BPL; ++i) {
+      int b = l + 32 * i;
+      bool in = b < NB;
+      cg[i] = in ? qg[b] : make_uint2(0u, 0u);
+      cu[i] = in ? qu[b] : make_uint2(0u, 0u);
+      fg[i] = in ? block_scale<WFMT>(sg, b) : 0.0f;
+      fu[i] = in ? block_scale<WFMT>(su, b) : 0.0f;
+    }
+    for (int t = 0; t < n; ++t) {
+      // keep the packed codes (not their 4x larger bf16 expansion) live
+      // across the token loop: the expansion is redone per token
+#pragma unroll
+      for (int i = 0; i < BPL; ++i) {
+        asm volatile("" : "+v"(cg[i].x), "+v"(cg[i].y), "+v"(cu[i].x), "+v"(cu[i].y));
+      }
+      const uint16_t* xrow = x + (int64_t)(pair_of_row[r0 + t] / k) * H;
+      float ag = 0.0f, au = 0.0f;
 #pragma unroll
       for (int i = 0; i < BPL; ++i) {
         int b = l + 32 * i;
+        uint32_t xr[8];
         if (b < NB) {
           const uint4* src = reinterpret_cast<const uint4*>(xrow + b * 16);
           uint4 a0 = src[0], a1 = src[1];
-          uint32_t n0[4] = {a0.x, a0.y, a0.z, a0.w}, n1[4] = {a1.x, a1.y, a1.z, a1.w};
-          uint32_t p0[4], p1[4];
-          permute_pairs_like_e2m1(n0, p0);
-          permute_pairs_like_e2m1(n1, p1);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            xr[t][i][q] = p0[q];
-            xr[t][i][4 + q] = p1[q];
-          }
+          xr[0] = a0.x; xr[1] = a0.y; xr[2] = a0.z; xr[3] = a0.w;
+          xr[4] = a1.x; xr[5] = a1.y; xr[6] = a1.z; xr[7] = a1.w;
         } else {
 #pragma unroll
-          for (int q = 0; q < 8; ++q) xr[t][i][q] = 0u;
+          for (int q = 0; q < 8; ++q) xr[q] = 0u;
         }
-      }
-    }
-    for (int jj = hw; jj < 32; jj += 8) {
-      const int j = j_begin + jj;
-      if (j >= I) break;
-      float ag[TB], au[TB];
-#pragma unroll
-      for (int t = 0; t < TB; ++t) ag[t] = au[t] = 0.0f;
-      const uint8_t* qg = wq + (int64_t)j * row_bytes;
-      const uint8_t* qu = wq + (int64_t)(I + j) * row_bytes;
-      const uint8_t* sg = ws + (int64_t)j * srow;
-      const uint8_t* su = ws + (int64_t)(I + j) * srow;
-      uint2 cg[BPL], cu[BPL];
-      float fg[BPL], fu[BPL];
-#pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        int b = l + 32 * i;
-        if (b < NB) {
-          cg[i] = reinterpret_cast<const uint2*>(qg)[b];
-          cu[i] = reinterpret_cast<const uint2*>(qu)[b];
-          fg[i] = block_scale<WFMT>(sg, b);
-          fu[i] = block_scale<WFMT>(su, b);
-        } else {
-          cg[i] = cu[i] = make_uint2(0u, 0u);
-          fg[i] = fu[i] = 0.0f;
-        }
+        ag = block_dot(cg[i], fg[i], xr, ag);
+        au = block_dot(cu[i], fu[i], xr, au);
       }
 #pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        uint32_t wg[8], wu[8];
-        {
-          uint32_t a[4], b[4];
-          e2m1x8_to_bf16x8(cg[i].x, a);
-          e2m1x8_to_bf16x8(cg[i].y, b);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) { wg[q] = a[q]; wg[4 + q] = b[q]; }
-          e2m1x8_to_bf16x8(cu[i].x, a);
-          e2m1x8_to_bf16x8(cu[i].y, b);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) { wu[q] = a[q]; wu[4 + q] = b[q]; }
-        }
-#pragma unroll
-        for (int t = 0; t < TB; ++t) {
-          float dg = 0.0f, du = 0.0f;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            dg = dot2_bf16(wg[q], xr[t][i][q], dg);
-            du = dot2_bf16(wu[q], xr[t][i][q], du);
-          }
-          ag[t] = fmaf(dg, fg[i], ag[t]);
-          au[t] = fmaf(du, fu[i], au[t]);
-        }
+      for (int off = 16; off > 0; off >>= 1) {
+        ag += __shfl_xor(ag, off, 32);
+        au += __shfl_xor(au, off, 32);
       }
-#pragma unroll
-      for (int t = 0; t < TB; ++t) {
-#pragma unroll
-        for (int off = 16; off > 0; off >>= 1) {
-          ag[t] += __shfl_xor(ag[t], off, 32);
-          au[t] += __shfl_xor(au[t], off, 32);
-        }
-      }
-      if (l == 0) {
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-          if (t < nt) {
-            float g = ag[t] * S, u = au[t] * S;
-            h[(int64_t)(r0 + t0 + t) * I + j] = silu_f32(g) * u;
-          }
-      }
+      if (l == 0) h[(int64_t)(r0 + t) * I + j] = silu_f32(ag * S) * (au * S);
     }
   }
 }
 
+constexpr int kGdTile = 128;  // output rows per workgroup of the down GEMV
+
 // Down projection o[row] = W2[e] h[row] for the rows of one expert, f32 h.
-// Grid: (ceil(H / 64) row tiles, max active experts).  8 lanes own one output
-// row n (K = I split into 16-value blocks, lane q taking blocks q, q+8, ...);
-// h of TB rows at a time is staged in LDS.
-template <int WFMT, int TB>
+// Grid: (ceil(H / 128) row tiles, max active experts).  A group of 8 lanes
+// owns output rows rg, rg + 32, ... of the tile (two in flight per step);
+// lane q of the group takes 16-value blocks q, q+8, ...  One token's h is held
+// in registers at a time; an expert's later tokens re-read its weights from L2.
+template <int WFMT, int BPL>
 __global__ void __launch_bounds__(256) gemv_down_kernel(
     const float* __restrict__ h, const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
     const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s, const float* __restrict__ w2s2,
     int H, int I, float* __restrict__ o) {
-  extern __shared__ float s_h[];  // [TB][I]
   const int ai = blockIdx.y;
   if (ai >= active[0]) return;
   const int e = active[1 + ai];
-  const int r0 = offsets[e], n = offsets[e + 1] - r0;
-  const int q = threadIdx.x & 7, rg = threadIdx.x >> 3;  // 32 row groups
+  const int q = threadIdx.x & 7, rg = threadIdx.x >> 3;
   const int NB = I >> 4;
   const int64_t row_bytes = I >> 1;
   const int64_t srow = scale_row_stride<WFMT>(I);
   const uint8_t* wq = w2 + (int64_t)e * H * row_bytes;
   const uint8_t* ws = w2s + (int64_t)e * H * srow;
   const float S = WFMT == FP4_FMT_NVFP4 ? w2s2[e] : 1.0f;
-
-  for (int t0 = 0; t0 < n; t0 += TB) {
-    const int nt = min(TB, n - t0);
-    __syncthreads();
-    for (int i = threadIdx.x; i < TB * I; i += 256) {
-      int t = i / I, c = i - t * I;
-      s_h[i] = t < nt ? h[(int64_t)(r0 + t0 + t) * I + c] : 0.0f;
+  const int n_begin = blockIdx.x * kGdTile, n_end = min(H, n_begin + kGdTile);
+  const int r0 = offsets[e], n = offsets[e + 1] - r0;
+  for (int t = 0; t < n; ++t) {
+    float hv[BPL][16];
+    const float* hrow = h + (int64_t)(r0 + t) * I;
+#pragma unroll
+    for (int i = 0; i < BPL; ++i) {
+      int b = q + 8 * i;
+      if (b < NB) {
+        const float4* src = reinterpret_cast<const float4*>(hrow + b * 16);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          float4 v = src[m];
+          hv[i][4 * m] = v.x; hv[i][4 * m + 1] = v.y; hv[i][4 * m + 2] = v.z; hv[i][4 * m + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) hv[i][m] = 0.0f;
+      }
     }
-    __syncthreads();
-    for (int nn = blockIdx.x * 64 + rg; nn < min(H, (int)blockIdx.x * 64 + 64); nn += 32) {
-      float acc[TB];
+    for (int nn0 = n_begin + rg; nn0 < n_end; nn0 += 64) {
+      const int nn1 = nn0 + 32;
+      const bool has1 = nn1 < n_end;
+      uint2 c0[BPL], c1[BPL];
+      float f0[BPL], f1[BPL];
+      const uint2* q0 = reinterpret_cast<const uint2*>(wq + (int64_t)nn0 * row_bytes);
+      const uint2* q1 = reinterpret_cast<const uint2*>(wq + (int64_t)(has1 ? nn1 : nn0) * row_bytes);
+      const uint8_t* s0 = ws + (int64_t)nn0 * srow;
+      const uint8_t* s1 = ws + (int64_t)(has1 ? nn1 : nn0) * srow;
 #pragma unroll
-      for (int t = 0; t < TB; ++t) acc[t] = 0.0f;
-      const uint8_t* qr = wq + (int64_t)nn * row_bytes;
-      const uint8_t* sr = ws + (int64_t)nn * srow;
-      for (int b = q; b < NB; b += 8) {
-        uint2 c = reinterpret_cast<const uint2*>(qr)[b];
-        float sb = block_scale<WFMT>(sr, b);
-        float wv[16];
+      for (int i = 0; i < BPL; ++i) {
+        int b = q + 8 * i;
+        bool in = b < NB;
+        c0[i] = in ? q0[b] : make_uint2(0u, 0u);
+        c1[i] = in ? q1[b] : make_uint2(0u, 0u);
+        f0[i] = in ? block_scale<WFMT>(s0, b) : 0.0f;
+        f1[i] = in ? block_scale<WFMT>(s1, b) : 0.0f;
+      }
+      float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          uint32_t n0 = (c.x >> (4 * m)) & 15u, n1 = (c.y >> (4 * m)) & 15u;
-          float v0 = e2m1_mag_to_f32(n0 & 7u), v1 = e2m1_mag_to_f32(n1 & 7u);
-          wv[m] = (n0 & 8u) ? -v0 : v0;
-          wv[8 + m] = (n1 & 8u) ? -v1 : v1;
-        }
+      for (int i = 0; i < BPL; ++i) {
+        float w[8], v[8];
+        float d0 = 0.0f, d1 = 0.0f;
+        e2m1x8_to_f32x8(c0[i].x, w);
+        e2m1x8_to_f32x8(c1[i].x, v);
 #pragma unroll
-        for (int t = 0; t < TB; ++t) {
-          const float4* hp = reinterpret_cast<const float4*>(s_h + t * I + b * 16);
-          float d = 0.0f;
+        for (int m = 0; m < 8; ++m) { d0 = fmaf(w[m], hv[i][m], d0); d1 = fmaf(v[m], hv[i][m], d1); }
+        e2m1x8_to_f32x8(c0[i].y, w);
+        e2m1x8_to_f32x8(c1[i].y, v);
 #pragma unroll
-          for (int m4 = 0; m4 < 4; ++m4) {
-            float4 hv = hp[m4];
-            d = fmaf(wv[4 * m4], hv.x, d);
-            d = fmaf(wv[4 * m4 + 1], hv.y, d);
-            d = fmaf(wv[4 * m4 + 2], hv.z, d);
-            d = fmaf(wv[4 * m4 + 3], hv.w, d);
-          }
-          acc[t] = fmaf(d, sb, acc[t]);
-        }
+        for (int m = 0; m < 8; ++m) { d0 = fmaf(w[m], hv[i][8 + m], d0); d1 = fmaf(v[m], hv[i][8 + m], d1); }
+        a0 = fmaf(d0, f0[i], a0);
+        a1 = fmaf(d1, f1[i], a1);
       }
 #pragma unroll
-      for (int t = 0; t < TB; ++t) {
-        acc[t] += __shfl_xor(acc[t], 4, 8);
-        acc[t] += __shfl_xor(acc[t], 2, 8);
-        acc[t] += __shfl_xor(acc[t], 1, 8);
+      for (int off = 4; off > 0; off >>= 1) {
+        a0 += __shfl_xor(a0, off, 8);
+        a1 += __shfl_xor(a1, off, 8);
       }
       if (q == 0) {
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-          if (t < nt) o[(int64_t)(r0 + t0 + t) * H + nn] = acc[t] * S;
+        o[(int64_t)(r0 + t) * H + nn0] = a0 * S;
+        if (has1) o[(int64_t)(r0 + t) * H + nn1] = a1 * S;
       }
     }
   }
@@ -458,7 +491,10 @@ __global__ void __launch_bounds__(256) gemv_down_kernel(
 
 // ------------------------------------------------------------------ combine
 
-// y[t, :] = sum_j w[t, j] * o[row(t, j), :] (+ extra[t, :]), slot order, f32.
+constexpr int kMaxTopK = 32;
+
+// y[t, :] = sum_j w[t, j] * o[row(t, j), :] (+ extra[t, :]), in slot order, f32.
+// All k row indices and weights are read before the o loads are issued.
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o,
                                                       const int32_t* __restrict__ row_of_pair,
                                                       const float* __restrict__ topk_w, int64_t T, int H,
@@ -468,63 +504,70 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   int64_t per_row = H / 4;
   if (i >= T * per_row) return;
   int64_t t = i / per_row, c4 = i - t * per_row;
+  int rows[kMaxTopK];
+  float w[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k) {
+      rows[j] = row_of_pair[t * k + j];
+      w[j] = topk_w[t * k + j];
+    }
+  float4 v[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k && rows[j] >= 0) v[j] = reinterpret_cast<const float4*>(o + (int64_t)rows[j] * H)[c4];
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; ++j) {
-    int row = row_of_pair[t * k + j];
-    if (row < 0) continue;
-    float w = topk_w[t * k + j];
-    float4 v = reinterpret_cast<const float4*>(o + (int64_t)row * H)[c4];
-    acc.x = fmaf(w, v.x, acc.x);
-    acc.y = fmaf(w, v.y, acc.y);
-    acc.z = fmaf(w, v.z, acc.z);
-    acc.w = fmaf(w, v.w, acc.w);
-  }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k && rows[j] >= 0) {
+      acc.x = fmaf(w[j], v[j].x, acc.x);
+      acc.y = fmaf(w[j], v[j].y, acc.y);
+      acc.z = fmaf(w[j], v[j].z, acc.z);
+      acc.w = fmaf(w[j], v[j].w, acc.w);
+    }
   if (extra) {
-    float4 v = reinterpret_cast<const float4*>(extra + t * H)[c4];
-    acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    float4 e = reinterpret_cast<const float4*>(extra + t * H)[c4];
+    acc.x += e.x; acc.y += e.y; acc.z += e.z; acc.w += e.w;
   }
   reinterpret_cast<float4*>(y + t * H)[c4] = acc;
 }
 
 // ---------------------------------------------------------- GEMV dispatch
 
-template <int WFMT, int TB>
-static int launch_gemv_gateup_tb(const uint16_t* x, const WsPtrs& w, const moe_fp4_layer* L,
-                                 int max_active, hipStream_t st) {
-  dim3 grid((unsigned)((L->inter + 31) / 32), (unsigned)max_active);
-  const int NB = L->hidden / 16;
-  const int bpl = (NB + 31) / 32;
-#define FP4_GV(B)                                                                                       \
-  case B:                                                                                               \
-    hipLaunchKernelGGL((gemv_gateup_kernel<WFMT, TB, B>), grid, dim3(256), 0, st, x, w.offsets,         \
-                       w.pair_of_row, w.active, L->w13, (const uint8_t*)L->w13_scale, L->w13_scale_2,  \
-                       L->hidden, L->inter, L->top_k, w.h);                                             \
+template <int WFMT>
+static int launch_gemv(const uint16_t* x, const WsPtrs& w, const moe_fp4_layer* L, int64_t P,
+                       int max_active, hipStream_t st, const Marker& mark) {
+  (void)P;
+  const int bpl = (L->hidden / 16 + 31) / 32;
+  dim3 grid((unsigned)((L->inter + kGvJTile - 1) / kGvJTile), (unsigned)max_active);
+#define FP4_GV(B)                                                                                      \
+  case B:                                                                                              \
+    hipLaunchKernelGGL((gemv_gateup_kernel<WFMT, B>), grid, dim3(256), 0, st, x, w.offsets,            \
+                       w.pair_of_row, w.active, L->w13, (const uint8_t*)L->w13_scale, L->w13_scale_2, \
+                       L->hidden, L->inter, L->top_k, w.h);                                            \
     break;
   switch (bpl) {
     FP4_GV(1) FP4_GV(2) FP4_GV(3) FP4_GV(4) FP4_GV(5) FP4_GV(6) FP4_GV(7) FP4_GV(8)
     default: return fail(FP4_ERR_UNSUPPORTED, "hidden %d too large for the GEMV path", L->hidden);
   }
 #undef FP4_GV
-  return check_launch("gemv_gateup");
-}
-
-template <int WFMT>
-static int launch_gemv(const uint16_t* x, const WsPtrs& w, const moe_fp4_layer* L, int64_t P,
-                       int max_active, hipStream_t st) {
-  const bool small = P <= 2 * (int64_t)L->num_experts;
-  if (small) FP4_CHECK((launch_gemv_gateup_tb<WFMT, 2>(x, w, L, max_active, st)));
-  else FP4_CHECK((launch_gemv_gateup_tb<WFMT, 4>(x, w, L, max_active, st)));
-  dim3 grid((unsigned)((L->hidden + 63) / 64), (unsigned)max_active);
-  if (small) {
-    hipLaunchKernelGGL((gemv_down_kernel<WFMT, 2>), grid, dim3(256), sizeof(float) * 2 * L->inter, st,
-                       w.h, w.offsets, w.active, L->w2, (const uint8_t*)L->w2_scale, L->w2_scale_2,
-                       L->hidden, L->inter, w.o);
-  } else {
-    hipLaunchKernelGGL((gemv_down_kernel<WFMT, 4>), grid, dim3(256), sizeof(float) * 4 * L->inter, st,
-                       w.h, w.offsets, w.active, L->w2, (const uint8_t*)L->w2_scale, L->w2_scale_2,
-                       L->hidden, L->inter, w.o);
+  FP4_CHECK(check_launch("gemv_gateup"));
+  FP4_CHECK(mark(3));
+  FP4_CHECK(mark(4));
+  const int bpl2 = (L->inter / 16 + 7) / 8;
+  dim3 grid2((unsigned)((L->hidden + kGdTile - 1) / kGdTile), (unsigned)max_active);
+#define FP4_GD(B)                                                                                      \
+  case B:                                                                                              \
+    hipLaunchKernelGGL((gemv_down_kernel<WFMT, B>), grid2, dim3(256), 0, st, w.h, w.offsets, w.active, \
+                       L->w2, (const uint8_t*)L->w2_scale, L->w2_scale_2, L->hidden, L->inter, w.o);   \
+    break;
+  switch (bpl2) {
+    FP4_GD(1) FP4_GD(2) FP4_GD(3) FP4_GD(4) FP4_GD(5) FP4_GD(6) FP4_GD(7) FP4_GD(8)
+    default: return fail(FP4_ERR_UNSUPPORTED, "inter %d too large for the GEMV path", L->inter);
   }
-  return check_launch("gemv_down");
+#undef FP4_GD
+  FP4_CHECK(check_launch("gemv_down"));
+  return mark(5);
 }
 
 WsPtrs ws_pointers(const WsPlan& p, void* base) {
@@ -561,7 +604,7 @@ static int validate_layer(const moe_fp4_layer* L, int64_t T) {
   if (T < 0) return fail(FP4_ERR_SHAPE, "negative token count");
   if (L->num_experts < 1 || L->hidden < 1 || L->inter < 1)
     return fail(FP4_ERR_SHAPE, "experts, hidden and inter must be positive");
-  if (L->top_k < 1 || L->top_k > L->num_experts)
+  if (L->top_k < 1 || L->top_k > L->num_experts || L->top_k > kMaxTopK)
     return fail(FP4_ERR_INVALID_ARG, "top_k %d outside [1, %d]", L->top_k, L->num_experts);
   if (L->num_experts > kMaxExperts) return fail(FP4_ERR_UNSUPPORTED, "more than %d experts", kMaxExperts);
   const int w = L->w_fmt, a = L->a_fmt;
@@ -618,9 +661,9 @@ int moe_fp4_workspace_size(const moe_fp4_layer* layer, int64_t tokens, size_t* b
   return FP4_OK;
 }
 
-int moe_fp4_forward(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const int32_t* topk_ids,
-                    const float* topk_weights, float* y, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+static int forward_impl(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const int32_t* topk_ids,
+                        const float* topk_weights, float* y, void* workspace, size_t workspace_bytes,
+                        void* stream, void* const* events) {
   FP4_CHECK(validate_layer(L, T));
   if (T == 0) return FP4_OK;
   if (!x || !topk_ids || !topk_weights || !y) return fail(FP4_ERR_INVALID_ARG, "null tensor pointer");
@@ -635,27 +678,48 @@ int moe_fp4_forward(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const 
   if (!workspace || workspace_bytes < p.total)
     return fail(FP4_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, p.total);
   hipStream_t st = as_stream(stream);
+  const Marker mark{events, st};
   WsPtrs w = ws_pointers(p, workspace);
   const int64_t P = T * L->top_k;
   const int max_active = (int)std::min<int64_t>(L->num_experts, P);
 
+  FP4_CHECK(mark(0));
   FP4_CHECK(launch_permute(topk_ids, P, L->num_experts, kGemmTileM, w, st));
-
+  FP4_CHECK(mark(1));
   if (L->a_fmt == FP4_FMT_NONE) {
-    if (L->w_fmt == FP4_FMT_NVFP4) FP4_CHECK(launch_gemv<FP4_FMT_NVFP4>(x, w, L, P, max_active, st));
-    else FP4_CHECK(launch_gemv<FP4_FMT_MXFP4>(x, w, L, P, max_active, st));
+    FP4_CHECK(mark(2));
+    if (L->w_fmt == FP4_FMT_NVFP4) FP4_CHECK(launch_gemv<FP4_FMT_NVFP4>(x, w, L, P, max_active, st, mark));
+    else FP4_CHECK(launch_gemv<FP4_FMT_MXFP4>(x, w, L, P, max_active, st, mark));
   } else {
-    FP4_CHECK(launch_grouped(L, x, T, w, max_active, st));
+    FP4_CHECK(launch_grouped(L, x, T, w, max_active, st, mark));
   }
   const float* extra = nullptr;
   if (L->shared_inter > 0) {
     FP4_CHECK(launch_shared_expert(L, x, T, w, st));
     extra = w.s_out;
   }
+  FP4_CHECK(mark(6));
   int64_t n4 = T * L->hidden / 4;
   hipLaunchKernelGGL(combine_kernel, dim3(grid_1d(n4, 256)), dim3(256), 0, st, w.o, w.row_of_pair,
                      topk_weights, T, L->hidden, L->top_k, extra, y);
-  return check_launch("combine");
+  FP4_CHECK(check_launch("combine"));
+  return mark(7);
+}
+
+int moe_fp4_forward(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const int32_t* topk_ids,
+                    const float* topk_weights, float* y, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return forward_impl(L, x, T, topk_ids, topk_weights, y, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_fp4_forward_profiled(const moe_fp4_layer* L, const uint16_t* x, int64_t T,
+                             const int32_t* topk_ids, const float* topk_weights, float* y,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* events, int n_events) {
+  if (!events || n_events != 8) return fail(FP4_ERR_INVALID_ARG, "profiled forward needs 8 events");
+  for (int i = 0; i < 8; ++i)
+    if (!events[i]) return fail(FP4_ERR_INVALID_ARG, "null event %d", i);
+  return forward_impl(L, x, T, topk_ids, topk_weights, y, workspace, workspace_bytes, stream, events);
 }
 
 }  // extern "C"

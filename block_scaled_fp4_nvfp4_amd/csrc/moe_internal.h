@@ -34,12 +34,23 @@ struct WsPtrs {
   float* s_out;
 };
 
+// Records the caller's stage events (moe_fp4_forward_profiled); no-op without events.
+struct Marker {
+  void* const* events;
+  hipStream_t st;
+  int operator()(int i) const {
+    if (events && hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), st) != hipSuccess)
+      return FP4_ERR_HIP;
+    return FP4_OK;
+  }
+};
+
 int plan_workspace(const moe_fp4_layer* L, int64_t T, WsPlan* w);
 WsPtrs ws_pointers(const WsPlan& p, void* base);
 
 // grouped MFMA path (quantized activations): steps 2-5 of the forward
 int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const WsPtrs& w,
-                   int max_active, hipStream_t st);
+                   int max_active, hipStream_t st, const Marker& mark);
 // shared expert: writes sigmoid(x . g) * shared(x) to w.s_out [T, H]
 int launch_shared_expert(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const WsPtrs& w,
                          hipStream_t st);

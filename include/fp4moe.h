@@ -183,6 +183,20 @@ int moe_fp4_forward(const moe_fp4_layer* layer, const uint16_t* x, int64_t token
                     const int32_t* topk_ids, const float* topk_weights, float* y,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * moe_fp4_forward_profiled - moe_fp4_forward that also records HIP events
+ * (hipEvent_t, created by the caller) on `stream` at the stage boundaries, for
+ * per-kernel timing: events[0] before the first launch, then after the
+ * permutation [1], activation quantization [2], gate_up [3], quantization of
+ * h [4], down [5], shared expert [6] and combine [7].  A stage that does not
+ * run in the layer's mode still gets its event (zero duration).  n_events
+ * must be 8.
+ */
+int moe_fp4_forward_profiled(const moe_fp4_layer* layer, const uint16_t* x, int64_t tokens,
+                             const int32_t* topk_ids, const float* topk_weights, float* y,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             void* const* events, int n_events);
+
 const char* fp4_status_string(int status);
 const char* fp4_last_error(void);
 

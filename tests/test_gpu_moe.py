@@ -140,3 +140,19 @@ def test_decode_layer_sampled_tokens(decode_layer):
     off, por, _ = moe.permute(ids, cfg.num_experts)
     np.testing.assert_array_equal(_ws_i32(ws, lay["pair_of_row"], cfg.pairs), por)
     assert np.all(np.isfinite(y)) and np.linalg.norm(y) > 0
+
+
+def test_many_tokens_uses_multipass_permutation(tiny):
+    """1200 pairs (> 1024) go through the three-pass permutation."""
+    print_case("tiny layer, 600 tokens")
+    cfg, w13, w2, _, _, _ = tiny
+    c = cfg.replace(tokens=600, input_seed=11)
+    x = synth.activations(c)
+    ids, wts = synth.routing(c)
+    y, ws, lay = _run(gpu_layer(c, w13, w2), x, ids, wts)
+    off, por, rop = moe.permute(ids, c.num_experts)
+    np.testing.assert_array_equal(_ws_i32(ws, lay["offsets"], c.num_experts + 1), off)
+    np.testing.assert_array_equal(_ws_i32(ws, lay["pair_of_row"], c.pairs), por)
+    np.testing.assert_array_equal(_ws_i32(ws, lay["row_of_pair"], c.pairs), rop)
+    y_ref = moe.moe_forward(OracleLayer(c, w13, w2).as_dict(), x, ids, wts)
+    assert rel_fro(y, y_ref) < 1e-5
