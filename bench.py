@@ -11,7 +11,10 @@ that successive steps cannot be served by the 256 MB Infinity Cache (a
 One JSON line: metric, value (tokens/s), ms_per_step, the roofline of the
 dominant kernel (gate_up: algorithmic bytes / its average HIP-event duration
 against 8 TB/s), per-stage times, and the CPU oracle timed on a bounded token
-sample of the same workload.  Other workloads: --workload.
+sample of the same workload.  The other workloads of the layer (8192-token
+prefill in NVFP4 W4A4 with the MXFP8 shared expert, MXFP4 x MXFP8, block FP8,
+and the 48-layer streaming 4/6 quantization) are reported in the same line
+under "workloads", each with its own roofline and oracle baseline.
 """
 from __future__ import annotations
 
@@ -67,10 +70,28 @@ def build_layer(cfg, torch, pkg):
     return q13, q2
 
 
-def make_layer(cfg, q13, q2, pkg):
-    return pkg.MoELayer(cfg.w_fmt, cfg.a_fmt, cfg.num_experts, cfg.hidden, cfg.inter, cfg.top_k,
-                        q13["codes"], q13["scales"], q2["codes"], q2["scales"],
-                        q13.get("tensor_scale"), q2.get("tensor_scale"))
+def make_layer(cfg, q13, q2, pkg, shared=None):
+    layer = pkg.MoELayer(cfg.w_fmt, cfg.a_fmt, cfg.num_experts, cfg.hidden, cfg.inter, cfg.top_k,
+                         q13["codes"], q13["scales"], q2["codes"], q2["scales"],
+                         q13.get("tensor_scale"), q2.get("tensor_scale"))
+    if shared is not None:
+        a, b, gate = shared
+        layer.shared_inter = cfg.shared_inter
+        layer.ws13, layer.ws13_scale = a["codes"], a["scales"]
+        layer.ws2, layer.ws2_scale = b["codes"], b["scales"]
+        layer.shared_gate = gate
+    return layer
+
+
+def build_shared(cfg, torch, pkg):
+    import numpy as np
+
+    import synth
+    s13, s2, gate = synth.shared_expert(cfg)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+    return pkg.quantize(up(s13), "mxfp8"), pkg.quantize(up(s2), "mxfp8"), up(gate)
 
 
 def clone_q(q):
@@ -78,7 +99,8 @@ def clone_q(q):
 
 
 def cpu_baseline(cfg, ids, wts, x_bits, budget_s=20.0):
-    """The oracle (float64 numpy) on the first tokens of the same workload."""
+    """The oracle (float64 numpy) on the first token of the same workload (for
+    NVFP4 activations the tensor scales then come from that token's rows)."""
     import numpy as np
 
     import synth
@@ -91,8 +113,13 @@ def cpu_baseline(cfg, ids, wts, x_bits, budget_s=20.0):
     pos = {e: i for i, e in enumerate(touched)}
     q13 = {e: moe.quantize_expert_weight(w13[pos[e]], cfg.w_fmt, cfg.rule) for e in touched}
     q2 = {e: moe.quantize_expert_weight(w2[pos[e]], cfg.w_fmt, cfg.rule) for e in touched}
-    layer = dict(w_fmt=cfg.w_fmt, a_fmt=cfg.a_fmt, num_experts=cfg.num_experts, hidden=cfg.hidden,
+    layer = dict(w_fmt=cfg.w_fmt, a_fmt=cfg.a_fmt,
+                 num_experts=cfg.num_experts, hidden=cfg.hidden,
                  inter=cfg.inter, w13=lambda e: q13[e], w2=lambda e: q2[e])
+    if cfg.shared_inter:
+        s13, s2, gate = synth.shared_expert(cfg)
+        layer["shared"] = dict(w13=moe.quantize_expert_weight(s13, "mxfp8"),
+                               w2=moe.quantize_expert_weight(s2, "mxfp8"), gate_bits=gate)
     ids_s, wts_s, x_s = ids[:n], wts[:n], x_bits[:n]
     t0 = time.perf_counter()
     reps = 0
@@ -184,12 +211,177 @@ def bench_decode(args, torch, pkg):
     return out
 
 
+def time_steps(pkg, torch, layers, x, tid, tw, ws, y, steps, warmup):
+    for i in range(warmup):
+        pkg.moe_forward(layers[i % len(layers)], x, tid, tw, ws, y)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        pkg.moe_forward(layers[i % len(layers)], x, tid, tw, ws, y)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    timer = pkg.StageTimer()
+    acc = {s_: 0.0 for s_ in pkg.STAGES}
+    for i in range(steps):
+        pkg.moe_forward_profiled(layers[i % len(layers)], x, tid, tw, ws, y, timer)
+        torch.cuda.synchronize()
+        for k_, v in timer.durations().items():
+            acc[k_] += v
+    return ms, {k_: v / steps for k_, v in acc.items()}
+
+
+def bench_prefill(name, args, torch, pkg):
+    import numpy as np
+
+    import synth
+    cfg = synth.CONFIGS[name]
+    T, P, H, I = cfg.tokens, cfg.pairs, cfg.hidden, cfg.inter
+    q13, q2 = build_layer(cfg, torch, pkg)
+    shared = build_shared(cfg, torch, pkg) if cfg.shared_inter else None
+    layers = [make_layer(cfg, q13, q2, pkg, shared)]
+    for _ in range(max(0, args.prefill_copies - 1)):
+        layers.append(make_layer(cfg, clone_q(q13), clone_q(q2), pkg, shared))
+    x_bits = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    tid, tw = torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()
+    ws = torch.empty(pkg.workspace_size(layers[0], T), dtype=torch.uint8, device="cuda")
+    y = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    ms, stages = time_steps(pkg, torch, layers, x, tid, tw, ws, y, args.prefill_steps, 2)
+    flops_gu = 4.0 * P * H * I
+    flops_down = 2.0 * P * H * I
+    flops_shared = 6.0 * T * H * cfg.shared_inter
+    counts = np.bincount(ids.reshape(-1), minlength=cfg.num_experts)
+    touched = int((counts > 0).sum())
+    b13, b2 = expert_bytes(cfg)
+    weight_bytes = touched * (b13 + b2)
+    peak_key = "bf16" if cfg.a_fmt == "nvfp4" else "fp8"
+    peak = MFMA_PEAK_TFLOPS[peak_key]
+    gu_ms = stages["gate_up"]
+    roof = {"bound": "mfma", "kernel": "grouped_gemm_kernel (gate_up)", "mfma_dtype":
+            {"bf16": "fp16 (exact NVFP4 decode)", "fp8": "fp8 x fp4" if cfg.w_fmt == "mxfp4" else "fp8"}[peak_key],
+            "achieved": flops_gu / (gu_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s", "traffic": None,
+            "flops_per_launch": flops_gu,
+            "unit_of_work": f"{P} (token, expert) rows x 2 x {2 * I} x {H} FLOPs"}
+    roof["frac"] = roof["achieved"] / peak
+    total_flops = flops_gu + flops_down + flops_shared
+    out = {"workload": f"{cfg.name}: {cfg.num_experts} experts, top-{cfg.top_k}, hidden {H}, inter {I}, "
+                       f"{T} tokens, {cfg.w_fmt} weights x {cfg.a_fmt} activations"
+                       + (f", MXFP8 shared expert {cfg.shared_inter}" if cfg.shared_inter else ""),
+           "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "steps": args.prefill_steps,
+           "dtype": {"nvfp4": "fp16", "mxfp8": "fp8", "fp8_row": "fp8"}[cfg.a_fmt],
+           "roofline": roof, "stages_ms": stages,
+           "step_mfma": {"flops": total_flops, "TFLOPs": total_flops / (ms * 1e-3) / 1e12,
+                         "frac_of_peak": total_flops / (ms * 1e-3) / 1e12 / peak},
+           "step_hbm": {"weight_bytes": weight_bytes, "touched_experts": touched,
+                        "max_rows_per_expert": int(counts.max())}}
+    if not args.no_cpu_baseline:
+        log(f"timing the CPU oracle on {name}")
+        out["cpu_baseline"] = cpu_baseline(cfg, ids, wts, x_bits, args.cpu_budget)
+    del layers, q13, q2
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_stream_quant(args, torch, pkg):
+    """48 layers x 512 experts x (gate_up 1280x2560, down 2560x640) NVFP4 4/6
+    quantization, one layer at a time, from bf16 Student-t (nu=4) source with
+    1% outlier rows x8 generated on the device for each layer."""
+    import numpy as np
+    E, H, I = 512, 2560, 640
+    layers = args.stream_layers
+    gen = torch.Generator(device="cuda")
+    tdist = torch.distributions.StudentT(torch.tensor(4.0, device="cuda"))
+
+    def source(layer, rows, cols):
+        gen.manual_seed(1000 + layer * 7 + rows)
+        torch.manual_seed(2000 + layer * 7 + rows)
+        v = tdist.sample((E, rows, cols)) * (0.02 / 2 ** 0.5)
+        n_out = int(round(0.01 * rows))
+        idx = torch.argsort(torch.rand(E, rows, device="cuda", generator=gen), dim=1)[:, :n_out]
+        v.scatter_(1, idx[:, :, None].expand(E, n_out, cols), v.gather(1, idx[:, :, None].expand(E, n_out, cols)) * 8)
+        return v.to(torch.bfloat16)
+
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total_ms = 0.0
+    stats = []
+    rd = wr = 0
+    for layer in range(layers):
+        w13 = source(layer, 2 * I, H)
+        w2 = source(layer, H, I)
+        torch.cuda.synchronize()
+        want = layer in (0, layers - 1)
+        start.record()
+        q13 = pkg.quantize(w13, "nvfp4", "4over6", want_m4=want)
+        q2 = pkg.quantize(w2, "nvfp4", "4over6", want_m4=want)
+        stop.record()
+        torch.cuda.synchronize()
+        total_ms += start.elapsed_time(stop)
+        for w, q in ((w13, q13), (w2, q2)):
+            rd += w.numel() * 2
+            wr += q["codes"].numel() + q["scales"].numel() + q["tensor_scale"].numel() * 4
+        if want:
+            for w, q, names in ((w13, q13, ("gate", "up")), (w2, q2, ("down",))):
+                xh = pkg.dequantize(q, "nvfp4", w.shape, torch.float32)
+                src = w.float()
+                parts = [(n, sl) for n, sl in zip(names, (slice(0, I), slice(I, 2 * I)))] if len(names) == 2 \
+                    else [("down", slice(0, H))]
+                for n, sl in parts:
+                    d = (xh[:, sl] - src[:, sl]).pow(2).sum(dim=(1, 2))
+                    nrm = src[:, sl].pow(2).sum(dim=(1, 2))
+                    rel = (d / nrm).sqrt()
+                    stats.append((n, float(rel.mean()), float(rel.max()), float(q["m4"][:, sl].float().mean()),
+                                  float(d.sum()), float(nrm.sum())))
+                del xh, src
+        del w13, w2, q13, q2
+    ms_layer = total_ms / layers
+    bytes_layer = (rd + wr) / layers
+    gbs = bytes_layer / (ms_layer * 1e-3) / 1e9
+    out = {"workload": f"streaming NVFP4 4/6 quantization: {layers} layers x {E} experts x "
+                       f"(gate_up {2 * I}x{H}, down {H}x{I}), bf16 Student-t(4) source with 1% outlier rows x8",
+           "value": gbs, "unit": "GB/s", "ms_per_layer": ms_layer, "layers": layers,
+           "values_per_layer": E * 3 * H * I,
+           "roofline": {"bound": "hbm", "kernel": "quant_fp4_kernel + tensor_amax_kernel",
+                        "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                        "traffic": None, "bytes_per_layer": bytes_layer,
+                        "unit_of_work": "2 B read + 0.5625 B written per value (+4 B per tensor)"},
+           "quality": {"per_tensor_rel_err": {n: {"mean": m, "max": mx} for n, m, mx, _, _, _ in stats},
+                       "m4_fraction": float(np.mean([f for _, _, _, f, _, _ in stats]))}}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on streaming quantization")
+        import synth
+        from oracle import quant
+        from oracle.formats import bf16_to_f64
+        t0 = time.perf_counter()
+        n_vals = 0
+        e = 0
+        while time.perf_counter() - t0 < args.cpu_budget and e < 64:
+            w13, w2 = synth.streaming_expert(0, e)
+            for w in (w13, w2):
+                quant.quantize_nvfp4(bf16_to_f64(w), "4over6")
+                n_vals += w.size
+            e += 1
+        el = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": n_vals * 2.5625 / el / 1e9, "unit": "GB/s", "values_per_s": n_vals / el,
+                               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                               "sample": f"{e} expert(s) of layer 0 (gate_up + down), source drawn on the host, "
+                                         f"{el:.1f} s"}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode"])
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "decode", "prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant"],
+                    help="'all': the decode headline plus every other workload under 'workloads'")
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--prefill-copies", type=int, default=2)
+    ap.add_argument("--stream-layers", type=int, default=48)
     ap.add_argument("--copies", type=int, default=8,
                     help="resident copies of the quantized layer rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -207,7 +399,33 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
-    out = bench_decode(args, torch, pkg)
+    if args.workload in ("all", "decode"):
+        dargs = argparse.Namespace(**vars(args))
+        dargs.workload = "decode"
+        out = bench_decode(dargs, torch, pkg)
+        torch.cuda.empty_cache()
+        others = ["prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant"] if args.workload == "all" else []
+    else:
+        out = None
+        others = [args.workload]
+    extra = {}
+    for name in others:
+        log(f"workload {name}")
+        extra[name] = bench_stream_quant(args, torch, pkg) if name == "stream_quant" else bench_prefill(name, args, torch, pkg)
+        torch.cuda.empty_cache()
+    if out is None:
+        name = others[0]
+        w = extra[name]
+        out = {"metric": METRIC, "value": w["value"], "unit": w["unit"], "n_gpus": 1,
+               "steps": w.get("steps", w.get("layers")), "warmup": 2,
+               "ms_per_step": w.get("ms_per_step", w.get("ms_per_layer")), "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": w.get("dtype", "bf16"), "data": "synthetic",
+               "config": {"workload": w["workload"]}, "roofline": w["roofline"]}
+        if "cpu_baseline" in w:
+            out["cpu_baseline"] = w["cpu_baseline"]
+        out["workloads"] = {name: w}
+    else:
+        out["workloads"] = extra
     print(json.dumps(out), flush=True)
 
 

@@ -101,7 +101,9 @@ __global__ void fill_u32_kernel(uint32_t* p, uint32_t v, int64_t n) {
 }
 
 // amax of each tensor (batch item) as float bits, combined with atomicMax on
-// the bit pattern (non-negative floats order like their bit patterns).
+// the bit pattern (non-negative floats order like their bit patterns).  Each
+// workgroup reduces in LDS first, so a tensor receives one atomic per
+// workgroup (a few per CU) rather than one per wave.
 template <typename T>
 __global__ void __launch_bounds__(256) tensor_amax_kernel(const T* x, int64_t per_tensor,
                                                           uint32_t* amax_bits) {
@@ -115,7 +117,13 @@ __global__ void __launch_bounds__(256) tensor_amax_kernel(const T* x, int64_t pe
     for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
   }
   m = wave_max(m);
-  if ((threadIdx.x & 63) == 0 && m > 0.0f) atomicMax(amax_bits + blockIdx.y, __float_as_uint(m));
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (a > 0.0f) atomicMax(amax_bits + blockIdx.y, __float_as_uint(a));
+  }
 }
 
 // S = fp32(fp64(amax) / 2688), in place over the amax bits.
@@ -473,8 +481,9 @@ int quantize_typed(int fmt, int rule, int ts_mode, const T* x, int64_t batch, in
     const int64_t bpt = per / bs;
     if (!mx && ts_mode == FP4_TS_DYNAMIC) {
       FP4_CHECK(launch_fill(reinterpret_cast<uint32_t*>(tensor_scale), 0u, batch, st));
+      // about 4 workgroups per CU in total, at least one per tensor
       int64_t chunks = (per / 8 + 255) / 256;
-      int64_t target = 4LL * device_cu_count() * 8 / (batch > 0 ? batch : 1);
+      int64_t target = 4LL * device_cu_count() / (batch > 0 ? batch : 1);
       unsigned gx = (unsigned)std::max<int64_t>(1, std::min<int64_t>(chunks, std::max<int64_t>(target, 1)));
       for (int64_t b0 = 0; b0 < batch; b0 += 65535) {
         unsigned gy = (unsigned)std::min<int64_t>(65535, batch - b0);

@@ -12,7 +12,8 @@ dynamic activation quantizers of the mode: identity for bf16 activations
 scale amax/2688 and plain amax/6 block scales (W4A4; "Local-Hessian NVFP4
 experts", opening section), MXFP8 per 32 ("MXFP4-FP8-R12", section
 "Quantization format"), or FP8 with one fp32 scale per (row, 128 columns)
-(the "Dynamic-FP8 routed-expert path", same card, runtime contract table).
+(the "Dynamic-FP8 routed-expert path", same card, runtime contract table;
+a_fmt "fp8_row").
 The fused gate_up weight holds gate rows first, then up rows (dabsLabs card:
 experts stored stacked as [512, out, in] with fused gate_up).  The shared
 expert ("FP4-Local AZ", section "The shared expert") is MXFP8 with MXFP8
@@ -104,7 +105,7 @@ def quantize_activation(v, a_fmt: str):
     if a_fmt == "mxfp8":
         q = quant.quantize_mxfp8(v)
         return quant.dequantize_mxfp8(q["codes"], q["scales"]), q
-    if a_fmt == "fp8_block":
+    if a_fmt in ("fp8_row", "fp8_block"):
         q = quant.quantize_fp8_rows(v)
         return quant.dequantize_fp8_rows(q["codes"], q["scales"]), q
     raise ValueError(a_fmt)

@@ -51,7 +51,7 @@ class MoEConfig:
     inter: int
     tokens: int
     w_fmt: str            # "nvfp4" | "mxfp4" | "fp8_block"
-    a_fmt: str            # "none" | "nvfp4" | "mxfp8" | "fp8_block"
+    a_fmt: str            # "none" | "nvfp4" | "mxfp8" | "fp8_row"
     rule: str = "4over6"  # weight block-scale rule: "4over6" | "rtn"
     router_bias: bool = False
     shared_inter: int = 0  # 0: no shared expert
@@ -82,7 +82,7 @@ CONFIGS = {
                                "mxfp4", "mxfp8", input_seed=4),
     # same inputs through the block-FP8 copy of the layer
     "prefill_fp8": MoEConfig("prefill_fp8", 512, 10, 2560, 640, 8192,
-                             "fp8_block", "fp8_block", input_seed=4),
+                             "fp8_block", "fp8_row", input_seed=4),
 }
 
 

@@ -26,10 +26,6 @@ def _run(layer, x_bits, ids, wts):
     return host(y), ws, m.workspace_layout(layer, T)
 
 
-def _oracle_fmt(a_fmt):
-    return {"fp8_row": "fp8_block"}.get(a_fmt, a_fmt)
-
-
 @pytest.fixture(scope="module")
 def tiny():
     cfg = synth.CONFIGS["tiny"]
@@ -43,7 +39,7 @@ def test_tiny_quantized_activations(tiny, w_fmt, a_fmt):
     cfg, w13, w2, x, ids, wts = tiny
     cfg = cfg.replace(w_fmt=w_fmt, a_fmt=a_fmt)
     y, ws, lay = _run(gpu_layer(cfg, w13, w2), x, ids, wts)
-    ol = OracleLayer(cfg.replace(a_fmt=_oracle_fmt(a_fmt)), w13, w2)
+    ol = OracleLayer(cfg, w13, w2)
     y_ref, st = moe.moe_forward(ol.as_dict(), x, ids, wts, return_stages=True)
     err = rel_fro(y, y_ref)
     print(f"relative Frobenius error {err:.3e}")
@@ -127,3 +123,54 @@ def test_tiny_invalid_ids_w4a4(tiny):
     y, ws, lay = _run(gpu_layer(cfg, w13, w2), x, bad, wts)
     assert host(ws[lay["error_flag"]:lay["error_flag"] + 4].view(torch.int32))[0] == 1
     assert np.all(np.isfinite(y))
+
+
+# ------------------------------------------------------------ full-size layers
+
+GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden",
+                                    "prefill_nvfp4_sampled.npz")
+
+
+@pytest.fixture(scope="module")
+def prefill_weights():
+    cfg = synth.CONFIGS["prefill_nvfp4"]
+    return synth.layer_weights(cfg)
+
+
+def test_prefill_nvfp4_full_size_sampled(prefill_weights):
+    """8192 tokens, top-5, biased router, NVFP4 W4A4 + MXFP8 shared expert 1280,
+    in the benchmark's launch configuration; sampled tokens against the stored
+    oracle outputs (tests/golden/make_prefill_golden.py)."""
+    print_case("prefill NVFP4 W4A4 full size")
+    cfg = synth.CONFIGS["prefill_nvfp4"]
+    gold = np.load(GOLDEN)
+    w13, w2 = prefill_weights
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    np.testing.assert_array_equal(np.bincount(ids.reshape(-1), minlength=cfg.num_experts), gold["counts"])
+    y, ws, lay = _run(gpu_layer(cfg, w13, w2, shared=synth.shared_expert(cfg)), x, ids, wts)
+    sx = host(ws[lay["x_tensor_scale"]:lay["x_tensor_scale"] + 4].view(torch.float32))[0]
+    assert sx == gold["s_x"]          # amax/2688 over all of x: exact
+    sh = host(ws[lay["h_tensor_scale"]:lay["h_tensor_scale"] + 4].view(torch.float32))[0]
+    assert abs(sh / gold["s_h"] - 1) < 1e-5
+    err = rel_fro(y[gold["sample"]], gold["y"])
+    print(f"relative Frobenius error on sampled tokens {err:.3e}")
+    assert err <= TOL
+    assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("name", ["prefill_mxfp4", "prefill_fp8"])
+def test_prefill_full_size_sampled(prefill_weights, name):
+    """8192 tokens, top-10: MXFP4 x MXFP8 and the block-FP8 copy; the oracle
+    computes sampled tokens directly (no whole-tensor activation scale)."""
+    print_case(f"{name} full size")
+    cfg = synth.CONFIGS[name]
+    w13, w2 = prefill_weights  # same bf16 source weights (shared seed)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    y, _, _ = _run(gpu_layer(cfg, w13, w2), x, ids, wts)
+    sample = [0, 4095, 8191]
+    y_ref = moe.moe_forward(OracleLayer(cfg, w13, w2).as_dict(), x, ids, wts, sample_tokens=sample)
+    err = rel_fro(y[sample], y_ref)
+    print(f"relative Frobenius error on sampled tokens {err:.3e}")
+    assert err <= TOL

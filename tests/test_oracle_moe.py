@@ -110,7 +110,7 @@ def test_activation_tensor_scale_is_amax_over_2688(tiny):
 
 
 @pytest.mark.parametrize("w_fmt,a_fmt", [("nvfp4", "none"), ("nvfp4", "nvfp4"),
-                                         ("mxfp4", "mxfp8"), ("fp8_block", "fp8_block")])
+                                         ("mxfp4", "mxfp8"), ("fp8_block", "fp8_row")])
 def test_quantized_layer_differs_by_a_plausible_amount(tiny, w_fmt, a_fmt):
     cfg, w13, w2, x, ids, wts = tiny
     layer, _, _ = _layer(cfg, w13, w2, w_fmt=w_fmt, a_fmt=a_fmt)
