@@ -50,6 +50,11 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 enum { GK_NV = 0, GK_MX = 1, GK_FP8 = 2 };
 enum { EPI_GATEUP = 0, EPI_DOWN = 1 };
@@ -110,24 +115,54 @@ __device__ __forceinline__ half8_t as_half8(const uint32_t* p) {
 }
 
 // ------------------------------------------------------------------ kernel
+//
+// One workgroup = 4 waves computes a 64-row x (64 * NSUB)-output tile of one
+// expert.  All waves share the tile's 64 activation rows; wave w owns outputs
+// [16 NSUB w, 16 NSUB (w+1)) of the tile (for gate_up: those gate rows and the
+// matching up rows).  Per 128-wide K step the workgroup stages the packed
+// operands and their scales in LDS (double buffered: the next step's global
+// loads are in flight while the current step's MFMAs run); NVFP4 activations
+// are decoded to fp16 once, on their way into LDS.
 
-template <int GK, int EPI>
+template <int GK, int EPI, int NSUB, bool WFP8>
+struct TileCfg {
+  static constexpr int BM = kBM;
+  static constexpr int BN = 64 * NSUB;                              // outputs per tile
+  static constexpr int NU = EPI == EPI_GATEUP ? 2 : 1;
+  static constexpr int WROWS = NU * BN;                             // weight rows per tile
+  static constexpr int W_STRIDE = WFP8 ? 128 + 16 : 64 + 16;       // weight row in LDS (bytes)
+  static constexpr int W_CPR = WFP8 ? 8 : 4;                        // 16-byte chunks per row per K step
+  static constexpr int A_BYTES = GK == GK_NV ? 256 : 128;           // per row per K step in LDS
+  static constexpr int A_STRIDE = A_BYTES + 16;
+  static constexpr int W_SCALE_BYTES = GK == GK_NV ? 8 : 4;        // per row per K step
+  static constexpr int A_SCALE_BYTES = 4;
+  static constexpr size_t STAGE =
+      ((size_t)BM * A_STRIDE + (size_t)BM * A_SCALE_BYTES + (size_t)WROWS * W_STRIDE + (size_t)WROWS * W_SCALE_BYTES +
+       15) / 16 * 16;
+};
+
+template <int GK, int EPI, int NSUB, bool WFP8>
 __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
-  extern __shared__ int s_toff[];  // [E + 1] tile offsets (routed mode)
-  const int NT = g.N / kBN;
-  // XCD-aware order: hardware places workgroup i on XCD i % 8; give each XCD
-  // a contiguous range of logical tiles.
+  using C = TileCfg<GK, EPI, NSUB, WFP8>;
+  constexpr int BM = C::BM, BN = C::BN, NU = C::NU, WROWS = C::WROWS;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  constexpr bool w_fp8 = WFP8;
+  constexpr int w_stride = C::W_STRIDE;
+  constexpr int w_cpr = C::W_CPR;
+  constexpr size_t stage = C::STAGE;
+  int* s_toff = reinterpret_cast<int*>(lds + 2 * stage);
+
+  const int NT = g.N / BN;
   const int G = gridDim.x;
   const int per_xcd = G / 8;
   const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 
-  int e, mt, nt;
-  int r_begin, n_rows;
+  int e, mt, nt, r_begin, n_rows;
   if (g.dense_rows > 0) {
     e = 0;
     nt = L % NT;
     mt = L / NT;
-    if (mt * kBM >= g.dense_rows) return;
+    if (mt * BM >= g.dense_rows) return;
     r_begin = 0;
     n_rows = g.dense_rows;
   } else {
@@ -147,174 +182,266 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
     n_rows = g.offsets[e + 1] - r_begin;
   }
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
   const int K = g.K;
-  const int NW = EPI == EPI_GATEUP ? 2 * g.N : g.N;  // weight rows per expert
-
-  // A rows handled by this lane (two 16-row subtiles)
-  const uint8_t* a_ptr[2];
-  bool a_ok[2];
-  int a_row[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int rr = mt * kBM + wm * 32 + i * 16 + lr;  // row within the expert
-    a_ok[i] = rr < n_rows;
-    int R = r_begin + (a_ok[i] ? rr : 0);
-    int arow = g.a_gather ? g.pair_of_row[R] / g.k : R;
-    a_row[i] = arow;
-    int64_t rb = GK == GK_NV ? (int64_t)K / 2 : (int64_t)K;
-    a_ptr[i] = g.a_codes + (int64_t)arow * rb;
-  }
-  // weight rows handled by this lane: [n-subtile j][gate/up u]
-  constexpr int NU = EPI == EPI_GATEUP ? 2 : 1;
-  int w_row[2][NU];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int u = 0; u < NU; ++u) w_row[j][u] = u * g.N + nt * kBN + wn * 32 + j * 16 + lr;
-  const int64_t w_rb = (GK == GK_NV || (GK == GK_MX && !g.w_fp8)) ? (int64_t)K / 2 : (int64_t)K;
+  const int KS = K / kBK;
+  const int NW = NU * g.N;  // weight rows per expert
+  const int64_t a_rb = GK == GK_NV ? (int64_t)K / 2 : (int64_t)K;
+  const int64_t w_rb = w_fp8 ? (int64_t)K : (int64_t)K / 2;
   const uint8_t* w_base = g.w_codes + (int64_t)e * NW * w_rb;
 
-  floatx4 acc[2][2][NU];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int u = 0; u < NU; ++u) acc[i][j][u] = floatx4{0.f, 0.f, 0.f, 0.f};
+  auto a_row_of = [&](int r, bool& ok) __attribute__((always_inline)) -> int {
+    const int rr = mt * BM + r;
+    ok = rr < n_rows;
+    const int R = r_begin + (ok ? rr : 0);
+    return g.a_gather ? g.pair_of_row[R] / g.k : R;
+  };
+  auto w_grow = [&](int i) __attribute__((always_inline)) -> int { return (i / BN) * g.N + nt * BN + (i % BN); };
 
-  for (int k0 = 0; k0 < K; k0 += kBK) {
-    if (GK == GK_NV) {
-      // A: 16 B of E2M1 at K [k0 + 32 lg, +32), scales 2 bytes
-      uint32_t ad[2][16];
+  // ---- per-thread global load assignments (fixed across K steps)
+  // A: MX/FP8 2 chunks of 16 B (rows tid/8 and 32 + tid/8); NV 1 chunk (row tid/4)
+  constexpr int A_CH = GK == GK_NV ? 1 : 2;
+  const uint8_t* a_src[A_CH];
+  bool a_ok[A_CH];
+  int a_lrow[A_CH], a_part[A_CH];
+  int64_t a_srow[A_CH];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        uint4 c = make_uint4(0u, 0u, 0u, 0u);
-        uint32_t s2 = 0;
-        if (a_ok[i]) {
-          c = *reinterpret_cast<const uint4*>(a_ptr[i] + (k0 + 32 * lg) / 2);
-          s2 = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(g.a_scales) +
-                                                  (int64_t)a_row[i] * (K / 16) + (k0 + 32 * lg) / 16);
-        }
-        nv_decode32(c, s2, ad[i]);
+  for (int c = 0; c < A_CH; ++c) {
+    const int ch = tid + 256 * c;
+    const int r = GK == GK_NV ? ch / 4 : ch / 8;
+    a_lrow[c] = r;
+    a_part[c] = GK == GK_NV ? ch % 4 : ch % 8;
+    bool ok;
+    const int arow = a_row_of(r, ok);
+    a_ok[c] = ok;
+    a_srow[c] = arow;
+    a_src[c] = g.a_codes + (int64_t)arow * a_rb;
+  }
+  // A scales (MX: 4 bytes, FP8: one float per row per K step): threads 0..63
+  bool as_ok = false;
+  int64_t as_row = 0;
+  if (GK != GK_NV && tid < BM) as_row = a_row_of(tid, as_ok);
+  // W: WROWS * w_cpr chunks
+  constexpr int W_CH_MAX = (WROWS * w_cpr + 255) / 256;
+
+  u32x4 pa[A_CH];
+  uint32_t pas = 0;            // A scales (MX dword / FP8 float bits)
+  uint32_t pan[A_CH];          // NV A scale pairs
+  u32x4 pw[W_CH_MAX];
+  u32x2 pws[(WROWS + 255) / 256];
+
+
+
+  floatx4 acc[4][NU * NSUB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int s = 0; s < NU * NSUB; ++s) acc[i][s] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // LDS row (within the tile's weight rows) of this wave's subtile s
+  auto w_lrow = [&](int s) __attribute__((always_inline)) -> int {
+    const int u = s / NSUB, j = s % NSUB;
+    return u * BN + wave * 16 * NSUB + j * 16 + lr;
+  };
+
+  // iteration -1 only stages K step 0; iteration ks computes step ks while
+  // step ks+1 is loaded from global memory and then written to the other buffer
+  for (int ks = -1; ks < KS; ++ks) {
+    if (ks + 1 < KS) {
+    const int k0 = (ks + 1) * kBK;
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      if (GK == GK_NV) {
+        const int kk = k0 + 32 * a_part[c];
+        pa[c] = a_ok[c] ? ld16(a_src[c] + kk / 2) : u32x4{0u, 0u, 0u, 0u};
+        pan[c] = a_ok[c] ? *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(g.a_scales) +
+                                                               a_srow[c] * (K / 16) + kk / 16)
+                         : 0u;
+      } else {
+        pa[c] = a_ok[c] ? ld16(a_src[c] + k0 + 16 * a_part[c]) : u32x4{0u, 0u, 0u, 0u};
       }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const int wr = w_row[j][u];
-          uint4 c = *reinterpret_cast<const uint4*>(w_base + (int64_t)wr * w_rb + (k0 + 32 * lg) / 2);
-          uint32_t s2 = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(g.w_scales) +
-                                                           ((int64_t)e * NW + wr) * (K / 16) + (k0 + 32 * lg) / 16);
-          uint32_t wd[16];
-          nv_decode32(c, s2, wd);
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-              acc[i][j][u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(&ad[i][4 * m]),
-                                                                    as_half8(&wd[4 * m]), acc[i][j][u], 0, 0, 0);
-        }
-    } else {
-      // A: E4M3 codes, K [k0+16lg, +16) and [k0+64+16lg, +16)
-      intx8 av[2];
-      int asc[2];
-      float afs[2][4];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        uint4 lo = make_uint4(0u, 0u, 0u, 0u), hi = make_uint4(0u, 0u, 0u, 0u);
-        if (a_ok[i]) {
-          lo = *reinterpret_cast<const uint4*>(a_ptr[i] + k0 + 16 * lg);
-          hi = *reinterpret_cast<const uint4*>(a_ptr[i] + k0 + 64 + 16 * lg);
-        }
-        av[i] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        if (GK == GK_MX) {
-          asc[i] = a_ok[i] ? reinterpret_cast<const uint8_t*>(g.a_scales)[(int64_t)a_row[i] * (K / 32) + k0 / 32 + lg] : 0;
-        } else {
-          asc[i] = 127;
-        }
-      }
-      if (GK == GK_FP8) {
-        // activation scale of the C rows this lane accumulates: rows 4 lg + r of subtile i
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            int rr = mt * kBM + wm * 32 + i * 16 + 4 * lg + r;
-            float sa = 0.0f;
-            if (rr < n_rows) {
-              int R = r_begin + rr;
-              int arow = g.a_gather ? g.pair_of_row[R] / g.k : R;
-              sa = reinterpret_cast<const float*>(g.a_scales)[(int64_t)arow * (K / 128) + k0 / 128];
-            }
-            afs[i][r] = sa;
-          }
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-          const int wr = w_row[j][u];
-          const uint8_t* wp = w_base + (int64_t)wr * w_rb;
-          intx8 bv;
-          int bsc = 127;
-          float wfs = 1.0f;
-          if (GK == GK_MX && !g.w_fp8) {
-            uint4 c = *reinterpret_cast<const uint4*>(wp + (k0 + 32 * lg) / 2);
-            bv = intx8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-          } else {
-            uint4 lo = *reinterpret_cast<const uint4*>(wp + k0 + 16 * lg);
-            uint4 hi = *reinterpret_cast<const uint4*>(wp + k0 + 64 + 16 * lg);
-            bv = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          }
-          if (GK == GK_MX) {
-            bsc = reinterpret_cast<const uint8_t*>(g.w_scales)[((int64_t)e * NW + wr) * (K / 32) + k0 / 32 + lg];
-          } else {
-            // one fp32 scale per 128 x 128 weight tile; the 16 rows of this subtile share it
-            wfs = reinterpret_cast<const float*>(g.w_scales)[((int64_t)e * (NW / 128) + wr / 128) * (K / 128) + k0 / 128];
-          }
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            if (GK == GK_MX) {
-              if (g.w_fp8)
-                acc[i][j][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[i], bv, acc[i][j][u], 0, 0, 0,
-                                                                                asc[i], 0, bsc);
-              else
-                acc[i][j][u] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[i], bv, acc[i][j][u], 0, 4, 0,
-                                                                                asc[i], 0, bsc);
-            } else {
-              floatx4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av[i], bv, floatx4{0.f, 0.f, 0.f, 0.f},
-                                                                           0, 0, 0, 127, 0, 127);
-#pragma unroll
-              for (int r = 0; r < 4; ++r) acc[i][j][u][r] = fmaf(p[r], afs[i][r] * wfs, acc[i][j][u][r]);
-            }
-          }
-        }
     }
+    if (GK == GK_MX && tid < BM)
+      pas = as_ok ? *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(g.a_scales) +
+                                                       as_row * (K / 32) + k0 / 32)
+                  : 0u;
+    if (GK == GK_FP8 && tid < BM)
+      pas = as_ok ? __float_as_uint(reinterpret_cast<const float*>(g.a_scales)[as_row * (K / 128) + k0 / 128]) : 0u;
+    const int nch = WROWS * w_cpr;
+#pragma unroll
+    for (int c = 0; c < W_CH_MAX; ++c) {
+      const int ch = tid + 256 * c;
+      if (ch < nch) {
+        const int row = ch / w_cpr, part = ch % w_cpr;
+        const int64_t gr = w_grow(row);
+        const int64_t kb = WFP8 ? k0 : k0 / 2;
+        pw[c] = ld16(w_base + gr * w_rb + kb + 16 * part);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < (WROWS + 255) / 256; ++c) {
+      const int row = tid + 256 * c;
+      if (row < WROWS) {
+        const int64_t gr = w_grow(row);
+        if (GK == GK_NV) {
+          pws[c] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(g.w_scales) +
+                                                  ((int64_t)e * NW + gr) * (K / 16) + k0 / 16);
+        } else if (GK == GK_MX) {
+          pws[c].x = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(g.w_scales) +
+                                                       ((int64_t)e * NW + gr) * (K / 32) + k0 / 32);
+        } else {
+          pws[c].x = __float_as_uint(reinterpret_cast<const float*>(g.w_scales)[
+              ((int64_t)e * (NW / 128) + gr / 128) * (K / 128) + k0 / 128]);
+        }
+      }
+    }
+    }
+    if (ks >= 0) {
+    const uint8_t* sb = lds + (ks & 1) * stage;
+    const uint8_t* s_a = sb;
+    const uint8_t* s_as = sb + BM * C::A_STRIDE;
+    const uint8_t* s_w = s_as + BM * C::A_SCALE_BYTES;
+    const uint8_t* s_ws = s_w + WROWS * w_stride;
+    if (GK == GK_NV) {
+      uint32_t af[4][16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4* src = reinterpret_cast<const uint4*>(s_a + (16 * i + lr) * C::A_STRIDE + 64 * lg);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint4 v = src[q];
+          af[i][4 * q] = v.x; af[i][4 * q + 1] = v.y; af[i][4 * q + 2] = v.z; af[i][4 * q + 3] = v.w;
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < NU * NSUB; ++s) {
+        const int wr = w_lrow(s);
+        const uint4 c = *reinterpret_cast<const uint4*>(s_w + wr * w_stride + 16 * lg);
+        const uint32_t s2 = *reinterpret_cast<const uint16_t*>(s_ws + wr * 8 + 2 * lg);
+        uint32_t wd[16];
+        nv_decode32(c, s2, wd);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(&af[i][4 * m]), as_half8(&wd[4 * m]),
+                                                               acc[i][s], 0, 0, 0);
+      }
+    } else {
+      intx8 af[4];
+      int asc[4];
+      float afs[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint8_t* row = s_a + (16 * i + lr) * C::A_STRIDE;
+        const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * lg);
+        const uint4 hi = *reinterpret_cast<const uint4*>(row + 64 + 16 * lg);
+        af[i] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        if (GK == GK_MX) asc[i] = s_as[(16 * i + lr) * 4 + lg];
+        if (GK == GK_FP8) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) afs[i][r] = reinterpret_cast<const float*>(s_as)[16 * i + 4 * lg + r];
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < NU * NSUB; ++s) {
+        const int wr = w_lrow(s);
+        intx8 bv;
+        if (w_fp8) {
+          const uint4 lo = *reinterpret_cast<const uint4*>(s_w + wr * w_stride + 16 * lg);
+          const uint4 hi = *reinterpret_cast<const uint4*>(s_w + wr * w_stride + 64 + 16 * lg);
+          bv = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        } else {
+          const uint4 c = *reinterpret_cast<const uint4*>(s_w + wr * w_stride + 16 * lg);
+          bv = intx8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+        }
+        if (GK == GK_MX) {
+          const int bsc = s_ws[wr * 4 + lg];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (w_fp8)
+              acc[i][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bv, acc[i][s], 0, 0, 0, asc[i],
+                                                                           0, bsc);
+            else
+              acc[i][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bv, acc[i][s], 0, 4, 0, asc[i],
+                                                                           0, bsc);
+          }
+        } else {
+          const float wfs = reinterpret_cast<const float*>(s_ws)[wave * 16 * NSUB + (s % NSUB) * 16 +
+                                                                (s / NSUB) * BN];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const floatx4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af[i], bv, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][s][r] = fmaf(p[r], afs[i][r] * wfs, acc[i][s][r]);
+          }
+        }
+      }
+    }
+    }
+    if (ks + 1 < KS) {
+    uint8_t* sb = lds + ((ks + 1) & 1) * stage;
+    uint8_t* s_a = sb;
+    uint8_t* s_as = sb + BM * C::A_STRIDE;
+    uint8_t* s_w = s_as + BM * C::A_SCALE_BYTES;
+    uint8_t* s_ws = s_w + WROWS * w_stride;
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      if (GK == GK_NV) {
+        uint32_t d[16];
+        nv_decode32(make_uint4(pa[c].x, pa[c].y, pa[c].z, pa[c].w), pan[c], d);
+        uint8_t* dst = s_a + a_lrow[c] * C::A_STRIDE + 64 * a_part[c];
+        st16(dst, u32x4{d[0], d[1], d[2], d[3]});
+        st16(dst + 16, u32x4{d[4], d[5], d[6], d[7]});
+        st16(dst + 32, u32x4{d[8], d[9], d[10], d[11]});
+        st16(dst + 48, u32x4{d[12], d[13], d[14], d[15]});
+      } else {
+        st16(s_a + a_lrow[c] * C::A_STRIDE + 16 * a_part[c], pa[c]);
+      }
+    }
+    if (GK != GK_NV && tid < BM) reinterpret_cast<uint32_t*>(s_as)[tid] = pas;
+    const int nch = WROWS * w_cpr;
+#pragma unroll
+    for (int c = 0; c < W_CH_MAX; ++c) {
+      const int ch = tid + 256 * c;
+      if (ch < nch) {
+        const int row = ch / w_cpr, part = ch % w_cpr;
+        st16(s_w + row * w_stride + 16 * part, pw[c]);
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < (WROWS + 255) / 256; ++c) {
+      const int row = tid + 256 * c;
+      if (row < WROWS) {
+        if (GK == GK_NV) reinterpret_cast<u32x2*>(s_ws)[row] = pws[c];
+        else reinterpret_cast<uint32_t*>(s_ws)[row] = pws[c].x;
+      }
+    }
+    }
+    __syncthreads();
   }
 
-  // epilogue
+  // ---- epilogue
   float scale = 1.0f;
   if (GK == GK_NV) scale = g.a_tensor_scale[0] * g.w_tensor_scale[e];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int n = nt * kBN + wn * 32 + j * 16 + lr;
+    for (int j = 0; j < NSUB; ++j) {
+      const int n = nt * BN + wave * 16 * NSUB + j * 16 + lr;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int rr = mt * kBM + wm * 32 + i * 16 + 4 * lg + r;
+        const int rr = mt * BM + 16 * i + 4 * lg + r;
         if (rr >= n_rows) continue;
         const int64_t R = r_begin + rr;
         float v;
         if (EPI == EPI_GATEUP) {
-          const float gt = acc[i][j][0][r] * scale;
-          const float up = acc[i][j][NU - 1][r] * scale;
-          v = silu_f32(gt) * up;
+          v = silu_f32(acc[i][j][r] * scale) * (acc[i][NSUB + j][r] * scale);
         } else {
-          v = acc[i][j][0][r] * scale;
+          v = acc[i][j][r] * scale;
           if (g.row_scale) v *= g.row_scale[R];
         }
         g.out[R * g.N + n] = v;
@@ -353,16 +480,42 @@ __global__ void __launch_bounds__(256) shared_gate_kernel(const uint16_t* __rest
 
 // ------------------------------------------------------------------- host
 
-template <int GK, int EPI>
-static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
-  const int NT = a.N / kBN;
+template <int GK, int EPI, int NSUB, bool WFP8>
+static int launch_gemm_n(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+  using C = TileCfg<GK, EPI, NSUB, WFP8>;
+  const int NT = a.N / C::BN;
   int64_t G = tiles_m_bound * NT;
   G = (G + 7) / 8 * 8;
   if (G <= 0) return FP4_OK;
   if (G > INT32_MAX) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM grid too large");
-  const size_t lds = a.dense_rows > 0 ? 0 : sizeof(int) * ((size_t)a.E + 1);
-  hipLaunchKernelGGL((grouped_gemm_kernel<GK, EPI>), dim3((unsigned)G), dim3(256), lds, st, a);
+  const size_t lds = 2 * C::STAGE + (a.dense_rows > 0 ? 0 : sizeof(int) * ((size_t)a.E + 1));
+  if (lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs %zu bytes of LDS", lds);
+  static bool attr_set = false;  // raise the dynamic-LDS limit once per kernel instance
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_kernel<GK, EPI, NSUB, WFP8>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+      return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((grouped_gemm_kernel<GK, EPI, NSUB, WFP8>), dim3((unsigned)G), dim3(256), lds, st, a);
   return check_launch("grouped_gemm");
+}
+
+// Widest tile (outputs per tile 64 * NSUB) that divides N and fits LDS.
+template <int GK, int EPI, bool WFP8>
+static int launch_gemm_w(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+  if (!WFP8 && a.N % 320 == 0) return launch_gemm_n<GK, EPI, WFP8 ? 2 : 5, WFP8>(a, tiles_m_bound, st);
+  if (a.N % 128 == 0) return launch_gemm_n<GK, EPI, 2, WFP8>(a, tiles_m_bound, st);
+  if (a.N % 64 == 0) return launch_gemm_n<GK, EPI, 1, WFP8>(a, tiles_m_bound, st);
+  return fail(FP4_ERR_SHAPE, "output width %d is not a multiple of 64", a.N);
+}
+
+template <int GK, int EPI>
+static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+  if (GK == GK_NV) return launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
+  if (GK == GK_FP8) return launch_gemm_w<GK, EPI, true>(a, tiles_m_bound, st);
+  return a.w_fp8 ? launch_gemm_w<GK, EPI, true>(a, tiles_m_bound, st)
+                 : launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
 }
 
 static int act_fmt_to_gk(int a_fmt) {
