@@ -56,6 +56,18 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// LDS rows hold 16-byte chunks in XOR-swizzled order so that the MFMA
+// fragment reads (16 lanes read the same chunk of 16 consecutive rows) and
+// the staging writes (consecutive lanes write consecutive chunks of a few
+// rows) touch distinct 16-byte bank groups within every 8 lanes and within
+// every 16 lanes.  Row widths: 64 B (4 chunks), 128 B (8), 256 B (16).
+template <int ROW_BYTES>
+__device__ __forceinline__ int swz(int row, int chunk) {
+  if (ROW_BYTES == 64) return row * 64 + 16 * (chunk ^ (((row >> 1) ^ (row >> 3)) & 3));
+  if (ROW_BYTES == 128) return row * 128 + 16 * (chunk ^ ((row ^ (row >> 3)) & 7));
+  return row * 256 + 16 * (chunk ^ (row & 15));
+}
+
 enum { GK_NV = 0, GK_MX = 1, GK_FP8 = 2 };
 enum { EPI_GATEUP = 0, EPI_DOWN = 1 };
 
@@ -130,10 +142,10 @@ struct TileCfg {
   static constexpr int BN = 64 * NSUB;                              // outputs per tile
   static constexpr int NU = EPI == EPI_GATEUP ? 2 : 1;
   static constexpr int WROWS = NU * BN;                             // weight rows per tile
-  static constexpr int W_STRIDE = WFP8 ? 128 + 16 : 64 + 16;       // weight row in LDS (bytes)
+  static constexpr int W_STRIDE = WFP8 ? 128 : 64;                 // weight row in LDS (bytes)
   static constexpr int W_CPR = WFP8 ? 8 : 4;                        // 16-byte chunks per row per K step
   static constexpr int A_BYTES = GK == GK_NV ? 256 : 128;           // per row per K step in LDS
-  static constexpr int A_STRIDE = A_BYTES + 16;
+  static constexpr int A_STRIDE = A_BYTES;
   static constexpr int W_SCALE_BYTES = GK == GK_NV ? 8 : 4;        // per row per K step
   static constexpr int A_SCALE_BYTES = 4;
   static constexpr size_t STAGE =
@@ -308,17 +320,17 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
       uint32_t af[4][16];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4* src = reinterpret_cast<const uint4*>(s_a + (16 * i + lr) * C::A_STRIDE + 64 * lg);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          uint4 v = src[q];
+          const u32x4 v = ld16(s_a + swz<256>(16 * i + lr, 4 * lg + q));
           af[i][4 * q] = v.x; af[i][4 * q + 1] = v.y; af[i][4 * q + 2] = v.z; af[i][4 * q + 3] = v.w;
         }
       }
 #pragma unroll
       for (int s = 0; s < NU * NSUB; ++s) {
         const int wr = w_lrow(s);
-        const uint4 c = *reinterpret_cast<const uint4*>(s_w + wr * w_stride + 16 * lg);
+        const u32x4 cv = ld16(s_w + swz<w_stride>(wr, lg));
+        const uint4 c = make_uint4(cv.x, cv.y, cv.z, cv.w);
         const uint32_t s2 = *reinterpret_cast<const uint16_t*>(s_ws + wr * 8 + 2 * lg);
         uint32_t wd[16];
         nv_decode32(c, s2, wd);
@@ -335,9 +347,8 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
       float afs[4][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint8_t* row = s_a + (16 * i + lr) * C::A_STRIDE;
-        const uint4 lo = *reinterpret_cast<const uint4*>(row + 16 * lg);
-        const uint4 hi = *reinterpret_cast<const uint4*>(row + 64 + 16 * lg);
+        const u32x4 lo = ld16(s_a + swz<128>(16 * i + lr, lg));
+        const u32x4 hi = ld16(s_a + swz<128>(16 * i + lr, 4 + lg));
         af[i] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         if (GK == GK_MX) asc[i] = s_as[(16 * i + lr) * 4 + lg];
         if (GK == GK_FP8) {
@@ -350,11 +361,11 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
         const int wr = w_lrow(s);
         intx8 bv;
         if (w_fp8) {
-          const uint4 lo = *reinterpret_cast<const uint4*>(s_w + wr * w_stride + 16 * lg);
-          const uint4 hi = *reinterpret_cast<const uint4*>(s_w + wr * w_stride + 64 + 16 * lg);
+          const u32x4 lo = ld16(s_w + swz<w_stride>(wr, lg));
+          const u32x4 hi = ld16(s_w + swz<w_stride>(wr, 4 + lg));
           bv = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         } else {
-          const uint4 c = *reinterpret_cast<const uint4*>(s_w + wr * w_stride + 16 * lg);
+          const u32x4 c = ld16(s_w + swz<w_stride>(wr, lg));
           bv = intx8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
         }
         if (GK == GK_MX) {
@@ -393,13 +404,13 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
       if (GK == GK_NV) {
         uint32_t d[16];
         nv_decode32(make_uint4(pa[c].x, pa[c].y, pa[c].z, pa[c].w), pan[c], d);
-        uint8_t* dst = s_a + a_lrow[c] * C::A_STRIDE + 64 * a_part[c];
-        st16(dst, u32x4{d[0], d[1], d[2], d[3]});
-        st16(dst + 16, u32x4{d[4], d[5], d[6], d[7]});
-        st16(dst + 32, u32x4{d[8], d[9], d[10], d[11]});
-        st16(dst + 48, u32x4{d[12], d[13], d[14], d[15]});
+        const int r = a_lrow[c], c0 = 4 * a_part[c];
+        st16(s_a + swz<256>(r, c0), u32x4{d[0], d[1], d[2], d[3]});
+        st16(s_a + swz<256>(r, c0 + 1), u32x4{d[4], d[5], d[6], d[7]});
+        st16(s_a + swz<256>(r, c0 + 2), u32x4{d[8], d[9], d[10], d[11]});
+        st16(s_a + swz<256>(r, c0 + 3), u32x4{d[12], d[13], d[14], d[15]});
       } else {
-        st16(s_a + a_lrow[c] * C::A_STRIDE + 16 * a_part[c], pa[c]);
+        st16(s_a + swz<128>(a_lrow[c], a_part[c]), pa[c]);
       }
     }
     if (GK != GK_NV && tid < BM) reinterpret_cast<uint32_t*>(s_as)[tid] = pas;
@@ -409,7 +420,7 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
       const int ch = tid + 256 * c;
       if (ch < nch) {
         const int row = ch / w_cpr, part = ch % w_cpr;
-        st16(s_w + row * w_stride + 16 * part, pw[c]);
+        st16(s_w + swz<w_stride>(row, part), pw[c]);
       }
     }
 #pragma unroll
@@ -504,7 +515,6 @@ static int launch_gemm_n(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t s
 // Widest tile (outputs per tile 64 * NSUB) that divides N and fits LDS.
 template <int GK, int EPI, bool WFP8>
 static int launch_gemm_w(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
-  if (!WFP8 && a.N % 320 == 0) return launch_gemm_n<GK, EPI, WFP8 ? 2 : 5, WFP8>(a, tiles_m_bound, st);
   if (a.N % 128 == 0) return launch_gemm_n<GK, EPI, 2, WFP8>(a, tiles_m_bound, st);
   if (a.N % 64 == 0) return launch_gemm_n<GK, EPI, 1, WFP8>(a, tiles_m_bound, st);
   return fail(FP4_ERR_SHAPE, "output width %d is not a multiple of 64", a.N);
