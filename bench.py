@@ -183,9 +183,10 @@ def bench_decode(args, torch, pkg):
     down_bytes = touched * b2 + P * cfg.inter * 4 + P * cfg.hidden * 4
     step_bytes = touched * (b13 + b2) + T * cfg.hidden * 2 + T * cfg.hidden * 4
     gu_ms = stages["gate_up"]
+    tr = measured_traffic("gemv_gateup_kernel", "decode")
     roof = {"bound": "hbm", "kernel": "gemv_gateup_kernel",
             "achieved": gateup_bytes / (gu_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "traffic": None,
+            "traffic": tr["bytes_per_launch"] if tr else None,
             "bytes_per_launch": gateup_bytes,
             "unit_of_work": f"{touched} touched experts x {b13} B of NVFP4 gate_up weights"
                             f" + x {T * cfg.hidden * 2} B + h {P * cfg.inter * 4} B"}
@@ -262,7 +263,9 @@ def bench_prefill(name, args, torch, pkg):
     gu_ms = stages["gate_up"]
     roof = {"bound": "mfma", "kernel": "grouped_gemm_kernel (gate_up)", "mfma_dtype":
             {"bf16": "fp16 (exact NVFP4 decode)", "fp8": "fp8 x fp4" if cfg.w_fmt == "mxfp4" else "fp8"}[peak_key],
-            "achieved": flops_gu / (gu_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s", "traffic": None,
+            "achieved": flops_gu / (gu_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
+            "traffic": (lambda t: t["bytes_per_launch"] if t else None)(
+                measured_traffic("grouped_gemm_kernel_gateup", name)),
             "flops_per_launch": flops_gu,
             "unit_of_work": f"{P} (token, expert) rows x 2 x {2 * I} x {H} FLOPs"}
     roof["frac"] = roof["achieved"] / peak
@@ -283,6 +286,55 @@ def bench_prefill(name, args, torch, pkg):
     del layers, q13, q2
     torch.cuda.empty_cache()
     return out
+
+
+def file_sha(rel):
+    import hashlib
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` in `workload` from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled by what the
+    same counters read for a plain copy of known size), or None when the
+    summary is absent or the kernel's source file changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    for line in open(path):
+        if line.startswith("#") or "=" not in line:
+            continue
+        kv = dict(t.split("=", 1) for t in line.split())
+        if kv.get("kernel") != kernel or kv.get("workload") != workload:
+            continue
+        if file_sha(kv["source"]) != kv["source_sha"]:
+            return None
+        return {"bytes_per_launch": float(kv["bytes_per_launch"]), "fetch_bytes": float(kv["fetch_bytes"]),
+                "write_bytes": float(kv["write_bytes"]), "copy_scale": float(kv["copy_scale"]),
+                "source": kv["source"]}
+    return None
+
+
+def bench_copy(args, torch):
+    """A plain device copy (elementwise negation of 2^28 float32 values: one
+    1 GiB read and one 1 GiB write per launch), used to calibrate the HBM byte
+    counters against a kernel of known traffic."""
+    n = 1 << 28
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(2):
+        torch.neg(a, out=b)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        torch.neg(a, out=b)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    return {"metric": "plain copy GB/s", "value": 2 * n * 4 / (ms * 1e-3) / 1e9, "unit": "GB/s",
+            "bytes_read": n * 4, "bytes_written": n * 4, "ms_per_launch": ms, "steps": args.steps}
 
 
 def bench_stream_quant(args, torch, pkg):
@@ -345,7 +397,9 @@ def bench_stream_quant(args, torch, pkg):
            "values_per_layer": E * 3 * H * I,
            "roofline": {"bound": "hbm", "kernel": "quant_fp4_kernel + tensor_amax_kernel",
                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
-                        "traffic": None, "bytes_per_layer": bytes_layer,
+                        "traffic": (lambda t: t["bytes_per_launch"] if t else None)(
+                            measured_traffic("quant_fp4_kernel", "stream_quant")),
+                        "bytes_per_layer": bytes_layer,
                         "unit_of_work": "2 B read + 0.5625 B written per value (+4 B per tensor)"},
            "quality": {"per_tensor_rel_err": {n: {"mean": m, "max": mx} for n, m, mx, _, _, _ in stats},
                        "m4_fraction": float(np.mean([f for _, _, _, f, _, _ in stats]))}}
@@ -377,8 +431,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
-                    choices=["all", "decode", "prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant"],
-                    help="'all': the decode headline plus every other workload under 'workloads'")
+                    choices=["all", "decode", "prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant",
+                             "copy"],
+                    help="'all': the decode headline plus every other workload under 'workloads'; "
+                         "'copy': a plain 1 GiB device copy that calibrates the HBM byte counters")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-copies", type=int, default=2)
     ap.add_argument("--stream-layers", type=int, default=48)
@@ -399,6 +455,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     torch.cuda.set_device(0)
+    if args.workload == "copy":
+        print(json.dumps(bench_copy(args, torch)), flush=True)
+        return
     if args.workload in ("all", "decode"):
         dargs = argparse.Namespace(**vars(args))
         dargs.workload = "decode"

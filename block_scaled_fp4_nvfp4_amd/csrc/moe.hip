@@ -295,195 +295,237 @@ int launch_permute(const int32_t* ids, int64_t P, int E, int tile_m, const WsPtr
 
 // --------------------------------------------- weight-only GEMV path (decode)
 
-// Scale of 16-value block b of a weight row: NVFP4 E4M3 per 16 (hardware
-// E4M3 -> f32 convert, exact), or MXFP4 UE8M0 per 32 shared by the block's two
-// 16-value halves (2^(c-127) built from its exponent bits; c = 0 is not a
-// normal float and is decoded separately).
-template <int WFMT>
-__device__ __forceinline__ float block_scale(const uint8_t* srow, int b) {
-  if (WFMT == FP4_FMT_NVFP4) return __builtin_amdgcn_cvt_f32_fp8((int)srow[b], 0);
-  uint32_t c = srow[b >> 1];
-  return c ? __uint_as_float(c << 23) : 5.877471754111438e-39f;  // 2^-127
-}
-
 template <int WFMT>
 __device__ __forceinline__ int64_t scale_row_stride(int64_t cols) {
   return WFMT == FP4_FMT_NVFP4 ? cols / 16 : cols / 32;
 }
 
-// acc += s_b * sum over the 16 values of block b of w * x (one token row)
-__device__ __forceinline__ float block_dot(uint2 c, float sb, const uint32_t (&x)[8], float acc) {
-  uint32_t a[4], b[4];
-  e2m1x8_to_bf16x8(c.x, a);
-  e2m1x8_to_bf16x8(c.y, b);
-  float d = 0.0f;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) d = dot2_bf16(a[q], x[q], d);
-#pragma unroll
-  for (int q = 0; q < 4; ++q) d = dot2_bf16(b[q], x[4 + q], d);
-  return fmaf(d, sb, acc);
+// Scale bytes of 16-byte code chunk c (32 values) of a weight row: NVFP4 has
+// two E4M3 scales (bytes 2c, 2c+1), MXFP4 one UE8M0 scale (byte c).
+template <int WFMT>
+__device__ __forceinline__ uint32_t chunk_scale_bits(const uint8_t* srow, int c) {
+  if (WFMT == FP4_FMT_NVFP4) return *reinterpret_cast<const uint16_t*>(srow + 2 * c);
+  return srow[c];
 }
 
-constexpr int kGvJTile = 32;  // outputs j per workgroup: 8 half-waves x 4 steps
+// Value of scale byte SEL (0 or 1) of a chunk's scale bits.
+template <int WFMT, int SEL>
+__device__ __forceinline__ float chunk_scale(uint32_t bits) {
+  if (WFMT == FP4_FMT_NVFP4) return __builtin_amdgcn_cvt_f32_fp8((int)bits, SEL);
+  return bits ? __uint_as_float(bits << 23) : 5.877471754111438e-39f;  // UE8M0 2^(c-127); c = 0: 2^-127
+}
+
+// acc + scale-weighted dot product of one 32-value code chunk with 32 bf16
+// activations (x[q] holds the pair (2q, 2q+1)).  NVFP4: two 16-value blocks,
+// each partial sum scaled by its own block scale; MXFP4: one block.
+template <int WFMT>
+__device__ __forceinline__ float chunk_dot_bf16(u32x4 c, uint32_t sbits, const uint32_t (&x)[16], float acc) {
+  uint32_t p[16];
+  e2m1x8_to_bf16x8(c.x, *reinterpret_cast<uint32_t(*)[4]>(&p[0]));
+  e2m1x8_to_bf16x8(c.y, *reinterpret_cast<uint32_t(*)[4]>(&p[4]));
+  e2m1x8_to_bf16x8(c.z, *reinterpret_cast<uint32_t(*)[4]>(&p[8]));
+  e2m1x8_to_bf16x8(c.w, *reinterpret_cast<uint32_t(*)[4]>(&p[12]));
+  float d0 = 0.0f, d1 = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) d0 = dot2_bf16(p[q], x[q], d0);
+#pragma unroll
+  for (int q = 8; q < 16; ++q) d1 = dot2_bf16(p[q], x[q], d1);
+  if (WFMT == FP4_FMT_NVFP4) return fmaf(d1, chunk_scale<WFMT, 1>(sbits), fmaf(d0, chunk_scale<WFMT, 0>(sbits), acc));
+  return fmaf(d0 + d1, chunk_scale<WFMT, 0>(sbits), acc);
+}
+
+// Same with f32 activations h[0..31].
+template <int WFMT>
+__device__ __forceinline__ float chunk_dot_f32(u32x4 c, uint32_t sbits, const float (&h)[32], float acc) {
+  float d0 = 0.0f, d1 = 0.0f;
+  float w[8];
+  e2m1x8_to_f32x8(c.x, w);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) d0 = fmaf(w[m], h[m], d0);
+  e2m1x8_to_f32x8(c.y, w);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) d0 = fmaf(w[m], h[8 + m], d0);
+  e2m1x8_to_f32x8(c.z, w);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) d1 = fmaf(w[m], h[16 + m], d1);
+  e2m1x8_to_f32x8(c.w, w);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) d1 = fmaf(w[m], h[24 + m], d1);
+  if (WFMT == FP4_FMT_NVFP4) return fmaf(d1, chunk_scale<WFMT, 1>(sbits), fmaf(d0, chunk_scale<WFMT, 0>(sbits), acc));
+  return fmaf(d0 + d1, chunk_scale<WFMT, 0>(sbits), acc);
+}
+
+constexpr int kGvOut = 16;      // outputs j per workgroup of the gate_up GEMV (one per 16 lanes)
+constexpr int kGvTokens = 4;    // tokens whose activations are staged in LDS per pass
+constexpr int kGdRows = 128;    // output rows per workgroup of the down GEMV (2 per 4 lanes)
+constexpr int kGdTokens = 8;
 
 // gate_up + SiLU*up for the pairs of one expert, bf16 activations.
-// Grid: (I / 32 output tiles, max active experts).  A half-wave (32 lanes)
-// owns one output j per step: gate row j and up row I+j, K = H split into
-// 16-value blocks, lane l taking blocks l, l+32, ...  The two rows' codes and
-// scales are loaded once per step and reused for every token of the expert;
-// the token's activations come through L1 (they are shared by all rows).
-template <int WFMT, int BPL>
+// Grid: (ceil(I / 16), max active experts).  Each group of 16 lanes owns one
+// output j: gate row j and up row I+j, split into 16-byte chunks of 32 codes
+// (lane l takes chunks l, l+16, ...).  All of a row pair's codes and scales
+// are loaded at once (about 2.9 KB per group at the decode shape) and reused
+// for every token of the expert; the tokens' activations are staged in LDS,
+// four tokens per pass, as [token][quarter q][chunk c] 16-byte pieces so
+// that the 16 lanes of a group read consecutive pieces.
+template <int WFMT, int CPL>
 __global__ void __launch_bounds__(256) gemv_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ pair_of_row, const int32_t* __restrict__ active,
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s, const float* __restrict__ w13s2,
     int H, int I, int k, float* __restrict__ h) {
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kGvTokens * 4 * CPL * 16 * 16];
   const int ai = blockIdx.y;
   if (ai >= active[0]) return;
   const int e = active[1 + ai];
-  const int hw = threadIdx.x >> 5, l = threadIdx.x & 31;
-  const int NB = H >> 4;
+  const int tid = threadIdx.x, l = tid & 15;
+  const int j = blockIdx.x * kGvOut + (tid >> 4);
+  const bool jv = j < I;
+  const int jj = jv ? j : I - 1;
+  const int NCH = H >> 5;  // 32-value chunks per row
   const int64_t row_bytes = H >> 1;
   const int64_t srow = scale_row_stride<WFMT>(H);
-  const uint8_t* wq = w13 + (int64_t)e * 2 * I * row_bytes;
-  const uint8_t* ws = w13s + (int64_t)e * 2 * I * srow;
+  const uint8_t* wg = w13 + ((int64_t)e * 2 * I + jj) * row_bytes;
+  const uint8_t* wu = wg + (int64_t)I * row_bytes;
+  const uint8_t* sg = w13s + ((int64_t)e * 2 * I + jj) * srow;
+  const uint8_t* su = sg + (int64_t)I * srow;
+  u32x4 cg[CPL], cu[CPL];
+  uint32_t bg[CPL], bu[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = l + 16 * i;
+    const bool in = c < NCH;
+    const int cc = in ? c : 0;
+    cg[i] = ld16(wg + 16 * cc);
+    cu[i] = ld16(wu + 16 * cc);
+    bg[i] = in ? chunk_scale_bits<WFMT>(sg, cc) : 0u;  // scale 0 zeroes the padding chunks
+    bu[i] = in ? chunk_scale_bits<WFMT>(su, cc) : 0u;
+    if (WFMT == FP4_FMT_MXFP4 && !in) { cg[i] = u32x4{0u, 0u, 0u, 0u}; cu[i] = cg[i]; }
+  }
   const float S = WFMT == FP4_FMT_NVFP4 ? w13s2[e] : 1.0f;
   const int r0 = offsets[e], n = offsets[e + 1] - r0;
-  for (int j = blockIdx.x * kGvJTile + hw; j < min(I, (int)(blockIdx.x + 1) * kGvJTile); j += 8) {
-    uint2 cg[BPL], cu[BPL];
-    float fg[BPL], fu[BPL];
-    const uint2* qg = reinterpret_cast<const uint2*>(wq + (int64_t)j * row_bytes);
-    const uint2* qu = reinterpret_cast<const uint2*>(wq + (int64_t)(I + j) * row_bytes);
-    const uint8_t* sg = ws + (int64_t)j * srow;
-    const uint8_t* su = ws + (int64_t)(I + j) * srow;
-#pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-      int b = l + 32 * i;
-      bool in = b < NB;
-      cg[i] = in ? qg[b] : make_uint2(0u, 0u);
-      cu[i] = in ? qu[b] : make_uint2(0u, 0u);
-      fg[i] = in ? block_scale<WFMT>(sg, b) : 0.0f;
-      fu[i] = in ? block_scale<WFMT>(su, b) : 0.0f;
+  const int pieces = 4 * NCH;  // 16-byte pieces per activation row
+  for (int t0 = 0; t0 < n; t0 += kGvTokens) {
+    const int nt = min(kGvTokens, n - t0);
+    if (t0 > 0) __syncthreads();
+    for (int idx = tid; idx < nt * pieces; idx += 256) {
+      const int t = idx / pieces, rem = idx - t * pieces;
+      const int c = rem >> 2, q = rem & 3;
+      const uint8_t* xrow = reinterpret_cast<const uint8_t*>(x + (int64_t)(pair_of_row[r0 + t0 + t] / k) * H);
+      st16(xs + ((t * 4 + q) * NCH + c) * 16, ld16(xrow + 64 * c + 16 * q));
     }
-    for (int t = 0; t < n; ++t) {
+    __syncthreads();
+    for (int t = 0; t < nt; ++t) {
       // keep the packed codes (not their 4x larger bf16 expansion) live
       // across the token loop: the expansion is redone per token
 #pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        asm volatile("" : "+v"(cg[i].x), "+v"(cg[i].y), "+v"(cu[i].x), "+v"(cu[i].y));
-      }
-      const uint16_t* xrow = x + (int64_t)(pair_of_row[r0 + t] / k) * H;
+      for (int i = 0; i < CPL; ++i) asm volatile("" : "+v"(cg[i]), "+v"(cu[i]));
       float ag = 0.0f, au = 0.0f;
 #pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        int b = l + 32 * i;
-        uint32_t xr[8];
-        if (b < NB) {
-          const uint4* src = reinterpret_cast<const uint4*>(xrow + b * 16);
-          uint4 a0 = src[0], a1 = src[1];
-          xr[0] = a0.x; xr[1] = a0.y; xr[2] = a0.z; xr[3] = a0.w;
-          xr[4] = a1.x; xr[5] = a1.y; xr[6] = a1.z; xr[7] = a1.w;
-        } else {
+      for (int i = 0; i < CPL; ++i) {
+        const int c = l + 16 * i;
+        if (c < NCH) {
+          uint32_t xv[16];
 #pragma unroll
-          for (int q = 0; q < 8; ++q) xr[q] = 0u;
+          for (int q = 0; q < 4; ++q) {
+            const u32x4 v = ld16(xs + ((t * 4 + q) * NCH + c) * 16);
+            xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
+          }
+          ag = chunk_dot_bf16<WFMT>(cg[i], bg[i], xv, ag);
+          au = chunk_dot_bf16<WFMT>(cu[i], bu[i], xv, au);
         }
-        ag = block_dot(cg[i], fg[i], xr, ag);
-        au = block_dot(cu[i], fu[i], xr, au);
       }
 #pragma unroll
-      for (int off = 16; off > 0; off >>= 1) {
-        ag += __shfl_xor(ag, off, 32);
-        au += __shfl_xor(au, off, 32);
+      for (int off = 8; off > 0; off >>= 1) {
+        ag += __shfl_xor(ag, off, 16);
+        au += __shfl_xor(au, off, 16);
       }
-      if (l == 0) h[(int64_t)(r0 + t) * I + j] = silu_f32(ag * S) * (au * S);
+      if (l == 0 && jv) h[(int64_t)(r0 + t0 + t) * I + j] = silu_f32(ag * S) * (au * S);
     }
   }
 }
 
-constexpr int kGdTile = 128;  // output rows per workgroup of the down GEMV
-
 // Down projection o[row] = W2[e] h[row] for the rows of one expert, f32 h.
-// Grid: (ceil(H / 128) row tiles, max active experts).  A group of 8 lanes
-// owns output rows rg, rg + 32, ... of the tile (two in flight per step);
-// lane q of the group takes 16-value blocks q, q+8, ...  One token's h is held
-// in registers at a time; an expert's later tokens re-read its weights from L2.
-template <int WFMT, int BPL>
+// Grid: (ceil(H / 128), max active experts).  Each group of 4 lanes owns two
+// output rows (n and n + 64 of the tile), split into 16-byte chunks of 32
+// codes (lane l takes chunks l, l+4, ...).  The tokens' h rows are staged in
+// LDS, eight tokens per pass, each 32-value chunk padded to 144 bytes so that
+// the four lanes of a group read different bank groups.
+template <int WFMT, int CPL>
 __global__ void __launch_bounds__(256) gemv_down_kernel(
     const float* __restrict__ h, const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
     const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s, const float* __restrict__ w2s2,
     int H, int I, float* __restrict__ o) {
+  constexpr int kChunkBytes = 144;
+  __shared__ __attribute__((aligned(16))) uint8_t hs[kGdTokens * 4 * CPL * kChunkBytes];
   const int ai = blockIdx.y;
   if (ai >= active[0]) return;
   const int e = active[1 + ai];
-  const int q = threadIdx.x & 7, rg = threadIdx.x >> 3;
-  const int NB = I >> 4;
+  const int tid = threadIdx.x, l = tid & 3;
+  const int n0 = blockIdx.x * kGdRows + (tid >> 2), n1 = n0 + kGdRows / 2;
+  const bool v0 = n0 < H, v1 = n1 < H;
+  const int NCH = I >> 5;
   const int64_t row_bytes = I >> 1;
   const int64_t srow = scale_row_stride<WFMT>(I);
-  const uint8_t* wq = w2 + (int64_t)e * H * row_bytes;
-  const uint8_t* ws = w2s + (int64_t)e * H * srow;
+  const uint8_t* wbase = w2 + (int64_t)e * H * row_bytes;
+  const uint8_t* sbase = w2s + (int64_t)e * H * srow;
+  const uint8_t* q0 = wbase + (int64_t)(v0 ? n0 : 0) * row_bytes;
+  const uint8_t* q1 = wbase + (int64_t)(v1 ? n1 : 0) * row_bytes;
+  const uint8_t* s0 = sbase + (int64_t)(v0 ? n0 : 0) * srow;
+  const uint8_t* s1 = sbase + (int64_t)(v1 ? n1 : 0) * srow;
+  u32x4 c0[CPL], c1[CPL];
+  uint32_t b0[CPL], b1[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) {
+    const int c = l + 4 * i;
+    const bool in = c < NCH;
+    const int cc = in ? c : 0;
+    c0[i] = ld16(q0 + 16 * cc);
+    c1[i] = ld16(q1 + 16 * cc);
+    b0[i] = in ? chunk_scale_bits<WFMT>(s0, cc) : 0u;
+    b1[i] = in ? chunk_scale_bits<WFMT>(s1, cc) : 0u;
+    if (WFMT == FP4_FMT_MXFP4 && !in) { c0[i] = u32x4{0u, 0u, 0u, 0u}; c1[i] = c0[i]; }
+  }
   const float S = WFMT == FP4_FMT_NVFP4 ? w2s2[e] : 1.0f;
-  const int n_begin = blockIdx.x * kGdTile, n_end = min(H, n_begin + kGdTile);
   const int r0 = offsets[e], n = offsets[e + 1] - r0;
-  for (int t = 0; t < n; ++t) {
-    float hv[BPL][16];
-    const float* hrow = h + (int64_t)(r0 + t) * I;
-#pragma unroll
-    for (int i = 0; i < BPL; ++i) {
-      int b = q + 8 * i;
-      if (b < NB) {
-        const float4* src = reinterpret_cast<const float4*>(hrow + b * 16);
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          float4 v = src[m];
-          hv[i][4 * m] = v.x; hv[i][4 * m + 1] = v.y; hv[i][4 * m + 2] = v.z; hv[i][4 * m + 3] = v.w;
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 16; ++m) hv[i][m] = 0.0f;
-      }
+  const int tok_bytes = NCH * kChunkBytes;
+  for (int t0 = 0; t0 < n; t0 += kGdTokens) {
+    const int nt = min(kGdTokens, n - t0);
+    if (t0 > 0) __syncthreads();
+    for (int idx = tid; idx < nt * NCH * 8; idx += 256) {  // 8 pieces of 16 bytes per chunk
+      const int t = idx / (NCH * 8), rem = idx - t * NCH * 8;
+      const int c = rem >> 3, q = rem & 7;
+      const uint8_t* hrow = reinterpret_cast<const uint8_t*>(h + (int64_t)(r0 + t0 + t) * I);
+      st16(hs + t * tok_bytes + c * kChunkBytes + 16 * q, ld16(hrow + 128 * c + 16 * q));
     }
-    for (int nn0 = n_begin + rg; nn0 < n_end; nn0 += 64) {
-      const int nn1 = nn0 + 32;
-      const bool has1 = nn1 < n_end;
-      uint2 c0[BPL], c1[BPL];
-      float f0[BPL], f1[BPL];
-      const uint2* q0 = reinterpret_cast<const uint2*>(wq + (int64_t)nn0 * row_bytes);
-      const uint2* q1 = reinterpret_cast<const uint2*>(wq + (int64_t)(has1 ? nn1 : nn0) * row_bytes);
-      const uint8_t* s0 = ws + (int64_t)nn0 * srow;
-      const uint8_t* s1 = ws + (int64_t)(has1 ? nn1 : nn0) * srow;
+    __syncthreads();
+    for (int t = 0; t < nt; ++t) {
 #pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        int b = q + 8 * i;
-        bool in = b < NB;
-        c0[i] = in ? q0[b] : make_uint2(0u, 0u);
-        c1[i] = in ? q1[b] : make_uint2(0u, 0u);
-        f0[i] = in ? block_scale<WFMT>(s0, b) : 0.0f;
-        f1[i] = in ? block_scale<WFMT>(s1, b) : 0.0f;
-      }
+      for (int i = 0; i < CPL; ++i) asm volatile("" : "+v"(c0[i]), "+v"(c1[i]));
       float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
-      for (int i = 0; i < BPL; ++i) {
-        float w[8], v[8];
-        float d0 = 0.0f, d1 = 0.0f;
-        e2m1x8_to_f32x8(c0[i].x, w);
-        e2m1x8_to_f32x8(c1[i].x, v);
+      for (int i = 0; i < CPL; ++i) {
+        const int c = l + 4 * i;
+        if (c < NCH) {
+          float hv[32];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) { d0 = fmaf(w[m], hv[i][m], d0); d1 = fmaf(v[m], hv[i][m], d1); }
-        e2m1x8_to_f32x8(c0[i].y, w);
-        e2m1x8_to_f32x8(c1[i].y, v);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) { d0 = fmaf(w[m], hv[i][8 + m], d0); d1 = fmaf(v[m], hv[i][8 + m], d1); }
-        a0 = fmaf(d0, f0[i], a0);
-        a1 = fmaf(d1, f1[i], a1);
+          for (int q = 0; q < 8; ++q) {
+            const u32x4 v = ld16(hs + t * tok_bytes + c * kChunkBytes + 16 * q);
+            hv[4 * q] = __uint_as_float(v.x); hv[4 * q + 1] = __uint_as_float(v.y);
+            hv[4 * q + 2] = __uint_as_float(v.z); hv[4 * q + 3] = __uint_as_float(v.w);
+          }
+          a0 = chunk_dot_f32<WFMT>(c0[i], b0[i], hv, a0);
+          a1 = chunk_dot_f32<WFMT>(c1[i], b1[i], hv, a1);
+        }
       }
 #pragma unroll
-      for (int off = 4; off > 0; off >>= 1) {
-        a0 += __shfl_xor(a0, off, 8);
-        a1 += __shfl_xor(a1, off, 8);
+      for (int off = 2; off > 0; off >>= 1) {
+        a0 += __shfl_xor(a0, off, 4);
+        a1 += __shfl_xor(a1, off, 4);
       }
-      if (q == 0) {
-        o[(int64_t)(r0 + t) * H + nn0] = a0 * S;
-        if (has1) o[(int64_t)(r0 + t) * H + nn1] = a1 * S;
+      if (l == 0) {
+        if (v0) o[(int64_t)(r0 + t0 + t) * H + n0] = a0 * S;
+        if (v1) o[(int64_t)(r0 + t0 + t) * H + n1] = a1 * S;
       }
     }
   }
@@ -538,15 +580,15 @@ template <int WFMT>
 static int launch_gemv(const uint16_t* x, const WsPtrs& w, const moe_fp4_layer* L, int64_t P,
                        int max_active, hipStream_t st, const Marker& mark) {
   (void)P;
-  const int bpl = (L->hidden / 16 + 31) / 32;
-  dim3 grid((unsigned)((L->inter + kGvJTile - 1) / kGvJTile), (unsigned)max_active);
+  const int cpl = (L->hidden / 32 + 15) / 16;
+  dim3 grid((unsigned)((L->inter + kGvOut - 1) / kGvOut), (unsigned)max_active);
 #define FP4_GV(B)                                                                                      \
   case B:                                                                                              \
     hipLaunchKernelGGL((gemv_gateup_kernel<WFMT, B>), grid, dim3(256), 0, st, x, w.offsets,            \
                        w.pair_of_row, w.active, L->w13, (const uint8_t*)L->w13_scale, L->w13_scale_2, \
                        L->hidden, L->inter, L->top_k, w.h);                                            \
     break;
-  switch (bpl) {
+  switch (cpl) {
     FP4_GV(1) FP4_GV(2) FP4_GV(3) FP4_GV(4) FP4_GV(5) FP4_GV(6) FP4_GV(7) FP4_GV(8)
     default: return fail(FP4_ERR_UNSUPPORTED, "hidden %d too large for the GEMV path", L->hidden);
   }
@@ -554,14 +596,14 @@ static int launch_gemv(const uint16_t* x, const WsPtrs& w, const moe_fp4_layer* 
   FP4_CHECK(check_launch("gemv_gateup"));
   FP4_CHECK(mark(3));
   FP4_CHECK(mark(4));
-  const int bpl2 = (L->inter / 16 + 7) / 8;
-  dim3 grid2((unsigned)((L->hidden + kGdTile - 1) / kGdTile), (unsigned)max_active);
+  const int cpl2 = (L->inter / 32 + 3) / 4;
+  dim3 grid2((unsigned)((L->hidden + kGdRows - 1) / kGdRows), (unsigned)max_active);
 #define FP4_GD(B)                                                                                      \
   case B:                                                                                              \
     hipLaunchKernelGGL((gemv_down_kernel<WFMT, B>), grid2, dim3(256), 0, st, w.h, w.offsets, w.active, \
                        L->w2, (const uint8_t*)L->w2_scale, L->w2_scale_2, L->hidden, L->inter, w.o);   \
     break;
-  switch (bpl2) {
+  switch (cpl2) {
     FP4_GD(1) FP4_GD(2) FP4_GD(3) FP4_GD(4) FP4_GD(5) FP4_GD(6) FP4_GD(7) FP4_GD(8)
     default: return fail(FP4_ERR_UNSUPPORTED, "inter %d too large for the GEMV path", L->inter);
   }
@@ -612,8 +654,8 @@ static int validate_layer(const moe_fp4_layer* L, int64_t T) {
             (w == FP4_FMT_MXFP4 && (a == FP4_FMT_NONE || a == FP4_FMT_MXFP8)) ||
             (w == FP4_FMT_FP8_BLOCK && a == FP4_FMT_FP8_ROW);
   if (!ok) return fail(FP4_ERR_UNSUPPORTED, "format pair (w=%d, a=%d) not provided", w, a);
-  int blk = 16;
-  if (w == FP4_FMT_MXFP4) blk = 32;
+  // 32: the weight-only GEMV reads weight rows in chunks of 32 codes
+  int blk = 32;
   if (w == FP4_FMT_FP8_BLOCK) blk = 128;
   if (a != FP4_FMT_NONE) blk = std::max(blk, 32);
   if (L->hidden % blk || L->inter % blk)

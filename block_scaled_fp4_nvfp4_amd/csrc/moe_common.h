@@ -9,6 +9,13 @@
 namespace fp4 {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// 16-byte loads and stores through native vector types (a struct-of-uint
+// array of such values would be demoted to scratch memory).
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // 8 E2M1 nibbles (one dword, element i in bits 4i..4i+3) -> 8 bf16 values
 // as 4 packed pairs (e0,e1), (e2,e3), (e4,e5), (e6,e7).  The gfx950 scaled

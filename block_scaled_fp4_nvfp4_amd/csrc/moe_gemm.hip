@@ -50,11 +50,6 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef int intx8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // LDS rows hold 16-byte chunks in XOR-swizzled order so that the MFMA
 // fragment reads (16 lanes read the same chunk of 16 consecutive rows) and
@@ -212,13 +207,15 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
   };
   auto w_grow = [&](int i) __attribute__((always_inline)) -> int { return (i / BN) * g.N + nt * BN + (i % BN); };
 
-  // ---- per-thread global load assignments (fixed across K steps)
+  // ---- per-thread global load assignments (fixed across K steps).  Rows
+  // past the expert's end load row 0 of the expert instead: MFMA rows are
+  // independent and those rows are never stored, so no load is predicated
+  // and the K loop body stays one basic block.
   // A: MX/FP8 2 chunks of 16 B (rows tid/8 and 32 + tid/8); NV 1 chunk (row tid/4)
   constexpr int A_CH = GK == GK_NV ? 1 : 2;
   const uint8_t* a_src[A_CH];
-  bool a_ok[A_CH];
+  const uint8_t* an_src[A_CH];
   int a_lrow[A_CH], a_part[A_CH];
-  int64_t a_srow[A_CH];
 #pragma unroll
   for (int c = 0; c < A_CH; ++c) {
     const int ch = tid + 256 * c;
@@ -226,25 +223,99 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
     a_lrow[c] = r;
     a_part[c] = GK == GK_NV ? ch % 4 : ch % 8;
     bool ok;
-    const int arow = a_row_of(r, ok);
-    a_ok[c] = ok;
-    a_srow[c] = arow;
-    a_src[c] = g.a_codes + (int64_t)arow * a_rb;
+    const int64_t arow = a_row_of(r, ok);
+    a_src[c] = g.a_codes + arow * a_rb + (GK == GK_NV ? 16 * a_part[c] : 16 * a_part[c]);
+    an_src[c] = reinterpret_cast<const uint8_t*>(g.a_scales) + arow * (K / 16) + 2 * a_part[c];
   }
-  // A scales (MX: 4 bytes, FP8: one float per row per K step): threads 0..63
-  bool as_ok = false;
+  // A scales (MX: 4 bytes, FP8: one float per row per K step): every thread
+  // loads the scale of row tid % 64 (the four waves store identical values)
+  const int as_lrow = tid & (BM - 1);
   int64_t as_row = 0;
-  if (GK != GK_NV && tid < BM) as_row = a_row_of(tid, as_ok);
-  // W: WROWS * w_cpr chunks
-  constexpr int W_CH_MAX = (WROWS * w_cpr + 255) / 256;
+  {
+    bool ok;
+    as_row = a_row_of(as_lrow, ok);
+  }
+  // W: WROWS * w_cpr chunks of 16 B, a multiple of 256
+  constexpr int W_CH = WROWS * w_cpr / 256;
+  static_assert(WROWS * w_cpr % 256 == 0, "weight tile must split evenly over 256 threads");
+  const uint8_t* w_src[W_CH];
+  int w_soff[W_CH];
+#pragma unroll
+  for (int c = 0; c < W_CH; ++c) {
+    const int ch = tid + 256 * c;
+    const int row = ch / w_cpr, part = ch % w_cpr;
+    w_src[c] = w_base + (int64_t)w_grow(row) * w_rb + 16 * part;
+    w_soff[c] = swz<w_stride>(row, part);
+  }
+  // W scales: row tid % WROWS (WROWS <= 256; duplicates store identical values)
+  static_assert(WROWS <= 256 && (WROWS & (WROWS - 1)) == 0, "weight rows per tile");
+  const int ws_lrow = tid & (WROWS - 1);
+  const int64_t ws_grow = w_grow(ws_lrow);
 
-  u32x4 pa[A_CH];
-  uint32_t pas = 0;            // A scales (MX dword / FP8 float bits)
-  uint32_t pan[A_CH];          // NV A scale pairs
-  u32x4 pw[W_CH_MAX];
-  u32x2 pws[(WROWS + 255) / 256];
+  // One K step's operands on their way from global memory to LDS.
+  struct Stage {
+    u32x4 pa[A_CH];
+    uint32_t pas;            // A scales (MX dword / FP8 float bits)
+    uint32_t pan[A_CH];      // NV A scale pairs
+    u32x4 pw[W_CH];
+    u32x2 pws;
+  };
 
+  auto load_step = [&](Stage& R, int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      if (GK == GK_NV) {
+        R.pa[c] = ld16(a_src[c] + k0 / 2);
+        R.pan[c] = *reinterpret_cast<const uint16_t*>(an_src[c] + k0 / 16);
+      } else {
+        R.pa[c] = ld16(a_src[c] + k0);
+      }
+    }
+    if (GK == GK_MX)
+      R.pas = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(g.a_scales) + as_row * (K / 32) +
+                                                 k0 / 32);
+    if (GK == GK_FP8)
+      R.pas = __float_as_uint(reinterpret_cast<const float*>(g.a_scales)[as_row * (K / 128) + k0 / 128]);
+#pragma unroll
+    for (int c = 0; c < W_CH; ++c) R.pw[c] = ld16(w_src[c] + (WFP8 ? k0 : k0 / 2));
+    if (GK == GK_NV) {
+      R.pws = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(g.w_scales) +
+                                              ((int64_t)e * NW + ws_grow) * (K / 16) + k0 / 16);
+    } else if (GK == GK_MX) {
+      R.pws.x = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(g.w_scales) +
+                                                   ((int64_t)e * NW + ws_grow) * (K / 32) + k0 / 32);
+    } else {
+      R.pws.x = __float_as_uint(reinterpret_cast<const float*>(g.w_scales)[
+          ((int64_t)e * (NW / 128) + ws_grow / 128) * (K / 128) + k0 / 128]);
+    }
+  };
 
+  auto store_step = [&](const Stage& R, int buf) __attribute__((always_inline)) {
+    uint8_t* sb = lds + buf * stage;
+    uint8_t* s_a = sb;
+    uint8_t* s_as = sb + BM * C::A_STRIDE;
+    uint8_t* s_w = s_as + BM * C::A_SCALE_BYTES;
+    uint8_t* s_ws = s_w + WROWS * w_stride;
+#pragma unroll
+    for (int c = 0; c < A_CH; ++c) {
+      if (GK == GK_NV) {
+        uint32_t d[16];
+        nv_decode32(make_uint4(R.pa[c].x, R.pa[c].y, R.pa[c].z, R.pa[c].w), R.pan[c], d);
+        const int r = a_lrow[c], c0 = 4 * a_part[c];
+        st16(s_a + swz<256>(r, c0), u32x4{d[0], d[1], d[2], d[3]});
+        st16(s_a + swz<256>(r, c0 + 1), u32x4{d[4], d[5], d[6], d[7]});
+        st16(s_a + swz<256>(r, c0 + 2), u32x4{d[8], d[9], d[10], d[11]});
+        st16(s_a + swz<256>(r, c0 + 3), u32x4{d[12], d[13], d[14], d[15]});
+      } else {
+        st16(s_a + swz<128>(a_lrow[c], a_part[c]), R.pa[c]);
+      }
+    }
+    if (GK != GK_NV) reinterpret_cast<uint32_t*>(s_as)[as_lrow] = R.pas;
+#pragma unroll
+    for (int c = 0; c < W_CH; ++c) st16(s_w + w_soff[c], R.pw[c]);
+    if (GK == GK_NV) reinterpret_cast<u32x2*>(s_ws)[ws_lrow] = R.pws;
+    else reinterpret_cast<uint32_t*>(s_ws)[ws_lrow] = R.pws.x;
+  };
 
   floatx4 acc[4][NU * NSUB];
 #pragma unroll
@@ -258,60 +329,8 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
     return u * BN + wave * 16 * NSUB + j * 16 + lr;
   };
 
-  // iteration -1 only stages K step 0; iteration ks computes step ks while
-  // step ks+1 is loaded from global memory and then written to the other buffer
-  for (int ks = -1; ks < KS; ++ks) {
-    if (ks + 1 < KS) {
-    const int k0 = (ks + 1) * kBK;
-#pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      if (GK == GK_NV) {
-        const int kk = k0 + 32 * a_part[c];
-        pa[c] = a_ok[c] ? ld16(a_src[c] + kk / 2) : u32x4{0u, 0u, 0u, 0u};
-        pan[c] = a_ok[c] ? *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(g.a_scales) +
-                                                               a_srow[c] * (K / 16) + kk / 16)
-                         : 0u;
-      } else {
-        pa[c] = a_ok[c] ? ld16(a_src[c] + k0 + 16 * a_part[c]) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    if (GK == GK_MX && tid < BM)
-      pas = as_ok ? *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(g.a_scales) +
-                                                       as_row * (K / 32) + k0 / 32)
-                  : 0u;
-    if (GK == GK_FP8 && tid < BM)
-      pas = as_ok ? __float_as_uint(reinterpret_cast<const float*>(g.a_scales)[as_row * (K / 128) + k0 / 128]) : 0u;
-    const int nch = WROWS * w_cpr;
-#pragma unroll
-    for (int c = 0; c < W_CH_MAX; ++c) {
-      const int ch = tid + 256 * c;
-      if (ch < nch) {
-        const int row = ch / w_cpr, part = ch % w_cpr;
-        const int64_t gr = w_grow(row);
-        const int64_t kb = WFP8 ? k0 : k0 / 2;
-        pw[c] = ld16(w_base + gr * w_rb + kb + 16 * part);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < (WROWS + 255) / 256; ++c) {
-      const int row = tid + 256 * c;
-      if (row < WROWS) {
-        const int64_t gr = w_grow(row);
-        if (GK == GK_NV) {
-          pws[c] = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(g.w_scales) +
-                                                  ((int64_t)e * NW + gr) * (K / 16) + k0 / 16);
-        } else if (GK == GK_MX) {
-          pws[c].x = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(g.w_scales) +
-                                                       ((int64_t)e * NW + gr) * (K / 32) + k0 / 32);
-        } else {
-          pws[c].x = __float_as_uint(reinterpret_cast<const float*>(g.w_scales)[
-              ((int64_t)e * (NW / 128) + gr / 128) * (K / 128) + k0 / 128]);
-        }
-      }
-    }
-    }
-    if (ks >= 0) {
-    const uint8_t* sb = lds + (ks & 1) * stage;
+  auto compute_step = [&](int buf) __attribute__((always_inline)) {
+    const uint8_t* sb = lds + buf * stage;
     const uint8_t* s_a = sb;
     const uint8_t* s_as = sb + BM * C::A_STRIDE;
     const uint8_t* s_w = s_as + BM * C::A_SCALE_BYTES;
@@ -326,14 +345,20 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
           af[i][4 * q] = v.x; af[i][4 * q + 1] = v.y; af[i][4 * q + 2] = v.z; af[i][4 * q + 3] = v.w;
         }
       }
+      // all of this step's fragments are read before the first MFMA, so the
+      // LDS latency is paid once per step
+      u32x4 wc[NU * NSUB];
+      uint32_t ws2[NU * NSUB];
 #pragma unroll
       for (int s = 0; s < NU * NSUB; ++s) {
         const int wr = w_lrow(s);
-        const u32x4 cv = ld16(s_w + swz<w_stride>(wr, lg));
-        const uint4 c = make_uint4(cv.x, cv.y, cv.z, cv.w);
-        const uint32_t s2 = *reinterpret_cast<const uint16_t*>(s_ws + wr * 8 + 2 * lg);
+        wc[s] = ld16(s_w + swz<w_stride>(wr, lg));
+        ws2[s] = *reinterpret_cast<const uint16_t*>(s_ws + wr * 8 + 2 * lg);
+      }
+#pragma unroll
+      for (int s = 0; s < NU * NSUB; ++s) {
         uint32_t wd[16];
-        nv_decode32(c, s2, wd);
+        nv_decode32(make_uint4(wc[s].x, wc[s].y, wc[s].z, wc[s].w), ws2[s], wd);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -356,83 +381,84 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
           for (int r = 0; r < 4; ++r) afs[i][r] = reinterpret_cast<const float*>(s_as)[16 * i + 4 * lg + r];
         }
       }
+      intx8 bv[NU * NSUB];
+      int bsc[NU * NSUB];
+      float wfs[NU * NSUB];
 #pragma unroll
       for (int s = 0; s < NU * NSUB; ++s) {
         const int wr = w_lrow(s);
-        intx8 bv;
         if (w_fp8) {
           const u32x4 lo = ld16(s_w + swz<w_stride>(wr, lg));
           const u32x4 hi = ld16(s_w + swz<w_stride>(wr, 4 + lg));
-          bv = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          bv[s] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
         } else {
           const u32x4 c = ld16(s_w + swz<w_stride>(wr, lg));
-          bv = intx8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+          bv[s] = intx8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
         }
+        if (GK == GK_MX) bsc[s] = s_ws[wr * 4 + lg];
+        else wfs[s] = reinterpret_cast<const float*>(s_ws)[wave * 16 * NSUB + (s % NSUB) * 16 + (s / NSUB) * BN];
+      }
+      // all of this step's fragments are read before the first MFMA, so the
+      // LDS latency is paid once per step
+#pragma unroll
+      for (int s = 0; s < NU * NSUB; ++s) {
         if (GK == GK_MX) {
-          const int bsc = s_ws[wr * 4 + lg];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (w_fp8)
-              acc[i][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bv, acc[i][s], 0, 0, 0, asc[i],
-                                                                           0, bsc);
+              acc[i][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bv[s], acc[i][s], 0, 0, 0, asc[i],
+                                                                           0, bsc[s]);
             else
-              acc[i][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bv, acc[i][s], 0, 4, 0, asc[i],
-                                                                           0, bsc);
+              acc[i][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bv[s], acc[i][s], 0, 4, 0, asc[i],
+                                                                           0, bsc[s]);
           }
         } else {
-          const float wfs = reinterpret_cast<const float*>(s_ws)[wave * 16 * NSUB + (s % NSUB) * 16 +
-                                                                (s / NSUB) * BN];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const floatx4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                af[i], bv, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+                af[i], bv[s], floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][s][r] = fmaf(p[r], afs[i][r] * wfs, acc[i][s][r]);
+            for (int r = 0; r < 4; ++r) acc[i][s][r] = fmaf(p[r], afs[i][r] * wfs[s], acc[i][s][r]);
           }
         }
       }
     }
-    }
+  };
+
+  // Pin this step's accumulators before the LDS stores that follow: without
+  // the empty asm uses the compiler sinks the MFMAs below the stores (and
+  // their vmcnt wait), and every step then exposes the full load latency.
+  // Accumulators live in AGPRs except on the FP8 path, which rescales them
+  // with VALU FMAs.
+  auto pin_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int s = 0; s < NU * NSUB; ++s) {
+        if (GK == GK_FP8) asm volatile("" ::"v"(acc[i][s]));
+        else asm volatile("" ::"a"(acc[i][s]));
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // K loop over two LDS buffers: step ks is computed from buffer ks&1 while
+  // the global loads of step ks+1 (issued at the end of the previous step)
+  // are in flight; they are stored to the other buffer once this step's
+  // MFMAs have been issued.  (A second register stage, to issue loads two
+  // steps ahead, measured no faster and costs occupancy.)
+  Stage R;
+  load_step(R, 0);
+  store_step(R, 0);
+  __syncthreads();
+  if (KS > 1) load_step(R, kBK);
+  for (int ks = 0; ks < KS; ++ks) {
+    compute_step(ks & 1);
     if (ks + 1 < KS) {
-    uint8_t* sb = lds + ((ks + 1) & 1) * stage;
-    uint8_t* s_a = sb;
-    uint8_t* s_as = sb + BM * C::A_STRIDE;
-    uint8_t* s_w = s_as + BM * C::A_SCALE_BYTES;
-    uint8_t* s_ws = s_w + WROWS * w_stride;
-#pragma unroll
-    for (int c = 0; c < A_CH; ++c) {
-      if (GK == GK_NV) {
-        uint32_t d[16];
-        nv_decode32(make_uint4(pa[c].x, pa[c].y, pa[c].z, pa[c].w), pan[c], d);
-        const int r = a_lrow[c], c0 = 4 * a_part[c];
-        st16(s_a + swz<256>(r, c0), u32x4{d[0], d[1], d[2], d[3]});
-        st16(s_a + swz<256>(r, c0 + 1), u32x4{d[4], d[5], d[6], d[7]});
-        st16(s_a + swz<256>(r, c0 + 2), u32x4{d[8], d[9], d[10], d[11]});
-        st16(s_a + swz<256>(r, c0 + 3), u32x4{d[12], d[13], d[14], d[15]});
-      } else {
-        st16(s_a + swz<128>(a_lrow[c], a_part[c]), pa[c]);
-      }
+      pin_acc();
+      store_step(R, (ks + 1) & 1);
+      __syncthreads();
+      if (ks + 2 < KS) load_step(R, (ks + 2) * kBK);
     }
-    if (GK != GK_NV && tid < BM) reinterpret_cast<uint32_t*>(s_as)[tid] = pas;
-    const int nch = WROWS * w_cpr;
-#pragma unroll
-    for (int c = 0; c < W_CH_MAX; ++c) {
-      const int ch = tid + 256 * c;
-      if (ch < nch) {
-        const int row = ch / w_cpr, part = ch % w_cpr;
-        st16(s_w + swz<w_stride>(row, part), pw[c]);
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < (WROWS + 255) / 256; ++c) {
-      const int row = tid + 256 * c;
-      if (row < WROWS) {
-        if (GK == GK_NV) reinterpret_cast<u32x2*>(s_ws)[row] = pws[c];
-        else reinterpret_cast<uint32_t*>(s_ws)[row] = pws[c].x;
-      }
-    }
-    }
-    __syncthreads();
   }
 
   // ---- epilogue
