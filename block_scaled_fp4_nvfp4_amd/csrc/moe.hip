@@ -89,22 +89,51 @@ int plan_workspace(const moe_fp4_layer* L, int64_t T, WsPlan* w) {
 
 // ----------------------------------------------------------------- permute
 
-// Exclusive scan over 1024 threads of one workgroup; returns the prefix of
-// `v` and writes the total to *total.  `tmp` holds 1024 ints of LDS.
-__device__ int block_scan_1024(int v, int* tmp, int* total) {
-  int tid = threadIdx.x;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    int add = tid >= d ? tmp[tid - d] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
+// Exclusive scan of up to three ints per thread over the 1024 threads of one
+// workgroup: shuffle scans within each wave, then one wave scans the 16 wave
+// totals (two barriers).  Returns the exclusive prefixes in v[] and the
+// totals in total[].  `tmp` holds 64 ints of LDS.
+template <int NV>
+__device__ void block_scan_1024(int (&v)[NV], int* tmp, int (&total)[NV]) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int x[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) x[i] = v[i];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int y = __shfl_up(x[i], d, 64);
+      if (lane >= d) x[i] += y;
+    }
   }
-  int incl = tmp[tid];
-  *total = tmp[1023];
+  if (lane == 63) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) tmp[i * 16 + w] = x[i];
+  }
   __syncthreads();
-  return incl - v;
+  if (w == 0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int t = lane < 16 ? tmp[i * 16 + lane] : 0;
+      int s = t;
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) {
+        const int y = __shfl_up(s, d, 64);
+        if (lane >= d) s += y;
+      }
+      if (lane < 16) tmp[i * 16 + lane] = s - t;  // exclusive wave prefix
+      if (lane == 15) tmp[48 + i] = s;             // total
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int incl = x[i] + tmp[i * 16 + w];
+    total[i] = tmp[48 + i];
+    v[i] = incl - v[i];
+  }
+  __syncthreads();
 }
 
 // Counts, offsets, active-expert list and GEMM tile offsets from per-expert
@@ -121,10 +150,10 @@ __device__ void finish_offsets(const int32_t* cnt, int E, int tile_m, int32_t* o
     s_act += c > 0;
     s_tile += (c + tile_m - 1) / tile_m;
   }
-  int tot_cnt, tot_act, tot_tile;
-  int b_cnt = block_scan_1024(s_cnt, tmp, &tot_cnt);
-  int b_act = block_scan_1024(s_act, tmp, &tot_act);
-  int b_tile = block_scan_1024(s_tile, tmp, &tot_tile);
+  int b[3] = {s_cnt, s_act, s_tile}, tot[3];
+  block_scan_1024<3>(b, tmp, tot);
+  int b_cnt = b[0], b_act = b[1], b_tile = b[2];
+  const int tot_cnt = tot[0], tot_act = tot[1], tot_tile = tot[2];
   for (int e = lo; e < hi; ++e) {
     int c = cnt[e];
     offsets[e] = b_cnt;
@@ -169,8 +198,9 @@ __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restr
   int r = 0;
   if (my >= 0)
     for (int q = 0; q < tid; ++q) r += s_ids[q] == my;
-  int bad_total;
-  (void)block_scan_1024(my == -2 ? 1 : 0, tmp, &bad_total);  // also orders the histogram updates
+  int bad[1] = {my == -2 ? 1 : 0}, bad_tot[1];
+  block_scan_1024<1>(bad, tmp, bad_tot);  // also orders the histogram updates
+  const int bad_total = bad_tot[0];
   for (int e = tid; e < E; e += 1024) counts[e] = s_hist[e];
   finish_offsets(s_hist, E, tile_m, offsets, active, tile_offsets, tmp, s_off);
   __syncthreads();
@@ -230,20 +260,30 @@ __global__ void __launch_bounds__(1024) perm_scan_kernel(int nb, int E, int tile
                                                          int32_t* __restrict__ active,
                                                          int32_t* __restrict__ tile_offsets,
                                                          int32_t* __restrict__ error_flag) {
-  __shared__ int tmp[1024];
+  __shared__ int tmp[64];
   for (int e = threadIdx.x; e < E; e += 1024) {
-    int run = 0;
-    for (int b = 0; b < nb; ++b) {
+    int run = 0, b = 0;
+    for (; b + 16 <= nb; b += 16) {  // 16 independent loads in flight
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) c[u] = block_counts[(int64_t)(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        block_counts[(int64_t)(b + u) * E + e] = run;
+        run += c[u];
+      }
+    }
+    for (; b < nb; ++b) {
       int c = block_counts[(int64_t)b * E + e];
       block_counts[(int64_t)b * E + e] = run;
       run += c;
     }
     counts[e] = run;
   }
-  int bad = 0;
-  for (int b = threadIdx.x; b < nb; b += 1024) bad += block_invalid[b];
-  int tot_bad;
-  (void)block_scan_1024(bad, tmp, &tot_bad);
+  int bad[1] = {0}, bad_tot[1];
+  for (int b = threadIdx.x; b < nb; b += 1024) bad[0] += block_invalid[b];
+  block_scan_1024<1>(bad, tmp, bad_tot);
+  const int tot_bad = bad_tot[0];
   __threadfence_block();
   __syncthreads();
   finish_offsets(counts, E, tile_m, offsets, active, tile_offsets, tmp);
@@ -355,52 +395,60 @@ __device__ __forceinline__ float chunk_dot_f32(u32x4 c, uint32_t sbits, const fl
   return fmaf(d0 + d1, chunk_scale<WFMT, 0>(sbits), acc);
 }
 
-constexpr int kGvOut = 16;      // outputs j per workgroup of the gate_up GEMV (one per 16 lanes)
+constexpr int kGvRounds = 2;    // rounds of 16 outputs per workgroup of the gate_up GEMV
+constexpr int kGvOut = 16 * kGvRounds;
 constexpr int kGvTokens = 4;    // tokens whose activations are staged in LDS per pass
 constexpr int kGdRows = 128;    // output rows per workgroup of the down GEMV (2 per 4 lanes)
 constexpr int kGdTokens = 8;
 
 // gate_up + SiLU*up for the pairs of one expert, bf16 activations.
-// Grid: (ceil(I / 16), max active experts).  Each group of 16 lanes owns one
-// output j: gate row j and up row I+j, split into 16-byte chunks of 32 codes
-// (lane l takes chunks l, l+16, ...).  All of a row pair's codes and scales
-// are loaded at once (about 2.9 KB per group at the decode shape) and reused
-// for every token of the expert; the tokens' activations are staged in LDS,
-// four tokens per pass, as [token][quarter q][chunk c] 16-byte pieces so
-// that the 16 lanes of a group read consecutive pieces.
+// Grid: (ceil(I / 32), max active experts).  Each group of 16 lanes owns two
+// outputs j (one per round, 16 apart): gate row j and up row I+j, split into
+// 16-byte chunks of 32 codes (lane l takes chunks l, l+16, ...).  Both
+// rounds' codes and scales are loaded up front (about 5.8 KB per group at
+// the decode shape, 92 KB per workgroup) and reused for every token of the
+// expert; the tokens' activations are staged in LDS, four tokens per pass, as
+// [token][quarter q][chunk c] 16-byte pieces so that the 16 lanes of a group
+// read consecutive pieces.
 template <int WFMT, int CPL>
 __global__ void __launch_bounds__(256) gemv_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ pair_of_row, const int32_t* __restrict__ active,
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s, const float* __restrict__ w13s2,
     int H, int I, int k, float* __restrict__ h) {
+  constexpr int kStageLoads = (kGvTokens * 4 * 16 * CPL + 255) / 256;  // 16-byte pieces per thread
   __shared__ __attribute__((aligned(16))) uint8_t xs[kGvTokens * 4 * CPL * 16 * 16];
+  __shared__ int s_tok[kGvTokens];
   const int ai = blockIdx.y;
   if (ai >= active[0]) return;
   const int e = active[1 + ai];
   const int tid = threadIdx.x, l = tid & 15;
-  const int j = blockIdx.x * kGvOut + (tid >> 4);
-  const bool jv = j < I;
-  const int jj = jv ? j : I - 1;
   const int NCH = H >> 5;  // 32-value chunks per row
   const int64_t row_bytes = H >> 1;
   const int64_t srow = scale_row_stride<WFMT>(H);
-  const uint8_t* wg = w13 + ((int64_t)e * 2 * I + jj) * row_bytes;
-  const uint8_t* wu = wg + (int64_t)I * row_bytes;
-  const uint8_t* sg = w13s + ((int64_t)e * 2 * I + jj) * srow;
-  const uint8_t* su = sg + (int64_t)I * srow;
-  u32x4 cg[CPL], cu[CPL];
-  uint32_t bg[CPL], bu[CPL];
+  int jr[kGvRounds];
+  u32x4 cg[kGvRounds][CPL], cu[kGvRounds][CPL];
+  uint32_t bg[kGvRounds][CPL], bu[kGvRounds][CPL];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = l + 16 * i;
-    const bool in = c < NCH;
-    const int cc = in ? c : 0;
-    cg[i] = ld16(wg + 16 * cc);
-    cu[i] = ld16(wu + 16 * cc);
-    bg[i] = in ? chunk_scale_bits<WFMT>(sg, cc) : 0u;  // scale 0 zeroes the padding chunks
-    bu[i] = in ? chunk_scale_bits<WFMT>(su, cc) : 0u;
-    if (WFMT == FP4_FMT_MXFP4 && !in) { cg[i] = u32x4{0u, 0u, 0u, 0u}; cu[i] = cg[i]; }
+  for (int rd = 0; rd < kGvRounds; ++rd) {
+    const int j = blockIdx.x * kGvOut + rd * 16 + (tid >> 4);
+    jr[rd] = j;
+    const int jj = j < I ? j : I - 1;
+    const uint8_t* wg = w13 + ((int64_t)e * 2 * I + jj) * row_bytes;
+    const uint8_t* wu = wg + (int64_t)I * row_bytes;
+    const uint8_t* sg = w13s + ((int64_t)e * 2 * I + jj) * srow;
+    const uint8_t* su = sg + (int64_t)I * srow;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = l + 16 * i;
+      const bool in = c < NCH;
+      const int cc = in ? c : 0;
+      cg[rd][i] = ld16(wg + 16 * cc);
+      cu[rd][i] = ld16(wu + 16 * cc);
+      bg[rd][i] = in ? chunk_scale_bits<WFMT>(sg, cc) : 0u;  // scale 0 zeroes the padding chunks
+      bu[rd][i] = in ? chunk_scale_bits<WFMT>(su, cc) : 0u;
+      if (WFMT == FP4_FMT_MXFP4 && !in) { cg[rd][i] = u32x4{0u, 0u, 0u, 0u}; cu[rd][i] = cg[rd][i]; }
+    }
   }
   const float S = WFMT == FP4_FMT_NVFP4 ? w13s2[e] : 1.0f;
   const int r0 = offsets[e], n = offsets[e + 1] - r0;
@@ -408,39 +456,57 @@ __global__ void __launch_bounds__(256) gemv_gateup_kernel(
   for (int t0 = 0; t0 < n; t0 += kGvTokens) {
     const int nt = min(kGvTokens, n - t0);
     if (t0 > 0) __syncthreads();
-    for (int idx = tid; idx < nt * pieces; idx += 256) {
-      const int t = idx / pieces, rem = idx - t * pieces;
-      const int c = rem >> 2, q = rem & 3;
-      const uint8_t* xrow = reinterpret_cast<const uint8_t*>(x + (int64_t)(pair_of_row[r0 + t0 + t] / k) * H);
-      st16(xs + ((t * 4 + q) * NCH + c) * 16, ld16(xrow + 64 * c + 16 * q));
+    if (tid < nt) s_tok[tid] = pair_of_row[r0 + t0 + tid] / k;
+    __syncthreads();
+    // all of the pass's activation pieces are loaded before any is stored
+    u32x4 buf[kStageLoads];
+    int dst[kStageLoads];
+#pragma unroll
+    for (int u = 0; u < kStageLoads; ++u) {
+      const int idx = tid + 256 * u;
+      dst[u] = -1;
+      if (idx < nt * pieces) {
+        int t = 0;
+#pragma unroll
+        for (int m = 1; m < kGvTokens; ++m) t += idx >= m * pieces;
+        const int rem = idx - t * pieces, c = rem >> 2, q = rem & 3;
+        buf[u] = ld16(reinterpret_cast<const uint8_t*>(x + (int64_t)s_tok[t] * H) + 64 * c + 16 * q);
+        dst[u] = ((t * 4 + q) * NCH + c) * 16;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < kStageLoads; ++u)
+      if (dst[u] >= 0) st16(xs + dst[u], buf[u]);
     __syncthreads();
     for (int t = 0; t < nt; ++t) {
-      // keep the packed codes (not their 4x larger bf16 expansion) live
-      // across the token loop: the expansion is redone per token
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) asm volatile("" : "+v"(cg[i]), "+v"(cu[i]));
-      float ag = 0.0f, au = 0.0f;
+      for (int rd = 0; rd < kGvRounds; ++rd) {
+        // keep the packed codes (not their 4x larger bf16 expansion) live
+        // across the token loop: the expansion is redone per token
 #pragma unroll
-      for (int i = 0; i < CPL; ++i) {
-        const int c = l + 16 * i;
-        if (c < NCH) {
-          uint32_t xv[16];
+        for (int i = 0; i < CPL; ++i) asm volatile("" : "+v"(cg[rd][i]), "+v"(cu[rd][i]));
+        float ag = 0.0f, au = 0.0f;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const u32x4 v = ld16(xs + ((t * 4 + q) * NCH + c) * 16);
-            xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
+        for (int i = 0; i < CPL; ++i) {
+          const int c = l + 16 * i;
+          if (c < NCH) {
+            uint32_t xv[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const u32x4 v = ld16(xs + ((t * 4 + q) * NCH + c) * 16);
+              xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
+            }
+            ag = chunk_dot_bf16<WFMT>(cg[rd][i], bg[rd][i], xv, ag);
+            au = chunk_dot_bf16<WFMT>(cu[rd][i], bu[rd][i], xv, au);
           }
-          ag = chunk_dot_bf16<WFMT>(cg[i], bg[i], xv, ag);
-          au = chunk_dot_bf16<WFMT>(cu[i], bu[i], xv, au);
         }
-      }
 #pragma unroll
-      for (int off = 8; off > 0; off >>= 1) {
-        ag += __shfl_xor(ag, off, 16);
-        au += __shfl_xor(au, off, 16);
+        for (int off = 8; off > 0; off >>= 1) {
+          ag += __shfl_xor(ag, off, 16);
+          au += __shfl_xor(au, off, 16);
+        }
+        if (l == 0 && jr[rd] < I) h[(int64_t)(r0 + t0 + t) * I + jr[rd]] = silu_f32(ag * S) * (au * S);
       }
-      if (l == 0 && jv) h[(int64_t)(r0 + t0 + t) * I + j] = silu_f32(ag * S) * (au * S);
     }
   }
 }
@@ -457,6 +523,7 @@ __global__ void __launch_bounds__(256) gemv_down_kernel(
     const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s, const float* __restrict__ w2s2,
     int H, int I, float* __restrict__ o) {
   constexpr int kChunkBytes = 144;
+  constexpr int kStageLoads = (kGdTokens * 4 * CPL * 8 + 255) / 256;  // 16-byte pieces per thread
   __shared__ __attribute__((aligned(16))) uint8_t hs[kGdTokens * 4 * CPL * kChunkBytes];
   const int ai = blockIdx.y;
   if (ai >= active[0]) return;
@@ -492,12 +559,27 @@ __global__ void __launch_bounds__(256) gemv_down_kernel(
   for (int t0 = 0; t0 < n; t0 += kGdTokens) {
     const int nt = min(kGdTokens, n - t0);
     if (t0 > 0) __syncthreads();
-    for (int idx = tid; idx < nt * NCH * 8; idx += 256) {  // 8 pieces of 16 bytes per chunk
-      const int t = idx / (NCH * 8), rem = idx - t * NCH * 8;
-      const int c = rem >> 3, q = rem & 7;
-      const uint8_t* hrow = reinterpret_cast<const uint8_t*>(h + (int64_t)(r0 + t0 + t) * I);
-      st16(hs + t * tok_bytes + c * kChunkBytes + 16 * q, ld16(hrow + 128 * c + 16 * q));
+    // all of the pass's h pieces (8 of 16 bytes per chunk) are loaded before
+    // any is stored
+    const int pieces = NCH * 8;
+    u32x4 buf[kStageLoads];
+    int dst[kStageLoads];
+#pragma unroll
+    for (int u = 0; u < kStageLoads; ++u) {
+      const int idx = tid + 256 * u;
+      dst[u] = -1;
+      if (idx < nt * pieces) {
+        int t = 0;
+#pragma unroll
+        for (int m = 1; m < kGdTokens; ++m) t += idx >= m * pieces;
+        const int rem = idx - t * pieces, c = rem >> 3, q = rem & 7;
+        buf[u] = ld16(reinterpret_cast<const uint8_t*>(h + (int64_t)(r0 + t0 + t) * I) + 128 * c + 16 * q);
+        dst[u] = t * tok_bytes + c * kChunkBytes + 16 * q;
+      }
     }
+#pragma unroll
+    for (int u = 0; u < kStageLoads; ++u)
+      if (dst[u] >= 0) st16(hs + dst[u], buf[u]);
     __syncthreads();
     for (int t = 0; t < nt; ++t) {
 #pragma unroll
