@@ -178,6 +178,11 @@ int moe_fp4_workspace_size(const moe_fp4_layer* layer, int64_t tokens,
  *  topk_weights f32 [T, k], routing weights, applied after the down projection.
  *  workspace    >= moe_fp4_workspace_size bytes of device memory.
  * Routing (softmax / top-k) is done by the caller.
+ * Shape errors (FP4_ERR_SHAPE): hidden or inter not a multiple of 32 (128 for
+ * the quantized-activation pairs and block FP8; shared width a multiple of
+ * 128).  FP4_ERR_UNSUPPORTED: k > 32, E > 8192, or, for weight-only layers,
+ * hidden > 4096 or inter > 1024 (the decode GEMVs hold a row pair's codes in
+ * registers).
  */
 int moe_fp4_forward(const moe_fp4_layer* layer, const uint16_t* x, int64_t tokens,
                     const int32_t* topk_ids, const float* topk_weights, float* y,

@@ -8,12 +8,12 @@ weights w_tj (j < k):
 
 with W~ the dequantized weights (exact values), x~ = Qx(x) and Qh the
 dynamic activation quantizers of the mode: identity for bf16 activations
-(W4A16: "weight-only NVFP4 (NVFP4A16)", dabsLabs card), NVFP4 with tensor
-scale amax/2688 and plain amax/6 block scales (W4A4; "Local-Hessian NVFP4
-experts", opening section), MXFP8 per 32 ("MXFP4-FP8-R12", section
+(W4A16, the weight-only NVFP4 mode of the dabsLabs NVFP4 card), NVFP4 with
+tensor scale amax/2688 and plain amax/6 block scales (W4A4; LocalHessian-
+Experts card, opening section), MXFP8 per 32 (MXFP4-FP8-R12 card, section
 "Quantization format"), or FP8 with one fp32 scale per (row, 128 columns)
-(the "Dynamic-FP8 routed-expert path", same card, runtime contract table;
-a_fmt "fp8_row").
+(the dynamic-FP8 path of the retained routed experts, same card, runtime
+contract table; a_fmt "fp8_row").
 The fused gate_up weight holds gate rows first, then up rows (dabsLabs card:
 experts stored stacked as [512, out, in] with fused gate_up).  The shared
 expert ("FP4-Local AZ", section "The shared expert") is MXFP8 with MXFP8
