@@ -486,6 +486,238 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
     }
 }
 
+// ------------------------------------------- MX path with LDS-DMA staging
+//
+// MXFP4 weights x MXFP8 activations.  Same tile as above (64 rows x 64*NSUB
+// outputs, 4 waves, 16 MFMAs of 16x16x128 per wave and step), but the
+// operands go from global memory straight into LDS (global_load_lds: lane l
+// of a DMA instruction writes LDS bytes base + 16 l .. + 15) through a ring
+// of three stages, so the loads of step ks+2 are in flight while step ks is
+// computed and no registers are spent on staging.  Each stage holds
+// [A 64 x 128 B | W WROWS x 64 B | A scales 64 dwords | W scales WROWS
+// dwords]; A and W rows keep the XOR-swizzled chunk order (a lane fetches
+// the global chunk that belongs in the LDS slot its lane number selects).
+// Every thread issues the same number of DMA instructions per step, so one
+// wait for vmcnt <= N_INS before the step's barrier completes its own
+// instructions for the step about to be read; the barrier then covers the
+// other waves' instructions.
+template <int EPI, int NSUB>
+struct MxCfg {
+  static constexpr int BM = kBM;
+  static constexpr int BN = 64 * NSUB;
+  static constexpr int NU = EPI == EPI_GATEUP ? 2 : 1;
+  static constexpr int WROWS = NU * BN;
+  static constexpr int A_BYTES = BM * 128;
+  static constexpr int W_BYTES = WROWS * 64;
+  static constexpr int A_INS = A_BYTES / 4096;  // 16-byte DMA instructions per thread per step
+  static constexpr int W_INS = W_BYTES / 4096;
+  static constexpr int SC_DW = BM + WROWS;      // scale dwords per step
+  static constexpr int S_INS = (SC_DW + 255) / 256;  // 4-byte DMA instructions per thread per step
+  static constexpr int N_INS = A_INS + W_INS + S_INS;
+  static constexpr int STAGE = A_BYTES + W_BYTES + SC_DW * 4;
+  static_assert(A_BYTES % 4096 == 0 && W_BYTES % 4096 == 0 && SC_DW % 64 == 0, "DMA tiling");
+};
+
+// One DMA instruction: lane l copies 16 (4) bytes from its global address to
+// LDS address lds + 16 l (lds + 4 l).
+__device__ __forceinline__ void dma16_to_lds(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4_to_lds(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8): vmcnt <= n only, and vmcnt <= n with lgkmcnt = 0.
+constexpr int vmcnt_only(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int vmcnt_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+
+template <int EPI, int NSUB>
+__global__ void __launch_bounds__(256, 2) grouped_gemm_mx_kernel(GemmArgs g) {
+  using C = MxCfg<EPI, NSUB>;
+  constexpr int BM = C::BM, BN = C::BN, NU = C::NU, WROWS = C::WROWS;
+  __shared__ __attribute__((aligned(16))) uint8_t st0[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st1[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t st2[C::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t dummy[256];  // target of the unused scale DMA lanes
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  int* s_toff = reinterpret_cast<int*>(lds_dyn);
+
+  const int NT = g.N / BN;
+  const int G = gridDim.x;
+  const int per_xcd = G / 8;
+  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+
+  int e, mt, nt, r_begin, n_rows;
+  if (g.dense_rows > 0) {
+    e = 0;
+    nt = L % NT;
+    mt = L / NT;
+    if (mt * BM >= g.dense_rows) return;
+    r_begin = 0;
+    n_rows = g.dense_rows;
+  } else {
+    for (int i = threadIdx.x; i <= g.E; i += 256) s_toff[i] = g.tile_offsets[i];
+    __syncthreads();
+    nt = L % NT;
+    const int mg = L / NT;
+    if (mg >= s_toff[g.E]) return;
+    int lo = 0, hi = g.E;
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (s_toff[mid] <= mg) lo = mid; else hi = mid;
+    }
+    e = lo;
+    mt = mg - s_toff[e];
+    r_begin = g.offsets[e];
+    n_rows = g.offsets[e + 1] - r_begin;
+  }
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int K = g.K;
+  const int KS = K / kBK;
+  const int NW = NU * g.N;
+  const int SKB = K / 32;  // scale bytes per row (one UE8M0 per 32)
+  const uint8_t* w_base = g.w_codes + (int64_t)e * NW * (K / 2);
+
+  // rows past the expert's end fetch row 0 of the expert (never stored)
+  auto a_row_of = [&](int r) __attribute__((always_inline)) -> int64_t {
+    const int rr = mt * BM + r;
+    const int R = r_begin + (rr < n_rows ? rr : 0);
+    return g.a_gather ? g.pair_of_row[R] / g.k : R;
+  };
+  auto w_grow = [&](int i) __attribute__((always_inline)) -> int { return (i / BN) * g.N + nt * BN + (i % BN); };
+
+  // global source of this lane for each DMA instruction (K step 0); the step
+  // advances A by 128 bytes, W by 64 bytes and the scales by 4 bytes
+  const uint8_t* a_src[C::A_INS];
+  const uint8_t* w_src[C::W_INS];
+  const uint8_t* s_src[C::S_INS];
+#pragma unroll
+  for (int q = 0; q < C::A_INS; ++q) {
+    const int row = (q * 4 + wave) * 8 + (lane >> 3), slot = lane & 7;
+    const int chunk = slot ^ ((row ^ (row >> 3)) & 7);  // inverse of swz<128>
+    a_src[q] = g.a_codes + a_row_of(row) * K + 16 * chunk;
+  }
+#pragma unroll
+  for (int q = 0; q < C::W_INS; ++q) {
+    const int row = (q * 4 + wave) * 16 + (lane >> 2), slot = lane & 3;
+    const int chunk = slot ^ (((row >> 1) ^ (row >> 3)) & 3);  // inverse of swz<64>
+    w_src[q] = w_base + (int64_t)w_grow(row) * (K / 2) + 16 * chunk;
+  }
+#pragma unroll
+  for (int q = 0; q < C::S_INS; ++q) {
+    const int d = (q * 4 + wave) * 64 + lane;
+    if (d < BM)
+      s_src[q] = reinterpret_cast<const uint8_t*>(g.a_scales) + a_row_of(d) * SKB;
+    else if (d < C::SC_DW)
+      s_src[q] = reinterpret_cast<const uint8_t*>(g.w_scales) + ((int64_t)e * NW + w_grow(d - BM)) * SKB;
+    else
+      s_src[q] = reinterpret_cast<const uint8_t*>(g.a_scales) + a_row_of(0) * SKB;
+  }
+
+  // ks < 0: the same instructions all read one 16-byte line (a stage that is
+  // never read again is refilled with it), so every step issues N_INS DMA
+  // instructions without moving data
+  auto dma_step = [&](uint8_t* st, int ks) __attribute__((always_inline)) {
+    const bool real = ks >= 0;
+#pragma unroll
+    for (int q = 0; q < C::A_INS; ++q)
+      dma16_to_lds(real ? a_src[q] + ks * 128 : g.a_codes, st + (q * 4 + wave) * 1024);
+#pragma unroll
+    for (int q = 0; q < C::W_INS; ++q)
+      dma16_to_lds(real ? w_src[q] + ks * 64 : g.a_codes, st + C::A_BYTES + (q * 4 + wave) * 1024);
+#pragma unroll
+    for (int q = 0; q < C::S_INS; ++q) {
+      const int d0 = (q * 4 + wave) * 64;
+      uint8_t* dst = d0 < C::SC_DW ? st + C::A_BYTES + C::W_BYTES + d0 * 4 : dummy;
+      dma4_to_lds(real ? s_src[q] + ks * 4 : g.a_codes, dst);
+    }
+  };
+
+  floatx4 acc[4][NU * NSUB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int s = 0; s < NU * NSUB; ++s) acc[i][s] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute_step = [&](const uint8_t* st) __attribute__((always_inline)) {
+    const uint8_t* s_a = st;
+    const uint8_t* s_w = st + C::A_BYTES;
+    const uint8_t* s_as = st + C::A_BYTES + C::W_BYTES;
+    const uint8_t* s_ws = s_as + BM * 4;
+    intx8 af[4];
+    int asc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 lo = ld16(s_a + swz<128>(16 * i + lr, lg));
+      const u32x4 hi = ld16(s_a + swz<128>(16 * i + lr, 4 + lg));
+      af[i] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      asc[i] = s_as[(16 * i + lr) * 4 + lg];
+    }
+#pragma unroll
+    for (int s = 0; s < NU * NSUB; ++s) {
+      const int wr = (s / NSUB) * BN + wave * 16 * NSUB + (s % NSUB) * 16 + lr;
+      const u32x4 c = ld16(s_w + swz<64>(wr, lg));
+      const intx8 bv = intx8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+      const int bsc = s_ws[wr * 4 + lg];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc[i][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bv, acc[i][s], 0, 4, 0, asc[i], 0, bsc);
+    }
+  };
+
+  // one step: wait for this thread's DMAs of the stage to be read (the
+  // next step's DMAs may stay in flight), barrier
+  // (everyone's DMAs done, everyone done reading the stage about to be
+  // refilled), refill the stage two steps ahead, compute
+  auto step = [&](const uint8_t* cur, uint8_t* refill, int ks) __attribute__((always_inline)) {
+    // own DMAs done; own LDS reads of the previous step done
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(C::N_INS));
+    // a bare barrier that the compiler cannot move memory operations across
+    // (a fenced __syncthreads would also wait for every DMA in flight)
+    asm volatile("s_barrier" ::: "memory");
+    dma_step(refill, ks + 2 < KS ? ks + 2 : -1);
+    compute_step(cur);
+  };
+
+  dma_step(st0, 0);
+  dma_step(st1, KS > 1 ? 1 : -1);
+  int ks = 0;
+  for (; ks + 3 <= KS; ks += 3) {
+    step(st0, st2, ks);
+    step(st1, st0, ks + 1);
+    step(st2, st1, ks + 2);
+  }
+  if (ks < KS) step(st0, st2, ks);
+  if (ks + 1 < KS) step(st1, st0, ks + 1);
+  __builtin_amdgcn_s_waitcnt(vmcnt_only(0));  // no DMA outstanding at exit
+
+  // ---- epilogue
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+      const int n = nt * BN + wave * 16 * NSUB + j * 16 + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = mt * BM + 16 * i + 4 * lg + r;
+        if (rr >= n_rows) continue;
+        const int64_t R = r_begin + rr;
+        float v;
+        if (EPI == EPI_GATEUP) {
+          v = silu_f32(acc[i][j][r]) * acc[i][NSUB + j][r];
+        } else {
+          v = acc[i][j][r];
+          if (g.row_scale) v *= g.row_scale[R];
+        }
+        g.out[R * g.N + n] = v;
+      }
+    }
+}
+
 // Zero rows [n_valid, P) of a [P, cols] f32 buffer (n_valid read on the device).
 __global__ void zero_rows_tail_kernel(float* __restrict__ buf, const int32_t* __restrict__ n_valid, int64_t P,
                                       int cols) {
@@ -538,6 +770,29 @@ static int launch_gemm_n(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t s
   return check_launch("grouped_gemm");
 }
 
+template <int EPI, int NSUB>
+static int launch_gemm_mx(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+  using C = MxCfg<EPI, NSUB>;
+  const int NT = a.N / C::BN;
+  int64_t G = tiles_m_bound * NT;
+  G = (G + 7) / 8 * 8;
+  if (G <= 0) return FP4_OK;
+  if (G > INT32_MAX) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM grid too large");
+  const size_t lds = a.dense_rows > 0 ? 0 : sizeof(int) * ((size_t)a.E + 1);
+  if (3 * (size_t)C::STAGE + 256 + lds > 160 * 1024)
+    return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_mx_kernel<EPI, NSUB>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)(160 * 1024 - 3 * C::STAGE - 256)) != hipSuccess)
+      return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((grouped_gemm_mx_kernel<EPI, NSUB>), dim3((unsigned)G), dim3(256), lds, st, a);
+  return check_launch("grouped_gemm_mx");
+}
+
 // Widest tile (outputs per tile 64 * NSUB) that divides N and fits LDS.
 template <int GK, int EPI, bool WFP8>
 static int launch_gemm_w(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
@@ -550,8 +805,14 @@ template <int GK, int EPI>
 static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   if (GK == GK_NV) return launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
   if (GK == GK_FP8) return launch_gemm_w<GK, EPI, true>(a, tiles_m_bound, st);
-  return a.w_fp8 ? launch_gemm_w<GK, EPI, true>(a, tiles_m_bound, st)
-                 : launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
+  if (a.w_fp8) return launch_gemm_w<GK, EPI, true>(a, tiles_m_bound, st);
+  // the DMA-staged kernel pays off over long K (gate_up, K = hidden); the
+  // short-K down projection is faster on the register-staged kernel
+  if constexpr (EPI == EPI_GATEUP) {
+    if (a.N % 128 == 0) return launch_gemm_mx<EPI, 2>(a, tiles_m_bound, st);
+    if (a.N % 64 == 0) return launch_gemm_mx<EPI, 1>(a, tiles_m_bound, st);
+  }
+  return launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
 }
 
 static int act_fmt_to_gk(int a_fmt) {
