@@ -79,14 +79,12 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat_f32(float v) {
 
 // Largest float <= T and smallest float >= T, for a non-negative double T.
 __device__ __forceinline__ float f32_round_down(double T) {
-  float f = (float)T;
-  if ((double)f > T) f = __uint_as_float(__float_as_uint(f) - 1u);
-  return f;
+  const float f = (float)T;
+  return __uint_as_float(__float_as_uint(f) - (uint32_t)((double)f > T));
 }
 __device__ __forceinline__ float f32_round_up(double T) {
-  float f = (float)T;
-  if ((double)f < T) f = __uint_as_float(__float_as_uint(f) + 1u);
-  return f;
+  const float f = (float)T;
+  return __uint_as_float(__float_as_uint(f) + (uint32_t)((double)f < T));
 }
 
 // Thresholds deciding the E2M1 code of |x| / unit.  The E2M1 midpoints are
@@ -104,25 +102,44 @@ struct E2M1Thresholds {
 __device__ __forceinline__ E2M1Thresholds e2m1_thresholds(double unit) {
   E2M1Thresholds th;
   const double mids[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  // computed for every unit and then raised to +inf when unit == 0 (a max,
+  // not a branch: the compiler would otherwise branch around each threshold)
+  const bool pos = unit > 0.0;
+  const double u = pos ? unit : 1.0;
+  const float floor_t = pos ? 0.0f : __builtin_inff();
 #pragma unroll
   for (int j = 0; j < 7; ++j) {
-    double T = mids[j] * unit;
-    th.t[j] = (unit > 0.0) ? ((j & 1) ? f32_round_up(T) : f32_round_down(T))
-                           : __builtin_inff();
+    const double T = mids[j] * u;
+    const float t = (j & 1) ? f32_round_up(T) : f32_round_down(T);
+    th.t[j] = fmaxf(t, floor_t);
   }
   return th;
 }
 
+// The count above is monotone in the thresholds, so it is found by a
+// three-level binary search (three exact comparisons instead of seven).
+// Thresholds are chosen by bit selects on all-ones / all-zero masks, so the
+// search compiles to straight-line code.
+__device__ __forceinline__ float bitsel(uint32_t mask, float if_set, float if_clear) {
+  return __uint_as_float((__float_as_uint(if_set) & mask) | (__float_as_uint(if_clear) & ~mask));
+}
 __device__ __forceinline__ uint32_t e2m1_code(float a, const E2M1Thresholds& th) {
-  uint32_t c = 0;
-  c += a > th.t[0];
-  c += a >= th.t[1];
-  c += a > th.t[2];
-  c += a >= th.t[3];
-  c += a > th.t[4];
-  c += a >= th.t[5];
-  c += a > th.t[6];
-  return c;
+  const uint32_t m3 = 0u - (uint32_t)(a >= th.t[3]);
+  const uint32_t mm = 0u - (uint32_t)(a >= bitsel(m3, th.t[5], th.t[1]));
+  const float tl = bitsel(m3, bitsel(mm, th.t[6], th.t[4]), bitsel(mm, th.t[2], th.t[0]));
+  return (m3 & 4u) | (mm & 2u) | (uint32_t)(a > tl);
+}
+
+// Eight magnitude codes (nibble i = code of element i, sign bits clear) ->
+// their E2M1 values, through the hardware convert (exact with scale 1.0).
+__device__ __forceinline__ void e2m1x8_mags(uint32_t d, float (&g)[8]) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  const f2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+  const f2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+  const f2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+  const f2 e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+  g[0] = a.x; g[1] = a.y; g[2] = b.x; g[3] = b.y;
+  g[4] = c.x; g[5] = c.y; g[6] = e.x; g[7] = e.y;
 }
 
 // Smallest e with M * 2^e >= a (a > 0 finite), M in {4, 6, 448}, clamped to

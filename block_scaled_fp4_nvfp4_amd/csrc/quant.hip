@@ -172,32 +172,34 @@ __global__ void __launch_bounds__(256) quant_fp4_kernel(
     }
   }
 
-  E2M1Thresholds th6 = e2m1_thresholds(s6 * S);
-  uint32_t c6[BS];
-  float g2_6 = 0.0f;
-  Acc gx_6 = 0;
+  // codes of one plan, packed 8 per dword (magnitudes; signs added at the
+  // end), and the plan's sums G2 = sum g^2 and GX = sum g*|x|
+  auto plan = [&](double unit, uint32_t (&pk)[BS / 8], float& g2, Acc& gx) __attribute__((always_inline)) {
+    const E2M1Thresholds th = e2m1_thresholds(unit);
+    g2 = 0.0f;
+    gx = 0;
 #pragma unroll
-  for (int i = 0; i < BS; ++i) {
-    float a = fabsf(v[i]);
-    c6[i] = e2m1_code(a, th6);
-    float gm = e2m1_mag_to_f32(c6[i]);
-    g2_6 += gm * gm;
-    gx_6 += (Acc)gm * (Acc)a;
-  }
-  bool use4 = false;
-  uint32_t c4[BS];
-  if (FOUR_SIX) {
-    E2M1Thresholds th4 = e2m1_thresholds(s4 * S);
-    float g2_4 = 0.0f;
-    Acc gx_4 = 0;
+    for (int w = 0; w < BS / 8; ++w) {
+      uint32_t d = 0;
 #pragma unroll
-    for (int i = 0; i < BS; ++i) {
-      float a = fabsf(v[i]);
-      c4[i] = e2m1_code(a, th4);
-      float gm = e2m1_mag_to_f32(c4[i]);
-      g2_4 += gm * gm;
-      gx_4 += (Acc)gm * (Acc)a;
+      for (int j = 0; j < 8; ++j) d |= e2m1_code(fabsf(v[8 * w + j]), th) << (4 * j);
+      pk[w] = d;
+      float gm[8];
+      e2m1x8_mags(d, gm);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        g2 = fmaf(gm[j], gm[j], g2);  // exact: a multiple of 1/4 below 2^12
+        gx += (Acc)gm[j] * (Acc)fabsf(v[8 * w + j]);
+      }
     }
+  };
+  uint32_t p6[BS / 8], p4[BS / 8];
+  float g2_6, g2_4 = 0.0f;
+  Acc gx_6, gx_4 = 0;
+  plan(s6 * S, p6, g2_6, gx_6);
+  bool use4 = false;
+  if (FOUR_SIX) {
+    plan(s4 * S, p4, g2_4, gx_4);
     double A = s6 * s6 * (double)g2_6 - s4 * s4 * (double)g2_4;
     double B = s6 * (double)gx_6 - s4 * (double)gx_4;
     use4 = (S * A - 2.0 * B) > 0.0;
@@ -206,14 +208,9 @@ __global__ void __launch_bounds__(256) quant_fp4_kernel(
   uint32_t packed[BS / 8];
 #pragma unroll
   for (int w = 0; w < BS / 8; ++w) {
-    uint32_t d = 0;
+    uint32_t d = (FOUR_SIX && use4) ? p4[w] : p6[w];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int i = 8 * w + j;
-      uint32_t c = (FOUR_SIX && use4) ? c4[i] : c6[i];
-      c |= (__float_as_uint(v[i]) >> 28) & 8u;  // sign bit of x
-      d |= c << (4 * j);
-    }
+    for (int j = 0; j < 8; ++j) d |= ((__float_as_uint(v[8 * w + j]) >> 28) & 8u) << (4 * j);  // sign of x
     packed[w] = d;
   }
   if (BS == 16) {
