@@ -401,28 +401,41 @@ constexpr int kGvTokens = 4;    // tokens whose activations are staged in LDS pe
 constexpr int kGdRows = 128;    // output rows per workgroup of the down GEMV (2 per 4 lanes)
 constexpr int kGdTokens = 8;
 
+// One DMA instruction: lane l copies 16 bytes from its global address to LDS
+// address lds + 16 l (lds is wave-uniform).
+__device__ __forceinline__ void dma16_to_lds(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Activation staging shared by both GEMVs: all of a pass's rows are copied
+// into LDS by DMA instructions issued after the weight loads, then every
+// wave waits for all of its loads (the weights are needed right after
+// anyway) and the workgroup synchronises.  Vector loads into registers
+// would instead have to wait for the older weight loads before their LDS
+// stores could be issued, serialising two memory latencies.
+
 // gate_up + SiLU*up for the pairs of one expert, bf16 activations.
 // Grid: (ceil(I / 32), max active experts).  Each group of 16 lanes owns two
 // outputs j (one per round, 16 apart): gate row j and up row I+j, split into
 // 16-byte chunks of 32 codes (lane l takes chunks l, l+16, ...).  Both
 // rounds' codes and scales are loaded up front (about 5.8 KB per group at
 // the decode shape, 92 KB per workgroup) and reused for every token of the
-// expert; the tokens' activations are staged in LDS, four tokens per pass, as
-// [token][quarter q][chunk c] 16-byte pieces so that the 16 lanes of a group
-// read consecutive pieces.
+// expert.  The tokens' activations are staged in LDS, four tokens per pass,
+// as [token][quarter q][chunk c] 16-byte pieces (rows padded to a multiple
+// of 64 chunks for the DMA) so that the 16 lanes of a group read consecutive
+// pieces.
 template <int WFMT, int CPL>
 __global__ void __launch_bounds__(256) gemv_gateup_kernel(
     const uint16_t* __restrict__ x, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ pair_of_row, const int32_t* __restrict__ active,
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ w13s, const float* __restrict__ w13s2,
     int H, int I, int k, float* __restrict__ h) {
-  constexpr int kStageLoads = (kGvTokens * 4 * 16 * CPL + 255) / 256;  // 16-byte pieces per thread
-  __shared__ __attribute__((aligned(16))) uint8_t xs[kGvTokens * 4 * CPL * 16 * 16];
-  __shared__ int s_tok[kGvTokens];
+  constexpr int CPAD = (16 * CPL + 63) / 64 * 64;  // chunks per staged (token, quarter) row
+  __shared__ __attribute__((aligned(16))) uint8_t xs[kGvTokens * 4 * CPAD * 16];
   const int ai = blockIdx.y;
   if (ai >= active[0]) return;
   const int e = active[1 + ai];
-  const int tid = threadIdx.x, l = tid & 15;
+  const int tid = threadIdx.x, l = tid & 15, wave = tid >> 6, lane = tid & 63;
   const int NCH = H >> 5;  // 32-value chunks per row
   const int64_t row_bytes = H >> 1;
   const int64_t srow = scale_row_stride<WFMT>(H);
@@ -441,50 +454,47 @@ __global__ void __launch_bounds__(256) gemv_gateup_kernel(
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = l + 16 * i;
-      const bool in = c < NCH;
-      const int cc = in ? c : 0;
+      const int cc = c < NCH ? c : 0;
       cg[rd][i] = ld16(wg + 16 * cc);
       cu[rd][i] = ld16(wu + 16 * cc);
-      bg[rd][i] = in ? chunk_scale_bits<WFMT>(sg, cc) : 0u;  // scale 0 zeroes the padding chunks
-      bu[rd][i] = in ? chunk_scale_bits<WFMT>(su, cc) : 0u;
-      if (WFMT == FP4_FMT_MXFP4 && !in) { cg[rd][i] = u32x4{0u, 0u, 0u, 0u}; cu[rd][i] = cg[rd][i]; }
+      // chunks past the row (c >= NCH) load chunk 0 and are skipped by the
+      // dot products; nothing here waits for a load
+      bg[rd][i] = chunk_scale_bits<WFMT>(sg, cc);
+      bu[rd][i] = chunk_scale_bits<WFMT>(su, cc);
     }
   }
   const float S = WFMT == FP4_FMT_NVFP4 ? w13s2[e] : 1.0f;
-  const int r0 = offsets[e], n = offsets[e + 1] - r0;
-  const int pieces = 4 * NCH;  // 16-byte pieces per activation row
-  for (int t0 = 0; t0 < n; t0 += kGvTokens) {
+  const int r0 = __builtin_amdgcn_readfirstlane(offsets[e]);
+  const int n = __builtin_amdgcn_readfirstlane(offsets[e + 1]) - r0;
+  // one pass over up to kGvTokens tokens; the first pass is peeled out of
+  // the loop so that no wait for the weight loads is placed ahead of its
+  // staging (a loop that uses registers loaded before it gets such a wait)
+  auto pass = [&](int t0) __attribute__((always_inline)) {
     const int nt = min(kGvTokens, n - t0);
-    if (t0 > 0) __syncthreads();
-    if (tid < nt) s_tok[tid] = pair_of_row[r0 + t0 + tid] / k;
-    __syncthreads();
-    // all of the pass's activation pieces are loaded before any is stored
-    u32x4 buf[kStageLoads];
-    int dst[kStageLoads];
+    if (t0 > 0) __syncthreads();  // the previous pass's reads are done
+    // DMA rows (t, q) for t < nt: 4 waves take the 4 quarters q; each row of
+    // CPAD chunks is CPAD/64 instructions (padding lanes re-read the last chunk)
+    for (int t = 0; t < nt; ++t) {
+      const int tok = __builtin_amdgcn_readfirstlane(pair_of_row[r0 + t0 + t]) / k;
+      const uint8_t* xrow = reinterpret_cast<const uint8_t*>(x + (int64_t)tok * H) + 16 * wave;
 #pragma unroll
-    for (int u = 0; u < kStageLoads; ++u) {
-      const int idx = tid + 256 * u;
-      dst[u] = -1;
-      if (idx < nt * pieces) {
-        int t = 0;
-#pragma unroll
-        for (int m = 1; m < kGvTokens; ++m) t += idx >= m * pieces;
-        const int rem = idx - t * pieces, c = rem >> 2, q = rem & 3;
-        buf[u] = ld16(reinterpret_cast<const uint8_t*>(x + (int64_t)s_tok[t] * H) + 64 * c + 16 * q);
-        dst[u] = ((t * 4 + q) * NCH + c) * 16;
+      for (int m = 0; m < CPAD / 64; ++m) {
+        const int c = min(64 * m + lane, NCH - 1);
+        dma16_to_lds(xrow + 64 * c, xs + ((t * 4 + wave) * CPAD + 64 * m) * 16);
       }
     }
-#pragma unroll
-    for (int u = 0; u < kStageLoads; ++u)
-      if (dst[u] >= 0) st16(xs + dst[u], buf[u]);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMAs (and weight loads) done
     __syncthreads();
     for (int t = 0; t < nt; ++t) {
+      // an opaque zero per token, XORed into the codes and scale bits: keeps
+      // the packed codes (not their 4x larger bf16 expansion) live across the
+      // token loop, and nothing derived from the weight loads is hoisted
+      // ahead of the activation staging (it would wait for those loads)
+      uint32_t z;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+      const u32x4 zz = u32x4{z, z, z, z};
 #pragma unroll
       for (int rd = 0; rd < kGvRounds; ++rd) {
-        // keep the packed codes (not their 4x larger bf16 expansion) live
-        // across the token loop: the expansion is redone per token
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) asm volatile("" : "+v"(cg[rd][i]), "+v"(cu[rd][i]));
         float ag = 0.0f, au = 0.0f;
 #pragma unroll
         for (int i = 0; i < CPL; ++i) {
@@ -493,11 +503,11 @@ __global__ void __launch_bounds__(256) gemv_gateup_kernel(
             uint32_t xv[16];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const u32x4 v = ld16(xs + ((t * 4 + q) * NCH + c) * 16);
+              const u32x4 v = ld16(xs + ((t * 4 + q) * CPAD + c) * 16);
               xv[4 * q] = v.x; xv[4 * q + 1] = v.y; xv[4 * q + 2] = v.z; xv[4 * q + 3] = v.w;
             }
-            ag = chunk_dot_bf16<WFMT>(cg[rd][i], bg[rd][i], xv, ag);
-            au = chunk_dot_bf16<WFMT>(cu[rd][i], bu[rd][i], xv, au);
+            ag = chunk_dot_bf16<WFMT>(cg[rd][i] ^ zz, bg[rd][i] ^ z, xv, ag);
+            au = chunk_dot_bf16<WFMT>(cu[rd][i] ^ zz, bu[rd][i] ^ z, xv, au);
           }
         }
 #pragma unroll
@@ -508,27 +518,30 @@ __global__ void __launch_bounds__(256) gemv_gateup_kernel(
         if (l == 0 && jr[rd] < I) h[(int64_t)(r0 + t0 + t) * I + jr[rd]] = silu_f32(ag * S) * (au * S);
       }
     }
-  }
+  };
+  if (n > 0) pass(0);
+  for (int t0 = kGvTokens; t0 < n; t0 += kGvTokens) pass(t0);
 }
 
 // Down projection o[row] = W2[e] h[row] for the rows of one expert, f32 h.
 // Grid: (ceil(H / 128), max active experts).  Each group of 4 lanes owns two
 // output rows (n and n + 64 of the tile), split into 16-byte chunks of 32
 // codes (lane l takes chunks l, l+4, ...).  The tokens' h rows are staged in
-// LDS, eight tokens per pass, each 32-value chunk padded to 144 bytes so that
-// the four lanes of a group read different bank groups.
+// LDS, eight tokens per pass; the eight 16-byte pieces of chunk c sit in
+// XOR-swizzled order (piece q at slot q ^ (c & 3)) so that the four lanes of
+// a group, which read four consecutive chunks, hit different bank groups.
 template <int WFMT, int CPL>
 __global__ void __launch_bounds__(256) gemv_down_kernel(
     const float* __restrict__ h, const int32_t* __restrict__ offsets, const int32_t* __restrict__ active,
     const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2s, const float* __restrict__ w2s2,
     int H, int I, float* __restrict__ o) {
-  constexpr int kChunkBytes = 144;
-  constexpr int kStageLoads = (kGdTokens * 4 * CPL * 8 + 255) / 256;  // 16-byte pieces per thread
-  __shared__ __attribute__((aligned(16))) uint8_t hs[kGdTokens * 4 * CPL * kChunkBytes];
+  constexpr int NCP = (4 * CPL + 7) / 8 * 8;  // staged chunks per token (a DMA instruction covers 8)
+  constexpr int TOKB = NCP * 128;             // staged bytes per token
+  __shared__ __attribute__((aligned(16))) uint8_t hs[kGdTokens * TOKB];
   const int ai = blockIdx.y;
   if (ai >= active[0]) return;
   const int e = active[1 + ai];
-  const int tid = threadIdx.x, l = tid & 3;
+  const int tid = threadIdx.x, l = tid & 3, wave = tid >> 6, lane = tid & 63;
   const int n0 = blockIdx.x * kGdRows + (tid >> 2), n1 = n0 + kGdRows / 2;
   const bool v0 = n0 < H, v1 = n1 < H;
   const int NCH = I >> 5;
@@ -545,45 +558,35 @@ __global__ void __launch_bounds__(256) gemv_down_kernel(
 #pragma unroll
   for (int i = 0; i < CPL; ++i) {
     const int c = l + 4 * i;
-    const bool in = c < NCH;
-    const int cc = in ? c : 0;
+    const int cc = c < NCH ? c : 0;
     c0[i] = ld16(q0 + 16 * cc);
     c1[i] = ld16(q1 + 16 * cc);
-    b0[i] = in ? chunk_scale_bits<WFMT>(s0, cc) : 0u;
-    b1[i] = in ? chunk_scale_bits<WFMT>(s1, cc) : 0u;
-    if (WFMT == FP4_FMT_MXFP4 && !in) { c0[i] = u32x4{0u, 0u, 0u, 0u}; c1[i] = c0[i]; }
+    b0[i] = chunk_scale_bits<WFMT>(s0, cc);  // chunks c >= NCH are skipped by the dot products
+    b1[i] = chunk_scale_bits<WFMT>(s1, cc);
   }
   const float S = WFMT == FP4_FMT_NVFP4 ? w2s2[e] : 1.0f;
-  const int r0 = offsets[e], n = offsets[e + 1] - r0;
-  const int tok_bytes = NCH * kChunkBytes;
-  for (int t0 = 0; t0 < n; t0 += kGdTokens) {
+  const int r0 = __builtin_amdgcn_readfirstlane(offsets[e]);
+  const int n = __builtin_amdgcn_readfirstlane(offsets[e + 1]) - r0;
+  auto pass = [&](int t0) __attribute__((always_inline)) {  // first pass peeled, as in gate_up
     const int nt = min(kGdTokens, n - t0);
     if (t0 > 0) __syncthreads();
-    // all of the pass's h pieces (8 of 16 bytes per chunk) are loaded before
-    // any is stored
-    const int pieces = NCH * 8;
-    u32x4 buf[kStageLoads];
-    int dst[kStageLoads];
+    // DMA: wave w stages tokens w, w + 4 of the pass; per token, instruction m
+    // covers chunks 8m .. 8m+7 (lane = 8 * (c - 8m) + slot; padding chunks re-read the last one)
+    for (int t = wave; t < nt; t += 4) {
+      const uint8_t* hrow = reinterpret_cast<const uint8_t*>(h + (int64_t)(r0 + t0 + t) * I);
 #pragma unroll
-    for (int u = 0; u < kStageLoads; ++u) {
-      const int idx = tid + 256 * u;
-      dst[u] = -1;
-      if (idx < nt * pieces) {
-        int t = 0;
-#pragma unroll
-        for (int m = 1; m < kGdTokens; ++m) t += idx >= m * pieces;
-        const int rem = idx - t * pieces, c = rem >> 3, q = rem & 7;
-        buf[u] = ld16(reinterpret_cast<const uint8_t*>(h + (int64_t)(r0 + t0 + t) * I) + 128 * c + 16 * q);
-        dst[u] = t * tok_bytes + c * kChunkBytes + 16 * q;
+      for (int m = 0; m < NCP / 8; ++m) {
+        const int c = min(8 * m + (lane >> 3), NCH - 1), slot = lane & 7;
+        const int q = slot ^ ((8 * m + (lane >> 3)) & 3);
+        dma16_to_lds(hrow + 128 * c + 16 * q, hs + t * TOKB + 8 * m * 128);
       }
     }
-#pragma unroll
-    for (int u = 0; u < kStageLoads; ++u)
-      if (dst[u] >= 0) st16(hs + dst[u], buf[u]);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int t = 0; t < nt; ++t) {
-#pragma unroll
-      for (int i = 0; i < CPL; ++i) asm volatile("" : "+v"(c0[i]), "+v"(c1[i]));
+      uint32_t z;  // opaque zero: the f32 expansion of the codes stays per token
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+      const u32x4 zz = u32x4{z, z, z, z};
       float a0 = 0.0f, a1 = 0.0f;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
@@ -592,12 +595,12 @@ __global__ void __launch_bounds__(256) gemv_down_kernel(
           float hv[32];
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
-            const u32x4 v = ld16(hs + t * tok_bytes + c * kChunkBytes + 16 * q);
+            const u32x4 v = ld16(hs + t * TOKB + c * 128 + 16 * (q ^ (c & 3)));
             hv[4 * q] = __uint_as_float(v.x); hv[4 * q + 1] = __uint_as_float(v.y);
             hv[4 * q + 2] = __uint_as_float(v.z); hv[4 * q + 3] = __uint_as_float(v.w);
           }
-          a0 = chunk_dot_f32<WFMT>(c0[i], b0[i], hv, a0);
-          a1 = chunk_dot_f32<WFMT>(c1[i], b1[i], hv, a1);
+          a0 = chunk_dot_f32<WFMT>(c0[i] ^ zz, b0[i] ^ z, hv, a0);
+          a1 = chunk_dot_f32<WFMT>(c1[i] ^ zz, b1[i] ^ z, hv, a1);
         }
       }
 #pragma unroll
@@ -610,7 +613,9 @@ __global__ void __launch_bounds__(256) gemv_down_kernel(
         if (v1) o[(int64_t)(r0 + t0 + t) * H + n1] = a1 * S;
       }
     }
-  }
+  };
+  if (n > 0) pass(0);
+  for (int t0 = kGdTokens; t0 < n; t0 += kGdTokens) pass(t0);
 }
 
 // ------------------------------------------------------------------ combine
