@@ -226,19 +226,65 @@ def moe_forward(layer: MoELayer, x: torch.Tensor, topk_ids: torch.Tensor,
     return y
 
 
+_HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+def _hip_runtime():
+    """The HIP runtime torch already loaded (for events without a system fence)."""
+    for name in ("libamdhip64.so", "libamdhip64.so.7", "libamdhip64.so.6"):
+        try:
+            return ctypes.CDLL(name)
+        except OSError:
+            continue
+    return None
+
+
 class StageTimer:
     """Eight HIP events recorded by moe_fp4_forward_profiled at the stage
-    boundaries; durations() gives milliseconds per stage of the last call."""
+    boundaries; durations() gives milliseconds per stage of the last call.
+
+    The events are created with hipEventDisableSystemFence when the HIP
+    runtime library can be loaded: a default event's system-scope release
+    writes back the L2 at every record, which adds several microseconds to
+    each stage of a short (decode) layer."""
 
     def __init__(self):
-        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
-        for e in self.events:  # create the underlying hipEvent_t
-            e.record()
-        torch.cuda.synchronize()
-        self._arr = (ctypes.c_void_p * 8)(*[e.cuda_event for e in self.events])
+        self._hip = _hip_runtime()
+        self._raw = None
+        if self._hip is not None:
+            evs = []
+            for _ in range(8):
+                ev = ctypes.c_void_p()
+                if self._hip.hipEventCreateWithFlags(ctypes.byref(ev), _HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                    evs = None
+                    break
+                evs.append(ev.value)
+            self._raw = evs
+        if self._raw is not None:
+            self._arr = (ctypes.c_void_p * 8)(*self._raw)
+        else:
+            self.events = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+            for e in self.events:  # create the underlying hipEvent_t
+                e.record()
+            torch.cuda.synchronize()
+            self._arr = (ctypes.c_void_p * 8)(*[e.cuda_event for e in self.events])
 
     def durations(self) -> dict:
-        return {name: self.events[i].elapsed_time(self.events[i + 1]) for i, name in enumerate(STAGES)}
+        if self._raw is None:
+            return {name: self.events[i].elapsed_time(self.events[i + 1]) for i, name in enumerate(STAGES)}
+        out = {}
+        for i, name in enumerate(STAGES):
+            ms = ctypes.c_float()
+            if self._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self._raw[i]),
+                                             ctypes.c_void_p(self._raw[i + 1])) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            out[name] = ms.value
+        return out
+
+    def __del__(self):
+        if getattr(self, "_raw", None) and self._hip is not None:
+            for ev in self._raw:
+                self._hip.hipEventDestroy(ctypes.c_void_p(ev))
 
 
 def moe_forward_profiled(layer: MoELayer, x: torch.Tensor, topk_ids: torch.Tensor,

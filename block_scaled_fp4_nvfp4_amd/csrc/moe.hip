@@ -180,7 +180,7 @@ __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restr
                                                          int32_t* __restrict__ active,
                                                          int32_t* __restrict__ tile_offsets,
                                                          int32_t* __restrict__ error_flag) {
-  extern __shared__ int smem[];
+  extern __shared__ __attribute__((aligned(16))) int smem[];
   int* s_ids = smem;            // 1024
   int* tmp = smem + 1024;       // 1024
   int* s_hist = smem + 2048;    // E
@@ -195,9 +195,19 @@ __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restr
   s_ids[tid] = my;
   __syncthreads();
   if (my >= 0) atomicAdd(&s_hist[my], 1);
+  // rank among the earlier pairs of the same expert: the earlier ids are
+  // read four at a time (16-byte LDS reads, several in flight)
   int r = 0;
-  if (my >= 0)
-    for (int q = 0; q < tid; ++q) r += s_ids[q] == my;
+  if (my >= 0) {
+    const int4* ids4 = reinterpret_cast<const int4*>(s_ids);
+    const int full = tid >> 2;
+#pragma unroll 4
+    for (int q = 0; q < full; ++q) {
+      const int4 v = ids4[q];
+      r += (v.x == my) + (v.y == my) + (v.z == my) + (v.w == my);
+    }
+    for (int q = full * 4; q < tid; ++q) r += s_ids[q] == my;
+  }
   int bad[1] = {my == -2 ? 1 : 0}, bad_tot[1];
   block_scan_1024<1>(bad, tmp, bad_tot);  // also orders the histogram updates
   const int bad_total = bad_tot[0];
@@ -237,9 +247,19 @@ __global__ void __launch_bounds__(kPermBlock) perm_count_kernel(const int32_t* _
   s_ids[tid] = my;
   __syncthreads();
   if (my >= 0) atomicAdd(&s_hist[my], 1);
+  // rank among the earlier pairs of the same expert: the earlier ids are
+  // read four at a time (16-byte LDS reads, several in flight)
   int r = 0;
-  if (my >= 0)
-    for (int q = 0; q < tid; ++q) r += s_ids[q] == my;
+  if (my >= 0) {
+    const int4* ids4 = reinterpret_cast<const int4*>(s_ids);
+    const int full = tid >> 2;
+#pragma unroll 4
+    for (int q = 0; q < full; ++q) {
+      const int4 v = ids4[q];
+      r += (v.x == my) + (v.y == my) + (v.z == my) + (v.w == my);
+    }
+    for (int q = full * 4; q < tid; ++q) r += s_ids[q] == my;
+  }
   __syncthreads();
   if (p < P) rank[p] = my >= 0 ? r : -1;
   for (int e = tid; e < E; e += kPermBlock) block_counts[(int64_t)blockIdx.x * E + e] = s_hist[e];
