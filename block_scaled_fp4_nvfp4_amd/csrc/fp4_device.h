@@ -77,6 +77,13 @@ __device__ __forceinline__ uint32_t e4m3_rne_sat_f32(float v) {
   return code > 0x7Eu ? 0x7Eu : code;
 }
 
+// E4M3 code of a non-negative float q <= 448 by the hardware convert
+// (round to nearest even; the bit-exact tests pin it against exact rounding,
+// subnormal codes and ties included).
+__device__ __forceinline__ uint32_t e4m3_hw(float q) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xFFu;
+}
+
 // Largest float <= T and smallest float >= T, for a non-negative double T.
 __device__ __forceinline__ float f32_round_down(double T) {
   const float f = (float)T;

@@ -243,7 +243,8 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const T* __restrict__ 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float a = v[4 * w + j];
-      uint32_t c = e4m3_rne_sat_f32(ldexpf(fabsf(a), -e)) | ((__float_as_uint(a) >> 24) & 0x80u);
+      // the power-of-two scaling is exact, so the convert rounds exactly
+      uint32_t c = e4m3_hw(fminf(ldexpf(fabsf(a), -e), kE4M3Max)) | ((__float_as_uint(a) >> 24) & 0x80u);
       d |= c << (8 * j);
     }
     out[w] = d;
@@ -254,21 +255,28 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const T* __restrict__ 
   scales[g] = (uint8_t)(e + 127);
 }
 
-// Exact E4M3 code of a / sigma (a >= 0, sigma > 0 float): a float quotient
-// picks a candidate, which is then corrected against the neighbouring
-// midpoints times sigma, compared exactly in double (5 + 24 bits).
-__device__ __forceinline__ uint32_t e4m3_exact_quotient(float a, float sigma) {
-  uint32_t c = e4m3_rne_sat_f32(a / sigma);
-  double A = (double)a, sg = (double)sigma;
-  if (c > 0) {
-    double mlo = 0.5 * ((double)e4m3_to_f32(c - 1) + (double)e4m3_to_f32(c)) * sg;
-    if (A < mlo || (A == mlo && ((c - 1) & 1u) == 0)) return c - 1;
-  }
-  if (c < 0x7Eu) {
-    double mhi = 0.5 * ((double)e4m3_to_f32(c) + (double)e4m3_to_f32(c + 1)) * sg;
-    if (A > mhi || (A == mhi && ((c + 1) & 1u) == 0)) return c + 1;
-  }
+// Exact E4M3 code (saturating) of a / sigma for a >= 0, sigma > 0 floats.
+// The float quotient q = RN(a / sigma) rounds to the same code as the exact
+// quotient unless q lands exactly on an E4M3 midpoint (RN is monotone and
+// every midpoint is a float); only then is a compared with midpoint * sigma,
+// exactly in double (5 + 24 significant bits), to pick the side.
+__device__ __forceinline__ bool e4m3_is_midpoint(float q) {
+  const bool normal_mid = (__float_as_uint(q) & 0x000FFFFFu) == 0x00080000u;  // half of the 3-bit ulp
+  const float t = q * 1024.0f;  // subnormal quantum 2^-9: midpoints are odd multiples of 2^-10
+  const bool sub_mid = (t == rintf(t)) & (((int)t & 1) != 0);
+  return q >= 0.015625f ? normal_mid : sub_mid;
+}
+__device__ __forceinline__ uint32_t e4m3_fix_midpoint(uint32_t c, float q, float a, float sigma) {
+  const double A = (double)a, M = (double)q * (double)sigma;
+  const float vc = __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
+  if (A > M && vc < q) return c + 1;
+  if (A < M && vc > q) return c - 1;
   return c;
+}
+__device__ __forceinline__ uint32_t e4m3_exact_quotient(float a, float sigma) {
+  const float q = fminf(a / sigma, kE4M3Max);
+  const uint32_t c = e4m3_hw(q);
+  return e4m3_is_midpoint(q) ? e4m3_fix_midpoint(c, q, a, sigma) : c;
 }
 
 // FP8 with one fp32 scale per (row, 128 columns): 4 lanes per group of 128.
@@ -293,15 +301,31 @@ __global__ void __launch_bounds__(256) quant_fp8_row_kernel(const T* __restrict_
   amax = fmaxf(amax, __shfl_xor(amax, 2));
   if (!active) return;
   float sigma = (float)((double)amax / 448.0);
+  // all 32 codes from the float quotients; the rare exact midpoints are
+  // corrected in one branch taken by the whole lane at most once
+  const float sg = sigma > 0.0f ? sigma : 1.0f;
+  float q[32];
+  uint32_t cm[32];
+  bool anymid = false;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    q[i] = fminf(fabsf(v[i]) / sg, kE4M3Max);
+    cm[i] = e4m3_hw(q[i]);
+    anymid |= e4m3_is_midpoint(q[i]);
+  }
+  if (anymid) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i)
+      if (e4m3_is_midpoint(q[i])) cm[i] = e4m3_fix_midpoint(cm[i], q[i], fabsf(v[i]), sg);
+  }
   uint32_t out[8];
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     uint32_t d = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float a = v[4 * w + j];
-      uint32_t c = sigma > 0.0f ? e4m3_exact_quotient(fabsf(a), sigma) : 0u;
-      c |= (__float_as_uint(a) >> 24) & 0x80u;
+      const float a = v[4 * w + j];
+      const uint32_t c = (sigma > 0.0f ? cm[4 * w + j] : 0u) | ((__float_as_uint(a) >> 24) & 0x80u);
       d |= c << (8 * j);
     }
     out[w] = d;

@@ -110,6 +110,37 @@ def test_fp8_formats_bit_exact(fmt):
     _compare(fmt, "rtn", dev(x), [x[b].astype(np.float64) for b in range(2)])
 
 
+def _e4m3_midpoint_rows():
+    """Rows of 128 values that put E4M3 quotients exactly on midpoints (normal
+    and subnormal, both parities) and one float step either side of them.
+    Each row's max is 448 * 1.25 (an FP8 row scale of exactly 1.25; an MXFP8
+    block exponent of 1 for its first 32 values), so every quotient is exact."""
+    grid = np.array(sorted(set(F.E4M3_GRID.tolist())), np.float64)
+    grid = grid[np.isfinite(grid) & (grid >= 0) & (grid <= 448)]
+    mids = (grid[:-1] + grid[1:]) / 2
+    rows = []
+    for sub in (mids[mids < 2.0 ** -6], mids[(mids >= 2.0 ** -6) & (mids < 2.0)], mids[mids >= 2.0]):
+        for lo in range(0, len(sub), 42):
+            part = sub[lo:lo + 42] * 1.25
+            a = np.concatenate([part, np.nextafter(part.astype(np.float32), np.float32(np.inf)),
+                                np.nextafter(part.astype(np.float32), np.float32(0))]).astype(np.float32)
+            row = np.zeros(128, np.float32)
+            row[0] = 448 * 1.25
+            row[1:1 + len(a)] = a[:127]
+            row[1::2] *= -1
+            rows.append(row)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8", "fp8_row"])
+def test_fp8_midpoints_and_subnormals_bit_exact(fmt):
+    """The E4M3 codes come from the hardware convert: exact ties (even code),
+    subnormal codes and one-ulp neighbours of ties against exact rounding."""
+    print_case(f"e4m3 midpoints {fmt}")
+    x = _e4m3_midpoint_rows()[None]
+    _compare(fmt, "rtn", dev(x), [x[0].astype(np.float64)])
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4", "mxfp8", "fp8_row", "fp8_block"])
 def test_dequantize_is_the_rounded_exact_value(fmt):
     print_case(f"dequantize {fmt}")
