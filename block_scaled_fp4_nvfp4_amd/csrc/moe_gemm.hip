@@ -804,7 +804,12 @@ static int launch_gemm_w(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t s
 template <int GK, int EPI>
 static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   if (GK == GK_NV) return launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
-  if (GK == GK_FP8) return launch_gemm_w<GK, EPI, true>(a, tiles_m_bound, st);
+  if (GK == GK_FP8) {
+    // FP8 weight tiles are twice the bytes: 64-output gate_up tiles keep two
+    // workgroups per CU in LDS and measure faster; the down tiles do not
+    if (EPI == EPI_GATEUP && a.N % 64 == 0) return launch_gemm_n<GK, EPI, 1, true>(a, tiles_m_bound, st);
+    return launch_gemm_w<GK, EPI, true>(a, tiles_m_bound, st);
+  }
   if (a.w_fp8) return launch_gemm_w<GK, EPI, true>(a, tiles_m_bound, st);
   // the DMA-staged kernel pays off over long K (gate_up, K = hidden); the
   // short-K down projection is faster on the register-staged kernel
