@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "fp4_device.h"
 #include "host_common.h"
@@ -810,6 +811,31 @@ int moe_fp4_workspace_size(const moe_fp4_layer* layer, int64_t tokens, size_t* b
   return FP4_OK;
 }
 
+// Per-device helper stream (default priority) and fork / join events for the
+// shared expert, created on first use and kept until the process ends.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxDevices = 64;
+static std::mutex g_side_mu;
+static SideStream g_side[kMaxDevices];
+
+static int side_stream(SideStream** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(FP4_ERR_HIP, "no current HIP device");
+  SideStream& ss = g_side[dev];
+  if (!ss.s) {
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      return fail(FP4_ERR_HIP, "creating the shared-expert stream failed");
+  }
+  *out = &ss;
+  return FP4_OK;
+}
+
 static int forward_impl(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const int32_t* topk_ids,
                         const float* topk_weights, float* y, void* workspace, size_t workspace_bytes,
                         void* stream, void* const* events) {
@@ -833,6 +859,23 @@ static int forward_impl(const moe_fp4_layer* L, const uint16_t* x, int64_t T, co
   const int max_active = (int)std::min<int64_t>(L->num_experts, P);
 
   FP4_CHECK(mark(0));
+  // The shared expert depends on x only: it runs on a helper stream of the
+  // device, forked from and joined back into the caller's stream, so that
+  // it overlaps the routed path.  The lock keeps the fork / join events of
+  // concurrent callers apart.
+  const float* extra = nullptr;
+  std::unique_lock<std::mutex> side_lock;
+  SideStream* side = nullptr;
+  if (L->shared_inter > 0) {
+    side_lock = std::unique_lock<std::mutex>(g_side_mu);
+    FP4_CHECK(side_stream(&side));
+    if (hipEventRecord(side->fork, st) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+      return fail(FP4_ERR_HIP, "fork to the shared-expert stream failed");
+    FP4_CHECK(launch_shared_expert(L, x, T, w, side->s));
+    if (hipEventRecord(side->join, side->s) != hipSuccess)
+      return fail(FP4_ERR_HIP, "shared-expert completion event failed");
+    extra = w.s_out;
+  }
   FP4_CHECK(launch_permute(topk_ids, P, L->num_experts, kGemmTileM, w, st));
   FP4_CHECK(mark(1));
   if (L->a_fmt == FP4_FMT_NONE) {
@@ -842,12 +885,9 @@ static int forward_impl(const moe_fp4_layer* L, const uint16_t* x, int64_t T, co
   } else {
     FP4_CHECK(launch_grouped(L, x, T, w, max_active, st, mark));
   }
-  const float* extra = nullptr;
-  if (L->shared_inter > 0) {
-    FP4_CHECK(launch_shared_expert(L, x, T, w, st));
-    extra = w.s_out;
-  }
-  FP4_CHECK(mark(6));
+  if (side && hipStreamWaitEvent(st, side->join, 0) != hipSuccess)
+    return fail(FP4_ERR_HIP, "join of the shared-expert stream failed");
+  FP4_CHECK(mark(6));  // the "shared" stage is the part of the shared expert not hidden by the routed path
   int64_t n4 = T * L->hidden / 4;
   hipLaunchKernelGGL(combine_kernel, dim3(grid_1d(n4, 256)), dim3(256), 0, st, w.o, w.row_of_pair,
                      topk_weights, T, L->hidden, L->top_k, extra, y);

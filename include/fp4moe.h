@@ -22,7 +22,11 @@
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers of the current HIP device; the
  *    caller owns every buffer.  The library never allocates or frees device
- *    memory and keeps no state between calls except a thread-local error text.
+ *    memory.  State kept between calls: a thread-local error text and, per
+ *    device, one helper stream with two events (created by the first forward
+ *    of a layer with a shared expert; the shared expert runs on it,
+ *    overlapped with the routed experts, forked from and joined back into
+ *    the caller's stream).
  *  - `stream` is a hipStream_t (NULL = default stream).  Calls only enqueue
  *    work and return; a launch failure returns FP4_ERR_HIP, asynchronous faults
  *    surface at the caller's next synchronisation.
