@@ -21,6 +21,7 @@
 #include <algorithm>
 #include <mutex>
 #include <string>
+#include <type_traits>
 
 #include "fp4_device.h"
 #include "host_common.h"
@@ -87,6 +88,9 @@ __device__ __forceinline__ void load_vals(const float* p, float (&v)[N]) {
   }
 }
 
+__device__ __forceinline__ float load_val(const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); }
+__device__ __forceinline__ float load_val(const float* p) { return *p; }
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
@@ -135,30 +139,146 @@ __global__ void nv_tensor_scale_kernel(float* s, int64_t n) {
 template <typename T> struct GxAcc { using type = float; };
 template <> struct GxAcc<float> { using type = double; };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
+
+// Signed E2M1 codes of eight values (nibble j <- element j) by the hardware
+// convert: round to nearest, ties to even, saturating at 6, sign kept for
+// values that round to zero.  The scaled forms divide by 2^(exponent of p2).
+__device__ __forceinline__ uint32_t fp4x8_of_product(const float* v, float r) {
+  uint32_t d = 0;
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[0] * r, v[1] * r, 1.0f, 0);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[2] * r, v[3] * r, 1.0f, 1);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[4] * r, v[5] * r, 1.0f, 2);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[6] * r, v[7] * r, 1.0f, 3);
+  return d;
+}
+__device__ __forceinline__ uint32_t fp4x8_scaled(const float* v, float p2) {
+  uint32_t d = 0;
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[0], v[1], p2, 0);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[2], v[3], p2, 1);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[4], v[5], p2, 2);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, v[6], v[7], p2, 3);
+  return d;
+}
+__device__ __forceinline__ uint32_t fp4x8_scaled(const uint32_t* raw, float p2) {
+  uint32_t d = 0;
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, as_bf16x2(raw[0]), p2, 0);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, as_bf16x2(raw[1]), p2, 1);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, as_bf16x2(raw[2]), p2, 2);
+  d = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d, as_bf16x2(raw[3]), p2, 3);
+  return d;
+}
+
+// G2 += sum g^2 and GX += sum g*x over eight signed codes and their inputs
+// (g and x share a sign, so g*x = g|x|).  bf16 inputs: the codes decode to
+// bf16 exactly and the bf16 dot products add exact terms whose sums are
+// exact in float (see the head of this file); f32 inputs: GX in double.
+__device__ __forceinline__ void fp4x8_sums(uint32_t d, const uint32_t* raw, float& g2, float& gx) {
+  bf16x2_t g;
+  g = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 0);
+  g2 = __builtin_amdgcn_fdot2_f32_bf16(g, g, g2, false);
+  gx = __builtin_amdgcn_fdot2_f32_bf16(g, as_bf16x2(raw[0]), gx, false);
+  g = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 1);
+  g2 = __builtin_amdgcn_fdot2_f32_bf16(g, g, g2, false);
+  gx = __builtin_amdgcn_fdot2_f32_bf16(g, as_bf16x2(raw[1]), gx, false);
+  g = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 2);
+  g2 = __builtin_amdgcn_fdot2_f32_bf16(g, g, g2, false);
+  gx = __builtin_amdgcn_fdot2_f32_bf16(g, as_bf16x2(raw[2]), gx, false);
+  g = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, 3);
+  g2 = __builtin_amdgcn_fdot2_f32_bf16(g, g, g2, false);
+  gx = __builtin_amdgcn_fdot2_f32_bf16(g, as_bf16x2(raw[3]), gx, false);
+}
+__device__ __forceinline__ void fp4x8_sums(uint32_t d, const float* v, float& g2, double& gx) {
+  float g[8];
+  e2m1x8_mags(d, g);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    g2 = fmaf(g[j], g[j], g2);  // exact: a multiple of 1/4 below 2^12
+    gx = fma((double)g[j], (double)v[j], gx);
+  }
+}
+
+// Reference plan by exact comparisons: signed codes of x / unit (unit exact
+// in double) and the plan's sums, for units outside [2^-100, 2^100] where the
+// hardware-convert plan is not shown exact.
+template <int BS, typename Acc>
+__device__ __forceinline__ void exact_plan(const float (&v)[BS], double unit, uint32_t (&pk)[BS / 8],
+                                           float& g2, Acc& gx) {
+  const E2M1Thresholds th = e2m1_thresholds(unit);
+  g2 = 0.0f;
+  gx = 0;
+#pragma unroll
+  for (int w = 0; w < BS / 8; ++w) {
+    uint32_t d = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d |= e2m1_code(fabsf(v[8 * w + j]), th) << (4 * j);
+    float gm[8];
+    e2m1x8_mags(d, gm);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      g2 = fmaf(gm[j], gm[j], g2);
+      gx += (Acc)gm[j] * (Acc)fabsf(v[8 * w + j]);
+      d |= ((__float_as_uint(v[8 * w + j]) >> 28) & 8u) << (4 * j);  // sign of x
+    }
+    pk[w] = d;
+  }
+}
+
 // One thread per block of BS values (16: NVFP4, 32: MXFP4).
+//
+// NVFP4 codes: with u = s*S (s the block's E4M3 scale) and r ~ 1/u within
+// 2^-23, the codes of x*r(1-2^-20) and x*r(1+2^-20) bracket the code of the
+// exact quotient x/u (the rounding is monotone), so where the two agree the
+// code is exact; where they differ one exact comparison decides.
+// MXFP4 codes: x / 2^e is exact, so the hardware convert is exact.
 template <int BS, bool MX, bool FOUR_SIX, typename T>
 __global__ void __launch_bounds__(256) quant_fp4_kernel(
     const T* __restrict__ x, int64_t blocks_per_tensor, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale,
     uint8_t* __restrict__ m4_flags) {
+  constexpr bool BF = std::is_same<T, uint16_t>::value;
+  constexpr int NW = BS / 8;
   using Acc = typename GxAcc<T>::type;
   int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (blk >= blocks_per_tensor) return;
   int64_t g = (int64_t)blockIdx.y * blocks_per_tensor + blk;
+  uint32_t raw[BF ? BS / 2 : 1];
   float v[BS];
-  load_vals<BS>(x + g * BS, v);
-  float amax = 0.0f;
+  float amax;
+  if constexpr (BF) {
+    const uint4* q = reinterpret_cast<const uint4*>(x + g * BS);
 #pragma unroll
-  for (int i = 0; i < BS; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    for (int i = 0; i < BS / 8; ++i) {
+      const uint4 w = q[i];
+      raw[4 * i] = w.x; raw[4 * i + 1] = w.y; raw[4 * i + 2] = w.z; raw[4 * i + 3] = w.w;
+    }
+    u16x2_t m = {0, 0};
+#pragma unroll
+    for (int i = 0; i < BS / 2; ++i) {
+      v[2 * i] = __uint_as_float(raw[i] << 16);
+      v[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
+      m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, raw[i] & 0x7FFF7FFFu));
+    }
+    amax = fmaxf(bf16_bits_to_f32(m.x), bf16_bits_to_f32(m.y));
+  } else {
+    load_vals<BS>(x + g * BS, v);
+    amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < BS; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  }
 
   double S = 1.0, s6, s4 = 0.0;
   uint32_t code6, code4 = 0;
+  int e6 = 0, e4 = 0;
   if (MX) {
-    int e6 = mx_exponent(amax, 6.0f);
+    e6 = mx_exponent(amax, 6.0f);
     code6 = (uint32_t)(e6 + 127);
     s6 = ldexp(1.0, e6);
     if (FOUR_SIX) {
-      int e4 = mx_exponent(amax, 4.0f);
+      e4 = mx_exponent(amax, 4.0f);
       code4 = (uint32_t)(e4 + 127);
       s4 = ldexp(1.0, e4);
     }
@@ -172,52 +292,87 @@ __global__ void __launch_bounds__(256) quant_fp4_kernel(
     }
   }
 
-  // codes of one plan, packed 8 per dword (magnitudes; signs added at the
-  // end), and the plan's sums G2 = sum g^2 and GX = sum g*|x|
-  auto plan = [&](double unit, uint32_t (&pk)[BS / 8], float& g2, Acc& gx) __attribute__((always_inline)) {
-    const E2M1Thresholds th = e2m1_thresholds(unit);
-    g2 = 0.0f;
-    gx = 0;
+  // codes and sums of one plan (scale s, or 2^e for MX)
+  auto plan = [&](double s, int e, uint32_t (&pk)[NW], float& g2, Acc& gx) __attribute__((always_inline)) {
+    bool exact = true;
+    if constexpr (MX) {
+      exact = e >= -100 || amax == 0.0f;  // a zero block gives signed zeros either way
+      const float p2 = __uint_as_float((uint32_t)(max(e, -126) + 127) << 23);
 #pragma unroll
-    for (int w = 0; w < BS / 8; ++w) {
-      uint32_t d = 0;
+      for (int w = 0; w < NW; ++w) {
+        if constexpr (BF) pk[w] = fp4x8_scaled(&raw[4 * w], p2);
+        else pk[w] = fp4x8_scaled(&v[8 * w], p2);
+      }
+    } else {
+      const float sf = (float)s, uf = sf * (float)S;  // one rounding of the exact s*S
+      const bool zero = sf == 0.0f;
+      const bool in_range = uf >= 0x1p-100f && uf <= 0x1p100f;
+      const float r0 = in_range ? __builtin_amdgcn_rcpf(uf) : 0.0f;
+      const float r = fmaf(r0, fmaf(-uf, r0, 1.0f), r0);  // one Newton step: |r*u - 1| < 2^-23
+      const float rl = r * 0x1.ffffe0p-1f, rh = r * 0x1.000010p+0f;  // r (1 -/+ 2^-20)
+      uint32_t hi[NW], diff = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) d |= e2m1_code(fabsf(v[8 * w + j]), th) << (4 * j);
-      pk[w] = d;
-      float gm[8];
-      e2m1x8_mags(d, gm);
+      for (int w = 0; w < NW; ++w) {
+        pk[w] = fp4x8_of_product(&v[8 * w], rl);
+        hi[w] = fp4x8_of_product(&v[8 * w], rh);
+        diff |= pk[w] ^ hi[w];
+      }
+      exact = zero || in_range;
+      // A value whose bracket straddles an E2M1 midpoint m (adjacent codes
+      // k, k+1) is decided by the sign of |x| - (m s) S, which one fma gives
+      // exactly (m s has at most 7 significant bits).  Such values are rare
+      // but not negligible: with S = amax/2688 and 2688 = 21 * 2^7, a
+      // threshold m s S with m s = 21 * 2^j sits within S's rounding error of
+      // the bf16 values that share the tensor amax's significand.
+      if (exact && diff) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        g2 = fmaf(gm[j], gm[j], g2);  // exact: a multiple of 1/4 below 2^12
-        gx += (Acc)gm[j] * (Acc)fabsf(v[8 * w + j]);
+        for (int w = 0; w < NW; ++w) {
+          uint32_t dw = pk[w] ^ hi[w];
+          while (dw) {
+            const int j = __builtin_ctz(dw) >> 2;
+            const uint32_t clo = (pk[w] >> (4 * j)) & 15u, chi = (hi[w] >> (4 * j)) & 15u;
+            const uint32_t k = min(clo & 7u, chi & 7u);
+            const float m = 0.5f * (e2m1_mag_to_f32(k) + e2m1_mag_to_f32(k + 1));
+            const float ax = fabsf(load_val(x + g * BS + 8 * w + j));
+            const float d = fmaf(-(m * sf), (float)S, ax);
+            const uint32_t c = d > 0.0f ? k + 1 : (d < 0.0f ? k : k + (k & 1u));
+            pk[w] = (pk[w] & ~(7u << (4 * j))) | (c << (4 * j));
+            dw &= ~(15u << (4 * j));
+          }
+        }
       }
     }
+    g2 = 0.0f;
+    gx = 0;
+    if constexpr (FOUR_SIX) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        if constexpr (BF) fp4x8_sums(pk[w], &raw[4 * w], g2, gx);
+        else fp4x8_sums(pk[w], &v[8 * w], g2, gx);
+      }
+    }
+    if (!exact) exact_plan<BS, Acc>(v, s * S, pk, g2, gx);
   };
-  uint32_t p6[BS / 8], p4[BS / 8];
+
+  uint32_t p6[NW], p4[NW];
   float g2_6, g2_4 = 0.0f;
   Acc gx_6, gx_4 = 0;
-  plan(s6 * S, p6, g2_6, gx_6);
+  plan(s6, e6, p6, g2_6, gx_6);
   bool use4 = false;
   if (FOUR_SIX) {
-    plan(s4 * S, p4, g2_4, gx_4);
+    plan(s4, e4, p4, g2_4, gx_4);
     double A = s6 * s6 * (double)g2_6 - s4 * s4 * (double)g2_4;
     double B = s6 * (double)gx_6 - s4 * (double)gx_4;
     use4 = (S * A - 2.0 * B) > 0.0;
   }
 
-  uint32_t packed[BS / 8];
+  uint32_t packed[NW];
 #pragma unroll
-  for (int w = 0; w < BS / 8; ++w) {
-    uint32_t d = (FOUR_SIX && use4) ? p4[w] : p6[w];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) d |= ((__float_as_uint(v[8 * w + j]) >> 28) & 8u) << (4 * j);  // sign of x
-    packed[w] = d;
-  }
+  for (int w = 0; w < NW; ++w) packed[w] = (FOUR_SIX && use4) ? p4[w] : p6[w];
   if (BS == 16) {
-    reinterpret_cast<uint2*>(codes)[g] = make_uint2(packed[0], packed[1]);
+    reinterpret_cast<uint2*>(codes)[g] = make_uint2(packed[0], packed[1 % NW]);
   } else {
-    reinterpret_cast<uint4*>(codes)[g] = make_uint4(packed[0], packed[1 % (BS / 8)],
-                                                    packed[2 % (BS / 8)], packed[3 % (BS / 8)]);
+    reinterpret_cast<uint4*>(codes)[g] = make_uint4(packed[0], packed[1 % NW], packed[2 % NW], packed[3 % NW]);
   }
   scales[g] = (uint8_t)((FOUR_SIX && use4) ? code4 : code6);
   if (m4_flags) m4_flags[g] = use4 ? 1 : 0;

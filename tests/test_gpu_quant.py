@@ -88,6 +88,37 @@ def test_fp4_adversarial_blocks_bit_exact():
             _compare(fmt, rule, dev_bf16(bits)[None], [x64])
 
 
+def _structured_near_tie_tensors():
+    """Tensors whose NVFP4 thresholds m*s*S land within S's rounding error of
+    bf16 inputs: S = amax/2688 with 2688 = 21 * 2^7, and m*s = 21 * 2^j for
+    (m, s) = (3.5, 6*2^j), (1.75, 12*2^j), (0.75, 28*2^j), so values a*2^-k that
+    share the tensor amax a's significand sit next to a threshold."""
+    amaxes = [1.0078125, 1.5234375, 1.2421875, 1.9921875, 1.3359375, 1.6640625]
+    tensors = []
+    for a in amaxes:
+        rows = [[a] + [a * 2.0 ** -k for k in range(1, 16)]]
+        for t in range(0, 8):  # block max a*2^-t: s6 = 448*2^-t (m = 0.75 ties)
+            rows.append([(-1) ** k * a * 2.0 ** -(t + k % 9) for k in range(16)])
+        for s_target in (6.0, 12.0, 24.0, 3.0):  # block max giving s6 = s_target
+            bmax = a * 6.0 * s_target / 2688.0
+            rows.append([bmax] + [(-1) ** k * a * 2.0 ** -(5 + k % 8) for k in range(15)])
+        rows.append([0.0] * 16)
+        tensors.append(np.array(rows, np.float32).reshape(-1, 32))
+    x = np.stack(tensors)
+    return F.bf16_bits_from_f32(x)
+
+
+def test_fp4_structured_near_ties_bit_exact():
+    print_case("structured near-ties of NVFP4 thresholds")
+    bits = _structured_near_tie_tensors()
+    x64 = [F.bf16_to_f64(bits[b]) for b in range(bits.shape[0])]
+    for rule in ("4over6", "rtn"):
+        _compare("nvfp4", rule, dev_bf16(bits), x64)
+    # the f32 path meets the same thresholds
+    xf = F.bf16_to_f64(bits).astype(np.float32)
+    _compare("nvfp4", "4over6", dev(xf), [xf[b].astype(np.float64) for b in range(xf.shape[0])])
+
+
 def test_fp4_f32_inputs_bit_exact():
     print_case("f32 inputs")
     rng = np.random.default_rng(1)
