@@ -31,11 +31,33 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 // E4M3 (FN) byte -> float; 0x7F/0xFF never occur in scales written here.
+// Branch-free: the subnormal form is selected, not branched to.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20))
-                : (float)m * 0.001953125f;  // m * 2^-9
-  return (c & 0x80u) ? -mag : mag;
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float nor = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const float sub = (float)m * 0.001953125f;  // m * 2^-9
+  const float mag = e ? nor : sub;
+  return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
+}
+
+// E4M3 code of the exact quotient Q = a / (M S) (a >= 0; M = 4 or 6; S a
+// float in [2^-100, 2^100]), round to nearest even, saturating at 448, given
+// any q within 2^-10 of Q relatively.  Rounding q's bit pattern to a multiple
+// of 2^19 gives the 5-significant-bit value nearest q: either an E4M3 value
+// (then Q rounds to it) or the midpoint of two adjacent E4M3 values c, c+1
+// (then Q lies between them and the sign of a - (M mid) S, exact in one fma
+// since M mid has at most 7 significant bits, picks the side; a tie picks the
+// even code).  Returns 0xFF when q is in the subnormal range (0, 2^-6), which
+// the caller settles exactly.
+__device__ __forceinline__ uint32_t e4m3_of_quotient(float a, float q, float M, float S) {
+  const uint32_t midb = (__float_as_uint(q) + 0x40000u) & 0xFFF80000u;
+  uint32_t c = (((midb >> 23) - 120u) << 3) | ((midb >> 20) & 7u);
+  const float d = fmaf(-(M * __uint_as_float(midb & 0x7FFFFFFFu)), S, a);
+  const bool is_mid = (midb & 0x80000u) != 0u;
+  c += (uint32_t)(is_mid && (d > 0.0f || (d == 0.0f && (c & 1u))));
+  c = q >= 448.0f ? 0x7Eu : c;
+  c = q < 0x1p-6f ? 0xFFu : c;
+  return q == 0.0f ? 0u : c;
 }
 
 // E2M1 magnitude code (0..7) -> float: 0, .5, 1, 1.5, 2, 3, 4, 6

@@ -142,6 +142,10 @@ template <> struct GxAcc<float> { using type = double; };
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
+// 4 x the E2M1 midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 in 5-bit fields
+constexpr uint64_t kE2M1Mid4 = 1ull | 3ull << 5 | 5ull << 10 | 7ull << 15 | 10ull << 20 | 14ull << 25 |
+                               20ull << 30;
+
 __device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t u) { return __builtin_bit_cast(bf16x2_t, u); }
 
 // Signed E2M1 codes of eight values (nibble j <- element j) by the hardware
@@ -221,9 +225,8 @@ __device__ __forceinline__ void exact_plan(const float (&v)[BS], double unit, ui
     for (int j = 0; j < 8; ++j) {
       g2 = fmaf(gm[j], gm[j], g2);
       gx += (Acc)gm[j] * (Acc)fabsf(v[8 * w + j]);
-      d |= ((__float_as_uint(v[8 * w + j]) >> 28) & 8u) << (4 * j);  // sign of x
     }
-    pk[w] = d;
+    pk[w] = d | (pk[w] & 0x88888888u);  // signs of x, as the hardware codes already carry them
   }
 }
 
@@ -255,6 +258,7 @@ __global__ void __launch_bounds__(256) quant_fp4_kernel(
       const uint4 w = q[i];
       raw[4 * i] = w.x; raw[4 * i + 1] = w.y; raw[4 * i + 2] = w.z; raw[4 * i + 3] = w.w;
     }
+    // |x| bit patterns order like |x|: a packed 16-bit max over the pairs
     u16x2_t m = {0, 0};
 #pragma unroll
     for (int i = 0; i < BS / 2; ++i) {
@@ -262,7 +266,7 @@ __global__ void __launch_bounds__(256) quant_fp4_kernel(
       v[2 * i + 1] = __uint_as_float(raw[i] & 0xFFFF0000u);
       m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, raw[i] & 0x7FFF7FFFu));
     }
-    amax = fmaxf(bf16_bits_to_f32(m.x), bf16_bits_to_f32(m.y));
+    amax = __uint_as_float((uint32_t)max(m.x, m.y) << 16);
   } else {
     load_vals<BS>(x + g * BS, v);
     amax = 0.0f;
@@ -283,13 +287,18 @@ __global__ void __launch_bounds__(256) quant_fp4_kernel(
       s4 = ldexp(1.0, e4);
     }
   } else {
-    S = (double)tensor_scale[blockIdx.y];
-    code6 = S > 0.0 ? e4m3_rne_sat_f64((double)amax / (6.0 * S)) : 0u;
-    s6 = (double)e4m3_to_f32(code6);
-    if (FOUR_SIX) {
-      code4 = S > 0.0 ? e4m3_rne_sat_f64((double)amax / (4.0 * S)) : 0u;
-      s4 = (double)e4m3_to_f32(code4);
+    const float Sf = tensor_scale[blockIdx.y];
+    S = (double)Sf;
+    const bool s_ok = Sf >= 0x1p-100f && Sf <= 0x1p100f;
+    const float R6 = s_ok ? __builtin_amdgcn_rcpf(6.0f * Sf) : 0.0f;  // ~1/(6S) within 2^-21
+    code6 = e4m3_of_quotient(amax, amax * R6, 6.0f, Sf);
+    if (FOUR_SIX) code4 = e4m3_of_quotient(amax, amax * (1.5f * R6), 4.0f, Sf);
+    if (!s_ok || code6 == 0xFFu || code4 == 0xFFu) {  // extreme S or a block in the E4M3 subnormal range
+      code6 = S > 0.0 ? e4m3_rne_sat_f64((double)amax / (6.0 * S)) : 0u;
+      if (FOUR_SIX) code4 = S > 0.0 ? e4m3_rne_sat_f64((double)amax / (4.0 * S)) : 0u;
     }
+    s6 = (double)e4m3_to_f32(code6);
+    if (FOUR_SIX) s4 = (double)e4m3_to_f32(code4);
   }
 
   // codes and sums of one plan (scale s, or 2^e for MX)
@@ -325,19 +334,28 @@ __global__ void __launch_bounds__(256) quant_fp4_kernel(
       // threshold m s S with m s = 21 * 2^j sits within S's rounding error of
       // the bf16 values that share the tensor amax's significand.
       if (exact && diff) {
+        const float sq = 0.25f * sf;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
           uint32_t dw = pk[w] ^ hi[w];
           while (dw) {
-            const int j = __builtin_ctz(dw) >> 2;
-            const uint32_t clo = (pk[w] >> (4 * j)) & 15u, chi = (hi[w] >> (4 * j)) & 15u;
-            const uint32_t k = min(clo & 7u, chi & 7u);
-            const float m = 0.5f * (e2m1_mag_to_f32(k) + e2m1_mag_to_f32(k + 1));
-            const float ax = fabsf(load_val(x + g * BS + 8 * w + j));
-            const float d = fmaf(-(m * sf), (float)S, ax);
-            const uint32_t c = d > 0.0f ? k + 1 : (d < 0.0f ? k : k + (k & 1u));
-            pk[w] = (pk[w] & ~(7u << (4 * j))) | (c << (4 * j));
-            dw &= ~(15u << (4 * j));
+            const uint32_t sh = (uint32_t)__builtin_ctz(dw) & ~3u;  // 4 * nibble index
+            const uint32_t k = min((pk[w] >> sh) & 7u, (hi[w] >> sh) & 7u);
+            const uint32_t m4 = (uint32_t)(kE2M1Mid4 >> (5u * k)) & 31u;  // 4 * midpoint(k, k+1)
+            float ax;
+            if constexpr (BF) {
+              const uint32_t p = sh >> 3;
+              const uint32_t a = (p & 1u) ? raw[4 * w + 1] : raw[4 * w];
+              const uint32_t b = (p & 1u) ? raw[4 * w + 3] : raw[4 * w + 2];
+              const uint32_t r2 = (p & 2u) ? b : a;
+              ax = __uint_as_float(((sh & 4u) ? (r2 & 0xFFFF0000u) : (r2 << 16)) & 0x7FFFFFFFu);
+            } else {
+              ax = fabsf(load_val(x + g * BS + 8 * w + (sh >> 2)));
+            }
+            const float d = fmaf(-((float)m4 * sq), (float)S, ax);
+            const uint32_t up = (uint32_t)(d > 0.0f) | ((uint32_t)(d == 0.0f) & k);
+            pk[w] = (pk[w] & ~(7u << sh)) | ((k + (up & 1u)) << sh);
+            dw &= ~(15u << sh);
           }
         }
       }
