@@ -419,7 +419,8 @@ __device__ __forceinline__ float chunk_dot_f32(u32x4 c, uint32_t sbits, const fl
 constexpr int kGvRounds = 2;    // rounds of 16 outputs per workgroup of the gate_up GEMV
 constexpr int kGvOut = 16 * kGvRounds;
 constexpr int kGvTokens = 4;    // tokens whose activations are staged in LDS per pass
-constexpr int kGdRows = 128;    // output rows per workgroup of the down GEMV (2 per 4 lanes)
+constexpr int kGdRpg = 2;            // output rows per 4 lanes of the down GEMV
+constexpr int kGdRows = 64 * kGdRpg;  // output rows per workgroup of the down GEMV
 constexpr int kGdTokens = 8;
 
 // One DMA instruction: lane l copies 16 bytes from its global address to LDS
@@ -463,8 +464,7 @@ __global__ void __launch_bounds__(256) gemv_gateup_kernel(
   int jr[kGvRounds];
   u32x4 cg[kGvRounds][CPL], cu[kGvRounds][CPL];
   uint32_t bg[kGvRounds][CPL], bu[kGvRounds][CPL];
-#pragma unroll
-  for (int rd = 0; rd < kGvRounds; ++rd) {
+  auto load_round = [&](int rd) __attribute__((always_inline)) {
     const int j = blockIdx.x * kGvOut + rd * 16 + (tid >> 4);
     jr[rd] = j;
     const int jj = j < I ? j : I - 1;
@@ -483,18 +483,15 @@ __global__ void __launch_bounds__(256) gemv_gateup_kernel(
       bg[rd][i] = chunk_scale_bits<WFMT>(sg, cc);
       bu[rd][i] = chunk_scale_bits<WFMT>(su, cc);
     }
-  }
+  };
   const float S = WFMT == FP4_FMT_NVFP4 ? w13s2[e] : 1.0f;
   const int r0 = __builtin_amdgcn_readfirstlane(offsets[e]);
   const int n = __builtin_amdgcn_readfirstlane(offsets[e + 1]) - r0;
-  // one pass over up to kGvTokens tokens; the first pass is peeled out of
-  // the loop so that no wait for the weight loads is placed ahead of its
-  // staging (a loop that uses registers loaded before it gets such a wait)
-  auto pass = [&](int t0) __attribute__((always_inline)) {
+  // DMA of the activation rows (t, q), t < nt, of one pass: the 4 waves take
+  // the 4 quarters q; each row of CPAD chunks is CPAD/64 instructions
+  // (padding lanes re-read the last chunk)
+  auto stage = [&](int t0) __attribute__((always_inline)) {
     const int nt = min(kGvTokens, n - t0);
-    if (t0 > 0) __syncthreads();  // the previous pass's reads are done
-    // DMA rows (t, q) for t < nt: 4 waves take the 4 quarters q; each row of
-    // CPAD chunks is CPAD/64 instructions (padding lanes re-read the last chunk)
     for (int t = 0; t < nt; ++t) {
       const int tok = __builtin_amdgcn_readfirstlane(pair_of_row[r0 + t0 + t]) / k;
       const uint8_t* xrow = reinterpret_cast<const uint8_t*>(x + (int64_t)tok * H) + 16 * wave;
@@ -504,13 +501,14 @@ __global__ void __launch_bounds__(256) gemv_gateup_kernel(
         dma16_to_lds(xrow + 64 * c, xs + ((t * 4 + wave) * CPAD + 64 * m) * 16);
       }
     }
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's DMAs (and weight loads) done
-    __syncthreads();
-    for (int t = 0; t < nt; ++t) {
+  };
+  // one token of a pass (t < number of tokens in the pass)
+  auto token = [&](int t0, int t) __attribute__((always_inline)) {
+    {
       // an opaque zero per token, XORed into the codes and scale bits: keeps
       // the packed codes (not their 4x larger bf16 expansion) live across the
       // token loop, and nothing derived from the weight loads is hoisted
-      // ahead of the activation staging (it would wait for those loads)
+      // ahead of the activation staging
       uint32_t z;
       asm volatile("v_mov_b32 %0, 0" : "=v"(z));
       const u32x4 zz = u32x4{z, z, z, z};
@@ -540,8 +538,32 @@ __global__ void __launch_bounds__(256) gemv_gateup_kernel(
       }
     }
   };
-  if (n > 0) pass(0);
-  for (int t0 = kGvTokens; t0 < n; t0 += kGvTokens) pass(t0);
+  // the first token is peeled out of the token loop: a loop that uses
+  // registers loaded before it starts with a wait for all of them
+  auto compute = [&](int t0) __attribute__((always_inline)) {
+    const int nt = min(kGvTokens, n - t0);
+    if (nt > 0) token(t0, 0);
+    for (int t = 1; t < nt; ++t) token(t0, t);
+  };
+  // First pass: round 0's weights, then the activation DMA, then the later
+  // rounds' weights, so that waiting for the DMA (vmcnt counts in issue
+  // order) leaves the later rounds in flight while round 0 is computed.
+  load_round(0);
+  stage(0);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int rd = 1; rd < kGvRounds; ++rd) load_round(rd);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(4 * CPL * (kGvRounds - 1)));
+  asm volatile("s_barrier" ::: "memory");
+  compute(0);
+  for (int t0 = kGvTokens; t0 < n; t0 += kGvTokens) {
+    __syncthreads();  // the previous pass's reads are done
+    stage(t0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    compute(t0);
+  }
 }
 
 // Down projection o[row] = W2[e] h[row] for the rows of one expert, f32 h.
@@ -563,27 +585,27 @@ __global__ void __launch_bounds__(256) gemv_down_kernel(
   if (ai >= active[0]) return;
   const int e = active[1 + ai];
   const int tid = threadIdx.x, l = tid & 3, wave = tid >> 6, lane = tid & 63;
-  const int n0 = blockIdx.x * kGdRows + (tid >> 2), n1 = n0 + kGdRows / 2;
-  const bool v0 = n0 < H, v1 = n1 < H;
   const int NCH = I >> 5;
   const int64_t row_bytes = I >> 1;
   const int64_t srow = scale_row_stride<WFMT>(I);
   const uint8_t* wbase = w2 + (int64_t)e * H * row_bytes;
   const uint8_t* sbase = w2s + (int64_t)e * H * srow;
-  const uint8_t* q0 = wbase + (int64_t)(v0 ? n0 : 0) * row_bytes;
-  const uint8_t* q1 = wbase + (int64_t)(v1 ? n1 : 0) * row_bytes;
-  const uint8_t* s0 = sbase + (int64_t)(v0 ? n0 : 0) * srow;
-  const uint8_t* s1 = sbase + (int64_t)(v1 ? n1 : 0) * srow;
-  u32x4 c0[CPL], c1[CPL];
-  uint32_t b0[CPL], b1[CPL];
+  int nr[kGdRpg];
+  u32x4 cw[kGdRpg][CPL];
+  uint32_t bw[kGdRpg][CPL];
 #pragma unroll
-  for (int i = 0; i < CPL; ++i) {
-    const int c = l + 4 * i;
-    const int cc = c < NCH ? c : 0;
-    c0[i] = ld16(q0 + 16 * cc);
-    c1[i] = ld16(q1 + 16 * cc);
-    b0[i] = chunk_scale_bits<WFMT>(s0, cc);  // chunks c >= NCH are skipped by the dot products
-    b1[i] = chunk_scale_bits<WFMT>(s1, cc);
+  for (int r = 0; r < kGdRpg; ++r) {
+    nr[r] = blockIdx.x * kGdRows + (tid >> 2) + 64 * r;
+    const int64_t row = nr[r] < H ? nr[r] : 0;
+    const uint8_t* q = wbase + row * row_bytes;
+    const uint8_t* sp = sbase + row * srow;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = l + 4 * i;
+      const int cc = c < NCH ? c : 0;
+      cw[r][i] = ld16(q + 16 * cc);
+      bw[r][i] = chunk_scale_bits<WFMT>(sp, cc);  // chunks c >= NCH are skipped by the dot products
+    }
   }
   const float S = WFMT == FP4_FMT_NVFP4 ? w2s2[e] : 1.0f;
   const int r0 = __builtin_amdgcn_readfirstlane(offsets[e]);
@@ -608,7 +630,9 @@ __global__ void __launch_bounds__(256) gemv_down_kernel(
       uint32_t z;  // opaque zero: the f32 expansion of the codes stays per token
       asm volatile("v_mov_b32 %0, 0" : "=v"(z));
       const u32x4 zz = u32x4{z, z, z, z};
-      float a0 = 0.0f, a1 = 0.0f;
+      float a[kGdRpg];
+#pragma unroll
+      for (int r = 0; r < kGdRpg; ++r) a[r] = 0.0f;
 #pragma unroll
       for (int i = 0; i < CPL; ++i) {
         const int c = l + 4 * i;
@@ -620,18 +644,15 @@ __global__ void __launch_bounds__(256) gemv_down_kernel(
             hv[4 * q] = __uint_as_float(v.x); hv[4 * q + 1] = __uint_as_float(v.y);
             hv[4 * q + 2] = __uint_as_float(v.z); hv[4 * q + 3] = __uint_as_float(v.w);
           }
-          a0 = chunk_dot_f32<WFMT>(c0[i] ^ zz, b0[i] ^ z, hv, a0);
-          a1 = chunk_dot_f32<WFMT>(c1[i] ^ zz, b1[i] ^ z, hv, a1);
+#pragma unroll
+          for (int r = 0; r < kGdRpg; ++r) a[r] = chunk_dot_f32<WFMT>(cw[r][i] ^ zz, bw[r][i] ^ z, hv, a[r]);
         }
       }
 #pragma unroll
-      for (int off = 2; off > 0; off >>= 1) {
-        a0 += __shfl_xor(a0, off, 4);
-        a1 += __shfl_xor(a1, off, 4);
-      }
-      if (l == 0) {
-        if (v0) o[(int64_t)(r0 + t0 + t) * H + n0] = a0 * S;
-        if (v1) o[(int64_t)(r0 + t0 + t) * H + n1] = a1 * S;
+      for (int r = 0; r < kGdRpg; ++r) {
+#pragma unroll
+        for (int off = 2; off > 0; off >>= 1) a[r] += __shfl_xor(a[r], off, 4);
+        if (l == 0 && nr[r] < H) o[(int64_t)(r0 + t0 + t) * H + nr[r]] = a[r] * S;
       }
     }
   };

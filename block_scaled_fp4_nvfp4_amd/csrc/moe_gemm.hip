@@ -527,10 +527,6 @@ __device__ __forceinline__ void dma4_to_lds(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 4, 0, 0);
 }
 
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8): vmcnt <= n only, and vmcnt <= n with lgkmcnt = 0.
-constexpr int vmcnt_only(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-constexpr int vmcnt_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
 
 template <int EPI, int NSUB>
 __global__ void __launch_bounds__(256, 2) grouped_gemm_mx_kernel(GemmArgs g) {
