@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <utility>
 
 #include "fp4_device.h"
 #include "host_common.h"
@@ -714,6 +715,268 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx_kernel(GemmArgs g) {
     }
 }
 
+// MXFP4 weights x MXFP8 activations for a reduction size fixed at compile
+// time (KS steps of 128).  The tile and MFMA layout are those of the kernel
+// above, but each wave fetches its own weight fragments straight into
+// registers D steps ahead (the 4 waves split the outputs, so no weight byte
+// is shared between waves and none goes through LDS), and only the
+// activation tile, which all 4 waves read, is staged by DMA through a ring of
+// RS LDS stages.  With the K loop fully unrolled, the compiler places exact
+// waits for the register loads, and the wait for a stage's DMA is a
+// compile-time count of the memory instructions issued after it
+// (mx2_wait_count); about 2.5x the bytes of the DMA-only kernel are in flight.
+template <int EPI, int NSUB, int KS>
+struct Mx2Cfg {
+  static constexpr int BM = kBM;
+  static constexpr int BN = 64 * NSUB;
+  static constexpr int NU = EPI == EPI_GATEUP ? 2 : 1;
+  static constexpr int NS = NU * NSUB;          // 16-column weight subtiles per wave
+  static constexpr int RS = KS < 8 ? KS : 8;    // activation stages in the LDS ring
+  static constexpr int D = KS < 3 ? KS : 3;     // steps of weight fragments in flight per wave
+  static constexpr int A_BYTES = BM * 128;
+  static constexpr int STAGE = A_BYTES + BM * 4;  // codes + one scale dword (4 blocks of 32) per row
+  static constexpr int A_INS = A_BYTES / 4096;    // 16-byte DMA instructions per thread and stage
+  static constexpr int OPS_A = A_INS + 1;         // + one 4-byte DMA of the scales
+  static constexpr int OPS_W = 2 * NS;            // per step: NS code loads + NS scale-byte loads
+};
+
+// Memory instructions a thread issues between the DMA of stage ks (or the
+// weight loads of step ks) and the wait at the top of step ks.  The prologue
+// issues W(0..D-1) then A(0..RS-2); step j issues A(j+RS-1) after its barrier
+// and W(j+D) after its MFMAs.  The wait covers both, so the compiler never
+// adds its own (it would wait for every load in flight).
+template <int KS, int RS, int D, int OA, int OW>
+constexpr int mx2_ops_between_steps(int j0, int ks) {  // steps j0+1 .. ks-1
+  int n = 0;
+  for (int j = j0 + 1; j < ks; ++j) {
+    if (j + RS - 1 < KS) n += OA;
+    if (j + D < KS) n += OW;
+  }
+  return n;
+}
+template <int KS, int RS, int D, int OA, int OW>
+constexpr int mx2_wait_count(int ks) {
+  const int last = (KS < RS - 1 ? KS : RS - 1) - 1;  // last stage of the prologue
+  int na, nw;
+  if (ks <= RS - 2) {
+    na = (last - ks) * OA + mx2_ops_between_steps<KS, RS, D, OA, OW>(-1, ks);
+  } else {
+    const int j0 = ks - RS + 1;
+    na = (j0 + D < KS ? OW : 0) + mx2_ops_between_steps<KS, RS, D, OA, OW>(j0, ks);
+  }
+  if (ks < D) {
+    nw = (D - 1 - ks) * OW + (last + 1) * OA + mx2_ops_between_steps<KS, RS, D, OA, OW>(-1, ks);
+  } else {
+    nw = mx2_ops_between_steps<KS, RS, D, OA, OW>(ks - D, ks);
+  }
+  const int n = na < nw ? na : nw;
+  return n < 63 ? n : 63;  // 63 outstanding is the counter's limit
+}
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N-1>): a loop
+// whose index is a constant expression in its body
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(N));
+}
+
+template <int EPI, int NSUB, int KS>
+__global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
+  using C = Mx2Cfg<EPI, NSUB, KS>;
+  constexpr int BM = C::BM, BN = C::BN, NU = C::NU, NS = C::NS, RS = C::RS, D = C::D;
+  static_assert(RS <= 8, "ring of at most 8 stages");
+  // one array per stage: the compiler then sees that reading a stage does
+  // not alias the DMAs into the others (one array would make it wait for
+  // every DMA in flight before each read)
+  __shared__ __attribute__((aligned(16))) uint8_t r0[C::STAGE], r1[RS > 1 ? C::STAGE : 16],
+      r2[RS > 2 ? C::STAGE : 16], r3[RS > 3 ? C::STAGE : 16], r4[RS > 4 ? C::STAGE : 16],
+      r5[RS > 5 ? C::STAGE : 16], r6[RS > 6 ? C::STAGE : 16], r7[RS > 7 ? C::STAGE : 16];
+  auto stage = [&](auto sc) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return r0;
+    else if constexpr (S == 1) return r1;
+    else if constexpr (S == 2) return r2;
+    else if constexpr (S == 3) return r3;
+    else if constexpr (S == 4) return r4;
+    else if constexpr (S == 5) return r5;
+    else if constexpr (S == 6) return r6;
+    else return r7;
+  };
+  __shared__ __attribute__((aligned(16))) uint8_t dummy[1024];  // target of the unused scale DMA lanes
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  int* s_toff = reinterpret_cast<int*>(lds_dyn);
+
+  const int NT = g.N / BN;
+  const int G = gridDim.x;
+  const int per_xcd = G / 8;
+  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+
+  int e, mt, nt, r_begin, n_rows;
+  if (g.dense_rows > 0) {
+    e = 0;
+    nt = L % NT;
+    mt = L / NT;
+    if (mt * BM >= g.dense_rows) return;
+    r_begin = 0;
+    n_rows = g.dense_rows;
+  } else {
+    for (int i = threadIdx.x; i <= g.E; i += 256) s_toff[i] = g.tile_offsets[i];
+    __syncthreads();
+    nt = L % NT;
+    const int mg = L / NT;
+    if (mg >= s_toff[g.E]) return;
+    int lo = 0, hi = g.E;
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (s_toff[mid] <= mg) lo = mid; else hi = mid;
+    }
+    e = lo;
+    mt = mg - s_toff[e];
+    r_begin = g.offsets[e];
+    n_rows = g.offsets[e + 1] - r_begin;
+  }
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  constexpr int K = KS * kBK;
+  constexpr int SKB = K / 32;  // scale bytes per row
+  const int NW = NU * g.N;
+  const uint8_t* w_base = g.w_codes + (int64_t)e * NW * (K / 2);
+  const uint8_t* ws_base = reinterpret_cast<const uint8_t*>(g.w_scales) + (int64_t)e * NW * SKB;
+
+  auto a_row_of = [&](int r) __attribute__((always_inline)) -> int64_t {
+    const int rr = mt * BM + r;
+    const int R = r_begin + (rr < n_rows ? rr : 0);  // rows past the expert's end fetch row 0 (never stored)
+    return g.a_gather ? g.pair_of_row[R] / g.k : R;
+  };
+  auto w_grow = [&](int i) __attribute__((always_inline)) -> int { return (i / BN) * g.N + nt * BN + (i % BN); };
+
+  // activation DMA sources (step 0; a step advances codes by 128 B, scales by 4 B)
+  const uint8_t* a_src[C::A_INS];
+#pragma unroll
+  for (int q = 0; q < C::A_INS; ++q) {
+    const int row = (q * 4 + wave) * 8 + (lane >> 3), slot = lane & 7;
+    const int chunk = slot ^ ((row ^ (row >> 3)) & 7);  // inverse of swz<128>
+    a_src[q] = g.a_codes + a_row_of(row) * K + 16 * chunk;
+  }
+  const uint8_t* as_src = reinterpret_cast<const uint8_t*>(g.a_scales) + a_row_of(tid < BM ? tid : 0) * SKB;
+  uint8_t* as_dst_base = tid < BM ? nullptr : dummy;  // resolved per stage below
+  // this lane's weight rows: column lr of subtile s, K block lg of each step
+  const uint8_t* w_src[NS];
+  const uint8_t* ws_src[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int wr = (s / NSUB) * BN + wave * 16 * NSUB + (s % NSUB) * 16 + lr;
+    w_src[s] = w_base + (int64_t)w_grow(wr) * (K / 2) + 16 * lg;
+    ws_src[s] = ws_base + (int64_t)w_grow(wr) * SKB;  // the step's 4 block scales as one dword
+  }
+
+  auto dma_a = [&](int ks, uint8_t* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < C::A_INS; ++q) dma16_to_lds(a_src[q] + ks * 128, st + (q * 4 + wave) * 1024);
+    dma4_to_lds(as_src + ks * 4, as_dst_base ? as_dst_base : st + C::A_BYTES);
+  };
+  u32x4 wq[D][NS];
+  int wsq[D][NS];
+  auto load_w = [&](int ks, u32x4 (&q)[NS], int (&sc)[NS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      q[s] = ld16(w_src[s] + 64 * ks);
+      sc[s] = (int)*reinterpret_cast<const uint32_t*>(ws_src[s] + 4 * ks);  // byte lg is this lane's
+    }
+  };
+
+  floatx4 acc[4][NS];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[i][s] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: weights of steps 0..D-1, then activation stages 0..RS-2
+#pragma unroll
+  for (int j = 0; j < D; ++j) load_w(j, wq[j], wsq[j]);
+  static_for<RS - 1>([&](auto jc) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j < KS) dma_a(j, stage(std::integral_constant<int, j>{}));
+  });
+  __builtin_amdgcn_sched_barrier(0);
+
+  static_for<KS>([&](auto kc) __attribute__((always_inline)) {
+    constexpr int ks = decltype(kc)::value;
+    // own DMAs of stage ks done (later ones may stay in flight); own LDS
+    // reads of the previous step done; then everyone's
+    wait_vm_lgkm0<mx2_wait_count<KS, RS, D, C::OPS_A, C::OPS_W>(ks)>();
+    asm volatile("s_barrier" ::: "memory");
+    if constexpr (ks + RS - 1 < KS) dma_a(ks + RS - 1, stage(std::integral_constant<int, (ks + RS - 1) % RS>{}));
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const uint8_t* s_a = stage(std::integral_constant<int, ks % RS>{});
+      const uint8_t* s_as = s_a + C::A_BYTES;
+      intx8 af[4];
+      int asc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 lo = ld16(s_a + swz<128>(16 * i + lr, lg));
+        const u32x4 hi = ld16(s_a + swz<128>(16 * i + lr, 4 + lg));
+        af[i] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+        asc[i] = s_as[(16 * i + lr) * 4 + lg];
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const u32x4 c = wq[ks % D][s];
+        const intx8 bv = intx8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+        const int bsc = (int)(((uint32_t)wsq[ks % D][s] >> (8 * lg)) & 0xFFu);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bv, acc[i][s], 0, 4, 0, asc[i], 0, bsc);
+      }
+    }
+    // the accumulators are used here, so the step's MFMAs are not sunk
+    // towards the epilogue (which would keep every step's operands live)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(acc[i][s]));
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (ks + D < KS) load_w(ks + D, wq[ks % D], wsq[ks % D]);
+  });
+
+  // ---- epilogue (its index arithmetic starts from an opaque zero so that
+  // none of it is hoisted into the unrolled K loop, where it would hold
+  // registers through every step)
+  int z0;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+      const int n = nt * BN + wave * 16 * NSUB + j * 16 + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = mt * BM + 16 * i + 4 * lg + r + z0;
+        if (rr >= n_rows) continue;
+        const int64_t R = r_begin + rr;
+        float v;
+        if (EPI == EPI_GATEUP) {
+          v = silu_f32(acc[i][j][r]) * acc[i][NSUB + j][r];
+        } else {
+          v = acc[i][j][r];
+          if (g.row_scale) v *= g.row_scale[R];
+        }
+        g.out[R * g.N + n] = v;
+      }
+    }
+}
+
 // Zero rows [n_valid, P) of a [P, cols] f32 buffer (n_valid read on the device).
 __global__ void zero_rows_tail_kernel(float* __restrict__ buf, const int32_t* __restrict__ n_valid, int64_t P,
                                       int cols) {
@@ -766,6 +1029,28 @@ static int launch_gemm_n(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t s
   return check_launch("grouped_gemm");
 }
 
+template <int EPI, int NSUB, int KS>
+static int launch_gemm_mx2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+  using C = Mx2Cfg<EPI, NSUB, KS>;
+  const int NT = a.N / C::BN;
+  int64_t G = tiles_m_bound * NT;
+  G = (G + 7) / 8 * 8;
+  if (G <= 0) return FP4_OK;
+  if (G > INT32_MAX) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM grid too large");
+  const size_t lds = a.dense_rows > 0 ? 0 : sizeof(int) * ((size_t)a.E + 1);
+  constexpr size_t fixed = (size_t)C::RS * C::STAGE + 1024;
+  if (fixed + lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_mx2_kernel<EPI, NSUB, KS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(160 * 1024 - fixed)) != hipSuccess)
+      return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((grouped_gemm_mx2_kernel<EPI, NSUB, KS>), dim3((unsigned)G), dim3(256), lds, st, a);
+  return check_launch("grouped_gemm_mx2");
+}
+
 template <int EPI, int NSUB>
 static int launch_gemm_mx(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   using C = MxCfg<EPI, NSUB>;
@@ -809,6 +1094,12 @@ static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st)
   if (a.w_fp8) return launch_gemm_w<GK, EPI, true>(a, tiles_m_bound, st);
   // the DMA-staged kernel pays off over long K (gate_up, K = hidden); the
   // short-K down projection is faster on the register-staged kernel
+  // down projection over the model's inter 640: the register-fed kernel with
+  // its K loop unrolled (measured faster than either staging kernel there;
+  // over K = 2560 the all-DMA kernel is faster)
+  if constexpr (EPI == EPI_DOWN) {
+    if (a.N % 128 == 0 && a.K == 640) return launch_gemm_mx2<EPI, 2, 5>(a, tiles_m_bound, st);
+  }
   if constexpr (EPI == EPI_GATEUP) {
     if (a.N % 128 == 0) return launch_gemm_mx<EPI, 2>(a, tiles_m_bound, st);
     if (a.N % 64 == 0) return launch_gemm_mx<EPI, 1>(a, tiles_m_bound, st);
