@@ -725,7 +725,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx_kernel(GemmArgs g) {
 // waits for the register loads, and the wait for a stage's DMA is a
 // compile-time count of the memory instructions issued after it
 // (mx2_wait_count); about 2.5x the bytes of the DMA-only kernel are in flight.
-template <int EPI, int NSUB, int KS>
+template <int GK, int EPI, int NSUB, int KS>
 struct Mx2Cfg {
   static constexpr int BM = kBM;
   static constexpr int BN = 64 * NSUB;
@@ -734,10 +734,13 @@ struct Mx2Cfg {
   static constexpr int RS = KS < 8 ? KS : 8;    // activation stages in the LDS ring
   static constexpr int D = KS < 3 ? KS : 3;     // steps of weight fragments in flight per wave
   static constexpr int A_BYTES = BM * 128;
-  static constexpr int STAGE = A_BYTES + BM * 4;  // codes + one scale dword (4 blocks of 32) per row
+  // per row and step one scale dword: 4 UE8M0 block scales (MX) or the f32
+  // scale of the 128-block (FP8); either way K/32 bytes per row
+  static constexpr int STAGE = A_BYTES + BM * 4;
   static constexpr int A_INS = A_BYTES / 4096;    // 16-byte DMA instructions per thread and stage
   static constexpr int OPS_A = A_INS + 1;         // + one 4-byte DMA of the scales
-  static constexpr int OPS_W = 2 * NS;            // per step: NS code loads + NS scale-byte loads
+  static constexpr int W_LD = GK == GK_FP8 ? 2 : 1;  // 16-byte code loads per subtile and step
+  static constexpr int OPS_W = (W_LD + 1) * NS;   // + one scale dword per subtile
 };
 
 // Memory instructions a thread issues between the DMA of stage ks (or the
@@ -788,9 +791,10 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(N));
 }
 
-template <int EPI, int NSUB, int KS>
+template <int GK, int EPI, int NSUB, int KS>
 __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
-  using C = Mx2Cfg<EPI, NSUB, KS>;
+  static_assert(GK == GK_MX || GK == GK_FP8, "MX or block-FP8 operands");
+  using C = Mx2Cfg<GK, EPI, NSUB, KS>;
   constexpr int BM = C::BM, BN = C::BN, NU = C::NU, NS = C::NS, RS = C::RS, D = C::D;
   static_assert(RS <= 8, "ring of at most 8 stages");
   // one array per stage: the compiler then sees that reading a stage does
@@ -850,8 +854,10 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   constexpr int K = KS * kBK;
   constexpr int SKB = K / 32;  // scale bytes per row
   const int NW = NU * g.N;
-  const uint8_t* w_base = g.w_codes + (int64_t)e * NW * (K / 2);
-  const uint8_t* ws_base = reinterpret_cast<const uint8_t*>(g.w_scales) + (int64_t)e * NW * SKB;
+  constexpr int W_ROW = GK == GK_FP8 ? K : K / 2;      // weight bytes per row
+  constexpr int W_STEP = GK == GK_FP8 ? 128 : 64;      // weight bytes per row and step
+  const uint8_t* w_base = g.w_codes + (int64_t)e * NW * W_ROW;
+  const uint8_t* ws_base = reinterpret_cast<const uint8_t*>(g.w_scales);
 
   auto a_row_of = [&](int r) __attribute__((always_inline)) -> int64_t {
     const int rr = mt * BM + r;
@@ -876,8 +882,11 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int wr = (s / NSUB) * BN + wave * 16 * NSUB + (s % NSUB) * 16 + lr;
-    w_src[s] = w_base + (int64_t)w_grow(wr) * (K / 2) + 16 * lg;
-    ws_src[s] = ws_base + (int64_t)w_grow(wr) * SKB;  // the step's 4 block scales as one dword
+    w_src[s] = w_base + (int64_t)w_grow(wr) * W_ROW + 16 * lg;
+    if (GK == GK_MX)  // the step's 4 UE8M0 block scales of the row as one dword
+      ws_src[s] = ws_base + ((int64_t)e * NW + w_grow(wr)) * SKB;
+    else  // the f32 scale of the row's 128 x 128 block
+      ws_src[s] = ws_base + (((int64_t)e * (NW / 128) + w_grow(wr) / 128) * KS) * 4;
   }
 
   auto dma_a = [&](int ks, uint8_t* st) __attribute__((always_inline)) {
@@ -885,13 +894,14 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
     for (int q = 0; q < C::A_INS; ++q) dma16_to_lds(a_src[q] + ks * 128, st + (q * 4 + wave) * 1024);
     dma4_to_lds(as_src + ks * 4, as_dst_base ? as_dst_base : st + C::A_BYTES);
   };
-  u32x4 wq[D][NS];
+  u32x4 wq[D][NS][C::W_LD];
   int wsq[D][NS];
-  auto load_w = [&](int ks, u32x4 (&q)[NS], int (&sc)[NS]) __attribute__((always_inline)) {
+  auto load_w = [&](int ks, u32x4 (&q)[NS][C::W_LD], int (&sc)[NS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      q[s] = ld16(w_src[s] + 64 * ks);
-      sc[s] = (int)*reinterpret_cast<const uint32_t*>(ws_src[s] + 4 * ks);  // byte lg is this lane's
+      q[s][0] = ld16(w_src[s] + W_STEP * ks);
+      if constexpr (GK == GK_FP8) q[s][C::W_LD - 1] = ld16(w_src[s] + W_STEP * ks + 64);
+      sc[s] = (int)*reinterpret_cast<const uint32_t*>(ws_src[s] + 4 * ks);  // MX: byte lg is this lane's
     }
   };
 
@@ -923,21 +933,43 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
       const uint8_t* s_as = s_a + C::A_BYTES;
       intx8 af[4];
       int asc[4];
+      float afs[4][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const u32x4 lo = ld16(s_a + swz<128>(16 * i + lr, lg));
         const u32x4 hi = ld16(s_a + swz<128>(16 * i + lr, 4 + lg));
         af[i] = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-        asc[i] = s_as[(16 * i + lr) * 4 + lg];
+        if constexpr (GK == GK_MX) {
+          asc[i] = s_as[(16 * i + lr) * 4 + lg];
+        } else {  // f32 scales of the accumulator rows 16 i + 4 lg + r
+          const u32x4 v = ld16(s_as + (16 * i + 4 * lg) * 4);
+          afs[i][0] = __uint_as_float(v.x); afs[i][1] = __uint_as_float(v.y);
+          afs[i][2] = __uint_as_float(v.z); afs[i][3] = __uint_as_float(v.w);
+        }
       }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const u32x4 c = wq[ks % D][s];
-        const intx8 bv = intx8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-        const int bsc = (int)(((uint32_t)wsq[ks % D][s] >> (8 * lg)) & 0xFFu);
+        if constexpr (GK == GK_MX) {
+          const u32x4 c = wq[ks % D][s][0];
+          const intx8 bv = intx8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+          const int bsc = (int)(((uint32_t)wsq[ks % D][s] >> (8 * lg)) & 0xFFu);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          acc[i][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bv, acc[i][s], 0, 4, 0, asc[i], 0, bsc);
+          for (int i = 0; i < 4; ++i)
+            acc[i][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bv, acc[i][s], 0, 4, 0, asc[i], 0, bsc);
+        } else {
+          // unit-scale E4M3 products of the 128-block, then the block's
+          // activation-row and weight scales in f32
+          const u32x4 lo = wq[ks % D][s][0], hi = wq[ks % D][s][C::W_LD - 1];
+          const intx8 bv = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+          const float ws = __uint_as_float((uint32_t)wsq[ks % D][s]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const floatx4 pp = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                af[i], bv, floatx4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[i][s][r] = fmaf(pp[r], afs[i][r] * ws, acc[i][s][r]);
+          }
+        }
       }
     }
     // the accumulators are used here, so the step's MFMAs are not sunk
@@ -1029,9 +1061,9 @@ static int launch_gemm_n(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t s
   return check_launch("grouped_gemm");
 }
 
-template <int EPI, int NSUB, int KS>
+template <int GK, int EPI, int NSUB, int KS>
 static int launch_gemm_mx2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
-  using C = Mx2Cfg<EPI, NSUB, KS>;
+  using C = Mx2Cfg<GK, EPI, NSUB, KS>;
   const int NT = a.N / C::BN;
   int64_t G = tiles_m_bound * NT;
   G = (G + 7) / 8 * 8;
@@ -1042,12 +1074,12 @@ static int launch_gemm_mx2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t
   if (fixed + lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_mx2_kernel<EPI, NSUB, KS>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)(160 * 1024 - fixed)) != hipSuccess)
       return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
     attr_set = true;
   }
-  hipLaunchKernelGGL((grouped_gemm_mx2_kernel<EPI, NSUB, KS>), dim3((unsigned)G), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS>), dim3((unsigned)G), dim3(256), lds, st, a);
   return check_launch("grouped_gemm_mx2");
 }
 
@@ -1086,6 +1118,9 @@ template <int GK, int EPI>
 static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   if (GK == GK_NV) return launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
   if (GK == GK_FP8) {
+    if constexpr (EPI == EPI_DOWN) {
+      if (a.N % 128 == 0 && a.K == 640) return launch_gemm_mx2<GK_FP8, EPI, 2, 5>(a, tiles_m_bound, st);
+    }
     // FP8 weight tiles are twice the bytes: 64-output gate_up tiles keep two
     // workgroups per CU in LDS and measure faster; the down tiles do not
     if (EPI == EPI_GATEUP && a.N % 64 == 0) return launch_gemm_n<GK, EPI, 1, true>(a, tiles_m_bound, st);
@@ -1098,7 +1133,7 @@ static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st)
   // its K loop unrolled (measured faster than either staging kernel there;
   // over K = 2560 the all-DMA kernel is faster)
   if constexpr (EPI == EPI_DOWN) {
-    if (a.N % 128 == 0 && a.K == 640) return launch_gemm_mx2<EPI, 2, 5>(a, tiles_m_bound, st);
+    if (a.N % 128 == 0 && a.K == 640) return launch_gemm_mx2<GK_MX, EPI, 2, 5>(a, tiles_m_bound, st);
   }
   if constexpr (EPI == EPI_GATEUP) {
     if (a.N % 128 == 0) return launch_gemm_mx<EPI, 2>(a, tiles_m_bound, st);
