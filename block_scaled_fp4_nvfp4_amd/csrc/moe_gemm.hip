@@ -1118,8 +1118,12 @@ template <int GK, int EPI>
 static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   if (GK == GK_NV) return launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
   if (GK == GK_FP8) {
+    // the model's reduction sizes on the register-fed kernel (gate_up with
+    // 64-output tiles: 128-output ones spill)
     if constexpr (EPI == EPI_DOWN) {
       if (a.N % 128 == 0 && a.K == 640) return launch_gemm_mx2<GK_FP8, EPI, 2, 5>(a, tiles_m_bound, st);
+    } else {
+      if (a.N % 64 == 0 && a.K == 2560) return launch_gemm_mx2<GK_FP8, EPI, 1, 20>(a, tiles_m_bound, st);
     }
     // FP8 weight tiles are twice the bytes: 64-output gate_up tiles keep two
     // workgroups per CU in LDS and measure faster; the down tiles do not
