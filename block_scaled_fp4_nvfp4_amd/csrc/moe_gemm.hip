@@ -1009,6 +1009,276 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
     }
 }
 
+// NVFP4 x NVFP4 on the same plan: each wave's weight fragments (E2M1 codes
+// and the two E4M3 scales of its 32 values) go straight into VGPRs D steps
+// ahead and are decoded to fp16 per MFMA fragment; the activation codes and
+// scales arrive by DMA in an LDS ring, and during step ks the workgroup
+// decodes step ks+1's tile once into one of two fp16 LDS buffers (one barrier
+// per step).  Waits are compile-time counts as in the kernel above.
+template <int EPI, int NSUB, int KS>
+struct Nv2Cfg {
+  static constexpr int BM = kBM;
+  static constexpr int BN = 64 * NSUB;
+  static constexpr int NU = EPI == EPI_GATEUP ? 2 : 1;
+  static constexpr int NS = NU * NSUB;
+  static constexpr int RS = KS < 6 ? KS : 6;         // raw activation stages
+  static constexpr int D = KS < 2 ? KS : 2;          // steps of weight fragments in flight per wave
+  static constexpr int RAW_A = BM * 64;              // E2M1 codes: 64 rows x 128 values
+  static constexpr int RAW = RAW_A + BM * 8;         // + 8 E4M3 scales per row
+  static constexpr int DEC = BM * 256;               // fp16 tile, 64 rows x 128 values
+  static constexpr int OPS_A = 2;                    // one 16-byte and one 4-byte DMA per thread
+  static constexpr int OPS_W = 2 * NS;               // per subtile: codes (16 B) + the row's 8 scales
+};
+
+// Memory instructions issued by a thread between a given raw stage's DMA (or
+// a step's weight loads) and the wait at the top of step ks.  Prologue:
+// W(0..D-1), raw(0..RS-2); step j: raw(j+RS-1) after the barrier, W(j+D)
+// after the MFMAs.
+template <int KS, int RS, int D, int OA, int OW>
+constexpr int nv2_ops_steps(int j0, int ks) {  // ops of steps j0+1 .. ks-1
+  int n = 0;
+  for (int j = j0 + 1; j < ks; ++j) {
+    if (j + RS - 1 < KS) n += OA;
+    if (j + D < KS) n += OW;
+  }
+  return n;
+}
+template <int KS, int RS, int D, int OA, int OW>
+constexpr int nv2_after_raw(int s, int ks) {  // raw stage s, wait of step ks
+  const int last = (KS < RS - 1 ? KS : RS - 1) - 1;
+  if (s <= RS - 2) return (last - s) * OA + nv2_ops_steps<KS, RS, D, OA, OW>(-1, ks);
+  const int j0 = s - RS + 1;
+  return (j0 + D < KS ? OW : 0) + nv2_ops_steps<KS, RS, D, OA, OW>(j0, ks);
+}
+template <int KS, int RS, int D, int OA, int OW>
+constexpr int nv2_wait_count(int ks) {  // raw(ks+1) and W(ks) done
+  const int last = (KS < RS - 1 ? KS : RS - 1) - 1;
+  const int nw = ks < D ? (D - 1 - ks) * OW + (last + 1) * OA + nv2_ops_steps<KS, RS, D, OA, OW>(-1, ks)
+                        : nv2_ops_steps<KS, RS, D, OA, OW>(ks - D, ks);
+  int n = nw;
+  if (ks + 1 < KS) {
+    const int na = nv2_after_raw<KS, RS, D, OA, OW>(ks + 1, ks);
+    n = na < n ? na : n;
+  }
+  return n < 63 ? n : 63;
+}
+
+template <int EPI, int NSUB, int KS>
+__global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
+  using C = Nv2Cfg<EPI, NSUB, KS>;
+  constexpr int BM = C::BM, BN = C::BN, NU = C::NU, NS = C::NS, RS = C::RS, D = C::D;
+  static_assert(RS <= 6, "ring of at most 6 raw stages");
+  __shared__ __attribute__((aligned(16))) uint8_t q0[C::RAW], q1[RS > 1 ? C::RAW : 16], q2[RS > 2 ? C::RAW : 16],
+      q3[RS > 3 ? C::RAW : 16], q4[RS > 4 ? C::RAW : 16], q5[RS > 5 ? C::RAW : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t d0[C::DEC], d1[C::DEC];
+  __shared__ __attribute__((aligned(16))) uint8_t dummy[512];
+  auto raw = [&](auto sc) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int S = decltype(sc)::value;
+    if constexpr (S == 0) return q0;
+    else if constexpr (S == 1) return q1;
+    else if constexpr (S == 2) return q2;
+    else if constexpr (S == 3) return q3;
+    else if constexpr (S == 4) return q4;
+    else return q5;
+  };
+  auto dec = [&](auto sc) __attribute__((always_inline)) -> uint8_t* {
+    if constexpr (decltype(sc)::value == 0) return d0;
+    else return d1;
+  };
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  int* s_toff = reinterpret_cast<int*>(lds_dyn);
+
+  const int NT = g.N / BN;
+  const int G = gridDim.x;
+  const int per_xcd = G / 8;
+  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  int e, mt, nt, r_begin, n_rows;
+  if (g.dense_rows > 0) {
+    e = 0;
+    nt = L % NT;
+    mt = L / NT;
+    if (mt * BM >= g.dense_rows) return;
+    r_begin = 0;
+    n_rows = g.dense_rows;
+  } else {
+    for (int i = threadIdx.x; i <= g.E; i += 256) s_toff[i] = g.tile_offsets[i];
+    __syncthreads();
+    nt = L % NT;
+    const int mg = L / NT;
+    if (mg >= s_toff[g.E]) return;
+    int lo = 0, hi = g.E;
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (s_toff[mid] <= mg) lo = mid; else hi = mid;
+    }
+    e = lo;
+    mt = mg - s_toff[e];
+    r_begin = g.offsets[e];
+    n_rows = g.offsets[e + 1] - r_begin;
+  }
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  constexpr int K = KS * kBK;
+  const int NW = NU * g.N;
+  auto a_row_of = [&](int r) __attribute__((always_inline)) -> int64_t {
+    const int rr = mt * BM + r;
+    const int R = r_begin + (rr < n_rows ? rr : 0);  // rows past the expert's end fetch row 0 (never stored)
+    return g.a_gather ? g.pair_of_row[R] / g.k : R;
+  };
+  auto w_grow = [&](int i) __attribute__((always_inline)) -> int { return (i / BN) * g.N + nt * BN + (i % BN); };
+
+  // raw activation DMA: thread t moves 16 code bytes of row t/4 (values
+  // 32 (t%4) .. +32) and, for t < 128, the 4 scale bytes t%2 of row t/2
+  const int arow = tid >> 2, apart = tid & 3;
+  const uint8_t* a_src = g.a_codes + a_row_of(arow) * (K / 2) + 16 * apart;
+  const uint8_t* as_src = reinterpret_cast<const uint8_t*>(g.a_scales) +
+                          a_row_of(tid < 128 ? tid >> 1 : 0) * (K / 16) + 4 * (tid & 1);
+  auto dma_raw = [&](int ks, uint8_t* st) __attribute__((always_inline)) {
+    dma16_to_lds(a_src + ks * 64, st + wave * 1024);
+    dma4_to_lds(as_src + ks * 8, wave < 2 ? st + C::RAW_A + wave * 256 : dummy);
+  };
+  // decode this thread's 32 raw values into the fp16 tile (swizzled rows of 256 B)
+  auto decode_raw = [&](const uint8_t* st, uint8_t* dt) __attribute__((always_inline)) {
+    const u32x4 c = ld16(st + 16 * tid);
+    const uint32_t s2 = *reinterpret_cast<const uint16_t*>(st + C::RAW_A + arow * 8 + 2 * apart);
+    uint32_t d[16];
+    nv_decode32(make_uint4(c.x, c.y, c.z, c.w), s2, d);
+    st16(dt + swz<256>(arow, 4 * apart), u32x4{d[0], d[1], d[2], d[3]});
+    st16(dt + swz<256>(arow, 4 * apart + 1), u32x4{d[4], d[5], d[6], d[7]});
+    st16(dt + swz<256>(arow, 4 * apart + 2), u32x4{d[8], d[9], d[10], d[11]});
+    st16(dt + swz<256>(arow, 4 * apart + 3), u32x4{d[12], d[13], d[14], d[15]});
+  };
+  // this lane's weight rows: column lr of subtile s, values 32 lg .. +32 of each step
+  const uint8_t* w_src[NS];
+  const uint8_t* ws_src[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int wr = (s / NSUB) * BN + wave * 16 * NSUB + (s % NSUB) * 16 + lr;
+    const int64_t grow = (int64_t)e * NW + w_grow(wr);
+    w_src[s] = g.w_codes + grow * (K / 2) + 16 * lg;
+    ws_src[s] = reinterpret_cast<const uint8_t*>(g.w_scales) + grow * (K / 16);
+  }
+  u32x4 wq[D][NS];
+  u32x2 wsq[D][NS];
+  auto load_w = [&](int ks, u32x4 (&q)[NS], u32x2 (&sc)[NS]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      q[s] = ld16(w_src[s] + 64 * ks);
+      sc[s] = *reinterpret_cast<const u32x2*>(ws_src[s] + 8 * ks);  // the row's 8 scales of the step
+    }
+  };
+
+  floatx4 acc[4][NS];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int s = 0; s < NS; ++s) acc[i][s] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  // prologue: weights of steps 0..D-1, raw stages 0..RS-2, then step 0's tile decoded
+#pragma unroll
+  for (int j = 0; j < D; ++j) load_w(j, wq[j], wsq[j]);
+  static_for<RS - 1>([&](auto jc) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    if constexpr (j < KS) dma_raw(j, raw(std::integral_constant<int, j>{}));
+  });
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm_lgkm0<nv2_after_raw<KS, RS, D, C::OPS_A, C::OPS_W>(0, 0)>();
+  asm volatile("s_barrier" ::: "memory");
+  decode_raw(raw(std::integral_constant<int, 0>{}), dec(std::integral_constant<int, 0>{}));
+  __builtin_amdgcn_sched_barrier(0);
+
+  static_for<KS>([&](auto kc) __attribute__((always_inline)) {
+    constexpr int ks = decltype(kc)::value;
+    wait_vm_lgkm0<nv2_wait_count<KS, RS, D, C::OPS_A, C::OPS_W>(ks)>();
+    asm volatile("s_barrier" ::: "memory");
+    if constexpr (ks + RS - 1 < KS) dma_raw(ks + RS - 1, raw(std::integral_constant<int, (ks + RS - 1) % RS>{}));
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (ks + 1 < KS)
+      decode_raw(raw(std::integral_constant<int, (ks + 1) % RS>{}), dec(std::integral_constant<int, (ks + 1) % 2>{}));
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const uint8_t* s_a = dec(std::integral_constant<int, ks % 2>{});
+      uint32_t af[4][16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 v = ld16(s_a + swz<256>(16 * i + lr, 4 * lg + q));
+          af[i][4 * q] = v.x; af[i][4 * q + 1] = v.y; af[i][4 * q + 2] = v.z; af[i][4 * q + 3] = v.w;
+        }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const u32x4 c = wq[ks % D][s];
+        const u32x2 sc = wsq[ks % D][s];
+        const uint32_t s2 = ((lg < 2 ? sc.x : sc.y) >> (16 * (lg & 1))) & 0xFFFFu;
+        uint32_t wd[16];
+        nv_decode32(make_uint4(c.x, c.y, c.z, c.w), s2, wd);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            acc[i][s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(&af[i][4 * m]), as_half8(&wd[4 * m]),
+                                                               acc[i][s], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(acc[i][s]));
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (ks + D < KS) load_w(ks + D, wq[ks % D], wsq[ks % D]);
+  });
+
+  // ---- epilogue (index arithmetic from an opaque zero: not hoisted into the K loop)
+  int z0;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+  const float scale = g.a_tensor_scale[0] * g.w_tensor_scale[e];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < NSUB; ++j) {
+      const int n = nt * BN + wave * 16 * NSUB + j * 16 + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rr = mt * BM + 16 * i + 4 * lg + r + z0;
+        if (rr >= n_rows) continue;
+        const int64_t R = r_begin + rr;
+        float v;
+        if (EPI == EPI_GATEUP) {
+          v = silu_f32(acc[i][j][r] * scale) * (acc[i][NSUB + j][r] * scale);
+        } else {
+          v = acc[i][j][r] * scale;
+          if (g.row_scale) v *= g.row_scale[R];
+        }
+        g.out[R * g.N + n] = v;
+      }
+    }
+}
+
+template <int EPI, int NSUB, int KS>
+static int launch_gemm_nv2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+  using C = Nv2Cfg<EPI, NSUB, KS>;
+  const int NT = a.N / C::BN;
+  int64_t G = tiles_m_bound * NT;
+  G = (G + 7) / 8 * 8;
+  if (G <= 0) return FP4_OK;
+  if (G > INT32_MAX) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM grid too large");
+  const size_t lds = a.dense_rows > 0 ? 0 : sizeof(int) * ((size_t)a.E + 1);
+  constexpr size_t fixed = (size_t)C::RS * C::RAW + 2 * (size_t)C::DEC + 512;
+  if (fixed + lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_nv2_kernel<EPI, NSUB, KS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(160 * 1024 - fixed)) != hipSuccess)
+      return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((grouped_gemm_nv2_kernel<EPI, NSUB, KS>), dim3((unsigned)G), dim3(256), lds, st, a);
+  return check_launch("grouped_gemm_nv2");
+}
+
 // Zero rows [n_valid, P) of a [P, cols] f32 buffer (n_valid read on the device).
 __global__ void zero_rows_tail_kernel(float* __restrict__ buf, const int32_t* __restrict__ n_valid, int64_t P,
                                       int cols) {
@@ -1116,7 +1386,14 @@ static int launch_gemm_w(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t s
 
 template <int GK, int EPI>
 static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
-  if (GK == GK_NV) return launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
+  if (GK == GK_NV) {
+    // down over the model's inter 640 on the register-fed kernel (measured
+    // faster there; over K = 2560 the register-staged kernel is faster)
+    if constexpr (EPI == EPI_DOWN) {
+      if (a.N % 128 == 0 && a.K == 640) return launch_gemm_nv2<EPI, 2, 5>(a, tiles_m_bound, st);
+    }
+    return launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
+  }
   if (GK == GK_FP8) {
     // the model's reduction sizes on the register-fed kernel (gate_up with
     // 64-output tiles: 128-output ones spill)
