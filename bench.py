@@ -395,7 +395,7 @@ def bench_stream_quant(args, torch, pkg):
                        f"(gate_up {2 * I}x{H}, down {H}x{I}), bf16 Student-t(4) source with 1% outlier rows x8",
            "value": gbs, "unit": "GB/s", "ms_per_layer": ms_layer, "layers": layers,
            "values_per_layer": E * 3 * H * I,
-           "roofline": {"bound": "hbm", "kernel": "quant_fp4_kernel + tensor_amax_kernel",
+           "roofline": {"bound": "hbm", "kernel": "quant_fp4_kernel (fused with the next chunk's amax) + tensor_amax_kernel (first chunk)",
                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                         "traffic": (lambda t: t["bytes_per_launch"] if t else None)(
                             measured_traffic("quant_fp4_kernel", "stream_quant")),

@@ -760,7 +760,7 @@ constexpr int mx2_ops_between_steps(int j0, int ks) {  // steps j0+1 .. ks-1
 template <int KS, int RS, int D, int OA, int OW>
 constexpr int mx2_wait_count(int ks) {
   const int last = (KS < RS - 1 ? KS : RS - 1) - 1;  // last stage of the prologue
-  int na, nw;
+  int na = 0, nw = 0;
   if (ks <= RS - 2) {
     na = (last - ks) * OA + mx2_ops_between_steps<KS, RS, D, OA, OW>(-1, ks);
   } else {

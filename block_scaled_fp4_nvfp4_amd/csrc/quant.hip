@@ -130,6 +130,28 @@ __global__ void __launch_bounds__(256) tensor_amax_kernel(const T* x, int64_t pe
   }
 }
 
+// S = fp32(fp64(amax) / 2688) of tensor y from its nparts partial maxima at
+// part + y * stride; one workgroup per tensor.
+__global__ void __launch_bounds__(256) nv_scale_from_parts_kernel(const float* __restrict__ part, int64_t stride,
+                                                                  int nparts, float* __restrict__ s) {
+  const float* p = part + (int64_t)blockIdx.x * stride;
+  float m = 0.0f;
+  int i = threadIdx.x;
+  for (; i + 3 * 256 < nparts; i += 4 * 256) {  // four loads in flight per lane
+    const float a = p[i], b = p[i + 256], c = p[i + 512], d = p[i + 768];
+    m = fmaxf(m, fmaxf(fmaxf(a, b), fmaxf(c, d)));
+  }
+  for (; i < nparts; i += 256) m = fmaxf(m, p[i]);
+  m = wave_max(m);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float a = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    s[blockIdx.x] = (float)((double)a / kNvTensorDivisor);
+  }
+}
+
 // S = fp32(fp64(amax) / 2688), in place over the amax bits.
 __global__ void nv_tensor_scale_kernel(float* s, int64_t n) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -241,8 +263,10 @@ template <int BS, bool MX, bool FOUR_SIX, typename T>
 __global__ void __launch_bounds__(256) quant_fp4_kernel(
     const T* __restrict__ x, int64_t blocks_per_tensor, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale,
-    uint8_t* __restrict__ m4_flags) {
+    uint8_t* __restrict__ m4_flags, const T* __restrict__ next_x, float* __restrict__ next_part,
+    int64_t part_stride, int next_tensors) {
   constexpr bool BF = std::is_same<T, uint16_t>::value;
+  constexpr bool FUSE = BF && !MX;
   constexpr int NW = BS / 8;
   using Acc = typename GxAcc<T>::type;
   int64_t blk = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -251,12 +275,29 @@ __global__ void __launch_bounds__(256) quant_fp4_kernel(
   uint32_t raw[BF ? BS / 2 : 1];
   float v[BS];
   float amax;
+  // The same block of tensor blockIdx.y of the next chunk, for its tensor
+  // amax: each workgroup stores its partial max at next_part[y * part_stride
+  // + x] (NVFP4 from bf16 only; the host launches this only when every lane
+  // of every workgroup holds a block, with next_tensors <= gridDim.y and
+  // gridDim.x <= part_stride).
+  const bool fuse = FUSE && (int)blockIdx.y < next_tensors;
+  uint32_t nraw[FUSE ? BS / 2 : 1];
   if constexpr (BF) {
     const uint4* q = reinterpret_cast<const uint4*>(x + g * BS);
 #pragma unroll
     for (int i = 0; i < BS / 8; ++i) {
       const uint4 w = q[i];
       raw[4 * i] = w.x; raw[4 * i + 1] = w.y; raw[4 * i + 2] = w.z; raw[4 * i + 3] = w.w;
+    }
+    if constexpr (FUSE) {
+      if (fuse) {
+        const uint4* nq = reinterpret_cast<const uint4*>(next_x + g * BS);
+#pragma unroll
+        for (int i = 0; i < BS / 8; ++i) {
+          const uint4 w = nq[i];
+          nraw[4 * i] = w.x; nraw[4 * i + 1] = w.y; nraw[4 * i + 2] = w.z; nraw[4 * i + 3] = w.w;
+        }
+      }
     }
     // |x| bit patterns order like |x|: a packed 16-bit max over the pairs
     u16x2_t m = {0, 0};
@@ -394,6 +435,20 @@ __global__ void __launch_bounds__(256) quant_fp4_kernel(
   }
   scales[g] = (uint8_t)((FOUR_SIX && use4) ? code4 : code6);
   if (m4_flags) m4_flags[g] = use4 ? 1 : 0;
+  if constexpr (FUSE) {
+    if (fuse) {
+      u16x2_t m = {0, 0};
+#pragma unroll
+      for (int i = 0; i < BS / 2; ++i)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, nraw[i] & 0x7FFF7FFFu));
+      const float a = wave_max(__uint_as_float((uint32_t)max(m.x, m.y) << 16));
+      __shared__ float red[4];
+      if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = a;
+      __syncthreads();
+      if (threadIdx.x == 0)
+        next_part[(int64_t)blockIdx.y * part_stride + blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    }
+  }
 }
 
 // MXFP8: one thread per block of 32; e = min{e : 448 * 2^e >= amax}.
@@ -664,6 +719,20 @@ int launch_fill(uint32_t* p, uint32_t v, int64_t n, hipStream_t st) {
   return check_launch("fill");
 }
 
+// Number of chunks a dynamic-scale NVFP4 batch from bf16 is cut into, so
+// that the amax of one chunk is taken while the previous one is quantized
+// (1: a separate amax pass first).  Each chunk must still fill the chip, and
+// every lane of every quantization workgroup must hold a block.  Eight
+// measured best on 512-tensor batches (four and sixteen within 2 %; smaller
+// chunks lose more to launch ramps than the fused amax saves).
+template <typename T>
+int amax_chunks(int64_t batch, int64_t per) {
+  if (!std::is_same<T, uint16_t>::value || batch < 16 || per < (1 << 20) || (per / 16) % 256 != 0) return 1;
+  int64_t n = std::max<int64_t>(1, std::min<int64_t>(8, batch / 8));
+  while ((batch + n - 1) / n > 65535) ++n;
+  return (int)n;
+}
+
 template <typename T>
 int quantize_typed(int fmt, int rule, int ts_mode, const T* x, int64_t batch, int64_t rows,
                    int64_t cols, uint8_t* codes, void* scales, float* tensor_scale,
@@ -673,40 +742,74 @@ int quantize_typed(int fmt, int rule, int ts_mode, const T* x, int64_t batch, in
     const bool mx = fmt == FP4_FMT_MXFP4;
     const int bs = mx ? 32 : 16;
     const int64_t bpt = per / bs;
-    if (!mx && ts_mode == FP4_TS_DYNAMIC) {
-      FP4_CHECK(launch_fill(reinterpret_cast<uint32_t*>(tensor_scale), 0u, batch, st));
+    // tensor amax of tensors [b0, b0 + nb), then their scales amax / 2688
+    auto amax_range = [&](int64_t b0, int64_t nb, hipStream_t sx) -> int {
       // about 4 workgroups per CU in total, at least one per tensor
       int64_t chunks = (per / 8 + 255) / 256;
-      int64_t target = 4LL * device_cu_count() / (batch > 0 ? batch : 1);
+      int64_t target = 4LL * device_cu_count() / nb;
       unsigned gx = (unsigned)std::max<int64_t>(1, std::min<int64_t>(chunks, std::max<int64_t>(target, 1)));
-      for (int64_t b0 = 0; b0 < batch; b0 += 65535) {
-        unsigned gy = (unsigned)std::min<int64_t>(65535, batch - b0);
-        hipLaunchKernelGGL(tensor_amax_kernel<T>, dim3(gx, gy), dim3(256), 0, st, x + b0 * per, per,
-                           reinterpret_cast<uint32_t*>(tensor_scale) + b0);
+      for (int64_t c0 = 0; c0 < nb; c0 += 65535) {
+        unsigned gy = (unsigned)std::min<int64_t>(65535, nb - c0);
+        hipLaunchKernelGGL(tensor_amax_kernel<T>, dim3(gx, gy), dim3(256), 0, sx, x + (b0 + c0) * per, per,
+                           reinterpret_cast<uint32_t*>(tensor_scale) + b0 + c0);
         FP4_CHECK(check_launch("tensor_amax"));
       }
-      hipLaunchKernelGGL(nv_tensor_scale_kernel, dim3(grid_1d(batch, 256)), dim3(256), 0, st,
-                         tensor_scale, batch);
-      FP4_CHECK(check_launch("tensor_scale"));
+      hipLaunchKernelGGL(nv_tensor_scale_kernel, dim3(grid_1d(nb, 256)), dim3(256), 0, sx, tensor_scale + b0, nb);
+      return check_launch("tensor_scale");
+    };
+    // quantization of tensors [b0, b0 + nb); with nn > 0 the same launch also
+    // takes partial maxima of the nn <= nb tensors that follow (bf16 NVFP4
+    // only), stored in the code bytes of those tensors, which are written
+    // only later, by their own quantization
+    auto quant_range = [&](int64_t b0, int64_t nb, hipStream_t sx, int64_t nn = 0) -> int {
+      unsigned gx = grid_1d(bpt, 256);
+      const T* nx = nn > 0 ? x + (b0 + nb) * per : nullptr;
+      float* np_ = nn > 0 ? reinterpret_cast<float*>(codes + (b0 + nb) * per / 2) : nullptr;
+      for (int64_t c0 = b0; c0 < b0 + nb; c0 += 65535) {
+        unsigned gy = (unsigned)std::min<int64_t>(65535, b0 + nb - c0);
+        const T* xb = x + c0 * per;
+        uint8_t* cb = codes + c0 * per / 2;
+        uint8_t* sb = reinterpret_cast<uint8_t*>(scales) + c0 * bpt;
+        const float* tb = tensor_scale ? tensor_scale + c0 : nullptr;
+        uint8_t* mb = m4 ? m4 + c0 * bpt : nullptr;
+        dim3 grid(gx, gy);
+        if (!mx && rule == FP4_RULE_4OVER6)
+          hipLaunchKernelGGL((quant_fp4_kernel<16, false, true, T>), grid, dim3(256), 0, sx, xb, bpt, cb, sb, tb, mb, nx, np_, per / 8, (int)nn);
+        else if (!mx)
+          hipLaunchKernelGGL((quant_fp4_kernel<16, false, false, T>), grid, dim3(256), 0, sx, xb, bpt, cb, sb, tb, mb, nx, np_, per / 8, (int)nn);
+        else if (rule == FP4_RULE_4OVER6)
+          hipLaunchKernelGGL((quant_fp4_kernel<32, true, true, T>), grid, dim3(256), 0, sx, xb, bpt, cb, sb, tb, mb, nx, np_, per / 8, (int)nn);
+        else
+          hipLaunchKernelGGL((quant_fp4_kernel<32, true, false, T>), grid, dim3(256), 0, sx, xb, bpt, cb, sb, tb, mb, nx, np_, per / 8, (int)nn);
+        FP4_CHECK(check_launch("quant_fp4"));
+      }
+      return FP4_OK;
+    };
+    if (mx || ts_mode != FP4_TS_DYNAMIC) return quant_range(0, batch, st);
+    FP4_CHECK(launch_fill(reinterpret_cast<uint32_t*>(tensor_scale), 0u, batch, st));
+    const int nch = amax_chunks<T>(batch, per);
+    if (nch <= 1) {
+      FP4_CHECK(amax_range(0, batch, st));
+      return quant_range(0, batch, st);
     }
-    unsigned gx = grid_1d(bpt, 256);
-    for (int64_t b0 = 0; b0 < batch; b0 += 65535) {
-      unsigned gy = (unsigned)std::min<int64_t>(65535, batch - b0);
-      const T* xb = x + b0 * per;
-      uint8_t* cb = codes + b0 * per / 2;
-      uint8_t* sb = reinterpret_cast<uint8_t*>(scales) + b0 * bpt;
-      const float* tb = tensor_scale ? tensor_scale + b0 : nullptr;
-      uint8_t* mb = m4 ? m4 + b0 * bpt : nullptr;
-      dim3 grid(gx, gy);
-      if (!mx && rule == FP4_RULE_4OVER6)
-        hipLaunchKernelGGL((quant_fp4_kernel<16, false, true, T>), grid, dim3(256), 0, st, xb, bpt, cb, sb, tb, mb);
-      else if (!mx)
-        hipLaunchKernelGGL((quant_fp4_kernel<16, false, false, T>), grid, dim3(256), 0, st, xb, bpt, cb, sb, tb, mb);
-      else if (rule == FP4_RULE_4OVER6)
-        hipLaunchKernelGGL((quant_fp4_kernel<32, true, true, T>), grid, dim3(256), 0, st, xb, bpt, cb, sb, tb, mb);
-      else
-        hipLaunchKernelGGL((quant_fp4_kernel<32, true, false, T>), grid, dim3(256), 0, st, xb, bpt, cb, sb, tb, mb);
-      FP4_CHECK(check_launch("quant_fp4"));
+    // The amax pass only streams from HBM while the quantization pass is
+    // bound by vector ALU work, so the batch is cut into chunks and the amax
+    // of chunk c+1 is taken inside the quantization launch of chunk c, from
+    // loads that hide under its arithmetic.  Stream order alone sequences
+    // the chunks: amax(c+1) lands before the scale kernel of c+1, which
+    // runs before the quantization of c+1.
+    const int64_t per_chunk = (batch + nch - 1) / nch;
+    FP4_CHECK(amax_range(0, std::min<int64_t>(per_chunk, batch), st));
+    for (int64_t b0 = 0; b0 < batch; b0 += per_chunk) {
+      const int64_t nb = std::min<int64_t>(per_chunk, batch - b0);
+      const int64_t nn = std::min<int64_t>(per_chunk, std::max<int64_t>(0, batch - b0 - nb));
+      FP4_CHECK(quant_range(b0, nb, st, nn));
+      if (nn > 0) {
+        hipLaunchKernelGGL(nv_scale_from_parts_kernel, dim3((unsigned)nn), dim3(256), 0, st,
+                           reinterpret_cast<const float*>(codes + (b0 + nb) * per / 2), per / 8,
+                           (int)grid_1d(bpt, 256), tensor_scale + b0 + nb);
+        FP4_CHECK(check_launch("tensor_scale"));
+      }
     }
     return FP4_OK;
   }

@@ -229,3 +229,39 @@ def test_static_tensor_scale_and_error_codes():
     np.testing.assert_array_equal(host(q["scales"])[0], o["scales"])
     with pytest.raises(m.Fp4Error):
         m.quantize(dev_bf16(x[:, :, :40]).contiguous(), "nvfp4")
+
+
+def test_nvfp4_large_batch_chunked_amax():
+    """A batch of 19 bf16 tensors of 1024 x 1024, large enough that the
+    library takes each chunk's tensor amax inside the previous chunk's
+    quantization launch.  Tensor scales must be the oracle's amax / 2688 of
+    each tensor (amaxes differ by orders of magnitude across the batch and sit
+    at scattered positions), codes and scales must match one-tensor calls
+    bit for bit, and sampled rows must match the oracle."""
+    print_case("nvfp4 19 x 1024 x 1024 chunked amax")
+    m = _lib()
+    B, R, C = 19, 1024, 1024
+    rng = np.random.default_rng(19)
+    x = rng.standard_normal((B, R * C), dtype=np.float32)
+    for b in range(B):
+        x[b] *= np.float32(2.0 ** (b - 9) * (1 + 0.1 * b))
+        x[b, (b * 104729 + 7) % (R * C)] = np.float32(7.5 * 2.0 ** (b - 9))
+    bits = F.bf16_bits_from_f32(x).reshape(B, R, C)
+    del x
+    t = dev_bf16(bits)
+    q = m.quantize(t, "nvfp4", "4over6")
+    torch.cuda.synchronize()
+    ts = host(q["tensor_scale"])
+    codes, scales = host(q["codes"]), host(q["scales"])
+    want_ts = [Q.nvfp4_tensor_scale(np.max(np.abs(F.bf16_to_f64(bits[b])))) for b in range(B)]
+    for b in range(B):
+        assert ts[b].view(np.uint32) == want_ts[b].view(np.uint32), f"tensor scale {b}"
+    for b in (0, 9, 10, 18):
+        one = m.quantize(t[b:b + 1], "nvfp4", "4over6")
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(codes[b], host(one["codes"])[0], err_msg=f"codes, tensor {b}")
+        np.testing.assert_array_equal(scales[b], host(one["scales"])[0], err_msg=f"scales, tensor {b}")
+        rows = slice(64 * (b % 16), 64 * (b % 16) + 64)
+        o = Q.quantize_nvfp4(F.bf16_to_f64(bits[b, rows]), "4over6", tensor_scale=want_ts[b])
+        np.testing.assert_array_equal(codes[b, rows], F.pack_nibbles(o["codes"]), err_msg=f"oracle rows {b}")
+        np.testing.assert_array_equal(scales[b, rows], o["scales"], err_msg=f"oracle scales {b}")
