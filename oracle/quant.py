@@ -24,6 +24,11 @@ Readings where the cards are silent (each is listed in the design notes):
     sign nibble bit is the sign bit of x (so -0 encodes as 0x8);
   * the block error of a plan is sum_i (|x_i| - g_i * s_M * S)^2 in exact
     arithmetic; plan M=4 is chosen iff its error is strictly smaller;
+  * the scale sweep (the "MSE sweep" the Local-Hessian card names in "What
+    is different about it", without defining it) tries every E4M3 scale from
+    the M=6 plan's to the M=4 plan's inclusive and keeps the first with the
+    smallest exact post-rounding squared error; it contains both 4/6 plans,
+    so its error never exceeds 4/6's;
   * MXFP4 plan M: e_M = min{e : M * 2^e >= amax_b}, clamped to [-127, 127]
     (the no-clip ceiling rule, as in the MXFP8 rule of the AZ card);
   * block FP8: one fp32 scale sigma = fp32(amax / 448) per 128 x 128 weight
@@ -73,28 +78,60 @@ def _plan(absx, unit):
     return mag, g, err
 
 
-def _choose(absx, unit6, unit4, plan6, plan4):
-    """Boolean per block: True iff plan M=4 has strictly smaller exact error.
+def _better(absx, unit_a, unit_b, plan_a, plan_b):
+    """Boolean per block: True iff plan b has a strictly smaller exact error
+    than plan a.
 
     The float64 errors decide unless they are within a relative 2^-40 of each
     other (their own rounding error is below 2^-48 relative); such near-ties
     are re-evaluated in exact rational arithmetic."""
-    (_, g6, e6), (_, g4, e4) = plan6, plan4
-    choose4 = e4 < e6
-    # identical plans (same scale) tie exactly and keep M=6
-    close = (np.abs(e6 - e4) <= 2.0 ** -40 * (e6 + e4)) & (unit6 != unit4)
+    (_, ga, ea), (_, gb, eb) = plan_a, plan_b
+    take = eb < ea
+    # identical plans (same scale) tie exactly and keep plan a
+    close = (np.abs(ea - eb) <= 2.0 ** -40 * (ea + eb)) & (unit_a != unit_b)
     for b in np.nonzero(close)[0]:
-        x6 = _exact_block_error(absx[b], g6[b], unit6[b])
-        x4 = _exact_block_error(absx[b], g4[b], unit4[b])
-        choose4[b] = x4 < x6
-    return choose4
+        xa = _exact_block_error(absx[b], ga[b], unit_a[b])
+        xb = _exact_block_error(absx[b], gb[b], unit_b[b])
+        take[b] = xb < xa
+    return take
+
+
+def _choose(absx, unit6, unit4, plan6, plan4):
+    """Boolean per block: True iff plan M=4 has strictly smaller exact error."""
+    return _better(absx, unit6, unit4, plan6, plan4)
+
+
+def _sweep(absx, S, s6, s4, unit6, p6):
+    """Scale sweep: every E4M3 code from the M=6 plan's to the M=4 plan's
+    (E4M3 codes of non-negative values order like the values), the first
+    with the smallest exact error wins.  Returns (codes, magnitude indices,
+    offset of the chosen code from the M=6 plan's)."""
+    width = s4.astype(np.int64) - s6.astype(np.int64)
+    best_s = s6.astype(np.int64)
+    best_unit = unit6
+    best = p6
+    choice = np.zeros(len(s6), np.int64)
+    for off in range(1, int(width.max(initial=0)) + 1):
+        live = off <= width
+        cand = np.where(live, s6.astype(np.int64) + off, s6.astype(np.int64))
+        unit = e4m3_decode(cand) * S
+        pc = _plan(absx, unit)
+        take = _better(absx, best_unit, unit, best, pc) & live
+        best_s = np.where(take, cand, best_s)
+        best_unit = np.where(take, unit, best_unit)
+        best = (np.where(take[:, None], pc[0], best[0]), np.where(take[:, None], pc[1], best[1]),
+                np.where(take, pc[2], best[2]))
+        choice = np.where(take, off, choice)
+    return best_s.astype(np.uint8), best[0], choice
 
 
 def quantize_nvfp4(x, rule: str = "4over6", tensor_scale=None):
     """NVFP4 quantization of one tensor [..., cols] (cols % 16 == 0).
 
     Returns dict: codes (uint8 nibbles, same shape as x), scales (uint8 E4M3,
-    [..., cols/16]), tensor_scale (float32), m4 (bool per block: plan M=4 chosen).
+    [..., cols/16]), tensor_scale (float32), m4 (bool per block: plan M=4
+    chosen; for the sweep, a scale other than the M=6 plan's), and for the
+    sweep `choice` (offset of the chosen E4M3 code from the M=6 plan's).
     """
     x = np.asarray(x, dtype=np.float64)
     blk = _blocks(x, NV_BLOCK)
@@ -120,6 +157,12 @@ def quantize_nvfp4(x, rule: str = "4over6", tensor_scale=None):
         unit4 = e4m3_decode(s4) * S
         p4 = _plan(absx, unit4)
         choose4 = _choose(absx, unit6, unit4, p6, p4)
+    elif rule == "sweep":
+        scales, mag, choice = _sweep(absx, S, s6, plan_scale(4.0), unit6, p6)
+        codes = (mag | (np.signbit(blk).astype(np.int64) << 3)).astype(np.uint8)
+        shp = x.shape[:-1] + (x.shape[-1] // NV_BLOCK,)
+        return {"codes": codes.reshape(x.shape), "scales": scales.reshape(shp), "tensor_scale": np.float32(S),
+                "m4": (choice > 0).reshape(shp), "choice": choice.astype(np.uint8).reshape(shp)}
     else:
         raise ValueError(rule)
     mag = np.where(choose4[:, None], p4[0], p6[0])

@@ -414,3 +414,112 @@ def test_negative_control_nibble_order_fires():
     codes = np.array([int(c) for c in g["codes_4over6"]], np.uint8)
     swapped = (codes[1::2] & 0xF) | (codes[0::2] << 4)
     assert not np.array_equal(swapped, [int(c, 16) for c in g["packed_4over6"]])
+
+
+# ------------------------------------------------------------ scale sweep
+#
+# Reading of the "plain amax/MSE sweep" that the LocalHessian-Experts card
+# names in "What is different about it" without defining it: per block, every
+# E4M3 scale from the M=6 plan's code to the M=4 plan's code (inclusive) is
+# tried and the first with the smallest exact post-rounding squared error is
+# kept.  The pins below do not call the sweep's own helpers.
+
+def _sweep_brute(absx, S: Fraction):
+    """(code, error, E2M1 indices, offset) of the sweep on one block by enumeration."""
+    amax = max(_fr(a) for a in absx)
+    if S == 0:
+        err, cs = _exact_err(absx, Fraction(0))
+        return 0, err, cs, 0
+    c6 = _nearest_e4m3(amax / (6 * S))
+    c4 = _nearest_e4m3(amax / (4 * S))
+    best = None
+    for c in range(c6, c4 + 1):
+        err, cs = _exact_err(absx, _fr(F.E4M3_GRID[c]) * S)
+        if best is None or err < best[1]:
+            best = (c, err, cs, c - c6)
+    return best
+
+
+def test_sweep_worked_example():
+    # S = 1 (static), block {6, 5 x4, 2.5 x11}.  The M=6 plan has s = 1.0 and
+    # the M=4 plan s = 1.5; the E4M3 codes between them are 1.125, 1.25, 1.375.
+    # Squared errors (grid values g*s, ties to the even E2M1 code):
+    #   s = 1.0  : 6 -> 6; 5 -> 4 (tie 4|6); 2.5 -> 2 (tie 2|3)      = 4*1 + 11/4   = 6.75
+    #   s = 1.125: 6 -> 6.75; 5 -> 4.5; 2.5 -> 2.25                   = 9/16 + 1 + 11/16 = 2.25
+    #   s = 1.25 : 6 -> 5 (4.8 -> 4); 5 -> 5 (4); 2.5 -> 2.5 (2)      = 1
+    #   s = 1.375: 6 -> 5.5; 5 -> 5.5; 2.5 -> 2.75                    = 1/4 + 1 + 11/16 = 1.9375
+    #   s = 1.5  : 6 -> 6 (4); 5 -> 4.5 (3); 2.5 -> 2.25 (1.5)        = 1 + 11/16 = 1.6875
+    # so the sweep keeps s = 1.25 (E4M3 0x3A), where 4/6 keeps 1.5 and RTN 1.0.
+    x = np.array([[6.0] + [5.0] * 4 + [2.5] * 11])
+    q = Q.quantize_nvfp4(x, "sweep", tensor_scale=np.float32(1.0))
+    assert q["scales"][0, 0] == 0x3A and q["choice"][0, 0] == 2 and q["m4"][0, 0]
+    np.testing.assert_array_equal(q["codes"][0], [6] * 5 + [4] * 11)
+    assert Q.quantize_nvfp4(x, "4over6", tensor_scale=np.float32(1.0))["scales"][0, 0] == 0x3C
+    assert Q.quantize_nvfp4(x, "rtn", tensor_scale=np.float32(1.0))["scales"][0, 0] == 0x38
+
+
+@pytest.mark.parametrize("seed,heavy,shape", [(10, False, (6, 64)), (11, True, (12, 32))])
+def test_sweep_matches_exact_brute_force(seed, heavy, shape):
+    x = _bf16_tensor(np.random.default_rng(seed), shape, heavy=heavy)
+    q = Q.quantize_nvfp4(x, "sweep")
+    q46 = Q.quantize_nvfp4(x, "4over6")
+    S = _fr(np.float32(np.float64(np.max(np.abs(x))) / 2688.0))
+    assert _fr(q["tensor_scale"]) == S
+    absx_all = np.abs(x).reshape(-1, 16)
+    signs = np.signbit(x.reshape(-1, 16))
+    codes, scales, choice = q["codes"].reshape(-1, 16), q["scales"].reshape(-1), q["choice"].reshape(-1)
+    interior = 0
+    for b in range(absx_all.shape[0]):
+        c, err, cs, off = _sweep_brute(absx_all[b], S)
+        assert scales[b] == c and choice[b] == off, f"block {b}"
+        np.testing.assert_array_equal(codes[b], np.array(cs) | (signs[b].astype(int) << 3))
+        err46, _ = _exact_err(absx_all[b], _fr(F.E4M3_GRID[q46["scales"].reshape(-1)[b]]) * S)
+        assert err <= err46
+        interior += err < err46
+    assert interior > 0   # the sweep does beat 4/6 on some blocks of this data
+
+
+def test_sweep_equals_four_over_six_without_interior_scales():
+    """Blocks whose M=6 and M=4 plans are adjacent E4M3 codes (or one code) have
+    no other candidate, so the sweep must reproduce 4/6 there."""
+    rng = np.random.default_rng(12)
+    x = _bf16_tensor(rng, (32, 64), heavy=True)
+    q = Q.quantize_nvfp4(x, "sweep")
+    q46 = Q.quantize_nvfp4(x, "4over6")
+    S = np.float64(q["tensor_scale"])
+    amax = np.max(np.abs(x).reshape(-1, 16), axis=1)
+    c6 = F.e4m3_encode(amax / (6 * S)).astype(int)
+    c4 = F.e4m3_encode(amax / (4 * S)).astype(int)
+    narrow = (c4 - c6) <= 1
+    assert narrow.any()
+    np.testing.assert_array_equal(q["scales"].reshape(-1)[narrow], q46["scales"].reshape(-1)[narrow])
+    np.testing.assert_array_equal(q["codes"].reshape(-1, 16)[narrow], q46["codes"].reshape(-1, 16)[narrow])
+
+
+def test_sweep_invariances():
+    rng = np.random.default_rng(13)
+    x = _bf16_tensor(rng, (8, 64))
+    q = Q.quantize_nvfp4(x, "sweep")
+    for j in (-5, 4):
+        qj = Q.quantize_nvfp4(np.ldexp(x, j), "sweep")
+        np.testing.assert_array_equal(qj["codes"], q["codes"])
+        np.testing.assert_array_equal(qj["scales"], q["scales"])
+    qn = Q.quantize_nvfp4(-x, "sweep")
+    np.testing.assert_array_equal(qn["codes"], q["codes"] ^ 8)
+    np.testing.assert_array_equal(qn["scales"], q["scales"])
+    perm = rng.permutation(16)
+    qp = Q.quantize_nvfp4(x.reshape(-1, 16)[:, perm].reshape(x.shape), "sweep")
+    np.testing.assert_array_equal(qp["codes"].reshape(-1, 16), q["codes"].reshape(-1, 16)[:, perm])
+    np.testing.assert_array_equal(qp["choice"], q["choice"])
+
+
+def test_negative_control_sweep_missing_endpoint_fires(monkeypatch):
+    """A sweep that stops one code short of the M=4 plan must fail the brute force."""
+    real = Q._sweep
+
+    def short(absx, S, s6, s4, unit6, p6):
+        return real(absx, S, s6, np.maximum(s4.astype(np.int64) - 1, s6).astype(np.uint8), unit6, p6)
+
+    monkeypatch.setattr(Q, "_sweep", short)
+    with pytest.raises(AssertionError):
+        test_sweep_matches_exact_brute_force(10, False, (6, 64))
