@@ -16,7 +16,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp4moe.so")
 
 FMT = {"nvfp4": 0, "mxfp4": 1, "mxfp8": 2, "fp8_block": 3, "fp8_row": 4, "none": 5}
-RULE = {"rtn": 0, "4over6": 1}
+RULE = {"rtn": 0, "4over6": 1, "sweep": 2}
 TS_DYNAMIC, TS_STATIC = 0, 1
 DT_BF16, DT_F32 = 0, 1
 STATUS = {0: "FP4_OK", -1: "FP4_ERR_INVALID_ARG", -2: "FP4_ERR_SHAPE",

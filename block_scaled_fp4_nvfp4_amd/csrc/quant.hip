@@ -259,7 +259,7 @@ __device__ __forceinline__ void exact_plan(const float (&v)[BS], double unit, ui
 // exact quotient x/u (the rounding is monotone), so where the two agree the
 // code is exact; where they differ one exact comparison decides.
 // MXFP4 codes: x / 2^e is exact, so the hardware convert is exact.
-template <int BS, bool MX, bool FOUR_SIX, typename T>
+template <int BS, bool MX, bool FOUR_SIX, typename T, bool SWEEP = false>
 __global__ void __launch_bounds__(256) quant_fp4_kernel(
     const T* __restrict__ x, int64_t blocks_per_tensor, uint8_t* __restrict__ codes,
     uint8_t* __restrict__ scales, const float* __restrict__ tensor_scale,
@@ -428,13 +428,46 @@ __global__ void __launch_bounds__(256) quant_fp4_kernel(
   uint32_t packed[NW];
 #pragma unroll
   for (int w = 0; w < NW; ++w) packed[w] = (FOUR_SIX && use4) ? p4[w] : p6[w];
+  uint32_t code = (FOUR_SIX && use4) ? code4 : code6;
+  uint32_t flag = use4 ? 1u : 0u;
+  if constexpr (SWEEP) {
+    // NVFP4 scale sweep: every E4M3 code strictly between the two plans'
+    // against the better of those two, by the same exact identity; ties keep
+    // the earlier (smaller) code, so the first minimum over the codes from
+    // code6 up wins
+    static_assert(!MX && FOUR_SIX, "the sweep extends the NVFP4 4/6 kernel");
+    double sb = use4 ? s4 : s6;
+    float g2b = use4 ? g2_4 : g2_6;
+    Acc gxb = use4 ? gx_4 : gx_6;
+    for (uint32_t c = code6 + 1; c < code4; ++c) {
+      const double sc = (double)e4m3_to_f32(c);
+      uint32_t pc[NW];
+      float g2c;
+      Acc gxc;
+      plan(sc, 0, pc, g2c, gxc);
+      const double A = sb * sb * (double)g2b - sc * sc * (double)g2c;
+      const double B = sb * (double)gxb - sc * (double)gxc;
+      // the best so far is code6 or an interior code (smaller than c) unless
+      // it is code4, which c < code4 may tie: then c, the smaller code, wins
+      const bool take = (S * A - 2.0 * B) > 0.0 || ((S * A - 2.0 * B) == 0.0 && code == code4 && use4);
+      if (take) {
+#pragma unroll
+        for (int w = 0; w < NW; ++w) packed[w] = pc[w];
+        sb = sc;
+        g2b = g2c;
+        gxb = gxc;
+        code = c;
+      }
+    }
+    flag = code - code6;
+  }
   if (BS == 16) {
     reinterpret_cast<uint2*>(codes)[g] = make_uint2(packed[0], packed[1 % NW]);
   } else {
     reinterpret_cast<uint4*>(codes)[g] = make_uint4(packed[0], packed[1 % NW], packed[2 % NW], packed[3 % NW]);
   }
-  scales[g] = (uint8_t)((FOUR_SIX && use4) ? code4 : code6);
-  if (m4_flags) m4_flags[g] = use4 ? 1 : 0;
+  scales[g] = (uint8_t)code;
+  if (m4_flags) m4_flags[g] = (uint8_t)flag;
   if constexpr (FUSE) {
     if (fuse) {
       u16x2_t m = {0, 0};
@@ -773,11 +806,13 @@ int quantize_typed(int fmt, int rule, int ts_mode, const T* x, int64_t batch, in
         const float* tb = tensor_scale ? tensor_scale + c0 : nullptr;
         uint8_t* mb = m4 ? m4 + c0 * bpt : nullptr;
         dim3 grid(gx, gy);
-        if (!mx && rule == FP4_RULE_4OVER6)
+        if (!mx && rule == FP4_RULE_SWEEP)
+          hipLaunchKernelGGL((quant_fp4_kernel<16, false, true, T, true>), grid, dim3(256), 0, sx, xb, bpt, cb, sb, tb, mb, nx, np_, per / 8, (int)nn);
+        else if (!mx && rule == FP4_RULE_4OVER6)
           hipLaunchKernelGGL((quant_fp4_kernel<16, false, true, T>), grid, dim3(256), 0, sx, xb, bpt, cb, sb, tb, mb, nx, np_, per / 8, (int)nn);
         else if (!mx)
           hipLaunchKernelGGL((quant_fp4_kernel<16, false, false, T>), grid, dim3(256), 0, sx, xb, bpt, cb, sb, tb, mb, nx, np_, per / 8, (int)nn);
-        else if (rule == FP4_RULE_4OVER6)
+        else if (rule == FP4_RULE_4OVER6 || rule == FP4_RULE_SWEEP)  // MX: the sweep's candidates are the two plans
           hipLaunchKernelGGL((quant_fp4_kernel<32, true, true, T>), grid, dim3(256), 0, sx, xb, bpt, cb, sb, tb, mb, nx, np_, per / 8, (int)nn);
         else
           hipLaunchKernelGGL((quant_fp4_kernel<32, true, false, T>), grid, dim3(256), 0, sx, xb, bpt, cb, sb, tb, mb, nx, np_, per / 8, (int)nn);
@@ -875,7 +910,7 @@ int fp4_quantize(int fmt, int rule, int ts_mode, const void* x, int x_dtype, int
                  uint8_t* m4_flags, void* stream) {
   int bs = block_of(fmt);
   if (bs == 0) return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: unknown format %d", fmt);
-  if (rule != FP4_RULE_RTN && rule != FP4_RULE_4OVER6)
+  if (rule != FP4_RULE_RTN && rule != FP4_RULE_4OVER6 && rule != FP4_RULE_SWEEP)
     return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: unknown rule %d", rule);
   if (ts_mode != FP4_TS_DYNAMIC && ts_mode != FP4_TS_STATIC)
     return fail(FP4_ERR_INVALID_ARG, "fp4_quantize: unknown tensor-scale mode %d", ts_mode);

@@ -66,8 +66,14 @@ typedef enum {
 
 typedef enum {
   FP4_RULE_RTN = 0,    /* block max mapped to 6 (the amax/6 plan)                       */
-  FP4_RULE_4OVER6 = 1  /* per block, the amax/6 or the block-max-to-4 plan, whichever has
+  FP4_RULE_4OVER6 = 1, /* per block, the amax/6 or the block-max-to-4 plan, whichever has
                           the strictly smaller exact squared error (ties keep amax/6)      */
+  FP4_RULE_SWEEP = 2   /* scale sweep (the "MSE sweep" the LocalHessian-Experts card names
+                          in "What is different about it"; reading: NVFP4 tries every E4M3
+                          scale from the amax/6 plan's code to the block-max-to-4 plan's
+                          code, keeping the first with the smallest exact squared error;
+                          for MXFP4 those plans are the only power-of-two candidates, so it
+                          equals FP4_RULE_4OVER6)                                          */
 } fp4_rule;
 
 typedef enum { FP4_DT_BF16 = 0, FP4_DT_F32 = 1 } fp4_dtype;
@@ -81,7 +87,8 @@ typedef enum {
  * fp4_quantize - quantize `batch` independent tensors x[batch][rows][cols].
  *
  *  fmt      NVFP4, MXFP4 (rule applies), MXFP8, FP8_BLOCK or FP8_ROW.
- *  rule     FP4_RULE_RTN or FP4_RULE_4OVER6 (NVFP4 and MXFP4 only; ignored otherwise).
+ *  rule     FP4_RULE_RTN, FP4_RULE_4OVER6 or FP4_RULE_SWEEP (NVFP4 and MXFP4 only;
+ *           ignored otherwise).
  *  x        bf16 or f32 values, `x_dtype`; must be finite.
  *  codes    out: packed E2M1 [batch, rows, cols/2] (NVFP4, MXFP4) or E4M3 bytes
  *           [batch, rows, cols] (MXFP8, FP8_*).
@@ -92,7 +99,8 @@ typedef enum {
  *           (FP4_TS_STATIC).  One tensor per batch item, so a fused gate_up
  *           [2I, H] quantized as one item shares its scale between gate and up.
  *  m4_flags optional out (may be NULL), one byte per block: 1 where the
- *           block-max-to-4 plan was chosen.
+ *           block-max-to-4 plan was chosen; under FP4_RULE_SWEEP with NVFP4, the
+ *           chosen scale code minus the amax/6 plan's code (0: the amax/6 plan).
  * Shape errors: cols % 16 (NVFP4), % 32 (MX), % 128 (FP8_*), rows % 128 (FP8_BLOCK).
  */
 int fp4_quantize(int fmt, int rule, int ts_mode, const void* x, int x_dtype,

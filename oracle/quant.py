@@ -218,6 +218,23 @@ def quantize_mxfp4(x, rule: str = "4over6"):
         unit4 = np.ldexp(1.0, e4)
         p4 = _plan(absx, unit4)
         choose4 = _choose(absx, unit6, unit4, p6, p4)
+    elif rule == "sweep":
+        # every power-of-two scale from the M=6 plan's to the M=4 plan's, the
+        # first with the smallest exact error (4/6 < 2, so at most two exist)
+        e4 = _mx_exponent(amax_b, 4.0)
+        best_e, best_unit, best = e6.copy(), unit6, p6
+        for off in range(1, int(np.max(e4 - e6, initial=0)) + 1):
+            live = off <= e4 - e6
+            cand = np.where(live, e6 + off, e6)
+            unit = np.ldexp(1.0, cand)
+            pc = _plan(absx, unit)
+            take = _better(absx, best_unit, unit, best, pc) & live
+            best_e = np.where(take, cand, best_e)
+            best_unit = np.where(take, unit, best_unit)
+            best = (np.where(take[:, None], pc[0], best[0]), np.where(take[:, None], pc[1], best[1]),
+                    np.where(take, pc[2], best[2]))
+        choose4 = best_e != e6
+        e4, p4 = best_e, best
     else:
         raise ValueError(rule)
     mag = np.where(choose4[:, None], p4[0], p6[0])

@@ -1,6 +1,7 @@
 """GPU quantizer / dequantizer parity through the C ABI: codes and scales are
-bit-exact against the oracle; dequantized values equal the oracle's exact
-values rounded once to f32 (bf16: then rounded to bf16)."""
+bit-exact against the oracle (all three scale rules: RTN, 4/6 and the
+scale sweep); dequantized values equal the oracle's exact values rounded once
+to f32 (bf16: then rounded to bf16)."""
 import numpy as np
 import pytest
 
@@ -51,11 +52,13 @@ def _compare(fmt, rule, xt, x64_per_tensor):
             assert host(q["tensor_scale"])[b].view(np.uint32) == np.float32(o["tensor_scale"]).view(np.uint32)
         if q["m4"] is not None:
             np.testing.assert_array_equal(host(q["m4"])[b].astype(bool), o["m4"])
+            if "choice" in o:  # NVFP4 sweep: offset of the chosen scale code
+                np.testing.assert_array_equal(host(q["m4"])[b], o["choice"], err_msg=f"{fmt}/{rule} choice, tensor {b}")
     return q
 
 
-@pytest.mark.parametrize("fmt,rule", [("nvfp4", "4over6"), ("nvfp4", "rtn"),
-                                      ("mxfp4", "4over6"), ("mxfp4", "rtn")])
+@pytest.mark.parametrize("fmt,rule", [("nvfp4", "4over6"), ("nvfp4", "rtn"), ("nvfp4", "sweep"),
+                                      ("mxfp4", "4over6"), ("mxfp4", "rtn"), ("mxfp4", "sweep")])
 def test_fp4_weights_bit_exact_tiny_layer(fmt, rule):
     print_case(f"tiny layer weights {fmt}/{rule}")
     cfg = synth.CONFIGS["tiny"]
@@ -84,7 +87,7 @@ def test_fp4_adversarial_blocks_bit_exact():
     bits = F.bf16_bits_from_f32(x)
     x64 = F.bf16_to_f64(bits)
     for fmt in ("nvfp4", "mxfp4"):
-        for rule in ("4over6", "rtn"):
+        for rule in ("4over6", "rtn", "sweep"):
             _compare(fmt, rule, dev_bf16(bits)[None], [x64])
 
 
@@ -112,11 +115,12 @@ def test_fp4_structured_near_ties_bit_exact():
     print_case("structured near-ties of NVFP4 thresholds")
     bits = _structured_near_tie_tensors()
     x64 = [F.bf16_to_f64(bits[b]) for b in range(bits.shape[0])]
-    for rule in ("4over6", "rtn"):
+    for rule in ("4over6", "rtn", "sweep"):
         _compare("nvfp4", rule, dev_bf16(bits), x64)
     # the f32 path meets the same thresholds
     xf = F.bf16_to_f64(bits).astype(np.float32)
-    _compare("nvfp4", "4over6", dev(xf), [xf[b].astype(np.float64) for b in range(xf.shape[0])])
+    for rule in ("4over6", "sweep"):
+        _compare("nvfp4", rule, dev(xf), [xf[b].astype(np.float64) for b in range(xf.shape[0])])
 
 
 def test_fp4_f32_inputs_bit_exact():
@@ -125,7 +129,7 @@ def test_fp4_f32_inputs_bit_exact():
     x = (rng.standard_t(3, (3, 64, 256)) * 0.03).astype(np.float32)
     x[0, 0, :16] = np.float32(1e-40)  # subnormal block
     for fmt in ("nvfp4", "mxfp4"):
-        for rule in ("4over6", "rtn"):
+        for rule in ("4over6", "rtn", "sweep"):
             _compare(fmt, rule, dev(x), [x[b].astype(np.float64) for b in range(3)])
 
 
@@ -231,14 +235,15 @@ def test_static_tensor_scale_and_error_codes():
         m.quantize(dev_bf16(x[:, :, :40]).contiguous(), "nvfp4")
 
 
-def test_nvfp4_large_batch_chunked_amax():
+@pytest.mark.parametrize("rule", ["4over6", "sweep"])
+def test_nvfp4_large_batch_chunked_amax(rule):
     """A batch of 19 bf16 tensors of 1024 x 1024, large enough that the
     library takes each chunk's tensor amax inside the previous chunk's
     quantization launch.  Tensor scales must be the oracle's amax / 2688 of
     each tensor (amaxes differ by orders of magnitude across the batch and sit
     at scattered positions), codes and scales must match one-tensor calls
     bit for bit, and sampled rows must match the oracle."""
-    print_case("nvfp4 19 x 1024 x 1024 chunked amax")
+    print_case(f"nvfp4/{rule} 19 x 1024 x 1024 chunked amax")
     m = _lib()
     B, R, C = 19, 1024, 1024
     rng = np.random.default_rng(19)
@@ -249,7 +254,7 @@ def test_nvfp4_large_batch_chunked_amax():
     bits = F.bf16_bits_from_f32(x).reshape(B, R, C)
     del x
     t = dev_bf16(bits)
-    q = m.quantize(t, "nvfp4", "4over6")
+    q = m.quantize(t, "nvfp4", rule)
     torch.cuda.synchronize()
     ts = host(q["tensor_scale"])
     codes, scales = host(q["codes"]), host(q["scales"])
@@ -257,11 +262,11 @@ def test_nvfp4_large_batch_chunked_amax():
     for b in range(B):
         assert ts[b].view(np.uint32) == want_ts[b].view(np.uint32), f"tensor scale {b}"
     for b in (0, 9, 10, 18):
-        one = m.quantize(t[b:b + 1], "nvfp4", "4over6")
+        one = m.quantize(t[b:b + 1], "nvfp4", rule)
         torch.cuda.synchronize()
         np.testing.assert_array_equal(codes[b], host(one["codes"])[0], err_msg=f"codes, tensor {b}")
         np.testing.assert_array_equal(scales[b], host(one["scales"])[0], err_msg=f"scales, tensor {b}")
         rows = slice(64 * (b % 16), 64 * (b % 16) + 64)
-        o = Q.quantize_nvfp4(F.bf16_to_f64(bits[b, rows]), "4over6", tensor_scale=want_ts[b])
+        o = Q.quantize_nvfp4(F.bf16_to_f64(bits[b, rows]), rule, tensor_scale=want_ts[b])
         np.testing.assert_array_equal(codes[b, rows], F.pack_nibbles(o["codes"]), err_msg=f"oracle rows {b}")
         np.testing.assert_array_equal(scales[b, rows], o["scales"], err_msg=f"oracle scales {b}")

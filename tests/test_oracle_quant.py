@@ -523,3 +523,14 @@ def test_negative_control_sweep_missing_endpoint_fires(monkeypatch):
     monkeypatch.setattr(Q, "_sweep", short)
     with pytest.raises(AssertionError):
         test_sweep_matches_exact_brute_force(10, False, (6, 64))
+
+
+def test_mx_sweep_equals_four_over_six():
+    """MXFP4 scales are powers of two and 6/4 < 2, so the exponents from the
+    M=6 plan's to the M=4 plan's are at most those two: the sweep is 4/6."""
+    rng = np.random.default_rng(14)
+    for heavy in (False, True):
+        x = _bf16_tensor(rng, (16, 128), heavy=heavy)
+        a, b = Q.quantize_mxfp4(x, "sweep"), Q.quantize_mxfp4(x, "4over6")
+        for k in ("codes", "scales", "m4"):
+            np.testing.assert_array_equal(a[k], b[k])
