@@ -337,13 +337,15 @@ def bench_copy(args, torch):
             "bytes_read": n * 4, "bytes_written": n * 4, "ms_per_launch": ms, "steps": args.steps}
 
 
-def bench_stream_quant(args, torch, pkg):
-    """48 layers x 512 experts x (gate_up 1280x2560, down 2560x640) NVFP4 4/6
-    quantization, one layer at a time, from bf16 Student-t (nu=4) source with
-    1% outlier rows x8 generated on the device for each layer."""
+def bench_stream_quant(args, torch, pkg, rule="4over6"):
+    """48 layers x 512 experts x (gate_up 1280x2560, down 2560x640) NVFP4
+    quantization (4/6, or the scale sweep), one layer at a time, from bf16
+    Student-t (nu=4) source with 1% outlier rows x8 generated on the device
+    for each layer.  The sweep workload also reports, on its first and last
+    layer, the 4/6 error of the same tensors."""
     import numpy as np
     E, H, I = 512, 2560, 640
-    layers = args.stream_layers
+    layers = args.stream_layers if rule == "4over6" else args.sweep_layers
     gen = torch.Generator(device="cuda")
     tdist = torch.distributions.StudentT(torch.tensor(4.0, device="cuda"))
 
@@ -366,8 +368,8 @@ def bench_stream_quant(args, torch, pkg):
         torch.cuda.synchronize()
         want = layer in (0, layers - 1)
         start.record()
-        q13 = pkg.quantize(w13, "nvfp4", "4over6", want_m4=want)
-        q2 = pkg.quantize(w2, "nvfp4", "4over6", want_m4=want)
+        q13 = pkg.quantize(w13, "nvfp4", rule, want_m4=want)
+        q2 = pkg.quantize(w2, "nvfp4", rule, want_m4=want)
         stop.record()
         torch.cuda.synchronize()
         total_ms += start.elapsed_time(stop)
@@ -380,41 +382,54 @@ def bench_stream_quant(args, torch, pkg):
                 src = w.float()
                 parts = [(n, sl) for n, sl in zip(names, (slice(0, I), slice(I, 2 * I)))] if len(names) == 2 \
                     else [("down", slice(0, H))]
+                x46 = None
+                if rule != "4over6":  # the same tensors under 4/6, for comparison (untimed)
+                    x46 = pkg.dequantize(pkg.quantize(w, "nvfp4", "4over6"), "nvfp4", w.shape, torch.float32)
                 for n, sl in parts:
                     d = (xh[:, sl] - src[:, sl]).pow(2).sum(dim=(1, 2))
                     nrm = src[:, sl].pow(2).sum(dim=(1, 2))
                     rel = (d / nrm).sqrt()
-                    stats.append((n, float(rel.mean()), float(rel.max()), float(q["m4"][:, sl].float().mean()),
-                                  float(d.sum()), float(nrm.sum())))
-                del xh, src
+                    rel46 = None
+                    if x46 is not None:
+                        rel46 = float(((x46[:, sl] - src[:, sl]).pow(2).sum(dim=(1, 2)) / nrm).sqrt().mean())
+                    stats.append((n, float(rel.mean()), float(rel.max()),
+                                  float((q["m4"][:, sl] > 0).float().mean()), float(d.sum()), float(nrm.sum()),
+                                  rel46))
+                del xh, src, x46
         del w13, w2, q13, q2
     ms_layer = total_ms / layers
     bytes_layer = (rd + wr) / layers
     gbs = bytes_layer / (ms_layer * 1e-3) / 1e9
-    out = {"workload": f"streaming NVFP4 4/6 quantization: {layers} layers x {E} experts x "
+    rule_name = {"4over6": "4/6", "sweep": "scale-sweep"}[rule]
+    out = {"workload": f"streaming NVFP4 {rule_name} quantization: {layers} layers x {E} experts x "
                        f"(gate_up {2 * I}x{H}, down {H}x{I}), bf16 Student-t(4) source with 1% outlier rows x8",
            "value": gbs, "unit": "GB/s", "ms_per_layer": ms_layer, "layers": layers,
            "values_per_layer": E * 3 * H * I,
            "roofline": {"bound": "hbm", "kernel": "quant_fp4_kernel (fused with the next chunk's amax) + tensor_amax_kernel (first chunk)",
                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                         "traffic": (lambda t: t["bytes_per_launch"] if t else None)(
-                            measured_traffic("quant_fp4_kernel", "stream_quant")),
+                            measured_traffic("quant_fp4_kernel", "stream_quant" if rule == "4over6" else "sweep_quant")),
                         "bytes_per_layer": bytes_layer,
                         "unit_of_work": "2 B read + 0.5625 B written per value (+4 B per tensor)"},
-           "quality": {"per_tensor_rel_err": {n: {"mean": m, "max": mx} for n, m, mx, _, _, _ in stats},
-                       "m4_fraction": float(np.mean([f for _, _, _, f, _, _ in stats]))}}
+           "quality": {"per_tensor_rel_err": {n: {"mean": m, "max": mx} for n, m, mx, *_ in stats},
+                       "m4_fraction": float(np.mean([st[3] for st in stats]))}}
+    if rule != "4over6":
+        out["quality"]["per_tensor_rel_err_4over6_same_data"] = {st[0]: {"mean": st[6]} for st in stats}
+        out["quality"]["note"] = ("m4_fraction: blocks whose scale is not the amax/6 plan's; "
+                                  "first and last layer")
     if not args.no_cpu_baseline:
-        log("timing the CPU oracle on streaming quantization")
+        log(f"timing the CPU oracle on streaming quantization ({rule})")
         import synth
         from oracle import quant
         from oracle.formats import bf16_to_f64
         t0 = time.perf_counter()
         n_vals = 0
         e = 0
-        while time.perf_counter() - t0 < args.cpu_budget and e < 64:
+        budget = args.cpu_budget if rule == "4over6" else args.cpu_budget / 2
+        while time.perf_counter() - t0 < budget and e < 64:
             w13, w2 = synth.streaming_expert(0, e)
             for w in (w13, w2):
-                quant.quantize_nvfp4(bf16_to_f64(w), "4over6")
+                quant.quantize_nvfp4(bf16_to_f64(w), rule)
                 n_vals += w.size
             e += 1
         el = time.perf_counter() - t0
@@ -432,12 +447,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
                     choices=["all", "decode", "prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant",
-                             "copy"],
+                             "sweep_quant", "copy"],
                     help="'all': the decode headline plus every other workload under 'workloads'; "
                          "'copy': a plain 1 GiB device copy that calibrates the HBM byte counters")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-copies", type=int, default=2)
     ap.add_argument("--stream-layers", type=int, default=48)
+    ap.add_argument("--sweep-layers", type=int, default=16,
+                    help="layers of the streaming workload under the scale-sweep rule")
     ap.add_argument("--copies", type=int, default=8,
                     help="resident copies of the quantized layer rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -463,14 +480,20 @@ def main():
         dargs.workload = "decode"
         out = bench_decode(dargs, torch, pkg)
         torch.cuda.empty_cache()
-        others = ["prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant"] if args.workload == "all" else []
+        others = (["prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant", "sweep_quant"]
+                  if args.workload == "all" else [])
     else:
         out = None
         others = [args.workload]
     extra = {}
     for name in others:
         log(f"workload {name}")
-        extra[name] = bench_stream_quant(args, torch, pkg) if name == "stream_quant" else bench_prefill(name, args, torch, pkg)
+        if name == "stream_quant":
+            extra[name] = bench_stream_quant(args, torch, pkg)
+        elif name == "sweep_quant":
+            extra[name] = bench_stream_quant(args, torch, pkg, rule="sweep")
+        else:
+            extra[name] = bench_prefill(name, args, torch, pkg)
         torch.cuda.empty_cache()
     if out is None:
         name = others[0]
