@@ -24,7 +24,7 @@ STATUS = {0: "FP4_OK", -1: "FP4_ERR_INVALID_ARG", -2: "FP4_ERR_SHAPE",
 
 EXPORTED = ["fp4_quantize", "fp4_dequantize", "moe_fp4_workspace_layout",
             "moe_fp4_workspace_size", "moe_fp4_forward", "moe_fp4_forward_profiled",
-            "fp4_status_string", "fp4_last_error"]
+            "moe_fp4_route", "fp4_status_string", "fp4_last_error"]
 STAGES = ["permute", "x_quant", "gate_up", "h_quant", "down", "shared", "combine"]
 
 
@@ -80,6 +80,8 @@ def lib():
         L.moe_fp4_forward_profiled.argtypes = [ctypes.POINTER(LayerStruct), vp, i64, vp, vp, vp, vp, sz, vp,
                                                ctypes.POINTER(vp), i32]
         L.moe_fp4_forward_profiled.restype = i32
+        L.moe_fp4_route.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
+        L.moe_fp4_route.restype = i32
         L.fp4_status_string.argtypes = [i32]
         L.fp4_status_string.restype = ctypes.c_char_p
         L.fp4_last_error.argtypes = []
@@ -151,6 +153,20 @@ def quantize(x: torch.Tensor, fmt: str, rule: str = "4over6",
     _check(lib().fp4_quantize(f, RULE[rule], ts_mode, _ptr(x), _dtype_code(x), b, r, c,
                               _ptr(codes), _ptr(scales), _ptr(ts), _ptr(m4), _stream()))
     return {"codes": codes, "scales": scales, "tensor_scale": ts, "m4": m4}
+
+
+def route(logits: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None):
+    """moe_fp4_route.  logits: contiguous f32 device tensor [T, E]; bias: f32
+    [E] or None.  Returns (topk_ids int32 [T, k], topk_weights f32 [T, k])."""
+    assert logits.is_cuda and logits.is_contiguous() and logits.dtype == torch.float32 and logits.dim() == 2
+    T, E = (int(v) for v in logits.shape)
+    if bias is not None:
+        bias = bias.to(device=logits.device, dtype=torch.float32).contiguous()
+        assert bias.numel() == E
+    ids = torch.empty(T, k, dtype=torch.int32, device=logits.device)
+    w = torch.empty(T, k, dtype=torch.float32, device=logits.device)
+    _check(lib().moe_fp4_route(_ptr(logits), _ptr(bias), T, E, k, _ptr(ids), _ptr(w), _stream()))
+    return ids, w
 
 
 def dequantize(q: dict, fmt: str, shape, out_dtype=torch.float32) -> torch.Tensor:

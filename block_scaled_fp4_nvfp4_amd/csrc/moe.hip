@@ -660,6 +660,58 @@ __global__ void __launch_bounds__(256) gemv_down_kernel(
   for (int t0 = kGdTokens; t0 < n; t0 += kGdTokens) pass(t0);
 }
 
+// ------------------------------------------------------------------ routing
+
+// Top-k routing of one token per wave: l'_e = fp32(logit_e + bias_e); the k
+// largest l' in order (equal values: lower expert id first); weights = the
+// softmax over the k selected l' (the renormalized top-k softmax), in fp64,
+// rounded once to f32.  Lane i holds experts i, i + 64, ... (up to PL each).
+template <int PL>
+__global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict__ logits,
+                                                         const float* __restrict__ bias, int64_t T, int E,
+                                                         int k, int32_t* __restrict__ ids,
+                                                         float* __restrict__ weights) {
+  const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (t >= T) return;
+  float v[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? logits[t * E + e] + (bias ? bias[e] : 0.0f) : -__builtin_huge_valf();
+  }
+  float sel = 0.0f;   // lane j < k keeps the j-th selected value
+  float top = 0.0f;   // the largest selected value
+  for (int j = 0; j < k; ++j) {
+    // this lane's best: largest value, lowest expert id among equals
+    float bv = v[0];
+    int be = lane;
+#pragma unroll
+    for (int i = 1; i < PL; ++i)
+      if (v[i] > bv) { bv = v[i]; be = lane + 64 * i; }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const float ov = __shfl_xor(bv, off);
+      const int oe = __shfl_xor(be, off);
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    }
+    if (j == 0) top = bv;
+    if (lane == j) sel = bv;
+    if ((be & 63) == lane) {
+#pragma unroll
+      for (int i = 0; i < PL; ++i)
+        if (lane + 64 * i == be) v[i] = -__builtin_huge_valf();
+    }
+    if (lane == 0) ids[t * k + j] = be;
+  }
+  const double z = lane < k ? exp((double)sel - (double)top) : 0.0;
+  double sum = z;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  sum = __shfl(sum, 0);  // one summation order for every weight of the token
+  if (lane < k) weights[t * k + lane] = (float)(z / sum);
+}
+
 // ------------------------------------------------------------------ combine
 
 constexpr int kMaxTopK = 32;
@@ -920,6 +972,34 @@ int moe_fp4_forward(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const 
                     const float* topk_weights, float* y, void* workspace, size_t workspace_bytes,
                     void* stream) {
   return forward_impl(L, x, T, topk_ids, topk_weights, y, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_fp4_route(const float* logits, const float* bias, int64_t tokens, int num_experts, int top_k,
+                  int32_t* topk_ids, float* topk_weights, void* stream) {
+  if (tokens < 0) return fail(FP4_ERR_SHAPE, "negative token count");
+  if (num_experts < 1 || top_k < 1 || top_k > num_experts || top_k > kMaxTopK)
+    return fail(FP4_ERR_INVALID_ARG, "route: need 1 <= top_k <= min(num_experts, %d), got k=%d, E=%d", kMaxTopK,
+                top_k, num_experts);
+  if (num_experts > 1024) return fail(FP4_ERR_UNSUPPORTED, "route: more than 1024 experts");
+  if (tokens == 0) return FP4_OK;
+  if (!logits || !topk_ids || !topk_weights) return fail(FP4_ERR_INVALID_ARG, "route: null pointer");
+  if ((tokens + 3) / 4 > INT32_MAX) return fail(FP4_ERR_UNSUPPORTED, "route: too many tokens");
+  hipStream_t st = as_stream(stream);
+  const dim3 grid((unsigned)((tokens + 3) / 4));
+  const int pl = (num_experts + 63) / 64;
+  if (pl <= 2)
+    hipLaunchKernelGGL(route_topk_kernel<2>, grid, dim3(256), 0, st, logits, bias, tokens, num_experts, top_k,
+                       topk_ids, topk_weights);
+  else if (pl <= 4)
+    hipLaunchKernelGGL(route_topk_kernel<4>, grid, dim3(256), 0, st, logits, bias, tokens, num_experts, top_k,
+                       topk_ids, topk_weights);
+  else if (pl <= 8)
+    hipLaunchKernelGGL(route_topk_kernel<8>, grid, dim3(256), 0, st, logits, bias, tokens, num_experts, top_k,
+                       topk_ids, topk_weights);
+  else
+    hipLaunchKernelGGL(route_topk_kernel<16>, grid, dim3(256), 0, st, logits, bias, tokens, num_experts, top_k,
+                       topk_ids, topk_weights);
+  return check_launch("route_topk");
 }
 
 int moe_fp4_forward_profiled(const moe_fp4_layer* L, const uint16_t* x, int64_t T,

@@ -201,6 +201,24 @@ int moe_fp4_forward(const moe_fp4_layer* layer, const uint16_t* x, int64_t token
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * moe_fp4_route - top-k routing of `tokens` tokens over E experts, on the GPU:
+ * the caller-side step in front of moe_fp4_forward.  The routing width k is a
+ * runtime value (FP4-Local-AZ card, "What is different from NVIDIA's
+ * checkpoint": 10 or 5 routed experts per token, read from the configuration).
+ *  logits       f32 [tokens, E], router logits (finite).
+ *  bias         f32 [E] per-expert bias added to the logits, or NULL.
+ *  topk_ids     out int32 [tokens, k]: the experts of the k largest
+ *               l' = fp32(logit + bias), largest first; equal values keep the
+ *               lower expert id first.
+ *  topk_weights out f32 [tokens, k]: softmax over the k selected l'
+ *               (renormalized top-k), computed in fp64 and rounded to f32.
+ * Errors: k < 1, k > E or k > 32 -> FP4_ERR_INVALID_ARG; E > 1024 ->
+ * FP4_ERR_UNSUPPORTED; tokens == 0 is a no-op.  Stream-ordered, asynchronous.
+ */
+int moe_fp4_route(const float* logits, const float* bias, int64_t tokens, int num_experts,
+                  int top_k, int32_t* topk_ids, float* topk_weights, void* stream);
+
+/*
  * moe_fp4_forward_profiled - moe_fp4_forward that also records HIP events
  * (hipEvent_t, created by the caller) on `stream` at the stage boundaries, for
  * per-kernel timing: events[0] before the first launch, then after the

@@ -26,6 +26,8 @@ whole x [T, H] and over the whole h [T*k, I]; y is float32-comparable float64.
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 from . import quant
@@ -47,6 +49,34 @@ def permute(topk_ids, num_experts: int):
     row_of_pair = np.empty_like(pair_of_row)
     row_of_pair[pair_of_row] = np.arange(flat.size)
     return offsets, pair_of_row, row_of_pair
+
+
+def route(logits, bias, k: int):
+    """Top-k routing of T tokens over E experts (the caller's step in front of
+    the layer; routing width k a runtime value, FP4-Local-AZ card, "What is
+    different from NVIDIA's checkpoint").
+
+    Reading: l'_e = fp32(logit_e + bias_e); the experts in order of
+    decreasing l', equal values by increasing id; the first k; weights the
+    softmax over those k l' (the renormalized top-k softmax) in float64 with
+    an exactly rounded sum, rounded to float32.  Returns (ids int32 [T, k],
+    weights float32 [T, k])."""
+    lp = np.asarray(logits, dtype=np.float32)
+    T, E = lp.shape
+    if not 1 <= k <= E:
+        raise ValueError("k outside [1, E]")
+    if bias is not None:
+        lp = (lp + np.asarray(bias, dtype=np.float32)[None, :]).astype(np.float32)
+    eid = np.broadcast_to(np.arange(E), lp.shape)
+    order = np.lexsort((eid, -lp), axis=-1)[:, :k]  # primary key -l', then the id
+    ids = order.astype(np.int32)
+    w = np.empty((T, k), np.float32)
+    for t in range(T):
+        sel = [float(lp[t, e]) for e in order[t]]
+        z = [math.exp(v - sel[0]) for v in sel]
+        tot = math.fsum(z)
+        w[t] = [np.float32(v / tot) for v in z]
+    return ids, w
 
 
 def silu(v):

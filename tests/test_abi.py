@@ -64,6 +64,13 @@ def test_host_validation_errors(L):
     # FP8 block weights need rows % 128
     assert L.fp4_quantize(3, 0, 0, fake, 0, 1, 64, 128, fake, fake, None, None, None) == -2
     assert L.fp4_dequantize(0, fake, fake, None, 1, 4, 32, fake, 1, None) == -1
+    # routing: k outside [1, min(E, 32)], too many experts, empty batch, null outputs
+    assert L.moe_fp4_route(fake, None, 4, 8, 0, fake, fake, None) == -1
+    assert L.moe_fp4_route(fake, None, 4, 8, 9, fake, fake, None) == -1
+    assert L.moe_fp4_route(fake, None, 4, 64, 33, fake, fake, None) == -1
+    assert L.moe_fp4_route(fake, None, 4, 2048, 8, fake, fake, None) == -3
+    assert L.moe_fp4_route(None, None, 0, 8, 2, None, None, None) == 0
+    assert L.moe_fp4_route(fake, None, 4, 8, 2, None, fake, None) == -1
 
 
 def _layer(**kw):

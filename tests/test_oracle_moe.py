@@ -3,6 +3,8 @@ dense SwiGLU, invariances (expert relabeling, routing-weight scaling, zero
 padding: "silu(0) * 0 = 0", FP4-Local AZ card, section "The shared expert"),
 and the quantization-error sanity band (QAD5500-Hybrid card, "Verification":
 a quantized copy differs by a few percent, an unrelated one by ~100 %)."""
+import math
+
 import numpy as np
 import pytest
 
@@ -155,3 +157,52 @@ def test_shared_expert_gate_and_band():
     g0 = moe.shared_forward(sh0, x)
     np.testing.assert_array_equal(2 * g0, moe.shared_forward(dict(sh0), x) * 2)
     np.testing.assert_allclose(g0 / out, (0.5 / gate)[:, None] * np.ones_like(out), rtol=1e-12)
+
+
+# ----------------------------------------------------------------- routing
+
+def test_route_hand_example_and_ties():
+    # l' = [0, ln 2, 0, -1]: ln 2 first, then the tie at 0 goes to the lower id;
+    # weights e^(ln2)/(e^(ln2)+1) = 2/3 and 1/3 (ln 2 rounded to f32 moves them < 1e-7)
+    lg = np.array([[0.0, math.log(2.0), 0.0, -1.0]], np.float32)
+    ids, w = moe.route(lg, None, 2)
+    assert ids.tolist() == [[1, 0]]
+    np.testing.assert_allclose(w[0], [2 / 3, 1 / 3], rtol=2e-7)
+    # all equal: k = E keeps id order and weights 1/E
+    ids, w = moe.route(np.zeros((2, 8), np.float32), None, 8)
+    assert ids.tolist() == [list(range(8))] * 2
+    assert np.all(w == np.float32(1 / 8))
+
+
+def test_route_bias_and_invariants():
+    rng = np.random.default_rng(3)
+    lg = rng.standard_normal((64, 40)).astype(np.float32)
+    bias = np.zeros(40, np.float32)
+    bias[17] = 100.0
+    ids, w = moe.route(lg, bias, 5)
+    assert np.all(ids[:, 0] == 17) and np.all(w[:, 0] > 0.99)
+    ids, w = moe.route(lg, None, 6)
+    np.testing.assert_allclose(w.astype(np.float64).sum(1), 1.0, rtol=0, atol=3e-7)
+    assert np.all(np.diff(w, axis=1) <= 0)                       # weights follow the logit order
+    sel = np.take_along_axis(lg, ids, axis=1)
+    assert np.all(np.diff(sel, axis=1) <= 0)
+    assert np.all(np.sort(lg, axis=1)[:, -6][:, None] <= sel)    # the k largest
+    # relabeling experts relabels the ids and leaves the weights
+    perm = rng.permutation(40)
+    ids2, w2 = moe.route(lg[:, np.argsort(perm)], None, 6)
+    np.testing.assert_array_equal(np.argsort(perm)[ids2], ids)   # no ties in continuous data
+    np.testing.assert_array_equal(w2, w)
+    # the first k' of a top-k selection are the top-k' selection
+    ids3, _ = moe.route(lg, None, 3)
+    np.testing.assert_array_equal(ids3, ids[:, :3])
+
+
+def test_route_agrees_with_the_input_generator():
+    """synth.route writes the same reading with numpy's stable argsort and a
+    plain float64 sum: selections must be identical, weights within 1 ulp."""
+    cfg = synth.CONFIGS["prefill_nvfp4"].replace(tokens=256)
+    lg, b = synth.router_logits(cfg), synth.router_bias(cfg)
+    a_ids, a_w = moe.route(lg, b, cfg.top_k)
+    s_ids, s_w = synth.route(lg, b, cfg.top_k)
+    np.testing.assert_array_equal(a_ids, s_ids)
+    np.testing.assert_array_max_ulp(a_w, s_w, maxulp=1)
