@@ -137,6 +137,31 @@ def cpu_baseline(cfg, ids, wts, x_bits, budget_s=20.0):
                       f"{el:.1f} s"}
 
 
+def time_route(cfg, torch, pkg, reps=50):
+    """GPU top-k routing (moe_fp4_route) of the workload's router logits: the
+    caller-side step in front of the layer, timed on its own (it is not part
+    of the layer step above)."""
+    import numpy as np
+
+    import synth
+    lg = torch.from_numpy(synth.router_logits(cfg)).cuda()
+    bias = torch.from_numpy(synth.router_bias(cfg)).cuda() if cfg.router_bias else None
+    for _ in range(3):
+        pkg.route(lg, cfg.top_k, bias)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        pkg.route(lg, cfg.top_k, bias)
+    stop.record()
+    torch.cuda.synchronize()
+    us = start.elapsed_time(stop) / reps * 1e3
+    ids, _ = pkg.route(lg, cfg.top_k, bias)
+    same = bool(np.array_equal(ids.cpu().numpy(), synth.routing(cfg)[0]))
+    return {"us_per_call": us, "tokens": cfg.tokens, "experts": cfg.num_experts, "k": cfg.top_k,
+            "biased": bool(cfg.router_bias), "ids_equal_host_routing": same}
+
+
 def bench_decode(args, torch, pkg):
     import numpy as np
 
@@ -205,6 +230,7 @@ def bench_decode(args, torch, pkg):
         "stages_ms": stages,
         "down": {"bytes_per_launch": down_bytes,
                  "GBps": down_bytes / (stages["down"] * 1e-3) / 1e9 if stages["down"] > 0 else None},
+        "route": time_route(cfg, torch, pkg),
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
@@ -279,7 +305,8 @@ def bench_prefill(name, args, torch, pkg):
            "step_mfma": {"flops": total_flops, "TFLOPs": total_flops / (ms * 1e-3) / 1e12,
                          "frac_of_peak": total_flops / (ms * 1e-3) / 1e12 / peak},
            "step_hbm": {"weight_bytes": weight_bytes, "touched_experts": touched,
-                        "max_rows_per_expert": int(counts.max())}}
+                        "max_rows_per_expert": int(counts.max())},
+           "route": time_route(cfg, torch, pkg, reps=20)}
     if not args.no_cpu_baseline:
         log(f"timing the CPU oracle on {name}")
         out["cpu_baseline"] = cpu_baseline(cfg, ids, wts, x_bits, args.cpu_budget)
