@@ -467,6 +467,131 @@ def bench_stream_quant(args, torch, pkg, rule="4over6"):
     return out
 
 
+def bench_stack(args, torch, pkg):
+    """Decode of 16 tokens through the 48-layer mixed-precision routed-expert
+    stack of the MXFP4-FP8-R12 card (layers 19, 20, 21, 23, 28, 32, 33, 40,
+    41, 43, 44, 45 block FP8 x dynamic FP8, the other 36 MXFP4 x dynamic
+    MXFP8; 512 experts, top-10, hidden 2560, inter 640), all 48 layers resident
+    (78.3 GB of expert weights) and run as one captured HIP graph per step.
+    Weights N(0, 0.02) bf16 drawn on the device per layer and quantized by the
+    library; each layer gets its own synthetic tokens and routing."""
+    import numpy as np
+
+    import synth
+    from block_scaled_fp4_nvfp4_amd.stack import LayerStack
+    cfgs = synth.stack_configs(n_layers=args.stack_layers)
+    gen = torch.Generator(device="cuda")
+    layers, xs, ids_l, ws_l, touched, wbytes = [], [], [], [], [], 0
+    t0 = time.perf_counter()
+    for cfg in cfgs:
+        qs = []
+        for proj, rows, cols in ((0, 2 * cfg.inter, cfg.hidden), (1, cfg.hidden, cfg.inter)):
+            gen.manual_seed(cfg.weight_seed * 10 + proj)
+            w = (torch.randn(cfg.num_experts, rows, cols, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+            qs.append(pkg.quantize(w, cfg.w_fmt, cfg.rule))
+            del w
+        layers.append(make_layer(cfg, qs[0], qs[1], pkg))
+        x = synth.activations(cfg)
+        i, wt = synth.routing(cfg)
+        xs.append(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda())
+        ids_l.append(torch.from_numpy(i).cuda())
+        ws_l.append(torch.from_numpy(wt).cuda())
+        t = len(np.unique(i))
+        touched.append(t)
+        b13, b2 = expert_bytes(cfg)
+        wbytes += t * (b13 + b2)
+    torch.cuda.synchronize()
+    log(f"built {len(cfgs)} layers in {time.perf_counter() - t0:.1f} s, "
+        f"{torch.cuda.memory_allocated() / 1e9:.1f} GB resident")
+    st = LayerStack(layers, xs, ids_l, ws_l)
+    T = cfgs[0].tokens
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(2):
+        st.eager()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.stack_steps):
+        st.eager()
+    stop.record()
+    torch.cuda.synchronize()
+    eager_ms = start.elapsed_time(stop) / args.stack_steps
+    st.capture()
+    for _ in range(2):
+        st.replay()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.stack_steps):
+        st.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.stack_steps
+    # per-stage times of one layer of each format (the library's stage events)
+    timer = pkg.StageTimer()
+    per_fmt = {}
+    for fmt in ("mxfp4", "fp8_block"):
+        l = next(j for j, c in enumerate(cfgs) if c.w_fmt == fmt) if any(c.w_fmt == fmt for c in cfgs) else None
+        if l is None:
+            continue
+        acc = {k: 0.0 for k in pkg.STAGES}
+        for _ in range(5):
+            pkg.moe_forward_profiled(layers[l], xs[l], ids_l[l], ws_l[l], st.workspace, st.ys[l], timer)
+            torch.cuda.synchronize()
+            for k, v in timer.durations().items():
+                acc[k] += v / 5
+        b13, b2 = expert_bytes(cfgs[l])
+        per_fmt[fmt] = {"layer": l, "stages_ms": acc, "touched_experts": touched[l],
+                        "gate_up_GBps": touched[l] * b13 / (acc["gate_up"] * 1e-3) / 1e9}
+    mx = per_fmt.get("mxfp4")
+    roof = None
+    if mx:
+        b13 = expert_bytes(cfgs[mx["layer"]])[0]
+        ach = mx["gate_up_GBps"]
+        roof = {"bound": "hbm", "kernel": "gemv_gateup_kernel<MXFP4> on the dequantized MXFP8 x (36 of the 48 layers)",
+                "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                "traffic": None, "bytes_per_launch": mx["touched_experts"] * b13,
+                "unit_of_work": f"{mx['touched_experts']} touched experts x {b13} B of MXFP4 gate_up weights"}
+    n_fp8 = sum(c.w_fmt == "fp8_block" for c in cfgs)
+    out = {"workload": f"decode through a {len(cfgs)}-layer routed-expert stack: {len(cfgs) - n_fp8} MXFP4 x "
+                       f"MXFP8 layers and {n_fp8} block-FP8 x FP8 layers ({list(synth.FP8_ROUTED_LAYERS)}), "
+                       f"512 experts, top-10, hidden 2560, inter 640, {T} tokens, one HIP graph per step",
+           "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "steps": args.stack_steps,
+           "eager_ms_per_step": eager_ms, "dtype": "fp8",
+           "roofline": roof,
+           "step_hbm": {"weight_bytes": wbytes, "GBps": wbytes / (ms * 1e-3) / 1e9,
+                        "frac": wbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "touched_experts_mean": float(np.mean(touched))},
+           "per_format_layer": per_fmt}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the stack (first token, first layers)")
+        from oracle import moe
+        t0 = time.perf_counter()
+        done = 0
+        for cfg in cfgs:
+            i, wt = synth.routing(cfg)
+            touched1 = sorted({int(e) for e in i[0]})
+            w13, w2 = synth.layer_weights(cfg, experts=touched1)
+            pos = {e: j for j, e in enumerate(touched1)}
+            x = synth.activations(cfg)[:1]
+            ol = dict(w_fmt=cfg.w_fmt, a_fmt=cfg.a_fmt, num_experts=cfg.num_experts, hidden=cfg.hidden,
+                      inter=cfg.inter,
+                      w13=lambda e, w=w13, c=cfg, p=pos: moe.quantize_expert_weight(w[p[e]], c.w_fmt, c.rule),
+                      w2=lambda e, w=w2, c=cfg, p=pos: moe.quantize_expert_weight(w[p[e]], c.w_fmt, c.rule))
+            moe.moe_forward(ol, x, i[:1], wt[:1])
+            done += 1
+            if time.perf_counter() - t0 >= args.cpu_budget / 2:
+                break
+        el = time.perf_counter() - t0
+        per_layer = el / done
+        out["cpu_baseline"] = {"value": 1.0 / (per_layer * len(cfgs)), "unit": "tokens/s",
+                               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+                               "sample": f"1 token through the first {done} layer(s) ({el:.1f} s, weights of the "
+                                         f"token's experts drawn on the host and quantized by the oracle inside "
+                                         f"the timing), scaled to {len(cfgs)} layers"}
+    del st, layers
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -474,12 +599,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
                     choices=["all", "decode", "prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant",
-                             "sweep_quant", "copy"],
+                             "sweep_quant", "stack_decode", "copy"],
                     help="'all': the decode headline plus every other workload under 'workloads'; "
                          "'copy': a plain 1 GiB device copy that calibrates the HBM byte counters")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-copies", type=int, default=2)
     ap.add_argument("--stream-layers", type=int, default=48)
+    ap.add_argument("--stack-layers", type=int, default=48)
+    ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--sweep-layers", type=int, default=16,
                     help="layers of the streaming workload under the scale-sweep rule")
     ap.add_argument("--copies", type=int, default=8,
@@ -507,7 +634,7 @@ def main():
         dargs.workload = "decode"
         out = bench_decode(dargs, torch, pkg)
         torch.cuda.empty_cache()
-        others = (["prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant", "sweep_quant"]
+        others = (["prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant", "sweep_quant", "stack_decode"]
                   if args.workload == "all" else [])
     else:
         out = None
@@ -519,6 +646,8 @@ def main():
             extra[name] = bench_stream_quant(args, torch, pkg)
         elif name == "sweep_quant":
             extra[name] = bench_stream_quant(args, torch, pkg, rule="sweep")
+        elif name == "stack_decode":
+            extra[name] = bench_stack(args, torch, pkg)
         else:
             extra[name] = bench_prefill(name, args, torch, pkg)
         torch.cuda.empty_cache()

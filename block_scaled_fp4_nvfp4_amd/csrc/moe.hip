@@ -29,6 +29,17 @@ namespace fp4 {
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// MXFP4 weights x MXFP8 activations at decode sizes (at most 1024 pairs, the
+// single-workgroup permutation) take the weight-streaming GEMVs on the exactly
+// dequantized MXFP8 activations: every MXFP8 value (E4M3 times a power of two)
+// is a bf16 value, so the products and the f32 sums are those of the MFMA
+// path up to summation order, while each weight is read once per expert
+// instead of once per 64-row tile.
+bool w4a8_gemv(const moe_fp4_layer* L, int64_t T) {
+  return L->w_fmt == FP4_FMT_MXFP4 && L->a_fmt == FP4_FMT_MXFP8 && T * L->top_k <= 1024 &&
+         L->hidden <= 4096 && L->inter <= 1024;
+}
+
 int plan_workspace(const moe_fp4_layer* L, int64_t T, WsPlan* w) {
   const int64_t E = L->num_experts, H = L->hidden, I = L->inter, k = L->top_k;
   const int64_t P = T * k;
@@ -74,6 +85,10 @@ int plan_workspace(const moe_fp4_layer* L, int64_t T, WsPlan* w) {
   p.hq_codes = take(hq_codes);
   p.hq_scales = take(hq_scales);
   p.o = take(sizeof(float) * P * H);
+  if (w4a8_gemv(L, T)) {
+    p.x_deq = take(2 * T * H);
+    p.h_deq = take(sizeof(float) * P * I);
+  }
   if (L->shared_inter > 0) {
     const int64_t S = L->shared_inter;
     p.sx_codes = take(T * H);
@@ -759,8 +774,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 
 template <int WFMT>
 static int launch_gemv(const uint16_t* x, const WsPtrs& w, const moe_fp4_layer* L, int64_t P,
-                       int max_active, hipStream_t st, const Marker& mark) {
-  (void)P;
+                       int max_active, hipStream_t st, const Marker& mark, bool requant_h = false) {
   const int cpl = (L->hidden / 32 + 15) / 16;
   dim3 grid((unsigned)((L->inter + kGvOut - 1) / kGvOut), (unsigned)max_active);
 #define FP4_GV(B)                                                                                      \
@@ -776,12 +790,20 @@ static int launch_gemv(const uint16_t* x, const WsPtrs& w, const moe_fp4_layer* 
 #undef FP4_GV
   FP4_CHECK(check_launch("gemv_gateup"));
   FP4_CHECK(mark(3));
+  const float* hin = w.h;
+  if (requant_h) {  // rows past the valid pairs hold no h; their blocks are never read back
+    FP4_CHECK(fp4_quantize(FP4_FMT_MXFP8, FP4_RULE_RTN, FP4_TS_DYNAMIC, w.h, FP4_DT_F32, 1, P, L->inter,
+                           w.hq_codes, w.hq_scales, nullptr, nullptr, st));
+    FP4_CHECK(fp4_dequantize(FP4_FMT_MXFP8, w.hq_codes, w.hq_scales, nullptr, 1, P, L->inter, w.h_deq,
+                             FP4_DT_F32, st));
+    hin = w.h_deq;
+  }
   FP4_CHECK(mark(4));
   const int cpl2 = (L->inter / 32 + 3) / 4;
   dim3 grid2((unsigned)((L->hidden + kGdRows - 1) / kGdRows), (unsigned)max_active);
 #define FP4_GD(B)                                                                                      \
   case B:                                                                                              \
-    hipLaunchKernelGGL((gemv_down_kernel<WFMT, B>), grid2, dim3(256), 0, st, w.h, w.offsets, w.active, \
+    hipLaunchKernelGGL((gemv_down_kernel<WFMT, B>), grid2, dim3(256), 0, st, hin, w.offsets, w.active, \
                        L->w2, (const uint8_t*)L->w2_scale, L->w2_scale_2, L->hidden, L->inter, w.o);   \
     break;
   switch (cpl2) {
@@ -819,6 +841,8 @@ WsPtrs ws_pointers(const WsPlan& p, void* base) {
   w.sh_codes = reinterpret_cast<uint8_t*>(b + p.sh_codes);
   w.sh_scales = reinterpret_cast<uint8_t*>(b + p.sh_scales);
   w.s_out = reinterpret_cast<float*>(b + p.s_out);
+  w.x_deq = reinterpret_cast<uint16_t*>(b + p.x_deq);
+  w.h_deq = reinterpret_cast<float*>(b + p.h_deq);
   return w;
 }
 
@@ -955,6 +979,14 @@ static int forward_impl(const moe_fp4_layer* L, const uint16_t* x, int64_t T, co
     FP4_CHECK(mark(2));
     if (L->w_fmt == FP4_FMT_NVFP4) FP4_CHECK(launch_gemv<FP4_FMT_NVFP4>(x, w, L, P, max_active, st, mark));
     else FP4_CHECK(launch_gemv<FP4_FMT_MXFP4>(x, w, L, P, max_active, st, mark));
+  } else if (w4a8_gemv(L, T)) {
+    // x -> MXFP8 -> its exact bf16 values; h -> MXFP8 -> its exact f32 values
+    FP4_CHECK(fp4_quantize(FP4_FMT_MXFP8, FP4_RULE_RTN, FP4_TS_DYNAMIC, x, FP4_DT_BF16, 1, T, L->hidden,
+                           w.xq_codes, w.xq_scales, nullptr, nullptr, st));
+    FP4_CHECK(fp4_dequantize(FP4_FMT_MXFP8, w.xq_codes, w.xq_scales, nullptr, 1, T, L->hidden, w.x_deq,
+                             FP4_DT_BF16, st));
+    FP4_CHECK(mark(2));
+    FP4_CHECK(launch_gemv<FP4_FMT_MXFP4>(w.x_deq, w, L, P, max_active, st, mark, true));
   } else {
     FP4_CHECK(launch_grouped(L, x, T, w, max_active, st, mark));
   }

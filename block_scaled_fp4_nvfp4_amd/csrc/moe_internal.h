@@ -17,6 +17,7 @@ struct WsPlan {
   size_t block_counts, block_invalid, x_tensor_scale, h_tensor_scale, h;
   size_t xq_codes, xq_scales, hq_codes, hq_scales, o;
   size_t sx_codes, sx_scales, sh, sh_codes, sh_scales, s_out;
+  size_t x_deq, h_deq;  // MXFP4 x MXFP8 decode: dequantized MXFP8 x (bf16) and h (f32)
 };
 
 struct WsPtrs {
@@ -32,6 +33,8 @@ struct WsPtrs {
   float* sh;
   uint8_t *sh_codes, *sh_scales;
   float* s_out;
+  uint16_t* x_deq;
+  float* h_deq;
 };
 
 // Records the caller's stage events (moe_fp4_forward_profiled); no-op without events.
@@ -46,6 +49,7 @@ struct Marker {
 };
 
 int plan_workspace(const moe_fp4_layer* L, int64_t T, WsPlan* w);
+bool w4a8_gemv(const moe_fp4_layer* L, int64_t T);
 WsPtrs ws_pointers(const WsPlan& p, void* base);
 
 // grouped MFMA path (quantized activations): steps 2-5 of the forward

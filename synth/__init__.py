@@ -30,7 +30,7 @@ import os
 import numpy as np
 
 __all__ = [
-    "MoEConfig", "CONFIGS", "rng", "f32_to_bf16_bits", "bf16_bits_to_f32",
+    "MoEConfig", "CONFIGS", "FP8_ROUTED_LAYERS", "stack_configs", "rng", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "normal_bf16", "expert_weights", "layer_weights", "activations",
     "router_logits", "router_bias", "route", "routing", "shared_expert",
     "streaming_expert",
@@ -84,6 +84,25 @@ CONFIGS = {
     "prefill_fp8": MoEConfig("prefill_fp8", 512, 10, 2560, 640, 8192,
                              "fp8_block", "fp8_row", input_seed=4),
 }
+
+
+# The mixed-precision 48-layer routed-expert stack of the MXFP4-FP8-R12 card
+# ("Quantization format", "Retained layers"): these zero-based layers keep
+# block-FP8 experts with dynamic FP8 activations, the other 36 run MXFP4 x
+# dynamic MXFP8.
+FP8_ROUTED_LAYERS = (19, 20, 21, 23, 28, 32, 33, 40, 41, 43, 44, 45)
+
+
+def stack_configs(n_layers: int = 48, tokens: int = 16, num_experts: int = 512, top_k: int = 10,
+                  hidden: int = 2560, inter: int = 640, fp8_layers=FP8_ROUTED_LAYERS):
+    """Per-layer configurations of the decode stack (seeds differ per layer)."""
+    out = []
+    for l in range(n_layers):
+        fp8 = l in fp8_layers
+        out.append(MoEConfig(f"stack{l}", num_experts, top_k, hidden, inter, tokens,
+                             "fp8_block" if fp8 else "mxfp4", "fp8_row" if fp8 else "mxfp8",
+                             weight_seed=100 + l, input_seed=300 + l))
+    return out
 
 
 def rng(seed: int, *key: int) -> np.random.Generator:
