@@ -156,3 +156,27 @@ def test_many_tokens_uses_multipass_permutation(tiny):
     np.testing.assert_array_equal(_ws_i32(ws, lay["row_of_pair"], c.pairs), rop)
     y_ref = moe.moe_forward(OracleLayer(c, w13, w2).as_dict(), x, ids, wts)
     assert rel_fro(y, y_ref) < 1e-5
+
+
+def test_decode_layer_mxfp4_x_mxfp8_gemv_path(decode_layer):
+    """MXFP4 weights x dynamic MXFP8 activations at the decode shape (160
+    pairs): the GEMVs on the exactly dequantized MXFP8 x and h; sampled tokens
+    vs the oracle, and the quantized h bit-exact against the oracle's MXFP8
+    of the GPU's own h."""
+    print_case("decode layer, MXFP4 x MXFP8 GEMV path")
+    cfg, w13, w2 = decode_layer
+    c = cfg.replace(w_fmt="mxfp4", a_fmt="mxfp8")
+    x = synth.activations(c)
+    ids, wts = synth.routing(c)
+    y, ws, lay = _run(gpu_layer(c, w13, w2), x, ids, wts)
+    sample = [0, 9, 15]
+    y_ref = moe.moe_forward(OracleLayer(c, w13, w2).as_dict(), x, ids, wts, sample_tokens=sample)
+    err = rel_fro(y[sample], y_ref)
+    print(f"relative Frobenius error {err:.3e}")
+    assert err <= TOL
+    from oracle import quant
+    P, I = c.pairs, c.inter
+    h = _ws_f32(ws, lay["h"], P * I).reshape(P, I)
+    q = quant.quantize_mxfp8(h.astype(np.float64))
+    codes = host(ws[lay["hq_codes"]:lay["hq_codes"] + P * I])
+    np.testing.assert_array_equal(codes.reshape(P, I), q["codes"])
