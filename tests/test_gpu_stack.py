@@ -60,3 +60,30 @@ def test_mixed_stack_eager_and_graph():
                                           err_msg=f"replay {rep}, layer {l}")
         scratch.normal_()      # other work on the stream between replays
         torch.cuda.synchronize()
+
+
+def test_graph_capture_with_the_shared_expert_stream():
+    """A W4A4 layer with the MXFP8 shared expert, whose launches fork onto the
+    library's helper stream and join back: captured as one graph, every replay
+    equals the eager pass bit for bit, and the eager pass matches the oracle."""
+    print_case("graph capture of a layer with the shared expert")
+    from block_scaled_fp4_nvfp4_amd.stack import LayerStack
+    cfg = synth.CONFIGS["tiny"].replace(a_fmt="nvfp4", shared_inter=128)
+    w13, w2 = synth.layer_weights(cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    shared = synth.shared_expert(cfg)
+    st = LayerStack([gpu_layer(cfg, w13, w2, shared=shared)], [dev_bf16(x)], [dev(ids)], [dev(wts)])
+    st.eager()
+    torch.cuda.synchronize()
+    eager = host(st.ys[0]).copy()
+    ref = moe.moe_forward(OracleLayer(cfg, w13, w2, shared=shared).as_dict(), x, ids, wts)
+    assert rel_fro(eager, ref) <= 2e-3
+    st.capture()
+    for rep in range(3):
+        st.ys[0].fill_(float("nan"))
+        torch.cuda.synchronize()
+        st.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(st.ys[0]).view(np.uint32), eager.view(np.uint32),
+                                      err_msg=f"replay {rep}")
