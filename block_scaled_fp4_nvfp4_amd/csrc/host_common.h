@@ -38,6 +38,11 @@ inline unsigned grid_1d(int64_t n, int threads) {
 // number of compute units of the current device (cached per device id)
 int device_cu_count();
 
+// MXFP8 quantization of rows x cols (bf16 -> bf16 or f32 -> f32) that also
+// writes the exact values of the codes to `deq` (the layout of the input)
+int mxfp8_quantize_dequant(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                           uint8_t* scales, void* deq, int deq_dtype, hipStream_t st);
+
 }  // namespace fp4
 
 #define FP4_CHECK(expr)                  \

@@ -792,10 +792,8 @@ static int launch_gemv(const uint16_t* x, const WsPtrs& w, const moe_fp4_layer* 
   FP4_CHECK(mark(3));
   const float* hin = w.h;
   if (requant_h) {  // rows past the valid pairs hold no h; their blocks are never read back
-    FP4_CHECK(fp4_quantize(FP4_FMT_MXFP8, FP4_RULE_RTN, FP4_TS_DYNAMIC, w.h, FP4_DT_F32, 1, P, L->inter,
-                           w.hq_codes, w.hq_scales, nullptr, nullptr, st));
-    FP4_CHECK(fp4_dequantize(FP4_FMT_MXFP8, w.hq_codes, w.hq_scales, nullptr, 1, P, L->inter, w.h_deq,
-                             FP4_DT_F32, st));
+    FP4_CHECK(mxfp8_quantize_dequant(w.h, FP4_DT_F32, P, L->inter, w.hq_codes,
+                                     reinterpret_cast<uint8_t*>(w.hq_scales), w.h_deq, FP4_DT_F32, st));
     hin = w.h_deq;
   }
   FP4_CHECK(mark(4));
@@ -980,11 +978,9 @@ static int forward_impl(const moe_fp4_layer* L, const uint16_t* x, int64_t T, co
     if (L->w_fmt == FP4_FMT_NVFP4) FP4_CHECK(launch_gemv<FP4_FMT_NVFP4>(x, w, L, P, max_active, st, mark));
     else FP4_CHECK(launch_gemv<FP4_FMT_MXFP4>(x, w, L, P, max_active, st, mark));
   } else if (w4a8_gemv(L, T)) {
-    // x -> MXFP8 -> its exact bf16 values; h -> MXFP8 -> its exact f32 values
-    FP4_CHECK(fp4_quantize(FP4_FMT_MXFP8, FP4_RULE_RTN, FP4_TS_DYNAMIC, x, FP4_DT_BF16, 1, T, L->hidden,
-                           w.xq_codes, w.xq_scales, nullptr, nullptr, st));
-    FP4_CHECK(fp4_dequantize(FP4_FMT_MXFP8, w.xq_codes, w.xq_scales, nullptr, 1, T, L->hidden, w.x_deq,
-                             FP4_DT_BF16, st));
+    // x -> MXFP8 codes and their exact bf16 values in one pass; likewise h (f32)
+    FP4_CHECK(mxfp8_quantize_dequant(x, FP4_DT_BF16, T, L->hidden, w.xq_codes,
+                                     reinterpret_cast<uint8_t*>(w.xq_scales), w.x_deq, FP4_DT_BF16, st));
     FP4_CHECK(mark(2));
     FP4_CHECK(launch_gemv<FP4_FMT_MXFP4>(w.x_deq, w, L, P, max_active, st, mark, true));
   } else {

@@ -486,18 +486,14 @@ __global__ void __launch_bounds__(256) quant_fp4_kernel(
 
 // MXFP8: one thread per block of 32; e = min{e : 448 * 2^e >= amax}.
 template <typename T>
-__global__ void __launch_bounds__(256) quant_mxfp8_kernel(const T* __restrict__ x, int64_t nblocks,
-                                                          uint8_t* __restrict__ codes,
-                                                          uint8_t* __restrict__ scales) {
-  int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (g >= nblocks) return;
+__device__ __forceinline__ int mxfp8_block(const T* __restrict__ x, int64_t g, uint8_t* __restrict__ codes,
+                                           uint8_t* __restrict__ scales, uint32_t (&out)[8]) {
   float v[32];
   load_vals<32>(x + g * 32, v);
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
   int e = mx_exponent(amax, kE4M3Max);
-  uint32_t out[8];
 #pragma unroll
   for (int w = 0; w < 8; ++w) {
     uint32_t d = 0;
@@ -514,6 +510,17 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const T* __restrict__ 
   dst[0] = make_uint4(out[0], out[1], out[2], out[3]);
   dst[1] = make_uint4(out[4], out[5], out[6], out[7]);
   scales[g] = (uint8_t)(e + 127);
+  return e;
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) quant_mxfp8_kernel(const T* __restrict__ x, int64_t nblocks,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= nblocks) return;
+  uint32_t out[8];
+  (void)mxfp8_block<T>(x, g, codes, scales, out);
 }
 
 // Exact E4M3 code (saturating) of a / sigma for a >= 0, sigma > 0 floats.
@@ -677,6 +684,31 @@ __device__ __forceinline__ void store8<uint16_t>(uint16_t* out, int64_t i, const
   for (int j = 0; j < 4; ++j)
     w[j] = f32_to_bf16_bits(f[2 * j]) | (f32_to_bf16_bits(f[2 * j + 1]) << 16);
   *reinterpret_cast<uint4*>(out + i) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// MXFP8 quantization that also writes the exact values of the codes, e4m3(c)
+// * 2^e: four significant bits, so exact in f32 and in bf16 (both outputs keep
+// every finite result of an f32 or bf16 input's block).
+template <typename T, typename OutT>
+__global__ void __launch_bounds__(256) quant_mxfp8_deq_kernel(const T* __restrict__ x, int64_t nblocks,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales,
+                                                              OutT* __restrict__ deq) {
+  int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= nblocks) return;
+  uint32_t out[8];
+  const int e = mxfp8_block<T>(x, g, codes, scales, out);
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    float f[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t c = (out[2 * h + j / 4] >> (8 * (j % 4))) & 0xFFu;
+      const float m = ldexpf(e4m3_to_f32(c & 0x7Fu), e);
+      f[j] = (c & 0x80u) ? -m : m;
+    }
+    store8<OutT>(deq, g * 32 + 8 * h, f);
+  }
 }
 
 // fmt: 0 NVFP4, 1 MXFP4, 2 MXFP8, 3 FP8_BLOCK, 4 FP8_ROW.  One thread per 8 values.
@@ -888,6 +920,25 @@ int block_of(int fmt) {
 }
 
 }  // namespace
+
+namespace fp4 {
+int mxfp8_quantize_dequant(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* codes,
+                           uint8_t* scales, void* deq, int deq_dtype, hipStream_t st) {
+  if (cols % 32) return fail(FP4_ERR_SHAPE, "MXFP8 needs cols %% 32 == 0");
+  const int64_t nb = rows * cols / 32;
+  if (nb == 0) return FP4_OK;
+  const dim3 grid(grid_1d(nb, 256));
+  if (x_dtype == FP4_DT_BF16 && deq_dtype == FP4_DT_BF16)
+    hipLaunchKernelGGL((quant_mxfp8_deq_kernel<uint16_t, uint16_t>), grid, dim3(256), 0, st,
+                       reinterpret_cast<const uint16_t*>(x), nb, codes, scales, reinterpret_cast<uint16_t*>(deq));
+  else if (x_dtype == FP4_DT_F32 && deq_dtype == FP4_DT_F32)
+    hipLaunchKernelGGL((quant_mxfp8_deq_kernel<float, float>), grid, dim3(256), 0, st,
+                       reinterpret_cast<const float*>(x), nb, codes, scales, reinterpret_cast<float*>(deq));
+  else
+    return fail(FP4_ERR_UNSUPPORTED, "MXFP8 quantize-dequantize: bf16->bf16 or f32->f32 only");
+  return check_launch("quant_mxfp8_deq");
+}
+}  // namespace fp4
 
 extern "C" {
 
