@@ -431,10 +431,10 @@ __device__ __forceinline__ float chunk_dot_f32(u32x4 c, uint32_t sbits, const fl
   return fmaf(d0 + d1, chunk_scale<WFMT, 0>(sbits), acc);
 }
 
-constexpr int kGvRounds = 2;    // rounds of 16 outputs per workgroup of the gate_up GEMV
+constexpr int kGvRounds = 1;    // rounds of 16 outputs per workgroup of the gate_up GEMV
 constexpr int kGvOut = 16 * kGvRounds;
 constexpr int kGvTokens = 4;    // tokens whose activations are staged in LDS per pass
-constexpr int kGdRpg = 2;            // output rows per 4 lanes of the down GEMV
+constexpr int kGdRpg = 1;            // output rows per 4 lanes of the down GEMV
 constexpr int kGdRows = 64 * kGdRpg;  // output rows per workgroup of the down GEMV
 constexpr int kGdTokens = 8;
 
@@ -452,12 +452,14 @@ __device__ __forceinline__ void dma16_to_lds(const void* g, void* lds) {
 // stores could be issued, serialising two memory latencies.
 
 // gate_up + SiLU*up for the pairs of one expert, bf16 activations.
-// Grid: (ceil(I / 32), max active experts).  Each group of 16 lanes owns two
-// outputs j (one per round, 16 apart): gate row j and up row I+j, split into
-// 16-byte chunks of 32 codes (lane l takes chunks l, l+16, ...).  Both
-// rounds' codes and scales are loaded up front (about 5.8 KB per group at
-// the decode shape, 92 KB per workgroup) and reused for every token of the
-// expert.  The tokens' activations are staged in LDS, four tokens per pass,
+// Grid: (ceil(I / (16 kGvRounds)), max active experts).  Each group of 16
+// lanes owns one output j per round (rounds 16 apart): gate row j and up
+// row I+j, split into 16-byte chunks of 32 codes (lane l takes chunks l,
+// l+16, ...).  Every round's codes and scales are loaded up front (about
+// 2.9 KB per group and round at the decode shape) and reused for every
+// token of the expert.  One round (46 KB per workgroup, twice the
+// workgroups of two rounds) streams the weights faster than two or three.
+// The tokens' activations are staged in LDS, four tokens per pass,
 // as [token][quarter q][chunk c] 16-byte pieces (rows padded to a multiple
 // of 64 chunks for the DMA) so that the 16 lanes of a group read consecutive
 // pieces.
@@ -582,8 +584,9 @@ __global__ void __launch_bounds__(256) gemv_gateup_kernel(
 }
 
 // Down projection o[row] = W2[e] h[row] for the rows of one expert, f32 h.
-// Grid: (ceil(H / 128), max active experts).  Each group of 4 lanes owns two
-// output rows (n and n + 64 of the tile), split into 16-byte chunks of 32
+// Grid: (ceil(H / (64 kGdRpg)), max active experts).  Each group of 4 lanes
+// owns kGdRpg output rows (n, n + 64, ... of the tile; one row measured
+// faster than two), each split into 16-byte chunks of 32
 // codes (lane l takes chunks l, l+4, ...).  The tokens' h rows are staged in
 // LDS, eight tokens per pass; the eight 16-byte pieces of chunk c sit in
 // XOR-swizzled order (piece q at slot q ^ (c & 3)) so that the four lanes of
