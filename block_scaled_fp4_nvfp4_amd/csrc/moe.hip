@@ -735,7 +735,12 @@ __global__ void __launch_bounds__(256) route_topk_kernel(const float* __restrict
 constexpr int kMaxTopK = 32;
 
 // y[t, :] = sum_j w[t, j] * o[row(t, j), :] (+ extra[t, :]), in slot order, f32.
-// All k row indices and weights are read before the o loads are issued.
+// The k slots are taken CW at a time: a chunk's row indices and weights are
+// read before its o loads are issued.  CW is the smallest of 4, 8, 12, 16
+// that covers k (16 and a loop above that), so the registers, and with them
+// the waves in flight per SIMD, follow the routing width instead of its
+// maximum.
+template <int CW>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ o,
                                                       const int32_t* __restrict__ row_of_pair,
                                                       const float* __restrict__ topk_w, int64_t T, int H,
@@ -745,32 +750,43 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   int64_t per_row = H / 4;
   if (i >= T * per_row) return;
   int64_t t = i / per_row, c4 = i - t * per_row;
-  int rows[kMaxTopK];
-  float w[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j)
-    if (j < k) {
-      rows[j] = row_of_pair[t * k + j];
-      w[j] = topk_w[t * k + j];
-    }
-  float4 v[kMaxTopK];
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j)
-    if (j < k && rows[j] >= 0) v[j] = reinterpret_cast<const float4*>(o + (int64_t)rows[j] * H)[c4];
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j0 = 0; j0 < k; j0 += CW) {
+    int rows[CW];
+    float w[CW];
 #pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j)
-    if (j < k && rows[j] >= 0) {
-      acc.x = fmaf(w[j], v[j].x, acc.x);
-      acc.y = fmaf(w[j], v[j].y, acc.y);
-      acc.z = fmaf(w[j], v[j].z, acc.z);
-      acc.w = fmaf(w[j], v[j].w, acc.w);
-    }
+    for (int u = 0; u < CW; ++u)
+      if (j0 + u < k) {
+        rows[u] = row_of_pair[t * k + j0 + u];
+        w[u] = topk_w[t * k + j0 + u];
+      }
+    float4 v[CW];
+#pragma unroll
+    for (int u = 0; u < CW; ++u)
+      if (j0 + u < k && rows[u] >= 0) v[u] = reinterpret_cast<const float4*>(o + (int64_t)rows[u] * H)[c4];
+#pragma unroll
+    for (int u = 0; u < CW; ++u)
+      if (j0 + u < k && rows[u] >= 0) {
+        acc.x = fmaf(w[u], v[u].x, acc.x);
+        acc.y = fmaf(w[u], v[u].y, acc.y);
+        acc.z = fmaf(w[u], v[u].z, acc.z);
+        acc.w = fmaf(w[u], v[u].w, acc.w);
+      }
+  }
   if (extra) {
     float4 e = reinterpret_cast<const float4*>(extra + t * H)[c4];
     acc.x += e.x; acc.y += e.y; acc.z += e.z; acc.w += e.w;
   }
   reinterpret_cast<float4*>(y + t * H)[c4] = acc;
+}
+
+static void launch_combine(const float* o, const int32_t* row_of_pair, const float* topk_w, int64_t T, int H,
+                           int k, const float* extra, float* y, hipStream_t st) {
+  const dim3 grid(grid_1d(T * H / 4, 256)), block(256);
+  if (k <= 4) hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, st, o, row_of_pair, topk_w, T, H, k, extra, y);
+  else if (k <= 8) hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, st, o, row_of_pair, topk_w, T, H, k, extra, y);
+  else if (k <= 12) hipLaunchKernelGGL(combine_kernel<12>, grid, block, 0, st, o, row_of_pair, topk_w, T, H, k, extra, y);
+  else hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, st, o, row_of_pair, topk_w, T, H, k, extra, y);
 }
 
 // ---------------------------------------------------------- GEMV dispatch
@@ -992,9 +1008,7 @@ static int forward_impl(const moe_fp4_layer* L, const uint16_t* x, int64_t T, co
   if (side && hipStreamWaitEvent(st, side->join, 0) != hipSuccess)
     return fail(FP4_ERR_HIP, "join of the shared-expert stream failed");
   FP4_CHECK(mark(6));  // the "shared" stage is the part of the shared expert not hidden by the routed path
-  int64_t n4 = T * L->hidden / 4;
-  hipLaunchKernelGGL(combine_kernel, dim3(grid_1d(n4, 256)), dim3(256), 0, st, w.o, w.row_of_pair,
-                     topk_weights, T, L->hidden, L->top_k, extra, y);
+  launch_combine(w.o, w.row_of_pair, topk_weights, T, L->hidden, L->top_k, extra, y, st);
   FP4_CHECK(check_launch("combine"));
   return mark(7);
 }

@@ -90,6 +90,11 @@ struct GemmArgs {
   int K, N;                     // reduction size; outputs (gate_up: I; down: H)
   float* out;                   // gate_up: h [rows][N]; down: o [rows][N]
   const float* row_scale;       // down epilogue: per-row multiplier (shared-expert gate), may be null
+  // MX gate_up on 128-output tiles only (grouped_gemm_mx_kernel<EPI_GATEUP, 2>):
+  // when set, h leaves the epilogue as MXFP8 (E4M3 codes [rows][N], UE8M0
+  // scales [rows][N/32]) and `out` is not written
+  uint8_t* q_codes;
+  uint8_t* q_scales;
 };
 
 // ---------------------------------------------------------------- operands
@@ -693,6 +698,39 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx_kernel(GemmArgs g) {
   __builtin_amdgcn_s_waitcnt(vmcnt_only(0));  // no DMA outstanding at exit
 
   // ---- epilogue
+  if constexpr (EPI == EPI_GATEUP && NSUB == 2) {
+    if (g.q_codes) {
+      // h straight to MXFP8: a wave's 32 outputs of a row are one block of
+      // 32 (two subtiles of 16 lanes each), so the block amax is a max over
+      // the lane's two values and its 15 partner lanes; exponent and codes
+      // as the standalone MXFP8 quantizer takes them (the max is exact in
+      // any order, and the power-of-two scaling makes each convert exact)
+      const int blk = (nt * BN) / 32 + wave;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v[2];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) v[j] = silu_f32(acc[i][j][r]) * acc[i][2 + j][r];
+          float amax = fmaxf(fabsf(v[0]), fabsf(v[1]));
+#pragma unroll
+          for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+          const int ex = mx_exponent(amax, kE4M3Max);
+          const int rr = mt * BM + 16 * i + 4 * lg + r;
+          if (rr >= n_rows) continue;
+          const int64_t R = r_begin + rr;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const uint32_t c = e4m3_hw(fminf(ldexpf(fabsf(v[j]), -ex), kE4M3Max)) |
+                               ((__float_as_uint(v[j]) >> 24) & 0x80u);
+            g.q_codes[R * g.N + 32 * blk + 16 * j + lr] = (uint8_t)c;
+          }
+          if (lr == 0) g.q_scales[R * (g.N / 32) + blk] = (uint8_t)(ex + 127);
+        }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1418,6 +1456,7 @@ static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st)
   }
   if constexpr (EPI == EPI_GATEUP) {
     if (a.N % 128 == 0) return launch_gemm_mx<EPI, 2>(a, tiles_m_bound, st);
+    if (a.q_codes) return fail(FP4_ERR_UNSUPPORTED, "MXFP8 h epilogue needs 128-output gate_up tiles");
     if (a.N % 64 == 0) return launch_gemm_mx<EPI, 1>(a, tiles_m_bound, st);
   }
   return launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
@@ -1463,18 +1502,25 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   a.N = I;
   a.out = w.h;
   a.row_scale = nullptr;
+  // MXFP8 h has one scale per 32 outputs, which the MX gate_up kernel's
+  // 128-output tiles hold whole: its epilogue writes h quantized (no f32 h)
+  const bool h_in_epilogue = gk == GK_MX && I % 128 == 0;
+  a.q_codes = h_in_epilogue ? w.hq_codes : nullptr;
+  a.q_scales = h_in_epilogue ? static_cast<uint8_t*>(w.hq_scales) : nullptr;
   if (gk == GK_NV) FP4_CHECK((launch_gemm<GK_NV, EPI_GATEUP>(a, tiles_bound, st)));
   else if (gk == GK_MX) FP4_CHECK((launch_gemm<GK_MX, EPI_GATEUP>(a, tiles_bound, st)));
   else FP4_CHECK((launch_gemm<GK_FP8, EPI_GATEUP>(a, tiles_bound, st)));
   FP4_CHECK(mark(3));
   // 4. quantization of h (sorted rows; NVFP4 tensor scale over all of h).
   //    Rows of skipped pairs (invalid expert ids) hold no h: zero them first.
-  hipLaunchKernelGGL(zero_rows_tail_kernel, dim3(64), dim3(256), 0, st, w.h, w.offsets + E, P, I);
-  FP4_CHECK(check_launch("zero_rows_tail"));
   const bool static_h = L->a_fmt == FP4_FMT_NVFP4 && L->inter_scale;
   float* h_ts = static_h ? const_cast<float*>(L->inter_scale) : w.h_ts;
-  FP4_CHECK(fp4_quantize(L->a_fmt, FP4_RULE_RTN, static_h ? FP4_TS_STATIC : FP4_TS_DYNAMIC, w.h, FP4_DT_F32, 1,
-                         P, I, w.hq_codes, w.hq_scales, h_ts, nullptr, st));
+  if (!h_in_epilogue) {
+    hipLaunchKernelGGL(zero_rows_tail_kernel, dim3(64), dim3(256), 0, st, w.h, w.offsets + E, P, I);
+    FP4_CHECK(check_launch("zero_rows_tail"));
+    FP4_CHECK(fp4_quantize(L->a_fmt, FP4_RULE_RTN, static_h ? FP4_TS_STATIC : FP4_TS_DYNAMIC, w.h, FP4_DT_F32, 1,
+                           P, I, w.hq_codes, w.hq_scales, h_ts, nullptr, st));
+  }
   FP4_CHECK(mark(4));
   // 5. down -> o
   GemmArgs d = a;
@@ -1482,6 +1528,8 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   d.a_scales = w.hq_scales;
   d.a_tensor_scale = h_ts;
   d.a_gather = 0;
+  d.q_codes = nullptr;
+  d.q_scales = nullptr;
   d.w_codes = L->w2;
   d.w_scales = L->w2_scale;
   d.w_tensor_scale = L->w2_scale_2;

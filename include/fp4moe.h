@@ -161,7 +161,9 @@ typedef struct {
 } moe_fp4_layer;
 
 /* Byte offsets of the stage buffers inside the forward's workspace, for
- * inspection by tests (all buffers are written by moe_fp4_forward). */
+ * inspection by tests (written by moe_fp4_forward, except h on the MXFP4 x
+ * MXFP8 grouped path with inter a multiple of 128: there h leaves the gate_up
+ * GEMM already quantized and only hq_codes / hq_scales hold it). */
 typedef struct {
   size_t total;          /* required workspace bytes                              */
   size_t error_flag;     /* int32: nonzero if a topk id was out of range           */

@@ -33,6 +33,47 @@ def tiny():
     return cfg, w13, w2, synth.activations(cfg), *synth.routing(cfg)
 
 
+def _check_mxfp8_h(ws, lay, P, I, rows, ref, h, rel=1e-4):
+    """MXFP4 x MXFP8 with I a multiple of 128: h leaves the gate_up GEMM's
+    epilogue as MXFP8 codes and scales (no f32 h).  The GPU's sorted rows
+    `rows` against the oracle's quantization `ref` of its own float64 h (same
+    row order).  That h differs from the GPU's f32 h by the MFMA's
+    accumulation rounding, whose size follows the row's products rather than
+    each value (measured: within 1e-5 of the block amax); so every block
+    exponent equal except where the oracle's block amax / 448 lies within
+    `rel` of a power of two, and every code equal except, in blocks of equal
+    exponent, adjacent codes whose midpoint lies within `rel` times the block
+    amax of the oracle's value."""
+    from oracle.formats import E4M3_MAX, e4m3_decode
+    codes = host(ws[lay["hq_codes"]:lay["hq_codes"] + P * I]).reshape(P, I)[rows].astype(np.int64)
+    scales = host(ws[lay["hq_scales"]:lay["hq_scales"] + P * I // 32]).reshape(P, I // 32)[rows].astype(np.int64)
+    ref_c = ref["codes"].astype(np.int64)
+    ref_s = ref["scales"].astype(np.int64)
+    n = len(rows)
+    # exponents
+    ds = scales != ref_s
+    amax = np.abs(h).reshape(n, I // 32, 32).max(axis=2) / E4M3_MAX
+    l2 = np.log2(np.where(amax > 0, amax, 1.0))
+    assert np.all(np.abs(l2 - np.round(l2))[ds] < 2 * rel / np.log(2)), \
+        "exponent differs away from a power-of-two boundary"
+    print(f"h blocks with another exponent: {int(ds.sum())} of {ds.size}")
+    # codes, in blocks of equal exponent
+    same = np.repeat(~ds, 32, axis=1)
+    zero = ((codes & 0x7F) == 0) & ((ref_c & 0x7F) == 0)  # +0 / -0: h within rounding of zero
+    dc = (codes != ref_c) & same & ~zero
+    sign = lambda c: np.where(c & 0x80, -1.0, 1.0)
+    vg = sign(codes) * e4m3_decode(codes & 0x7F)
+    vr = sign(ref_c) * e4m3_decode(ref_c & 0x7F)
+    unit = np.ldexp(1.0, np.repeat(ref_s - 127, 32, axis=1))
+    q = h / unit
+    mid = (vg + vr) / 2
+    bound = rel * np.repeat(amax * E4M3_MAX, 32, axis=1) / unit
+    assert np.all(np.abs((codes & 0x7F) - (ref_c & 0x7F))[dc] == 1), "codes differ by more than one step"
+    assert np.all(np.abs(q - mid)[dc] <= bound[dc]), "codes differ away from a rounding tie"
+    print(f"h codes differing at a tie: {int(dc.sum())} of {dc.size}")
+    assert dc.sum() <= 1e-3 * dc.size
+
+
 @pytest.mark.parametrize("w_fmt,a_fmt", MODES)
 def test_tiny_quantized_activations(tiny, w_fmt, a_fmt):
     print_case(f"tiny {w_fmt} x {a_fmt}")
@@ -44,12 +85,16 @@ def test_tiny_quantized_activations(tiny, w_fmt, a_fmt):
     err = rel_fro(y, y_ref)
     print(f"relative Frobenius error {err:.3e}")
     assert err <= TOL
-    # stage: h before its quantization, sorted rows
     P = cfg.pairs
     _, por, _ = moe.permute(ids, cfg.num_experts)
+    if a_fmt == "mxfp8":
+        _check_mxfp8_h(ws, lay, P, cfg.inter, np.arange(P), {k_: v[por] for k_, v in st["hrec"].items()},
+                       st["h"][por])
+        return
+    # stage: h before its quantization, sorted rows
     h = host(ws[lay["h"]:lay["h"] + 4 * P * cfg.inter].view(torch.float32)).reshape(P, cfg.inter)
     # fp16 MFMA products and sums of exact values: ~1e-7; the block-scaled FP8
-    # MFMA accumulates its 128 products with ~1e-5 relative error (measured)
+    # MFMA accumulates with ~1e-5 relative error (measured)
     assert rel_fro(h, st["h"][por]) < (1e-5 if a_fmt == "nvfp4" else 1e-4)
     if a_fmt == "nvfp4":
         sx = host(ws[lay["x_tensor_scale"]:lay["x_tensor_scale"] + 4].view(torch.float32))[0]
@@ -168,9 +213,16 @@ def test_prefill_full_size_sampled(prefill_weights, name):
     w13, w2 = prefill_weights  # same bf16 source weights (shared seed)
     x = synth.activations(cfg)
     ids, wts = synth.routing(cfg)
-    y, _, _ = _run(gpu_layer(cfg, w13, w2), x, ids, wts)
+    y, ws, lay = _run(gpu_layer(cfg, w13, w2), x, ids, wts)
     sample = [0, 4095, 8191]
-    y_ref = moe.moe_forward(OracleLayer(cfg, w13, w2).as_dict(), x, ids, wts, sample_tokens=sample)
+    y_ref, st = moe.moe_forward(OracleLayer(cfg, w13, w2).as_dict(), x, ids, wts, sample_tokens=sample,
+                                return_stages=True)
     err = rel_fro(y[sample], y_ref)
     print(f"relative Frobenius error on sampled tokens {err:.3e}")
     assert err <= TOL
+    if cfg.a_fmt == "mxfp8" and cfg.inter % 128 == 0:
+        # h of the sampled tokens' pairs, quantized in the gate_up epilogue
+        k = cfg.top_k
+        pairs = np.concatenate([np.arange(t * k, (t + 1) * k) for t in sample])
+        _, _, rop = moe.permute(ids, cfg.num_experts)
+        _check_mxfp8_h(ws, lay, cfg.pairs, cfg.inter, rop[pairs], st["hrec"], st["h"][pairs])
