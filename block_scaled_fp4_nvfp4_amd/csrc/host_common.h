@@ -43,6 +43,10 @@ int device_cu_count();
 int mxfp8_quantize_dequant(const void* x, int x_dtype, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, void* deq, int deq_dtype, hipStream_t st);
 
+// NVFP4 tensor scale s[0] = fp32(fp64(amax) / 2688) of one tensor whose amax
+// is the max of nparts non-negative partial maxima at part (device)
+int nv_tensor_scale_from_parts(const float* part, int64_t nparts, float* s, hipStream_t st);
+
 }  // namespace fp4
 
 #define FP4_CHECK(expr)                  \

@@ -89,6 +89,12 @@ int plan_workspace(const moe_fp4_layer* L, int64_t T, WsPlan* w) {
     p.x_deq = take(2 * T * H);
     p.h_deq = take(sizeof(float) * P * I);
   }
+  if (L->a_fmt == FP4_FMT_NVFP4) {
+    // one per gate_up workgroup: M-tile bound x (I / 64) tiles at most, in
+    // whole rounds of the 8 XCDs
+    const int64_t tiles = (P + kGemmTileM - 1) / kGemmTileM + std::min<int64_t>(E, P);
+    p.h_amax_part = take(sizeof(float) * ((tiles * (I / 64) + 7) / 8 * 8));
+  }
   if (L->shared_inter > 0) {
     const int64_t S = L->shared_inter;
     p.sx_codes = take(T * H);
@@ -860,6 +866,7 @@ WsPtrs ws_pointers(const WsPlan& p, void* base) {
   w.s_out = reinterpret_cast<float*>(b + p.s_out);
   w.x_deq = reinterpret_cast<uint16_t*>(b + p.x_deq);
   w.h_deq = reinterpret_cast<float*>(b + p.h_deq);
+  w.h_amax_part = reinterpret_cast<float*>(b + p.h_amax_part);
   return w;
 }
 

@@ -95,6 +95,11 @@ struct GemmArgs {
   // scales [rows][N/32]) and `out` is not written
   uint8_t* q_codes;
   uint8_t* q_scales;
+  // NVFP4 gate_up on the register-staged kernel only: when set, workgroup L
+  // of the amax_nparts launched writes max |h| over the h values it stores to
+  // amax_part[L] (0 if it has no tile), for the tensor scale of h
+  float* amax_part;
+  int64_t amax_nparts;
 };
 
 // ---------------------------------------------------------------- operands
@@ -183,7 +188,10 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
     __syncthreads();
     nt = L % NT;
     const int mg = L / NT;
-    if (mg >= s_toff[g.E]) return;
+    if (mg >= s_toff[g.E]) {
+      if (GK == GK_NV && EPI == EPI_GATEUP && g.amax_part && threadIdx.x == 0) g.amax_part[L] = 0.0f;
+      return;
+    }
     int lo = 0, hi = g.E;
     while (hi - lo > 1) {
       int mid = (lo + hi) >> 1;
@@ -470,6 +478,7 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
   // ---- epilogue
   float scale = 1.0f;
   if (GK == GK_NV) scale = g.a_tensor_scale[0] * g.w_tensor_scale[e];
+  float vmax = 0.0f;  // max |h| stored by this lane (NVFP4 gate_up)
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -483,6 +492,7 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
         float v;
         if (EPI == EPI_GATEUP) {
           v = silu_f32(acc[i][j][r] * scale) * (acc[i][NSUB + j][r] * scale);
+          vmax = fmaxf(vmax, fabsf(v));
         } else {
           v = acc[i][j][r] * scale;
           if (g.row_scale) v *= g.row_scale[R];
@@ -490,6 +500,18 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
         g.out[R * g.N + n] = v;
       }
     }
+  if constexpr (GK == GK_NV && EPI == EPI_GATEUP) {
+    if (g.amax_part) {
+      // max is exact in any order, so the tensor amax is the one a separate
+      // pass over h would find
+      __shared__ float red[4];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+      if (lane == 0) red[wave] = vmax;
+      __syncthreads();
+      if (tid == 0) g.amax_part[L] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    }
+  }
 }
 
 // ------------------------------------------- MX path with LDS-DMA staging
@@ -1317,6 +1339,12 @@ static int launch_gemm_nv2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t
   return check_launch("grouped_gemm_nv2");
 }
 
+// Workgroups of a grouped GEMM launch: M-tile bound x output tiles, rounded
+// up to a multiple of the 8 XCDs (the tile remapping needs whole rounds).
+static int64_t gemm_grid(int64_t tiles_m_bound, int N, int BN) {
+  return (tiles_m_bound * (N / BN) + 7) / 8 * 8;
+}
+
 // Zero rows [n_valid, P) of a [P, cols] f32 buffer (n_valid read on the device).
 __global__ void zero_rows_tail_kernel(float* __restrict__ buf, const int32_t* __restrict__ n_valid, int64_t P,
                                       int cols) {
@@ -1351,17 +1379,20 @@ __global__ void __launch_bounds__(256) shared_gate_kernel(const uint16_t* __rest
 template <int GK, int EPI, int NSUB, bool WFP8>
 static int launch_gemm_n(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   using C = TileCfg<GK, EPI, NSUB, WFP8>;
-  const int NT = a.N / C::BN;
-  int64_t G = tiles_m_bound * NT;
-  G = (G + 7) / 8 * 8;
+  const int64_t G = gemm_grid(tiles_m_bound, a.N, C::BN);
+  if (a.amax_part && G != a.amax_nparts)
+    return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM: %lld partial maxima expected, %lld workgroups",
+                (long long)a.amax_nparts, (long long)G);
   if (G <= 0) return FP4_OK;
   if (G > INT32_MAX) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM grid too large");
+  // 256 bytes stay for the kernel's static LDS (the epilogue's reduction)
+  constexpr size_t dyn_max = 160 * 1024 - 256;
   const size_t lds = 2 * C::STAGE + (a.dense_rows > 0 ? 0 : sizeof(int) * ((size_t)a.E + 1));
-  if (lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs %zu bytes of LDS", lds);
+  if (lds > dyn_max) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs %zu bytes of LDS", lds);
   static bool attr_set = false;  // raise the dynamic-LDS limit once per kernel instance
   if (!attr_set) {
     if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_kernel<GK, EPI, NSUB, WFP8>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_max) != hipSuccess)
       return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
     attr_set = true;
   }
@@ -1507,19 +1538,26 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   const bool h_in_epilogue = gk == GK_MX && I % 128 == 0;
   a.q_codes = h_in_epilogue ? w.hq_codes : nullptr;
   a.q_scales = h_in_epilogue ? static_cast<uint8_t*>(w.hq_scales) : nullptr;
+  // NVFP4 h with a dynamic tensor scale: the gate_up workgroups (register-
+  // staged kernel, 128- or 64-output tiles) leave their max |h| behind, so
+  // the scale needs no second pass over h
+  const bool static_h = L->a_fmt == FP4_FMT_NVFP4 && L->inter_scale;
+  const bool h_parts = gk == GK_NV && !static_h;
+  a.amax_part = h_parts ? w.h_amax_part : nullptr;
+  a.amax_nparts = h_parts ? gemm_grid(tiles_bound, I, I % 128 == 0 ? 128 : 64) : 0;
   if (gk == GK_NV) FP4_CHECK((launch_gemm<GK_NV, EPI_GATEUP>(a, tiles_bound, st)));
   else if (gk == GK_MX) FP4_CHECK((launch_gemm<GK_MX, EPI_GATEUP>(a, tiles_bound, st)));
   else FP4_CHECK((launch_gemm<GK_FP8, EPI_GATEUP>(a, tiles_bound, st)));
   FP4_CHECK(mark(3));
   // 4. quantization of h (sorted rows; NVFP4 tensor scale over all of h).
   //    Rows of skipped pairs (invalid expert ids) hold no h: zero them first.
-  const bool static_h = L->a_fmt == FP4_FMT_NVFP4 && L->inter_scale;
   float* h_ts = static_h ? const_cast<float*>(L->inter_scale) : w.h_ts;
   if (!h_in_epilogue) {
     hipLaunchKernelGGL(zero_rows_tail_kernel, dim3(64), dim3(256), 0, st, w.h, w.offsets + E, P, I);
     FP4_CHECK(check_launch("zero_rows_tail"));
-    FP4_CHECK(fp4_quantize(L->a_fmt, FP4_RULE_RTN, static_h ? FP4_TS_STATIC : FP4_TS_DYNAMIC, w.h, FP4_DT_F32, 1,
-                           P, I, w.hq_codes, w.hq_scales, h_ts, nullptr, st));
+    if (h_parts) FP4_CHECK(nv_tensor_scale_from_parts(w.h_amax_part, a.amax_nparts, h_ts, st));
+    FP4_CHECK(fp4_quantize(L->a_fmt, FP4_RULE_RTN, (static_h || h_parts) ? FP4_TS_STATIC : FP4_TS_DYNAMIC, w.h,
+                           FP4_DT_F32, 1, P, I, w.hq_codes, w.hq_scales, h_ts, nullptr, st));
   }
   FP4_CHECK(mark(4));
   // 5. down -> o
@@ -1530,6 +1568,8 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   d.a_gather = 0;
   d.q_codes = nullptr;
   d.q_scales = nullptr;
+  d.amax_part = nullptr;
+  d.amax_nparts = 0;
   d.w_codes = L->w2;
   d.w_scales = L->w2_scale;
   d.w_tensor_scale = L->w2_scale_2;

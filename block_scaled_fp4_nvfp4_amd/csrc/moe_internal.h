@@ -18,6 +18,7 @@ struct WsPlan {
   size_t xq_codes, xq_scales, hq_codes, hq_scales, o;
   size_t sx_codes, sx_scales, sh, sh_codes, sh_scales, s_out;
   size_t x_deq, h_deq;  // MXFP4 x MXFP8 decode: dequantized MXFP8 x (bf16) and h (f32)
+  size_t h_amax_part;   // NVFP4 grouped path: max |h| per gate_up workgroup
 };
 
 struct WsPtrs {
@@ -35,6 +36,7 @@ struct WsPtrs {
   float* s_out;
   uint16_t* x_deq;
   float* h_deq;
+  float* h_amax_part;
 };
 
 // Records the caller's stage events (moe_fp4_forward_profiled); no-op without events.

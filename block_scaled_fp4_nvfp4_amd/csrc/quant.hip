@@ -938,6 +938,13 @@ int mxfp8_quantize_dequant(const void* x, int x_dtype, int64_t rows, int64_t col
     return fail(FP4_ERR_UNSUPPORTED, "MXFP8 quantize-dequantize: bf16->bf16 or f32->f32 only");
   return check_launch("quant_mxfp8_deq");
 }
+
+int nv_tensor_scale_from_parts(const float* part, int64_t nparts, float* s, hipStream_t st) {
+  if (nparts < 1 || nparts > INT32_MAX) return fail(FP4_ERR_INVALID_ARG, "tensor scale from %lld partial maxima",
+                                                    (long long)nparts);
+  hipLaunchKernelGGL(nv_scale_from_parts_kernel, dim3(1), dim3(256), 0, st, part, (int64_t)0, (int)nparts, s);
+  return check_launch("nv_scale_from_parts");
+}
 }  // namespace fp4
 
 extern "C" {

@@ -99,6 +99,14 @@ def test_tiny_quantized_activations(tiny, w_fmt, a_fmt):
     if a_fmt == "nvfp4":
         sx = host(ws[lay["x_tensor_scale"]:lay["x_tensor_scale"] + 4].view(torch.float32))[0]
         assert sx == st["xrec"]["tensor_scale"]
+        _check_h_tensor_scale(ws, lay, h)
+
+
+def _check_h_tensor_scale(ws, lay, h):
+    """S_h = fp32(amax / 2688) over the GPU's own f32 h, exactly (the amax
+    comes from partial maxima left by the gate_up workgroups)."""
+    sh = host(ws[lay["h_tensor_scale"]:lay["h_tensor_scale"] + 4].view(torch.float32))[0]
+    assert sh == np.float32(np.float64(np.abs(h).max()) / 2688.0)
 
 
 def test_tiny_w4a4_static_scales(tiny):
@@ -198,6 +206,8 @@ def test_prefill_nvfp4_full_size_sampled(prefill_weights):
     assert sx == gold["s_x"]          # amax/2688 over all of x: exact
     sh = host(ws[lay["h_tensor_scale"]:lay["h_tensor_scale"] + 4].view(torch.float32))[0]
     assert abs(sh / gold["s_h"] - 1) < 1e-5
+    P, I = cfg.pairs, cfg.inter
+    _check_h_tensor_scale(ws, lay, host(ws[lay["h"]:lay["h"] + 4 * P * I].view(torch.float32)))
     err = rel_fro(y[gold["sample"]], gold["y"])
     print(f"relative Frobenius error on sampled tokens {err:.3e}")
     assert err <= TOL
