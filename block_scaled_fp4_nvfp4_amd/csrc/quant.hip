@@ -130,6 +130,37 @@ __global__ void __launch_bounds__(256) tensor_amax_kernel(const T* x, int64_t pe
   }
 }
 
+// Partial maxima of |x| over one tensor of n values (n % 8 == 0): workgroup b
+// writes the max over its share to part[b].  Each lane keeps four 8-value
+// loads in flight.
+template <typename T>
+__global__ void __launch_bounds__(256) amax_parts_kernel(const T* __restrict__ x, int64_t n,
+                                                         float* __restrict__ part) {
+  const int64_t S = (int64_t)gridDim.x * 256 * 8;
+  float m = 0.0f;
+  int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  for (; i + 3 * S < n; i += 4 * S) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) load_vals<8>(x + i + u * S, v[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[u][j]));
+  }
+  for (; i < n; i += S) {
+    float v[8];
+    load_vals<8>(x + i, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+  }
+  m = wave_max(m);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
 // S = fp32(fp64(amax) / 2688) of tensor y from its nparts partial maxima at
 // part + y * stride; one workgroup per tensor.
 __global__ void __launch_bounds__(256) nv_scale_from_parts_kernel(const float* __restrict__ part, int64_t stride,
@@ -853,6 +884,20 @@ int quantize_typed(int fmt, int rule, int ts_mode, const T* x, int64_t batch, in
       return FP4_OK;
     };
     if (mx || ts_mode != FP4_TS_DYNAMIC) return quant_range(0, batch, st);
+    if (batch == 1 && reinterpret_cast<uintptr_t>(codes) % 4 == 0) {
+      // One tensor: the workgroups' maxima are parked in its code bytes,
+      // which only the quantization below writes (per / 2 bytes hold the
+      // at most per / 2048 + 1 floats), and one small kernel turns them into
+      // the scale; no fill and no atomics.
+      const int64_t gx = std::max<int64_t>(1, std::min<int64_t>((per / 8 + 255) / 256, 8LL * device_cu_count()));
+      float* part = reinterpret_cast<float*>(codes);
+      hipLaunchKernelGGL(amax_parts_kernel<T>, dim3((unsigned)gx), dim3(256), 0, st, x, per, part);
+      FP4_CHECK(check_launch("amax_parts"));
+      hipLaunchKernelGGL(nv_scale_from_parts_kernel, dim3(1), dim3(256), 0, st, part, (int64_t)0, (int)gx,
+                         tensor_scale);
+      FP4_CHECK(check_launch("tensor_scale"));
+      return quant_range(0, 1, st);
+    }
     FP4_CHECK(launch_fill(reinterpret_cast<uint32_t*>(tensor_scale), 0u, batch, st));
     const int nch = amax_chunks<T>(batch, per);
     if (nch <= 1) {
