@@ -6,8 +6,8 @@ block_scaled_fp4_nvfp4_amd.build`).  This package is its thin Python binding.
 """
 from ._lib import (FMT, RULE, STAGES, Fp4Error, MoELayer, StageTimer, dequantize, lib,
                    moe_forward, moe_forward_profiled, quantize, route, status_string,
-                   workspace_layout, workspace_size)
+                   tile_weights, workspace_layout, workspace_size)
 
 __all__ = ["FMT", "RULE", "STAGES", "Fp4Error", "MoELayer", "StageTimer", "dequantize", "lib",
            "moe_forward", "moe_forward_profiled", "quantize", "route", "status_string",
-           "workspace_layout", "workspace_size"]
+           "tile_weights", "workspace_layout", "workspace_size"]

@@ -24,7 +24,7 @@ STATUS = {0: "FP4_OK", -1: "FP4_ERR_INVALID_ARG", -2: "FP4_ERR_SHAPE",
 
 EXPORTED = ["fp4_quantize", "fp4_dequantize", "moe_fp4_workspace_layout",
             "moe_fp4_workspace_size", "moe_fp4_forward", "moe_fp4_forward_profiled",
-            "moe_fp4_route", "fp4_status_string", "fp4_last_error"]
+            "moe_fp4_route", "moe_fp4_tile_weights", "fp4_status_string", "fp4_last_error"]
 STAGES = ["permute", "x_quant", "gate_up", "h_quant", "down", "shared", "combine"]
 
 
@@ -46,6 +46,7 @@ class LayerStruct(ctypes.Structure):
         ("ws13", ctypes.c_void_p), ("ws13_scale", ctypes.c_void_p),
         ("ws2", ctypes.c_void_p), ("ws2_scale", ctypes.c_void_p),
         ("shared_gate", ctypes.c_void_p),
+        ("w13_tiled", ctypes.c_void_p), ("w13_scale_tiled", ctypes.c_void_p),
     ]
 
 
@@ -82,6 +83,8 @@ def lib():
         L.moe_fp4_forward_profiled.restype = i32
         L.moe_fp4_route.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
         L.moe_fp4_route.restype = i32
+        L.moe_fp4_tile_weights.argtypes = [i32, vp, vp, i64, i64, i64, vp, vp, vp]
+        L.moe_fp4_tile_weights.restype = i32
         L.fp4_status_string.argtypes = [i32]
         L.fp4_status_string.restype = ctypes.c_char_p
         L.fp4_last_error.argtypes = []
@@ -169,6 +172,19 @@ def route(logits: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None):
     return ids, w
 
 
+def tile_weights(codes: torch.Tensor, scales: torch.Tensor, fmt: str = "mxfp4"):
+    """moe_fp4_tile_weights.  codes uint8 [E, rows, cols/2], scales uint8
+    [E, rows, cols/32] (MXFP4, contiguous, on the device).  Returns the tiled
+    (codes, scales), same shapes and dtypes, for MoELayer.w13_tiled /
+    w13_scale_tiled."""
+    assert codes.is_cuda and codes.is_contiguous() and scales.is_contiguous() and codes.dim() == 3
+    E, rows, half = (int(v) for v in codes.shape)
+    tc, ts = torch.empty_like(codes), torch.empty_like(scales)
+    _check(lib().moe_fp4_tile_weights(FMT[fmt], _ptr(codes), _ptr(scales), E, rows, 2 * half,
+                                      _ptr(tc), _ptr(ts), _stream()))
+    return tc, ts
+
+
 def dequantize(q: dict, fmt: str, shape, out_dtype=torch.float32) -> torch.Tensor:
     """fp4_dequantize of a record produced by quantize(); shape = x's shape."""
     codes = q["codes"]
@@ -202,6 +218,8 @@ class MoELayer:
     ws2: Optional[torch.Tensor] = None
     ws2_scale: Optional[torch.Tensor] = None
     shared_gate: Optional[torch.Tensor] = None
+    w13_tiled: Optional[torch.Tensor] = None
+    w13_scale_tiled: Optional[torch.Tensor] = None
 
     def struct(self) -> LayerStruct:
         p = lambda t: None if t is None else t.data_ptr()
@@ -210,7 +228,8 @@ class MoELayer:
             p(self.w13), p(self.w13_scale), p(self.w13_scale_2),
             p(self.w2), p(self.w2_scale), p(self.w2_scale_2),
             p(self.input_scale), p(self.inter_scale), self.shared_inter,
-            p(self.ws13), p(self.ws13_scale), p(self.ws2), p(self.ws2_scale), p(self.shared_gate))
+            p(self.ws13), p(self.ws13_scale), p(self.ws2), p(self.ws2_scale), p(self.shared_gate),
+            p(self.w13_tiled), p(self.w13_scale_tiled))
 
 
 def workspace_layout(layer: MoELayer, tokens: int) -> dict:

@@ -100,6 +100,9 @@ struct GemmArgs {
   // amax_part[L] (0 if it has no tile), for the tensor scale of h
   float* amax_part;
   int64_t amax_nparts;
+  // MX gate_up (grouped_gemm_mx_kernel): w_codes / w_scales are in the tiled
+  // order of moe_fp4_tile_weights
+  int w_tiled;
 };
 
 // ---------------------------------------------------------------- operands
@@ -528,7 +531,11 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
 // Every thread issues the same number of DMA instructions per step, so one
 // wait for vmcnt <= N_INS before the step's barrier completes its own
 // instructions for the step about to be read; the barrier then covers the
-// other waves' instructions.
+// other waves' instructions.  With WT the weights are in the tiled order of
+// moe_fp4_tile_weights: a W instruction, which covers 16 consecutive rows of
+// one K step, then reads one contiguous kilobyte (row-major: sixteen 64-byte
+// pieces 2 KB apart at the model's hidden size), and the 64 W scale lanes
+// read four 64-byte runs.
 template <int EPI, int NSUB>
 struct MxCfg {
   static constexpr int BM = kBM;
@@ -556,7 +563,7 @@ __device__ __forceinline__ void dma4_to_lds(const void* g, void* lds) {
 }
 
 
-template <int EPI, int NSUB>
+template <int EPI, int NSUB, bool WT>
 __global__ void __launch_bounds__(256, 2) grouped_gemm_mx_kernel(GemmArgs g) {
   using C = MxCfg<EPI, NSUB>;
   constexpr int BM = C::BM, BN = C::BN, NU = C::NU, WROWS = C::WROWS;
@@ -613,9 +620,19 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx_kernel(GemmArgs g) {
     return g.a_gather ? g.pair_of_row[R] / g.k : R;
   };
   auto w_grow = [&](int i) __attribute__((always_inline)) -> int { return (i / BN) * g.N + nt * BN + (i % BN); };
+  // offsets within the expert of weight row gr's K-step-0 code piece and
+  // scale dword, and what one K step adds to them
+  constexpr int W_STEP = WT ? 1024 : 64, WS_STEP = WT ? 64 : 4;
+  auto w_code_at = [&](int gr) __attribute__((always_inline)) -> int64_t {
+    return WT ? (int64_t)(gr >> 4) * (KS * 1024) + (gr & 15) * 64 : (int64_t)gr * (K / 2);
+  };
+  auto w_scale_at = [&](int gr) __attribute__((always_inline)) -> int64_t {
+    return WT ? (int64_t)(gr >> 4) * (KS * 64) + (gr & 15) * 4 : (int64_t)gr * SKB;
+  };
 
   // global source of this lane for each DMA instruction (K step 0); the step
-  // advances A by 128 bytes, W by 64 bytes and the scales by 4 bytes
+  // advances A by 128 bytes, W by W_STEP bytes, the A scales by 4 bytes and
+  // the W scales by WS_STEP bytes
   const uint8_t* a_src[C::A_INS];
   const uint8_t* w_src[C::W_INS];
   const uint8_t* s_src[C::S_INS];
@@ -629,7 +646,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx_kernel(GemmArgs g) {
   for (int q = 0; q < C::W_INS; ++q) {
     const int row = (q * 4 + wave) * 16 + (lane >> 2), slot = lane & 3;
     const int chunk = slot ^ (((row >> 1) ^ (row >> 3)) & 3);  // inverse of swz<64>
-    w_src[q] = w_base + (int64_t)w_grow(row) * (K / 2) + 16 * chunk;
+    w_src[q] = w_base + w_code_at(w_grow(row)) + 16 * chunk;
   }
 #pragma unroll
   for (int q = 0; q < C::S_INS; ++q) {
@@ -637,10 +654,16 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx_kernel(GemmArgs g) {
     if (d < BM)
       s_src[q] = reinterpret_cast<const uint8_t*>(g.a_scales) + a_row_of(d) * SKB;
     else if (d < C::SC_DW)
-      s_src[q] = reinterpret_cast<const uint8_t*>(g.w_scales) + ((int64_t)e * NW + w_grow(d - BM)) * SKB;
+      s_src[q] = reinterpret_cast<const uint8_t*>(g.w_scales) + (int64_t)e * NW * SKB + w_scale_at(w_grow(d - BM));
     else
       s_src[q] = reinterpret_cast<const uint8_t*>(g.a_scales) + a_row_of(0) * SKB;
   }
+  // K-step advance of scale lane (q, lane): W scale lanes move WS_STEP bytes
+  auto s_step = [&](int q) __attribute__((always_inline)) -> int {
+    if constexpr (!WT) return 4;
+    const int d = (q * 4 + wave) * 64 + lane;
+    return d >= BM && d < C::SC_DW ? WS_STEP : 4;
+  };
 
   // ks < 0: the same instructions all read one 16-byte line (a stage that is
   // never read again is refilled with it), so every step issues N_INS DMA
@@ -652,12 +675,12 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx_kernel(GemmArgs g) {
       dma16_to_lds(real ? a_src[q] + ks * 128 : g.a_codes, st + (q * 4 + wave) * 1024);
 #pragma unroll
     for (int q = 0; q < C::W_INS; ++q)
-      dma16_to_lds(real ? w_src[q] + ks * 64 : g.a_codes, st + C::A_BYTES + (q * 4 + wave) * 1024);
+      dma16_to_lds(real ? w_src[q] + ks * W_STEP : g.a_codes, st + C::A_BYTES + (q * 4 + wave) * 1024);
 #pragma unroll
     for (int q = 0; q < C::S_INS; ++q) {
       const int d0 = (q * 4 + wave) * 64;
       uint8_t* dst = d0 < C::SC_DW ? st + C::A_BYTES + C::W_BYTES + d0 * 4 : dummy;
-      dma4_to_lds(real ? s_src[q] + ks * 4 : g.a_codes, dst);
+      dma4_to_lds(real ? s_src[q] + ks * s_step(q) : g.a_codes, dst);
     }
   };
 
@@ -1339,6 +1362,29 @@ static int launch_gemm_nv2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t
   return check_launch("grouped_gemm_nv2");
 }
 
+// Tiled order of moe_fp4_tile_weights.  The E stacked [rows, cols] tensors
+// are one run of E * rows rows (rows % 16 == 0, so no 16-row group straddles
+// two experts); thread i copies 16-byte code chunk i and scale dword i.
+__global__ void __launch_bounds__(256) tile_weights_kernel(const uint8_t* __restrict__ codes,
+                                                           const uint8_t* __restrict__ scales,
+                                                           int64_t rows_total, int KS,
+                                                           uint8_t* __restrict__ tiled_codes,
+                                                           uint8_t* __restrict__ tiled_scales) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < rows_total * KS * 4) {  // code chunks: row r, K step ks, 16-byte piece u of its 64 bytes
+    const int64_t r = i / (KS * 4);
+    const int c = (int)(i - r * KS * 4), ks = c >> 2, u = c & 3;
+    const int64_t dst = (r >> 4) * ((int64_t)KS * 1024) + ks * 1024 + (r & 15) * 64 + u * 16;
+    *reinterpret_cast<uint4*>(tiled_codes + dst) = *reinterpret_cast<const uint4*>(codes + i * 16);
+  }
+  if (i < rows_total * KS) {  // scale dwords: row r, K step ks
+    const int64_t r = i / KS;
+    const int ks = (int)(i - r * KS);
+    const int64_t dst = (r >> 4) * ((int64_t)KS * 64) + ks * 64 + (r & 15) * 4;
+    *reinterpret_cast<uint32_t*>(tiled_scales + dst) = *reinterpret_cast<const uint32_t*>(scales + i * 4);
+  }
+}
+
 // Workgroups of a grouped GEMM launch: M-tile bound x output tiles, rounded
 // up to a multiple of the 8 XCDs (the tile remapping needs whole rounds).
 static int64_t gemm_grid(int64_t tiles_m_bound, int N, int BN) {
@@ -1422,8 +1468,8 @@ static int launch_gemm_mx2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t
   return check_launch("grouped_gemm_mx2");
 }
 
-template <int EPI, int NSUB>
-static int launch_gemm_mx(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+template <int EPI, int NSUB, bool WT>
+static int launch_gemm_mx_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   using C = MxCfg<EPI, NSUB>;
   const int NT = a.N / C::BN;
   int64_t G = tiles_m_bound * NT;
@@ -1435,14 +1481,20 @@ static int launch_gemm_mx(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t 
     return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_mx_kernel<EPI, NSUB>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_mx_kernel<EPI, NSUB, WT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)(160 * 1024 - 3 * C::STAGE - 256)) != hipSuccess)
       return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
     attr_set = true;
   }
-  hipLaunchKernelGGL((grouped_gemm_mx_kernel<EPI, NSUB>), dim3((unsigned)G), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((grouped_gemm_mx_kernel<EPI, NSUB, WT>), dim3((unsigned)G), dim3(256), lds, st, a);
   return check_launch("grouped_gemm_mx");
+}
+
+template <int EPI, int NSUB>
+static int launch_gemm_mx(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+  return a.w_tiled ? launch_gemm_mx_t<EPI, NSUB, true>(a, tiles_m_bound, st)
+                   : launch_gemm_mx_t<EPI, NSUB, false>(a, tiles_m_bound, st);
 }
 
 // Widest tile (outputs per tile 64 * NSUB) that divides N and fits LDS.
@@ -1490,6 +1542,7 @@ static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st)
     if (a.q_codes) return fail(FP4_ERR_UNSUPPORTED, "MXFP8 h epilogue needs 128-output gate_up tiles");
     if (a.N % 64 == 0) return launch_gemm_mx<EPI, 1>(a, tiles_m_bound, st);
   }
+  if (a.w_tiled) return fail(FP4_ERR_UNSUPPORTED, "tiled weights need the MX gate_up kernel (inter % 64 == 0)");
   return launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
 }
 
@@ -1519,8 +1572,10 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   a.a_scales = w.xq_scales;
   a.a_tensor_scale = x_ts;
   a.a_gather = 1;
-  a.w_codes = L->w13;
-  a.w_scales = L->w13_scale;
+  // the tiled copy of W13, when the layer has one, on the MX path that reads it
+  a.w_tiled = gk == GK_MX && L->w13_tiled ? 1 : 0;
+  a.w_codes = a.w_tiled ? L->w13_tiled : L->w13;
+  a.w_scales = a.w_tiled ? static_cast<const void*>(L->w13_scale_tiled) : L->w13_scale;
   a.w_tensor_scale = L->w13_scale_2;
   a.w_fp8 = 0;
   a.offsets = w.offsets;
@@ -1570,6 +1625,7 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   d.q_scales = nullptr;
   d.amax_part = nullptr;
   d.amax_nparts = 0;
+  d.w_tiled = 0;
   d.w_codes = L->w2;
   d.w_scales = L->w2_scale;
   d.w_tensor_scale = L->w2_scale_2;
@@ -1630,3 +1686,26 @@ int launch_shared_expert(const moe_fp4_layer* L, const uint16_t* x, int64_t T, c
 }
 
 }  // namespace fp4
+
+extern "C" int moe_fp4_tile_weights(int w_fmt, const uint8_t* codes, const uint8_t* scales, int64_t experts,
+                                    int64_t rows, int64_t cols, uint8_t* tiled_codes, uint8_t* tiled_scales,
+                                    void* stream) {
+  using namespace fp4;
+  if (w_fmt != FP4_FMT_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "tile_weights: MXFP4 weights only (got %d)", w_fmt);
+  if (experts < 0 || rows < 0 || cols < 0) return fail(FP4_ERR_SHAPE, "tile_weights: negative dimension");
+  if (rows % 16 || cols % 128)
+    return fail(FP4_ERR_SHAPE, "tile_weights: rows %lld must be a multiple of 16, cols %lld of 128", (long long)rows,
+                (long long)cols);
+  if (experts == 0 || rows == 0 || cols == 0) return FP4_OK;
+  if (!codes || !scales || !tiled_codes || !tiled_scales)
+    return fail(FP4_ERR_INVALID_ARG, "tile_weights: null pointer");
+  if (reinterpret_cast<uintptr_t>(codes) % 16 || reinterpret_cast<uintptr_t>(tiled_codes) % 16 ||
+      reinterpret_cast<uintptr_t>(scales) % 4 || reinterpret_cast<uintptr_t>(tiled_scales) % 4)
+    return fail(FP4_ERR_INVALID_ARG, "tile_weights: codes need 16-byte and scales 4-byte alignment");
+  const int64_t rows_total = experts * rows;
+  const int KS = (int)(cols / 128);
+  const int64_t n = rows_total * KS * 4;  // code chunks (at least the scale dwords)
+  hipLaunchKernelGGL(tile_weights_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, as_stream(stream), codes, scales,
+                     rows_total, KS, tiled_codes, tiled_scales);
+  return check_launch("tile_weights");
+}

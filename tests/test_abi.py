@@ -101,3 +101,25 @@ def test_moe_validation_and_workspace(L):
     assert L.moe_fp4_forward(ctypes.byref(s), fake, 64, fake, fake, fake, fake, 16, None) == -4
     # T == 0 is a no-op
     assert L.moe_fp4_forward(ctypes.byref(s), None, 0, None, None, None, None, 0, None) == 0
+
+
+def test_tile_weights_and_tiled_layer_validation(L):
+    fake, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1004)
+    # MXFP4 only; rows % 16 and cols % 128; null and misaligned pointers; empty is a no-op
+    assert L.moe_fp4_tile_weights(0, fake, fake, 2, 32, 256, fake, fake, None) == -3
+    assert L.moe_fp4_tile_weights(1, fake, fake, 2, 24, 256, fake, fake, None) == -2
+    assert L.moe_fp4_tile_weights(1, fake, fake, 2, 32, 192, fake, fake, None) == -2
+    assert L.moe_fp4_tile_weights(1, fake, None, 2, 32, 256, fake, fake, None) == -1
+    assert L.moe_fp4_tile_weights(1, odd, fake, 2, 32, 256, fake, fake, None) == -1
+    assert L.moe_fp4_tile_weights(1, None, None, 0, 32, 256, None, None, None) == 0
+    sz = ctypes.c_size_t()
+    # tiled W13: both pointers or neither, MXFP4 weights only
+    s = _layer(w_fmt=1, a_fmt=2)
+    assert L.moe_fp4_workspace_size(ctypes.byref(s), 64, ctypes.byref(sz)) == 0
+    s.w13_tiled = 0x2000
+    assert L.moe_fp4_workspace_size(ctypes.byref(s), 64, ctypes.byref(sz)) == -1
+    s.w13_scale_tiled = 0x3000
+    assert L.moe_fp4_workspace_size(ctypes.byref(s), 64, ctypes.byref(sz)) == 0
+    s = _layer(w_fmt=0, a_fmt=0)
+    s.w13_tiled, s.w13_scale_tiled = 0x2000, 0x3000
+    assert L.moe_fp4_workspace_size(ctypes.byref(s), 64, ctypes.byref(sz)) == -3

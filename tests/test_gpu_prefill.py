@@ -109,6 +109,44 @@ def _check_h_tensor_scale(ws, lay, h):
     assert sh == np.float32(np.float64(np.abs(h).max()) / 2688.0)
 
 
+def test_tile_weights_layout():
+    """moe_fp4_tile_weights only moves bytes: against the same rearrangement
+    done in numpy, on random bytes (codes [E][rows/16][K steps][16][64],
+    scales [E][rows/16][K steps][16][4])."""
+    import block_scaled_fp4_nvfp4_amd as m
+    print_case("tile_weights layout")
+    rng = np.random.default_rng(7)
+    E, rows, cols = 3, 48, 384
+    KS = cols // 128
+    codes = rng.integers(0, 256, (E, rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, (E, rows, cols // 32), dtype=np.uint8)
+    tc, ts = m.tile_weights(dev(codes), dev(scales))
+    torch.cuda.synchronize()
+    want_c = codes.reshape(E, rows // 16, 16, KS, 64).transpose(0, 1, 3, 2, 4).reshape(E, rows, cols // 2)
+    want_s = scales.reshape(E, rows // 16, 16, KS, 4).transpose(0, 1, 3, 2, 4).reshape(E, rows, cols // 32)
+    np.testing.assert_array_equal(host(tc), want_c)
+    np.testing.assert_array_equal(host(ts), want_s)
+
+
+def _same_bits(a, b):
+    return np.array_equal(np.asarray(a, np.float32).view(np.uint32), np.asarray(b, np.float32).view(np.uint32))
+
+
+def test_tiny_tiled_w13_bit_identical(tiny):
+    """MXFP4 x MXFP8 with the tiled copy of W13: the gate_up GEMM reads the
+    same bytes in another order and computes the same sums, so y is
+    bit-identical to the row-major layer's."""
+    import block_scaled_fp4_nvfp4_amd as m
+    print_case("tiny MXFP4 x MXFP8, tiled W13")
+    cfg, w13, w2, x, ids, wts = tiny
+    cfg = cfg.replace(w_fmt="mxfp4", a_fmt="mxfp8")
+    layer = gpu_layer(cfg, w13, w2)
+    y0, _, _ = _run(layer, x, ids, wts)
+    layer.w13_tiled, layer.w13_scale_tiled = m.tile_weights(layer.w13, layer.w13_scale)
+    y1, _, _ = _run(layer, x, ids, wts)
+    assert _same_bits(y0, y1)
+
+
 def test_tiny_w4a4_static_scales(tiny):
     """Static input_scale / intermediate scale (calibrated export, Local-Hessian card)."""
     print_case("tiny W4A4 static scales")
@@ -223,7 +261,8 @@ def test_prefill_full_size_sampled(prefill_weights, name):
     w13, w2 = prefill_weights  # same bf16 source weights (shared seed)
     x = synth.activations(cfg)
     ids, wts = synth.routing(cfg)
-    y, ws, lay = _run(gpu_layer(cfg, w13, w2), x, ids, wts)
+    layer = gpu_layer(cfg, w13, w2)
+    y, ws, lay = _run(layer, x, ids, wts)
     sample = [0, 4095, 8191]
     y_ref, st = moe.moe_forward(OracleLayer(cfg, w13, w2).as_dict(), x, ids, wts, sample_tokens=sample,
                                 return_stages=True)
@@ -236,3 +275,9 @@ def test_prefill_full_size_sampled(prefill_weights, name):
         pairs = np.concatenate([np.arange(t * k, (t + 1) * k) for t in sample])
         _, _, rop = moe.permute(ids, cfg.num_experts)
         _check_mxfp8_h(ws, lay, cfg.pairs, cfg.inter, rop[pairs], st["hrec"], st["h"][pairs])
+        # the tiled copy of W13 (the benchmark's prefill layer): the whole y bit-identical
+        import block_scaled_fp4_nvfp4_amd as m
+        layer.w13_tiled, layer.w13_scale_tiled = m.tile_weights(layer.w13, layer.w13_scale)
+        del ws
+        y1, _, _ = _run(layer, x, ids, wts)
+        assert _same_bits(y, y1)
