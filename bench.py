@@ -270,10 +270,11 @@ def bench_prefill(name, args, torch, pkg):
     layers = [make_layer(cfg, q13, q2, pkg, shared)]
     for _ in range(max(0, args.prefill_copies - 1)):
         layers.append(make_layer(cfg, clone_q(q13), clone_q(q2), pkg, shared))
-    tiled = cfg.w_fmt == "mxfp4" and args.w13_layout == "tiled"
+    tiled = cfg.w_fmt == "mxfp4" and args.weight_layout == "tiled"
     if tiled:  # once per layer, like its quantization: outside the timed region
         for layer in layers:
             layer.w13_tiled, layer.w13_scale_tiled = pkg.tile_weights(layer.w13, layer.w13_scale)
+            layer.w2_tiled, layer.w2_scale_tiled = pkg.tile_weights(layer.w2, layer.w2_scale)
         torch.cuda.synchronize()
     x_bits = synth.activations(cfg)
     ids, wts = synth.routing(cfg)
@@ -304,7 +305,7 @@ def bench_prefill(name, args, torch, pkg):
     out = {"workload": f"{cfg.name}: {cfg.num_experts} experts, top-{cfg.top_k}, hidden {H}, inter {I}, "
                        f"{T} tokens, {cfg.w_fmt} weights x {cfg.a_fmt} activations"
                        + (f", MXFP8 shared expert {cfg.shared_inter}" if cfg.shared_inter else "")
-                       + (", W13 tiled for the gate_up GEMM" if tiled else ""),
+                       + (", W13 and W2 tiled for the GEMMs" if tiled else ""),
            "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "steps": args.prefill_steps,
            "dtype": {"nvfp4": "fp16", "mxfp8": "fp8", "fp8_row": "fp8"}[cfg.a_fmt],
            "roofline": roof, "stages_ms": stages,
@@ -610,8 +611,8 @@ def main():
                          "'copy': a plain 1 GiB device copy that calibrates the HBM byte counters")
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-copies", type=int, default=2)
-    ap.add_argument("--w13-layout", choices=["tiled", "rows"], default="tiled",
-                    help="MXFP4 prefill: gate_up weights in the tiled order of moe_fp4_tile_weights "
+    ap.add_argument("--weight-layout", choices=["tiled", "rows"], default="tiled",
+                    help="MXFP4 prefill: expert weights in the tiled order of moe_fp4_tile_weights "
                          "(made once per layer) or row-major")
     ap.add_argument("--stream-layers", type=int, default=48)
     ap.add_argument("--stack-layers", type=int, default=48)

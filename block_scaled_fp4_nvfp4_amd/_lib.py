@@ -47,6 +47,7 @@ class LayerStruct(ctypes.Structure):
         ("ws2", ctypes.c_void_p), ("ws2_scale", ctypes.c_void_p),
         ("shared_gate", ctypes.c_void_p),
         ("w13_tiled", ctypes.c_void_p), ("w13_scale_tiled", ctypes.c_void_p),
+        ("w2_tiled", ctypes.c_void_p), ("w2_scale_tiled", ctypes.c_void_p),
     ]
 
 
@@ -176,7 +177,7 @@ def tile_weights(codes: torch.Tensor, scales: torch.Tensor, fmt: str = "mxfp4"):
     """moe_fp4_tile_weights.  codes uint8 [E, rows, cols/2], scales uint8
     [E, rows, cols/32] (MXFP4, contiguous, on the device).  Returns the tiled
     (codes, scales), same shapes and dtypes, for MoELayer.w13_tiled /
-    w13_scale_tiled."""
+    w13_scale_tiled (or w2_tiled / w2_scale_tiled)."""
     assert codes.is_cuda and codes.is_contiguous() and scales.is_contiguous() and codes.dim() == 3
     E, rows, half = (int(v) for v in codes.shape)
     tc, ts = torch.empty_like(codes), torch.empty_like(scales)
@@ -220,6 +221,8 @@ class MoELayer:
     shared_gate: Optional[torch.Tensor] = None
     w13_tiled: Optional[torch.Tensor] = None
     w13_scale_tiled: Optional[torch.Tensor] = None
+    w2_tiled: Optional[torch.Tensor] = None
+    w2_scale_tiled: Optional[torch.Tensor] = None
 
     def struct(self) -> LayerStruct:
         p = lambda t: None if t is None else t.data_ptr()
@@ -229,7 +232,7 @@ class MoELayer:
             p(self.w2), p(self.w2_scale), p(self.w2_scale_2),
             p(self.input_scale), p(self.inter_scale), self.shared_inter,
             p(self.ws13), p(self.ws13_scale), p(self.ws2), p(self.ws2_scale), p(self.shared_gate),
-            p(self.w13_tiled), p(self.w13_scale_tiled))
+            p(self.w13_tiled), p(self.w13_scale_tiled), p(self.w2_tiled), p(self.w2_scale_tiled))
 
 
 def workspace_layout(layer: MoELayer, tokens: int) -> dict:

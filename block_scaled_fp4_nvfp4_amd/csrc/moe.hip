@@ -894,10 +894,13 @@ static int validate_layer(const moe_fp4_layer* L, int64_t T) {
   if (L->shared_inter < 0) return fail(FP4_ERR_SHAPE, "negative shared width");
   if (L->shared_inter > 0 && (L->shared_inter % 128 || L->hidden % 128))
     return fail(FP4_ERR_SHAPE, "shared width and hidden must be multiples of 128");
-  if ((L->w13_tiled != nullptr) != (L->w13_scale_tiled != nullptr))
-    return fail(FP4_ERR_INVALID_ARG, "w13_tiled and w13_scale_tiled go together");
-  if (L->w13_tiled && w != FP4_FMT_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "tiled W13 is MXFP4 only");
-  if (L->w13_tiled && L->hidden % 128) return fail(FP4_ERR_SHAPE, "tiled W13 needs hidden % 128 == 0");
+  if ((L->w13_tiled != nullptr) != (L->w13_scale_tiled != nullptr) ||
+      (L->w2_tiled != nullptr) != (L->w2_scale_tiled != nullptr))
+    return fail(FP4_ERR_INVALID_ARG, "a tiled weight tensor and its tiled scales go together");
+  if ((L->w13_tiled || L->w2_tiled) && w != FP4_FMT_MXFP4)
+    return fail(FP4_ERR_UNSUPPORTED, "tiled weights are MXFP4 only");
+  if ((L->w13_tiled && L->hidden % 128) || (L->w2_tiled && L->inter % 128))
+    return fail(FP4_ERR_SHAPE, "tiled weights need a reduction size that is a multiple of 128");
   return FP4_OK;
 }
 

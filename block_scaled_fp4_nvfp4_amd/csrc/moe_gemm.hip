@@ -874,9 +874,10 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(N));
 }
 
-template <int GK, int EPI, int NSUB, int KS>
+template <int GK, int EPI, int NSUB, int KS, bool WT>
 __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   static_assert(GK == GK_MX || GK == GK_FP8, "MX or block-FP8 operands");
+  static_assert(!WT || GK == GK_MX, "tiled weights are MXFP4");
   using C = Mx2Cfg<GK, EPI, NSUB, KS>;
   constexpr int BM = C::BM, BN = C::BN, NU = C::NU, NS = C::NS, RS = C::RS, D = C::D;
   static_assert(RS <= 8, "ring of at most 8 stages");
@@ -938,7 +939,11 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   constexpr int SKB = K / 32;  // scale bytes per row
   const int NW = NU * g.N;
   constexpr int W_ROW = GK == GK_FP8 ? K : K / 2;      // weight bytes per row
-  constexpr int W_STEP = GK == GK_FP8 ? 128 : 64;      // weight bytes per row and step
+  // what one K step adds to a lane's weight address and (MX) scale address:
+  // row-major, the next 64 (FP8: 128) bytes of the row and its next scale
+  // dword; tiled (moe_fp4_tile_weights), the next kilobyte / 64 bytes
+  constexpr int W_STEP = WT ? 1024 : (GK == GK_FP8 ? 128 : 64);
+  constexpr int WS_STEP = WT ? 64 : 4;
   const uint8_t* w_base = g.w_codes + (int64_t)e * NW * W_ROW;
   const uint8_t* ws_base = reinterpret_cast<const uint8_t*>(g.w_scales);
 
@@ -965,9 +970,15 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int wr = (s / NSUB) * BN + wave * 16 * NSUB + (s % NSUB) * 16 + lr;
-    w_src[s] = w_base + (int64_t)w_grow(wr) * W_ROW + 16 * lg;
+    const int gr = w_grow(wr);
+    if constexpr (WT) {  // 16 consecutive rows (gr % 16 == lr): one kilobyte per K step
+      w_src[s] = w_base + (int64_t)(gr >> 4) * (KS * 1024) + (gr & 15) * 64 + 16 * lg;
+      ws_src[s] = ws_base + (int64_t)e * NW * SKB + (int64_t)(gr >> 4) * (KS * 64) + (gr & 15) * 4;
+      continue;
+    }
+    w_src[s] = w_base + (int64_t)gr * W_ROW + 16 * lg;
     if (GK == GK_MX)  // the step's 4 UE8M0 block scales of the row as one dword
-      ws_src[s] = ws_base + ((int64_t)e * NW + w_grow(wr)) * SKB;
+      ws_src[s] = ws_base + ((int64_t)e * NW + gr) * SKB;
     else  // the f32 scale of the row's 128 x 128 block
       ws_src[s] = ws_base + (((int64_t)e * (NW / 128) + w_grow(wr) / 128) * KS) * 4;
   }
@@ -984,7 +995,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
     for (int s = 0; s < NS; ++s) {
       q[s][0] = ld16(w_src[s] + W_STEP * ks);
       if constexpr (GK == GK_FP8) q[s][C::W_LD - 1] = ld16(w_src[s] + W_STEP * ks + 64);
-      sc[s] = (int)*reinterpret_cast<const uint32_t*>(ws_src[s] + 4 * ks);  // MX: byte lg is this lane's
+      sc[s] = (int)*reinterpret_cast<const uint32_t*>(ws_src[s] + WS_STEP * ks);  // MX: byte lg is this lane's
     }
   };
 
@@ -1385,6 +1396,10 @@ __global__ void __launch_bounds__(256) tile_weights_kernel(const uint8_t* __rest
   }
 }
 
+// The MX down projection runs on the register-fed kernel (which can read
+// tiled weights) for 128-multiple outputs over the model's inter of 640.
+static bool mx_down_on_mx2(int N, int K) { return N % 128 == 0 && K == 640; }
+
 // Workgroups of a grouped GEMM launch: M-tile bound x output tiles, rounded
 // up to a multiple of the 8 XCDs (the tile remapping needs whole rounds).
 static int64_t gemm_grid(int64_t tiles_m_bound, int N, int BN) {
@@ -1446,8 +1461,8 @@ static int launch_gemm_n(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t s
   return check_launch("grouped_gemm");
 }
 
-template <int GK, int EPI, int NSUB, int KS>
-static int launch_gemm_mx2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+template <int GK, int EPI, int NSUB, int KS, bool WT>
+static int launch_gemm_mx2_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   using C = Mx2Cfg<GK, EPI, NSUB, KS>;
   const int NT = a.N / C::BN;
   int64_t G = tiles_m_bound * NT;
@@ -1459,13 +1474,23 @@ static int launch_gemm_mx2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t
   if (fixed + lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS, WT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)(160 * 1024 - fixed)) != hipSuccess)
       return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
     attr_set = true;
   }
-  hipLaunchKernelGGL((grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS>), dim3((unsigned)G), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS, WT>), dim3((unsigned)G), dim3(256), lds, st, a);
   return check_launch("grouped_gemm_mx2");
+}
+
+template <int GK, int EPI, int NSUB, int KS>
+static int launch_gemm_mx2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+  if constexpr (GK == GK_MX) {
+    if (a.w_tiled) return launch_gemm_mx2_t<GK, EPI, NSUB, KS, true>(a, tiles_m_bound, st);
+  } else {
+    if (a.w_tiled) return fail(FP4_ERR_UNSUPPORTED, "tiled weights are MXFP4 only");
+  }
+  return launch_gemm_mx2_t<GK, EPI, NSUB, KS, false>(a, tiles_m_bound, st);
 }
 
 template <int EPI, int NSUB, bool WT>
@@ -1535,14 +1560,14 @@ static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st)
   // its K loop unrolled (measured faster than either staging kernel there;
   // over K = 2560 the all-DMA kernel is faster)
   if constexpr (EPI == EPI_DOWN) {
-    if (a.N % 128 == 0 && a.K == 640) return launch_gemm_mx2<GK_MX, EPI, 2, 5>(a, tiles_m_bound, st);
+    if (mx_down_on_mx2(a.N, a.K)) return launch_gemm_mx2<GK_MX, EPI, 2, 5>(a, tiles_m_bound, st);
   }
   if constexpr (EPI == EPI_GATEUP) {
     if (a.N % 128 == 0) return launch_gemm_mx<EPI, 2>(a, tiles_m_bound, st);
     if (a.q_codes) return fail(FP4_ERR_UNSUPPORTED, "MXFP8 h epilogue needs 128-output gate_up tiles");
     if (a.N % 64 == 0) return launch_gemm_mx<EPI, 1>(a, tiles_m_bound, st);
   }
-  if (a.w_tiled) return fail(FP4_ERR_UNSUPPORTED, "tiled weights need the MX gate_up kernel (inter % 64 == 0)");
+  if (a.w_tiled) return fail(FP4_ERR_UNSUPPORTED, "tiled weights on a GEMM kernel that reads rows");
   return launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
 }
 
@@ -1625,9 +1650,10 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   d.q_scales = nullptr;
   d.amax_part = nullptr;
   d.amax_nparts = 0;
-  d.w_tiled = 0;
-  d.w_codes = L->w2;
-  d.w_scales = L->w2_scale;
+  // the tiled copy of W2 where the down kernel that reads it runs
+  d.w_tiled = gk == GK_MX && L->w2_tiled && mx_down_on_mx2(H, I) ? 1 : 0;
+  d.w_codes = d.w_tiled ? L->w2_tiled : L->w2;
+  d.w_scales = d.w_tiled ? static_cast<const void*>(L->w2_scale_tiled) : L->w2_scale;
   d.w_tensor_scale = L->w2_scale_2;
   d.K = I;
   d.N = H;

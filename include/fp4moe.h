@@ -158,12 +158,17 @@ typedef struct {
   const uint8_t* ws2;       /* MXFP8 codes [H, Si] */
   const uint8_t* ws2_scale; /* UE8M0 [H, Si/32] */
   const uint16_t* shared_gate; /* bf16 [H] */
-  /* Optional (may be NULL), MXFP4 weights only: W13 and its scales in the
-   * tiled order of moe_fp4_tile_weights.  When set, the grouped gate_up GEMM
-   * (the (MXFP4, MXFP8) prefill path) reads these instead of w13 / w13_scale;
-   * the decode GEMVs still read w13 / w13_scale, which stay required. */
+  /* Optional (may be NULL), MXFP4 weights only: W13 / W2 and their scales in
+   * the tiled order of moe_fp4_tile_weights.  When set, the grouped GEMMs of
+   * the (MXFP4, MXFP8) prefill path read these instead of w13 / w13_scale
+   * and w2 / w2_scale where their kernels take that order (gate_up: always;
+   * down: inter = 640, the model's width) and the row-major tensors
+   * elsewhere; the decode GEMVs read the row-major tensors, which stay
+   * required.  Each pair goes together. */
   const uint8_t* w13_tiled;
   const uint8_t* w13_scale_tiled;
+  const uint8_t* w2_tiled;
+  const uint8_t* w2_scale_tiled;
 } moe_fp4_layer;
 
 /* Byte offsets of the stage buffers inside the forward's workspace, for
@@ -229,7 +234,7 @@ int moe_fp4_route(const float* logits, const float* bias, int64_t tokens, int nu
 /*
  * moe_fp4_tile_weights - copy of stacked MXFP4 expert weights (codes
  * [E, rows, cols/2] and UE8M0 scales [E, rows, cols/32], the layout of
- * fp4_quantize) into the order the grouped gate_up GEMM streams them: per
+ * fp4_quantize) into the order the grouped MX GEMMs stream them: per
  * expert, per group of 16 rows, per 128-wide K step, the 16 rows' 64 code
  * bytes (one kilobyte) and, separately, their 4 scale bytes (64 bytes):
  *   tiled_codes [E][rows/16][cols/128][16][64]
@@ -238,7 +243,8 @@ int moe_fp4_route(const float* logits, const float* bias, int64_t tokens, int nu
  * one contiguous kilobyte instead of sixteen 64-byte pieces of different
  * rows.  Done once when a layer is loaded; the output buffers (same sizes as
  * the inputs, device memory, caller-owned) go in moe_fp4_layer.w13_tiled /
- * w13_scale_tiled.  Errors: w_fmt other than MXFP4 -> FP4_ERR_UNSUPPORTED;
+ * w13_scale_tiled (or w2_tiled / w2_scale_tiled).  Errors: w_fmt other than
+ * MXFP4 -> FP4_ERR_UNSUPPORTED;
  * rows % 16 or cols % 128 -> FP4_ERR_SHAPE; null pointer ->
  * FP4_ERR_INVALID_ARG.  Stream-ordered, asynchronous.
  */

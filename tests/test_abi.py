@@ -120,6 +120,10 @@ def test_tile_weights_and_tiled_layer_validation(L):
     assert L.moe_fp4_workspace_size(ctypes.byref(s), 64, ctypes.byref(sz)) == -1
     s.w13_scale_tiled = 0x3000
     assert L.moe_fp4_workspace_size(ctypes.byref(s), 64, ctypes.byref(sz)) == 0
+    s.w2_scale_tiled = 0x4000
+    assert L.moe_fp4_workspace_size(ctypes.byref(s), 64, ctypes.byref(sz)) == -1
+    s.w2_tiled = 0x5000
+    assert L.moe_fp4_workspace_size(ctypes.byref(s), 64, ctypes.byref(sz)) == 0
     s = _layer(w_fmt=0, a_fmt=0)
     s.w13_tiled, s.w13_scale_tiled = 0x2000, 0x3000
     assert L.moe_fp4_workspace_size(ctypes.byref(s), 64, ctypes.byref(sz)) == -3

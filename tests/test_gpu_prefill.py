@@ -132,17 +132,23 @@ def _same_bits(a, b):
     return np.array_equal(np.asarray(a, np.float32).view(np.uint32), np.asarray(b, np.float32).view(np.uint32))
 
 
-def test_tiny_tiled_w13_bit_identical(tiny):
-    """MXFP4 x MXFP8 with the tiled copy of W13: the gate_up GEMM reads the
-    same bytes in another order and computes the same sums, so y is
-    bit-identical to the row-major layer's."""
+def _tile(layer):
     import block_scaled_fp4_nvfp4_amd as m
-    print_case("tiny MXFP4 x MXFP8, tiled W13")
+    layer.w13_tiled, layer.w13_scale_tiled = m.tile_weights(layer.w13, layer.w13_scale)
+    layer.w2_tiled, layer.w2_scale_tiled = m.tile_weights(layer.w2, layer.w2_scale)
+
+
+def test_tiny_tiled_weights_bit_identical(tiny):
+    """MXFP4 x MXFP8 with tiled copies of W13 and W2: the gate_up GEMM reads
+    the same bytes in another order and computes the same sums, so y is
+    bit-identical to the row-major layer's (at this inter of 128 the down
+    GEMM keeps reading row-major W2)."""
+    print_case("tiny MXFP4 x MXFP8, tiled weights")
     cfg, w13, w2, x, ids, wts = tiny
     cfg = cfg.replace(w_fmt="mxfp4", a_fmt="mxfp8")
     layer = gpu_layer(cfg, w13, w2)
     y0, _, _ = _run(layer, x, ids, wts)
-    layer.w13_tiled, layer.w13_scale_tiled = m.tile_weights(layer.w13, layer.w13_scale)
+    _tile(layer)
     y1, _, _ = _run(layer, x, ids, wts)
     assert _same_bits(y0, y1)
 
@@ -275,9 +281,9 @@ def test_prefill_full_size_sampled(prefill_weights, name):
         pairs = np.concatenate([np.arange(t * k, (t + 1) * k) for t in sample])
         _, _, rop = moe.permute(ids, cfg.num_experts)
         _check_mxfp8_h(ws, lay, cfg.pairs, cfg.inter, rop[pairs], st["hrec"], st["h"][pairs])
-        # the tiled copy of W13 (the benchmark's prefill layer): the whole y bit-identical
-        import block_scaled_fp4_nvfp4_amd as m
-        layer.w13_tiled, layer.w13_scale_tiled = m.tile_weights(layer.w13, layer.w13_scale)
+        # tiled copies of W13 and W2 (the benchmark's prefill layer; both
+        # GEMMs read them at inter 640): the whole y bit-identical
+        _tile(layer)
         del ws
         y1, _, _ = _run(layer, x, ids, wts)
         assert _same_bits(y, y1)
