@@ -877,7 +877,6 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
 template <int GK, int EPI, int NSUB, int KS, bool WT>
 __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   static_assert(GK == GK_MX || GK == GK_FP8, "MX or block-FP8 operands");
-  static_assert(!WT || GK == GK_MX, "tiled weights are MXFP4");
   using C = Mx2Cfg<GK, EPI, NSUB, KS>;
   constexpr int BM = C::BM, BN = C::BN, NU = C::NU, NS = C::NS, RS = C::RS, D = C::D;
   static_assert(RS <= 8, "ring of at most 8 stages");
@@ -939,11 +938,14 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   constexpr int SKB = K / 32;  // scale bytes per row
   const int NW = NU * g.N;
   constexpr int W_ROW = GK == GK_FP8 ? K : K / 2;      // weight bytes per row
-  // what one K step adds to a lane's weight address and (MX) scale address:
-  // row-major, the next 64 (FP8: 128) bytes of the row and its next scale
-  // dword; tiled (moe_fp4_tile_weights), the next kilobyte / 64 bytes
-  constexpr int W_STEP = WT ? 1024 : (GK == GK_FP8 ? 128 : 64);
-  constexpr int WS_STEP = WT ? 64 : 4;
+  // A row holds PH 64-byte pieces per K step.  What one K step adds to a
+  // lane's weight address and (MX) scale address: row-major, the row's next
+  // PH pieces and its next scale dword; tiled (moe_fp4_tile_weights), the
+  // next PH kilobytes and 64 bytes.  W_HALF: offset of a row's second piece.
+  constexpr int PH = GK == GK_FP8 ? 2 : 1;
+  constexpr int W_STEP = WT ? PH * 1024 : PH * 64;
+  constexpr int W_HALF = WT ? 1024 : 64;
+  constexpr int WS_STEP = WT && GK == GK_MX ? 64 : 4;
   const uint8_t* w_base = g.w_codes + (int64_t)e * NW * W_ROW;
   const uint8_t* ws_base = reinterpret_cast<const uint8_t*>(g.w_scales);
 
@@ -971,13 +973,13 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   for (int s = 0; s < NS; ++s) {
     const int wr = (s / NSUB) * BN + wave * 16 * NSUB + (s % NSUB) * 16 + lr;
     const int gr = w_grow(wr);
-    if constexpr (WT) {  // 16 consecutive rows (gr % 16 == lr): one kilobyte per K step
-      w_src[s] = w_base + (int64_t)(gr >> 4) * (KS * 1024) + (gr & 15) * 64 + 16 * lg;
+    if constexpr (WT)  // 16 consecutive rows (gr % 16 == lr): PH kilobytes per K step
+      w_src[s] = w_base + (int64_t)(gr >> 4) * (KS * PH * 1024) + (gr & 15) * 64 + 16 * lg;
+    else
+      w_src[s] = w_base + (int64_t)gr * W_ROW + 16 * lg;
+    if (GK == GK_MX && WT)
       ws_src[s] = ws_base + (int64_t)e * NW * SKB + (int64_t)(gr >> 4) * (KS * 64) + (gr & 15) * 4;
-      continue;
-    }
-    w_src[s] = w_base + (int64_t)gr * W_ROW + 16 * lg;
-    if (GK == GK_MX)  // the step's 4 UE8M0 block scales of the row as one dword
+    else if (GK == GK_MX)  // the step's 4 UE8M0 block scales of the row as one dword
       ws_src[s] = ws_base + ((int64_t)e * NW + gr) * SKB;
     else  // the f32 scale of the row's 128 x 128 block
       ws_src[s] = ws_base + (((int64_t)e * (NW / 128) + w_grow(wr) / 128) * KS) * 4;
@@ -994,7 +996,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       q[s][0] = ld16(w_src[s] + W_STEP * ks);
-      if constexpr (GK == GK_FP8) q[s][C::W_LD - 1] = ld16(w_src[s] + W_STEP * ks + 64);
+      if constexpr (GK == GK_FP8) q[s][C::W_LD - 1] = ld16(w_src[s] + W_STEP * ks + W_HALF);
       sc[s] = (int)*reinterpret_cast<const uint32_t*>(ws_src[s] + WS_STEP * ks);  // MX: byte lg is this lane's
     }
   };
@@ -1375,20 +1377,23 @@ static int launch_gemm_nv2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t
 
 // Tiled order of moe_fp4_tile_weights.  The E stacked [rows, cols] tensors
 // are one run of E * rows rows (rows % 16 == 0, so no 16-row group straddles
-// two experts); thread i copies 16-byte code chunk i and scale dword i.
+// two experts).  A row holds PH 64-byte pieces per 128-wide K step (MXFP4 1,
+// E4M3 2); piece h of the 16 rows of a group is one kilobyte.  Thread i
+// copies 16-byte code chunk i and (MX) scale dword i.
 __global__ void __launch_bounds__(256) tile_weights_kernel(const uint8_t* __restrict__ codes,
                                                            const uint8_t* __restrict__ scales,
-                                                           int64_t rows_total, int KS,
+                                                           int64_t rows_total, int KS, int PH,
                                                            uint8_t* __restrict__ tiled_codes,
                                                            uint8_t* __restrict__ tiled_scales) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < rows_total * KS * 4) {  // code chunks: row r, K step ks, 16-byte piece u of its 64 bytes
-    const int64_t r = i / (KS * 4);
-    const int c = (int)(i - r * KS * 4), ks = c >> 2, u = c & 3;
-    const int64_t dst = (r >> 4) * ((int64_t)KS * 1024) + ks * 1024 + (r & 15) * 64 + u * 16;
+  const int cpr = KS * PH * 4;  // 16-byte chunks per row
+  if (i < rows_total * cpr) {   // code chunks: row r, K step ks, piece h, 16 bytes u of its 64
+    const int64_t r = i / cpr;
+    const int c = (int)(i - r * cpr), ks = c / (PH * 4), h = (c >> 2) % PH, u = c & 3;
+    const int64_t dst = (r >> 4) * ((int64_t)KS * PH * 1024) + (ks * PH + h) * 1024 + (r & 15) * 64 + u * 16;
     *reinterpret_cast<uint4*>(tiled_codes + dst) = *reinterpret_cast<const uint4*>(codes + i * 16);
   }
-  if (i < rows_total * KS) {  // scale dwords: row r, K step ks
+  if (tiled_scales && i < rows_total * KS) {  // MX scale dwords: row r, K step ks
     const int64_t r = i / KS;
     const int ks = (int)(i - r * KS);
     const int64_t dst = (r >> 4) * ((int64_t)KS * 64) + ks * 64 + (r & 15) * 4;
@@ -1396,9 +1401,11 @@ __global__ void __launch_bounds__(256) tile_weights_kernel(const uint8_t* __rest
   }
 }
 
-// The MX down projection runs on the register-fed kernel (which can read
-// tiled weights) for 128-multiple outputs over the model's inter of 640.
+// Where the register-fed kernel (which can read tiled weights) runs: the MX
+// and block-FP8 down projections for 128-multiple outputs over the model's
+// inter of 640, and the block-FP8 gate_up over its hidden of 2560.
 static bool mx_down_on_mx2(int N, int K) { return N % 128 == 0 && K == 640; }
+static bool fp8_gateup_on_mx2(int N, int K) { return N % 64 == 0 && K == 2560; }
 
 // Workgroups of a grouped GEMM launch: M-tile bound x output tiles, rounded
 // up to a multiple of the 8 XCDs (the tile remapping needs whole rounds).
@@ -1485,12 +1492,8 @@ static int launch_gemm_mx2_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream
 
 template <int GK, int EPI, int NSUB, int KS>
 static int launch_gemm_mx2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
-  if constexpr (GK == GK_MX) {
-    if (a.w_tiled) return launch_gemm_mx2_t<GK, EPI, NSUB, KS, true>(a, tiles_m_bound, st);
-  } else {
-    if (a.w_tiled) return fail(FP4_ERR_UNSUPPORTED, "tiled weights are MXFP4 only");
-  }
-  return launch_gemm_mx2_t<GK, EPI, NSUB, KS, false>(a, tiles_m_bound, st);
+  return a.w_tiled ? launch_gemm_mx2_t<GK, EPI, NSUB, KS, true>(a, tiles_m_bound, st)
+                   : launch_gemm_mx2_t<GK, EPI, NSUB, KS, false>(a, tiles_m_bound, st);
 }
 
 template <int EPI, int NSUB, bool WT>
@@ -1544,10 +1547,11 @@ static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st)
     // the model's reduction sizes on the register-fed kernel (gate_up with
     // 64-output tiles: 128-output ones spill)
     if constexpr (EPI == EPI_DOWN) {
-      if (a.N % 128 == 0 && a.K == 640) return launch_gemm_mx2<GK_FP8, EPI, 2, 5>(a, tiles_m_bound, st);
+      if (mx_down_on_mx2(a.N, a.K)) return launch_gemm_mx2<GK_FP8, EPI, 2, 5>(a, tiles_m_bound, st);
     } else {
-      if (a.N % 64 == 0 && a.K == 2560) return launch_gemm_mx2<GK_FP8, EPI, 1, 20>(a, tiles_m_bound, st);
+      if (fp8_gateup_on_mx2(a.N, a.K)) return launch_gemm_mx2<GK_FP8, EPI, 1, 20>(a, tiles_m_bound, st);
     }
+    if (a.w_tiled) return fail(FP4_ERR_UNSUPPORTED, "tiled weights on a GEMM kernel that reads rows");
     // FP8 weight tiles are twice the bytes: 64-output gate_up tiles keep two
     // workgroups per CU in LDS and measure faster; the down tiles do not
     if (EPI == EPI_GATEUP && a.N % 64 == 0) return launch_gemm_n<GK, EPI, 1, true>(a, tiles_m_bound, st);
@@ -1597,10 +1601,11 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   a.a_scales = w.xq_scales;
   a.a_tensor_scale = x_ts;
   a.a_gather = 1;
-  // the tiled copy of W13, when the layer has one, on the MX path that reads it
-  a.w_tiled = gk == GK_MX && L->w13_tiled ? 1 : 0;
+  // the tiled copy of W13, when the layer has one, where the gate_up kernel
+  // reads it (block FP8: codes only, its block scales stay as they are)
+  a.w_tiled = L->w13_tiled && (gk == GK_MX || (gk == GK_FP8 && fp8_gateup_on_mx2(I, H))) ? 1 : 0;
   a.w_codes = a.w_tiled ? L->w13_tiled : L->w13;
-  a.w_scales = a.w_tiled ? static_cast<const void*>(L->w13_scale_tiled) : L->w13_scale;
+  a.w_scales = a.w_tiled && gk == GK_MX ? static_cast<const void*>(L->w13_scale_tiled) : L->w13_scale;
   a.w_tensor_scale = L->w13_scale_2;
   a.w_fp8 = 0;
   a.offsets = w.offsets;
@@ -1651,9 +1656,9 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   d.amax_part = nullptr;
   d.amax_nparts = 0;
   // the tiled copy of W2 where the down kernel that reads it runs
-  d.w_tiled = gk == GK_MX && L->w2_tiled && mx_down_on_mx2(H, I) ? 1 : 0;
+  d.w_tiled = L->w2_tiled && (gk == GK_MX || gk == GK_FP8) && mx_down_on_mx2(H, I) ? 1 : 0;
   d.w_codes = d.w_tiled ? L->w2_tiled : L->w2;
-  d.w_scales = d.w_tiled ? static_cast<const void*>(L->w2_scale_tiled) : L->w2_scale;
+  d.w_scales = d.w_tiled && gk == GK_MX ? static_cast<const void*>(L->w2_scale_tiled) : L->w2_scale;
   d.w_tensor_scale = L->w2_scale_2;
   d.K = I;
   d.N = H;
@@ -1717,21 +1722,23 @@ extern "C" int moe_fp4_tile_weights(int w_fmt, const uint8_t* codes, const uint8
                                     int64_t rows, int64_t cols, uint8_t* tiled_codes, uint8_t* tiled_scales,
                                     void* stream) {
   using namespace fp4;
-  if (w_fmt != FP4_FMT_MXFP4) return fail(FP4_ERR_UNSUPPORTED, "tile_weights: MXFP4 weights only (got %d)", w_fmt);
+  if (w_fmt != FP4_FMT_MXFP4 && w_fmt != FP4_FMT_FP8_BLOCK)
+    return fail(FP4_ERR_UNSUPPORTED, "tile_weights: MXFP4 or block-FP8 weights only (got %d)", w_fmt);
+  const bool mx = w_fmt == FP4_FMT_MXFP4;
   if (experts < 0 || rows < 0 || cols < 0) return fail(FP4_ERR_SHAPE, "tile_weights: negative dimension");
   if (rows % 16 || cols % 128)
     return fail(FP4_ERR_SHAPE, "tile_weights: rows %lld must be a multiple of 16, cols %lld of 128", (long long)rows,
                 (long long)cols);
   if (experts == 0 || rows == 0 || cols == 0) return FP4_OK;
-  if (!codes || !scales || !tiled_codes || !tiled_scales)
+  if (!codes || !tiled_codes || (mx && (!scales || !tiled_scales)))
     return fail(FP4_ERR_INVALID_ARG, "tile_weights: null pointer");
   if (reinterpret_cast<uintptr_t>(codes) % 16 || reinterpret_cast<uintptr_t>(tiled_codes) % 16 ||
-      reinterpret_cast<uintptr_t>(scales) % 4 || reinterpret_cast<uintptr_t>(tiled_scales) % 4)
+      (mx && (reinterpret_cast<uintptr_t>(scales) % 4 || reinterpret_cast<uintptr_t>(tiled_scales) % 4)))
     return fail(FP4_ERR_INVALID_ARG, "tile_weights: codes need 16-byte and scales 4-byte alignment");
   const int64_t rows_total = experts * rows;
-  const int KS = (int)(cols / 128);
-  const int64_t n = rows_total * KS * 4;  // code chunks (at least the scale dwords)
-  hipLaunchKernelGGL(tile_weights_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, as_stream(stream), codes, scales,
-                     rows_total, KS, tiled_codes, tiled_scales);
+  const int KS = (int)(cols / 128), PH = mx ? 1 : 2;
+  const int64_t n = rows_total * KS * PH * 4;  // code chunks (at least the scale dwords)
+  hipLaunchKernelGGL(tile_weights_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, as_stream(stream), codes,
+                     mx ? scales : nullptr, rows_total, KS, PH, tiled_codes, mx ? tiled_scales : nullptr);
   return check_launch("tile_weights");
 }

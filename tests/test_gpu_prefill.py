@@ -126,6 +126,13 @@ def test_tile_weights_layout():
     want_s = scales.reshape(E, rows // 16, 16, KS, 4).transpose(0, 1, 3, 2, 4).reshape(E, rows, cols // 32)
     np.testing.assert_array_equal(host(tc), want_c)
     np.testing.assert_array_equal(host(ts), want_s)
+    # block FP8: E4M3 rows of 128 bytes per K step, as two kilobyte halves; no scales
+    codes8 = rng.integers(0, 256, (E, rows, cols), dtype=np.uint8)
+    tc8, ts8 = m.tile_weights(dev(codes8), None, "fp8_block")
+    torch.cuda.synchronize()
+    assert ts8 is None
+    want8 = codes8.reshape(E, rows // 16, 16, KS, 2, 64).transpose(0, 1, 3, 4, 2, 5).reshape(E, rows, cols)
+    np.testing.assert_array_equal(host(tc8), want8)
 
 
 def _same_bits(a, b):
@@ -134,18 +141,20 @@ def _same_bits(a, b):
 
 def _tile(layer):
     import block_scaled_fp4_nvfp4_amd as m
-    layer.w13_tiled, layer.w13_scale_tiled = m.tile_weights(layer.w13, layer.w13_scale)
-    layer.w2_tiled, layer.w2_scale_tiled = m.tile_weights(layer.w2, layer.w2_scale)
+    f = layer.w_fmt
+    layer.w13_tiled, layer.w13_scale_tiled = m.tile_weights(layer.w13, layer.w13_scale, f)
+    layer.w2_tiled, layer.w2_scale_tiled = m.tile_weights(layer.w2, layer.w2_scale, f)
 
 
-def test_tiny_tiled_weights_bit_identical(tiny):
-    """MXFP4 x MXFP8 with tiled copies of W13 and W2: the gate_up GEMM reads
-    the same bytes in another order and computes the same sums, so y is
-    bit-identical to the row-major layer's (at this inter of 128 the down
-    GEMM keeps reading row-major W2)."""
-    print_case("tiny MXFP4 x MXFP8, tiled weights")
+@pytest.mark.parametrize("w_fmt,a_fmt", [("mxfp4", "mxfp8"), ("fp8_block", "fp8_row")])
+def test_tiny_tiled_weights_bit_identical(tiny, w_fmt, a_fmt):
+    """With tiled copies of W13 and W2 a GEMM reads the same bytes in another
+    order and computes the same sums, so y is bit-identical to the row-major
+    layer's.  At these sizes only the MX gate_up takes the tiled copy; the
+    other GEMMs fall back to the row-major tensors."""
+    print_case(f"tiny {w_fmt} x {a_fmt}, tiled weights")
     cfg, w13, w2, x, ids, wts = tiny
-    cfg = cfg.replace(w_fmt="mxfp4", a_fmt="mxfp8")
+    cfg = cfg.replace(w_fmt=w_fmt, a_fmt=a_fmt)
     layer = gpu_layer(cfg, w13, w2)
     y0, _, _ = _run(layer, x, ids, wts)
     _tile(layer)
@@ -281,9 +290,9 @@ def test_prefill_full_size_sampled(prefill_weights, name):
         pairs = np.concatenate([np.arange(t * k, (t + 1) * k) for t in sample])
         _, _, rop = moe.permute(ids, cfg.num_experts)
         _check_mxfp8_h(ws, lay, cfg.pairs, cfg.inter, rop[pairs], st["hrec"], st["h"][pairs])
-        # tiled copies of W13 and W2 (the benchmark's prefill layer; both
-        # GEMMs read them at inter 640): the whole y bit-identical
-        _tile(layer)
-        del ws
-        y1, _, _ = _run(layer, x, ids, wts)
-        assert _same_bits(y, y1)
+    # tiled copies of W13 and W2 (the benchmark's prefill layers; both GEMMs
+    # read them at these sizes): the whole y bit-identical
+    _tile(layer)
+    del ws
+    y1, _, _ = _run(layer, x, ids, wts)
+    assert _same_bits(y, y1)
