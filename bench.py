@@ -479,7 +479,8 @@ def bench_stack(args, torch, pkg):
     stack of the MXFP4-FP8-R12 card (layers 19, 20, 21, 23, 28, 32, 33, 40,
     41, 43, 44, 45 block FP8 x dynamic FP8, the other 36 MXFP4 x dynamic
     MXFP8; 512 experts, top-10, hidden 2560, inter 640), all 48 layers resident
-    (78.3 GB of expert weights) and run as one captured HIP graph per step.
+    (78.3 GB of expert weights; the block-FP8 layers also hold the tiled
+    copies their GEMMs read) and run as one captured HIP graph per step.
     Weights N(0, 0.02) bf16 drawn on the device per layer and quantized by the
     library; each layer gets its own synthetic tokens and routing."""
     import numpy as np
@@ -498,6 +499,11 @@ def bench_stack(args, torch, pkg):
             qs.append(pkg.quantize(w, cfg.w_fmt, cfg.rule))
             del w
         layers.append(make_layer(cfg, qs[0], qs[1], pkg))
+        if cfg.w_fmt == "fp8_block" and args.weight_layout == "tiled":
+            # its GEMMs read the tiled copies (the MXFP4 layers decode on GEMVs over rows)
+            lay = layers[-1]
+            lay.w13_tiled, lay.w13_scale_tiled = pkg.tile_weights(lay.w13, None, cfg.w_fmt)
+            lay.w2_tiled, lay.w2_scale_tiled = pkg.tile_weights(lay.w2, None, cfg.w_fmt)
         x = synth.activations(cfg)
         i, wt = synth.routing(cfg)
         xs.append(torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda())

@@ -180,3 +180,28 @@ def test_decode_layer_mxfp4_x_mxfp8_gemv_path(decode_layer):
     q = quant.quantize_mxfp8(h.astype(np.float64))
     codes = host(ws[lay["hq_codes"]:lay["hq_codes"] + P * I])
     np.testing.assert_array_equal(codes.reshape(P, I), q["codes"])
+
+
+def test_decode_layer_fp8_block_tiled_weights_bit_identical(decode_layer):
+    """16 tokens through a block-FP8 x FP8-row layer at the decode shape (the
+    stack's retained layers): with tiled copies of W13 and W2 both grouped
+    GEMMs read the same bytes in another order, so y is bit-identical to the
+    row-major layer's; and within the layer bar of the oracle."""
+    import block_scaled_fp4_nvfp4_amd as m
+    print_case("decode layer, block FP8, tiled weights")
+    cfg, w13, w2 = decode_layer
+    c = cfg.replace(w_fmt="fp8_block", a_fmt="fp8_row", rule="rtn")
+    x = synth.activations(c)
+    ids, wts = synth.routing(c)
+    layer = gpu_layer(c, w13, w2)
+    y0, _, _ = _run(layer, x, ids, wts)
+    layer.w13_tiled, _ = m.tile_weights(layer.w13, None, "fp8_block")
+    layer.w2_tiled, _ = m.tile_weights(layer.w2, None, "fp8_block")
+    y1, _, _ = _run(layer, x, ids, wts)
+    np.testing.assert_array_equal(np.asarray(y0, np.float32).view(np.uint32),
+                                  np.asarray(y1, np.float32).view(np.uint32))
+    sample = [0, 15]
+    y_ref = moe.moe_forward(OracleLayer(c, w13, w2).as_dict(), x, ids, wts, sample_tokens=sample)
+    err = rel_fro(y1[sample], y_ref)
+    print(f"relative Frobenius error {err:.3e}")
+    assert err <= TOL
