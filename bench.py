@@ -270,7 +270,7 @@ def bench_prefill(name, args, torch, pkg):
     layers = [make_layer(cfg, q13, q2, pkg, shared)]
     for _ in range(max(0, args.prefill_copies - 1)):
         layers.append(make_layer(cfg, clone_q(q13), clone_q(q2), pkg, shared))
-    tiled = cfg.w_fmt in ("mxfp4", "fp8_block") and args.weight_layout == "tiled"
+    tiled = args.weight_layout == "tiled"
     if tiled:  # once per layer, like its quantization: outside the timed region
         for layer in layers:
             layer.w13_tiled, layer.w13_scale_tiled = pkg.tile_weights(layer.w13, layer.w13_scale, cfg.w_fmt)
@@ -618,7 +618,8 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--prefill-copies", type=int, default=2)
     ap.add_argument("--weight-layout", choices=["tiled", "rows"], default="tiled",
-                    help="MXFP4 / block-FP8 prefill: expert weights in the tiled order of moe_fp4_tile_weights "
+                    help="prefill and the stack's block-FP8 layers: expert weights in the tiled order of "
+                         "moe_fp4_tile_weights "
                          "(made once per layer) or row-major")
     ap.add_argument("--stream-layers", type=int, default=48)
     ap.add_argument("--stack-layers", type=int, default=48)

@@ -174,18 +174,18 @@ def route(logits: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None):
 
 
 def tile_weights(codes: torch.Tensor, scales: Optional[torch.Tensor], fmt: str = "mxfp4"):
-    """moe_fp4_tile_weights.  MXFP4: codes uint8 [E, rows, cols/2], scales
-    uint8 [E, rows, cols/32]; block FP8 ("fp8_block"): codes uint8 [E, rows,
-    cols], scales unused.  Contiguous device tensors.  Returns the tiled
-    (codes, scales) for MoELayer.w13_tiled / w13_scale_tiled (or w2_tiled /
-    w2_scale_tiled); scales None for block FP8."""
+    """moe_fp4_tile_weights.  NVFP4 / MXFP4: codes uint8 [E, rows, cols/2],
+    scales [E, rows, cols/16] (E4M3) / [E, rows, cols/32] (UE8M0); block FP8
+    ("fp8_block"): codes uint8 [E, rows, cols], scales unused.  Contiguous
+    device tensors.  Returns the tiled (codes, scales) for MoELayer.w13_tiled /
+    w13_scale_tiled (or w2_tiled / w2_scale_tiled); scales None for block FP8."""
     assert codes.is_cuda and codes.is_contiguous() and codes.dim() == 3
     E, rows, width = (int(v) for v in codes.shape)
-    mx = fmt == "mxfp4"
-    cols = 2 * width if mx else width
+    fp4 = fmt in ("nvfp4", "mxfp4")
+    cols = 2 * width if fp4 else width
     tc = torch.empty_like(codes)
-    ts = torch.empty_like(scales) if mx else None
-    _check(lib().moe_fp4_tile_weights(FMT[fmt], _ptr(codes), _ptr(scales) if mx else None, E, rows, cols,
+    ts = torch.empty_like(scales) if fp4 else None
+    _check(lib().moe_fp4_tile_weights(FMT[fmt], _ptr(codes), _ptr(scales) if fp4 else None, E, rows, cols,
                                       _ptr(tc), _ptr(ts), _stream()))
     return tc, ts
 

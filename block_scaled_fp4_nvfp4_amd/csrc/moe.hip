@@ -894,14 +894,12 @@ static int validate_layer(const moe_fp4_layer* L, int64_t T) {
   if (L->shared_inter < 0) return fail(FP4_ERR_SHAPE, "negative shared width");
   if (L->shared_inter > 0 && (L->shared_inter % 128 || L->hidden % 128))
     return fail(FP4_ERR_SHAPE, "shared width and hidden must be multiples of 128");
-  if ((L->w13_tiled || L->w2_tiled) && w != FP4_FMT_MXFP4 && w != FP4_FMT_FP8_BLOCK)
-    return fail(FP4_ERR_UNSUPPORTED, "tiled weights are MXFP4 or block FP8 only");
-  // MXFP4: tiled codes and tiled scales together; block FP8: codes only
-  const bool scales_tiled = w == FP4_FMT_MXFP4;
+  // NVFP4 / MXFP4: tiled codes and tiled scales together; block FP8: codes only
+  const bool scales_tiled = w != FP4_FMT_FP8_BLOCK;
   if ((L->w13_tiled && (L->w13_scale_tiled != nullptr) != scales_tiled) ||
       (L->w2_tiled && (L->w2_scale_tiled != nullptr) != scales_tiled) ||
       (!L->w13_tiled && L->w13_scale_tiled) || (!L->w2_tiled && L->w2_scale_tiled))
-    return fail(FP4_ERR_INVALID_ARG, "tiled MXFP4 codes need tiled scales; tiled block-FP8 codes take none");
+    return fail(FP4_ERR_INVALID_ARG, "tiled FP4 codes need tiled scales; tiled block-FP8 codes take none");
   if ((L->w13_tiled && L->hidden % 128) || (L->w2_tiled && L->inter % 128))
     return fail(FP4_ERR_SHAPE, "tiled weights need a reduction size that is a multiple of 128");
   return FP4_OK;

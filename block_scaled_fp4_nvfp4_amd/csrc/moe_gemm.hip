@@ -162,8 +162,9 @@ struct TileCfg {
        15) / 16 * 16;
 };
 
-template <int GK, int EPI, int NSUB, bool WFP8>
+template <int GK, int EPI, int NSUB, bool WFP8, bool WT>
 __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
+  static_assert(!WT || (GK == GK_NV && !WFP8), "tiled weights on this kernel: NVFP4");
   using C = TileCfg<GK, EPI, NSUB, WFP8>;
   constexpr int BM = C::BM, BN = C::BN, NU = C::NU, WROWS = C::WROWS;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -261,7 +262,10 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
   for (int c = 0; c < W_CH; ++c) {
     const int ch = tid + 256 * c;
     const int row = ch / w_cpr, part = ch % w_cpr;
-    w_src[c] = w_base + (int64_t)w_grow(row) * w_rb + 16 * part;
+    const int gr = w_grow(row);
+    // tiled (moe_fp4_tile_weights): a wave's 16 rows (aligned) of a step are one kilobyte
+    w_src[c] = WT ? w_base + (int64_t)(gr >> 4) * (KS * 1024) + (gr & 15) * 64 + 16 * part
+                  : w_base + (int64_t)gr * w_rb + 16 * part;
     w_soff[c] = swz<w_stride>(row, part);
   }
   // W scales: row tid % WROWS (WROWS <= 256; duplicates store identical values)
@@ -294,8 +298,12 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
     if (GK == GK_FP8)
       R.pas = __float_as_uint(reinterpret_cast<const float*>(g.a_scales)[as_row * (K / 128) + k0 / 128]);
 #pragma unroll
-    for (int c = 0; c < W_CH; ++c) R.pw[c] = ld16(w_src[c] + (WFP8 ? k0 : k0 / 2));
-    if (GK == GK_NV) {
+    for (int c = 0; c < W_CH; ++c) R.pw[c] = ld16(w_src[c] + (WT ? k0 * 8 : (WFP8 ? k0 : k0 / 2)));
+    if (GK == GK_NV && WT) {  // tiled: 16 rows' 8 scale bytes of a step as 128 bytes
+      R.pws = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(g.w_scales) +
+                                              (int64_t)e * NW * (K / 16) + (int64_t)(ws_grow >> 4) * (KS * 128) +
+                                              k0 + (ws_grow & 15) * 8);
+    } else if (GK == GK_NV) {
       R.pws = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(g.w_scales) +
                                               ((int64_t)e * NW + ws_grow) * (K / 16) + k0 / 16);
     } else if (GK == GK_MX) {
@@ -1159,7 +1167,7 @@ constexpr int nv2_wait_count(int ks) {  // raw(ks+1) and W(ks) done
   return n < 63 ? n : 63;
 }
 
-template <int EPI, int NSUB, int KS>
+template <int EPI, int NSUB, int KS, bool WT>
 __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
   using C = Nv2Cfg<EPI, NSUB, KS>;
   constexpr int BM = C::BM, BN = C::BN, NU = C::NU, NS = C::NS, RS = C::RS, D = C::D;
@@ -1246,23 +1254,34 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
     st16(dt + swz<256>(arow, 4 * apart + 2), u32x4{d[8], d[9], d[10], d[11]});
     st16(dt + swz<256>(arow, 4 * apart + 3), u32x4{d[12], d[13], d[14], d[15]});
   };
-  // this lane's weight rows: column lr of subtile s, values 32 lg .. +32 of each step
+  // this lane's weight rows: column lr of subtile s, values 32 lg .. +32 of
+  // each step; a step moves row-major codes 64 bytes and scales 8, tiled
+  // ones (moe_fp4_tile_weights: 16 rows' step as one kilobyte / 128 bytes)
+  // 1024 and 128
+  constexpr int W_STEP = WT ? 1024 : 64, WS_STEP = WT ? 128 : 8;
   const uint8_t* w_src[NS];
   const uint8_t* ws_src[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int wr = (s / NSUB) * BN + wave * 16 * NSUB + (s % NSUB) * 16 + lr;
-    const int64_t grow = (int64_t)e * NW + w_grow(wr);
-    w_src[s] = g.w_codes + grow * (K / 2) + 16 * lg;
-    ws_src[s] = reinterpret_cast<const uint8_t*>(g.w_scales) + grow * (K / 16);
+    const int gr = w_grow(wr);
+    const int64_t grow = (int64_t)e * NW + gr;
+    if constexpr (WT) {  // 16 consecutive rows (gr % 16 == lr)
+      w_src[s] = g.w_codes + (int64_t)e * NW * (K / 2) + (int64_t)(gr >> 4) * (KS * 1024) + (gr & 15) * 64 + 16 * lg;
+      ws_src[s] = reinterpret_cast<const uint8_t*>(g.w_scales) + (int64_t)e * NW * (K / 16) +
+                  (int64_t)(gr >> 4) * (KS * 128) + (gr & 15) * 8;
+    } else {
+      w_src[s] = g.w_codes + grow * (K / 2) + 16 * lg;
+      ws_src[s] = reinterpret_cast<const uint8_t*>(g.w_scales) + grow * (K / 16);
+    }
   }
   u32x4 wq[D][NS];
   u32x2 wsq[D][NS];
   auto load_w = [&](int ks, u32x4 (&q)[NS], u32x2 (&sc)[NS]) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      q[s] = ld16(w_src[s] + 64 * ks);
-      sc[s] = *reinterpret_cast<const u32x2*>(ws_src[s] + 8 * ks);  // the row's 8 scales of the step
+      q[s] = ld16(w_src[s] + W_STEP * ks);
+      sc[s] = *reinterpret_cast<const u32x2*>(ws_src[s] + WS_STEP * ks);  // the row's 8 scales of the step
     }
   };
 
@@ -1353,8 +1372,8 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
     }
 }
 
-template <int EPI, int NSUB, int KS>
-static int launch_gemm_nv2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+template <int EPI, int NSUB, int KS, bool WT>
+static int launch_gemm_nv2_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   using C = Nv2Cfg<EPI, NSUB, KS>;
   const int NT = a.N / C::BN;
   int64_t G = tiles_m_bound * NT;
@@ -1366,23 +1385,30 @@ static int launch_gemm_nv2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t
   if (fixed + lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_nv2_kernel<EPI, NSUB, KS>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_nv2_kernel<EPI, NSUB, KS, WT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)(160 * 1024 - fixed)) != hipSuccess)
       return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
     attr_set = true;
   }
-  hipLaunchKernelGGL((grouped_gemm_nv2_kernel<EPI, NSUB, KS>), dim3((unsigned)G), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((grouped_gemm_nv2_kernel<EPI, NSUB, KS, WT>), dim3((unsigned)G), dim3(256), lds, st, a);
   return check_launch("grouped_gemm_nv2");
+}
+
+template <int EPI, int NSUB, int KS>
+static int launch_gemm_nv2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+  return a.w_tiled ? launch_gemm_nv2_t<EPI, NSUB, KS, true>(a, tiles_m_bound, st)
+                   : launch_gemm_nv2_t<EPI, NSUB, KS, false>(a, tiles_m_bound, st);
 }
 
 // Tiled order of moe_fp4_tile_weights.  The E stacked [rows, cols] tensors
 // are one run of E * rows rows (rows % 16 == 0, so no 16-row group straddles
-// two experts).  A row holds PH 64-byte pieces per 128-wide K step (MXFP4 1,
-// E4M3 2); piece h of the 16 rows of a group is one kilobyte.  Thread i
-// copies 16-byte code chunk i and (MX) scale dword i.
+// two experts).  A row holds PH 64-byte pieces per 128-wide K step (E2M1 1,
+// E4M3 2); piece h of the 16 rows of a group is one kilobyte.  A row's block
+// scales of a K step are SB bytes (MXFP4 4, NVFP4 8; block FP8: none).
+// Thread i copies 16-byte code chunk i and the scales of (row, step) i.
 __global__ void __launch_bounds__(256) tile_weights_kernel(const uint8_t* __restrict__ codes,
                                                            const uint8_t* __restrict__ scales,
-                                                           int64_t rows_total, int KS, int PH,
+                                                           int64_t rows_total, int KS, int PH, int SB,
                                                            uint8_t* __restrict__ tiled_codes,
                                                            uint8_t* __restrict__ tiled_scales) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1393,11 +1419,14 @@ __global__ void __launch_bounds__(256) tile_weights_kernel(const uint8_t* __rest
     const int64_t dst = (r >> 4) * ((int64_t)KS * PH * 1024) + (ks * PH + h) * 1024 + (r & 15) * 64 + u * 16;
     *reinterpret_cast<uint4*>(tiled_codes + dst) = *reinterpret_cast<const uint4*>(codes + i * 16);
   }
-  if (tiled_scales && i < rows_total * KS) {  // MX scale dwords: row r, K step ks
+  if (tiled_scales && i < rows_total * KS) {  // scales of row r, K step ks
     const int64_t r = i / KS;
     const int ks = (int)(i - r * KS);
-    const int64_t dst = (r >> 4) * ((int64_t)KS * 64) + ks * 64 + (r & 15) * 4;
-    *reinterpret_cast<uint32_t*>(tiled_scales + dst) = *reinterpret_cast<const uint32_t*>(scales + i * 4);
+    const int64_t dst = (r >> 4) * ((int64_t)KS * 16 * SB) + ks * 16 * SB + (r & 15) * SB;
+    if (SB == 8)
+      *reinterpret_cast<u32x2*>(tiled_scales + dst) = *reinterpret_cast<const u32x2*>(scales + i * 8);
+    else
+      *reinterpret_cast<uint32_t*>(tiled_scales + dst) = *reinterpret_cast<const uint32_t*>(scales + i * 4);
   }
 }
 
@@ -1444,8 +1473,8 @@ __global__ void __launch_bounds__(256) shared_gate_kernel(const uint16_t* __rest
 
 // ------------------------------------------------------------------- host
 
-template <int GK, int EPI, int NSUB, bool WFP8>
-static int launch_gemm_n(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+template <int GK, int EPI, int NSUB, bool WFP8, bool WT>
+static int launch_gemm_n_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   using C = TileCfg<GK, EPI, NSUB, WFP8>;
   const int64_t G = gemm_grid(tiles_m_bound, a.N, C::BN);
   if (a.amax_part && G != a.amax_nparts)
@@ -1459,13 +1488,23 @@ static int launch_gemm_n(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t s
   if (lds > dyn_max) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs %zu bytes of LDS", lds);
   static bool attr_set = false;  // raise the dynamic-LDS limit once per kernel instance
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_kernel<GK, EPI, NSUB, WFP8>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_kernel<GK, EPI, NSUB, WFP8, WT>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_max) != hipSuccess)
       return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
     attr_set = true;
   }
-  hipLaunchKernelGGL((grouped_gemm_kernel<GK, EPI, NSUB, WFP8>), dim3((unsigned)G), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((grouped_gemm_kernel<GK, EPI, NSUB, WFP8, WT>), dim3((unsigned)G), dim3(256), lds, st, a);
   return check_launch("grouped_gemm");
+}
+
+template <int GK, int EPI, int NSUB, bool WFP8>
+static int launch_gemm_n(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+  if constexpr (GK == GK_NV && !WFP8) {
+    if (a.w_tiled) return launch_gemm_n_t<GK, EPI, NSUB, WFP8, true>(a, tiles_m_bound, st);
+  } else {
+    if (a.w_tiled) return fail(FP4_ERR_UNSUPPORTED, "tiled weights on a GEMM kernel that reads rows");
+  }
+  return launch_gemm_n_t<GK, EPI, NSUB, WFP8, false>(a, tiles_m_bound, st);
 }
 
 template <int GK, int EPI, int NSUB, int KS, bool WT>
@@ -1602,10 +1641,11 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   a.a_tensor_scale = x_ts;
   a.a_gather = 1;
   // the tiled copy of W13, when the layer has one, where the gate_up kernel
-  // reads it (block FP8: codes only, its block scales stay as they are)
-  a.w_tiled = L->w13_tiled && (gk == GK_MX || (gk == GK_FP8 && fp8_gateup_on_mx2(I, H))) ? 1 : 0;
+  // reads it (NVFP4 and MXFP4: always; block FP8: on the register-fed
+  // kernel, codes only, its block scales stay as they are)
+  a.w_tiled = L->w13_tiled && (gk != GK_FP8 || fp8_gateup_on_mx2(I, H)) ? 1 : 0;
   a.w_codes = a.w_tiled ? L->w13_tiled : L->w13;
-  a.w_scales = a.w_tiled && gk == GK_MX ? static_cast<const void*>(L->w13_scale_tiled) : L->w13_scale;
+  a.w_scales = a.w_tiled && gk != GK_FP8 ? static_cast<const void*>(L->w13_scale_tiled) : L->w13_scale;
   a.w_tensor_scale = L->w13_scale_2;
   a.w_fp8 = 0;
   a.offsets = w.offsets;
@@ -1655,10 +1695,11 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   d.q_scales = nullptr;
   d.amax_part = nullptr;
   d.amax_nparts = 0;
-  // the tiled copy of W2 where the down kernel that reads it runs
-  d.w_tiled = L->w2_tiled && (gk == GK_MX || gk == GK_FP8) && mx_down_on_mx2(H, I) ? 1 : 0;
+  // the tiled copy of W2 where the down kernel reads it (NVFP4: always; MX
+  // and block FP8: on the register-fed kernel)
+  d.w_tiled = L->w2_tiled && (gk == GK_NV || mx_down_on_mx2(H, I)) ? 1 : 0;
   d.w_codes = d.w_tiled ? L->w2_tiled : L->w2;
-  d.w_scales = d.w_tiled && gk == GK_MX ? static_cast<const void*>(L->w2_scale_tiled) : L->w2_scale;
+  d.w_scales = d.w_tiled && gk != GK_FP8 ? static_cast<const void*>(L->w2_scale_tiled) : L->w2_scale;
   d.w_tensor_scale = L->w2_scale_2;
   d.K = I;
   d.N = H;
@@ -1722,23 +1763,24 @@ extern "C" int moe_fp4_tile_weights(int w_fmt, const uint8_t* codes, const uint8
                                     int64_t rows, int64_t cols, uint8_t* tiled_codes, uint8_t* tiled_scales,
                                     void* stream) {
   using namespace fp4;
-  if (w_fmt != FP4_FMT_MXFP4 && w_fmt != FP4_FMT_FP8_BLOCK)
-    return fail(FP4_ERR_UNSUPPORTED, "tile_weights: MXFP4 or block-FP8 weights only (got %d)", w_fmt);
-  const bool mx = w_fmt == FP4_FMT_MXFP4;
+  if (w_fmt != FP4_FMT_NVFP4 && w_fmt != FP4_FMT_MXFP4 && w_fmt != FP4_FMT_FP8_BLOCK)
+    return fail(FP4_ERR_UNSUPPORTED, "tile_weights: NVFP4, MXFP4 or block-FP8 weights only (got %d)", w_fmt);
+  const bool fp4 = w_fmt != FP4_FMT_FP8_BLOCK;  // E2M1 codes with per-row block scales
+  const int SB = w_fmt == FP4_FMT_NVFP4 ? 8 : 4;
   if (experts < 0 || rows < 0 || cols < 0) return fail(FP4_ERR_SHAPE, "tile_weights: negative dimension");
   if (rows % 16 || cols % 128)
     return fail(FP4_ERR_SHAPE, "tile_weights: rows %lld must be a multiple of 16, cols %lld of 128", (long long)rows,
                 (long long)cols);
   if (experts == 0 || rows == 0 || cols == 0) return FP4_OK;
-  if (!codes || !tiled_codes || (mx && (!scales || !tiled_scales)))
+  if (!codes || !tiled_codes || (fp4 && (!scales || !tiled_scales)))
     return fail(FP4_ERR_INVALID_ARG, "tile_weights: null pointer");
   if (reinterpret_cast<uintptr_t>(codes) % 16 || reinterpret_cast<uintptr_t>(tiled_codes) % 16 ||
-      (mx && (reinterpret_cast<uintptr_t>(scales) % 4 || reinterpret_cast<uintptr_t>(tiled_scales) % 4)))
-    return fail(FP4_ERR_INVALID_ARG, "tile_weights: codes need 16-byte and scales 4-byte alignment");
+      (fp4 && (reinterpret_cast<uintptr_t>(scales) % SB || reinterpret_cast<uintptr_t>(tiled_scales) % SB)))
+    return fail(FP4_ERR_INVALID_ARG, "tile_weights: codes need 16-byte and scales %d-byte alignment", SB);
   const int64_t rows_total = experts * rows;
-  const int KS = (int)(cols / 128), PH = mx ? 1 : 2;
-  const int64_t n = rows_total * KS * PH * 4;  // code chunks (at least the scale dwords)
+  const int KS = (int)(cols / 128), PH = fp4 ? 1 : 2;
+  const int64_t n = rows_total * KS * PH * 4;  // code chunks (at least the scale groups)
   hipLaunchKernelGGL(tile_weights_kernel, dim3(grid_1d(n, 256)), dim3(256), 0, as_stream(stream), codes,
-                     mx ? scales : nullptr, rows_total, KS, PH, tiled_codes, mx ? tiled_scales : nullptr);
+                     fp4 ? scales : nullptr, rows_total, KS, PH, SB, tiled_codes, fp4 ? tiled_scales : nullptr);
   return check_launch("tile_weights");
 }

@@ -158,14 +158,15 @@ typedef struct {
   const uint8_t* ws2;       /* MXFP8 codes [H, Si] */
   const uint8_t* ws2_scale; /* UE8M0 [H, Si/32] */
   const uint16_t* shared_gate; /* bf16 [H] */
-  /* Optional (may be NULL), MXFP4 or block-FP8 weights: W13 / W2 in the
-   * tiled order of moe_fp4_tile_weights, with (MXFP4 only) their scales;
-   * block FP8 keeps its 128 x 128 block scales in w13_scale / w2_scale and
-   * takes no tiled scales.  The grouped GEMMs of the quantized-activation
-   * path read the tiled copies where their kernels take that order (MXFP4
-   * gate_up: always; down: inter = 640, the model's width; block-FP8
-   * gate_up: hidden = 2560) and the row-major tensors elsewhere; the decode
-   * GEMVs read the row-major tensors, which stay required. */
+  /* Optional (may be NULL): W13 / W2 in the tiled order of
+   * moe_fp4_tile_weights, with (NVFP4, MXFP4) their tiled scales; block FP8
+   * keeps its 128 x 128 block scales in w13_scale / w2_scale and takes no
+   * tiled scales.  The grouped GEMMs of the quantized-activation paths read
+   * the tiled copies where their kernels take that order (NVFP4: always;
+   * MXFP4 gate_up: always, down: inter = 640, the model's width; block FP8:
+   * gate_up at hidden = 2560, down at inter = 640) and the row-major
+   * tensors elsewhere; the decode GEMVs read the row-major tensors, which
+   * stay required. */
   const uint8_t* w13_tiled;
   const uint8_t* w13_scale_tiled;
   const uint8_t* w2_tiled;
@@ -234,22 +235,23 @@ int moe_fp4_route(const float* logits, const float* bias, int64_t tokens, int nu
 
 /*
  * moe_fp4_tile_weights - copy of stacked expert weights in the layout of
- * fp4_quantize, MXFP4 (codes [E, rows, cols/2], UE8M0 scales [E, rows,
- * cols/32]) or block FP8 (E4M3 codes [E, rows, cols]; its block scales need
- * no copy: scales / tiled_scales are ignored and may be NULL), into the order
- * the grouped GEMMs stream them: per expert, per group of 16 rows, per
- * 128-wide K step, the 16 rows' code bytes as PH kilobytes of 64 bytes per
- * row (PH = 1 for MXFP4; 2 for E4M3, bytes 0-63 of each row then 64-127),
- * and (MXFP4) the 16 rows' 4 scale bytes as 64 bytes:
+ * fp4_quantize, NVFP4 (codes [E, rows, cols/2], E4M3 scales [E, rows,
+ * cols/16]), MXFP4 (codes [E, rows, cols/2], UE8M0 scales [E, rows, cols/32])
+ * or block FP8 (E4M3 codes [E, rows, cols]; its block scales need no copy:
+ * scales / tiled_scales are ignored and may be NULL), into the order the
+ * grouped GEMMs stream them: per expert, per group of 16 rows, per 128-wide
+ * K step, the 16 rows' code bytes as PH kilobytes of 64 bytes per row (PH = 1
+ * for E2M1; 2 for E4M3, bytes 0-63 of each row then 64-127), and the 16
+ * rows' SB scale bytes of the step (SB = 8 for NVFP4, 4 for MXFP4):
  *   tiled_codes [E][rows/16][cols/128][PH][16][64]
- *   tiled_scales[E][rows/16][cols/128][16][4]
+ *   tiled_scales[E][rows/16][cols/128][16][SB]
  * The same bytes, rearranged, so that one load instruction of the GEMM moves
  * one contiguous kilobyte instead of sixteen 64-byte pieces of different
  * rows.  Done once when a layer is loaded; the output buffers (same sizes as
  * the inputs, device memory, caller-owned) go in moe_fp4_layer.w13_tiled /
  * w13_scale_tiled (or w2_tiled / w2_scale_tiled).  Errors: other formats ->
  * FP4_ERR_UNSUPPORTED; rows % 16 or cols % 128 -> FP4_ERR_SHAPE; a null or
- * misaligned pointer (codes 16 bytes, scales 4) -> FP4_ERR_INVALID_ARG.
+ * misaligned pointer (codes 16 bytes, scales SB) -> FP4_ERR_INVALID_ARG.
  * Stream-ordered, asynchronous.
  */
 int moe_fp4_tile_weights(int w_fmt, const uint8_t* codes, const uint8_t* scales, int64_t experts,

@@ -105,9 +105,11 @@ def test_moe_validation_and_workspace(L):
 
 def test_tile_weights_and_tiled_layer_validation(L):
     fake, odd = ctypes.c_void_p(0x1000), ctypes.c_void_p(0x1004)
-    # MXFP4 or block FP8 only; rows % 16 and cols % 128; null and misaligned pointers; empty is a no-op
-    assert L.moe_fp4_tile_weights(0, fake, fake, 2, 32, 256, fake, fake, None) == -3
+    # weight formats only (not MXFP8 / FP8 rows); rows % 16 and cols % 128; null and misaligned
+    # pointers; empty is a no-op.  Every call here fails (or does nothing) before any launch.
     assert L.moe_fp4_tile_weights(2, fake, fake, 2, 32, 256, fake, fake, None) == -3
+    assert L.moe_fp4_tile_weights(4, fake, fake, 2, 32, 256, fake, fake, None) == -3
+    assert L.moe_fp4_tile_weights(0, fake, odd, 2, 32, 256, fake, fake, None) == -1  # NVFP4 scales: 8 bytes
     assert L.moe_fp4_tile_weights(3, fake, None, 2, 32, 256, None, None, None) == -1  # null tiled codes
     assert L.moe_fp4_tile_weights(1, fake, fake, 2, 24, 256, fake, fake, None) == -2
     assert L.moe_fp4_tile_weights(1, fake, fake, 2, 32, 192, fake, fake, None) == -2
@@ -127,8 +129,10 @@ def test_tile_weights_and_tiled_layer_validation(L):
     s.w2_tiled = 0x5000
     assert L.moe_fp4_workspace_size(ctypes.byref(s), 64, ctypes.byref(sz)) == 0
     s = _layer(w_fmt=0, a_fmt=0)
-    s.w13_tiled, s.w13_scale_tiled = 0x2000, 0x3000
-    assert L.moe_fp4_workspace_size(ctypes.byref(s), 64, ctypes.byref(sz)) == -3
+    s.w13_tiled = 0x2000
+    assert L.moe_fp4_workspace_size(ctypes.byref(s), 64, ctypes.byref(sz)) == -1
+    s.w13_scale_tiled = 0x3000
+    assert L.moe_fp4_workspace_size(ctypes.byref(s), 64, ctypes.byref(sz)) == 0
     # block FP8: tiled codes without tiled scales
     s = _layer(w_fmt=3, a_fmt=4)
     s.w13_tiled = 0x2000

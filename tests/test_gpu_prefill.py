@@ -126,6 +126,13 @@ def test_tile_weights_layout():
     want_s = scales.reshape(E, rows // 16, 16, KS, 4).transpose(0, 1, 3, 2, 4).reshape(E, rows, cols // 32)
     np.testing.assert_array_equal(host(tc), want_c)
     np.testing.assert_array_equal(host(ts), want_s)
+    # NVFP4: the same code order, 8 E4M3 scale bytes per row and step
+    scales16 = rng.integers(0, 256, (E, rows, cols // 16), dtype=np.uint8)
+    tcn, tsn = m.tile_weights(dev(codes), dev(scales16), "nvfp4")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(tcn), want_c)
+    want16 = scales16.reshape(E, rows // 16, 16, KS, 8).transpose(0, 1, 3, 2, 4).reshape(E, rows, cols // 16)
+    np.testing.assert_array_equal(host(tsn), want16)
     # block FP8: E4M3 rows of 128 bytes per K step, as two kilobyte halves; no scales
     codes8 = rng.integers(0, 256, (E, rows, cols), dtype=np.uint8)
     tc8, ts8 = m.tile_weights(dev(codes8), None, "fp8_block")
@@ -146,12 +153,12 @@ def _tile(layer):
     layer.w2_tiled, layer.w2_scale_tiled = m.tile_weights(layer.w2, layer.w2_scale, f)
 
 
-@pytest.mark.parametrize("w_fmt,a_fmt", [("mxfp4", "mxfp8"), ("fp8_block", "fp8_row")])
+@pytest.mark.parametrize("w_fmt,a_fmt", MODES)
 def test_tiny_tiled_weights_bit_identical(tiny, w_fmt, a_fmt):
     """With tiled copies of W13 and W2 a GEMM reads the same bytes in another
     order and computes the same sums, so y is bit-identical to the row-major
-    layer's.  At these sizes only the MX gate_up takes the tiled copy; the
-    other GEMMs fall back to the row-major tensors."""
+    layer's.  At these sizes the NVFP4 GEMMs and the MX gate_up take the
+    tiled copies; the other GEMMs fall back to the row-major tensors."""
     print_case(f"tiny {w_fmt} x {a_fmt}, tiled weights")
     cfg, w13, w2, x, ids, wts = tiny
     cfg = cfg.replace(w_fmt=w_fmt, a_fmt=a_fmt)
@@ -254,7 +261,8 @@ def test_prefill_nvfp4_full_size_sampled(prefill_weights):
     x = synth.activations(cfg)
     ids, wts = synth.routing(cfg)
     np.testing.assert_array_equal(np.bincount(ids.reshape(-1), minlength=cfg.num_experts), gold["counts"])
-    y, ws, lay = _run(gpu_layer(cfg, w13, w2, shared=synth.shared_expert(cfg)), x, ids, wts)
+    layer = gpu_layer(cfg, w13, w2, shared=synth.shared_expert(cfg))
+    y, ws, lay = _run(layer, x, ids, wts)
     sx = host(ws[lay["x_tensor_scale"]:lay["x_tensor_scale"] + 4].view(torch.float32))[0]
     assert sx == gold["s_x"]          # amax/2688 over all of x: exact
     sh = host(ws[lay["h_tensor_scale"]:lay["h_tensor_scale"] + 4].view(torch.float32))[0]
@@ -265,6 +273,11 @@ def test_prefill_nvfp4_full_size_sampled(prefill_weights):
     print(f"relative Frobenius error on sampled tokens {err:.3e}")
     assert err <= TOL
     assert np.all(np.isfinite(y))
+    # tiled copies of W13 and W2 (the benchmark's layer): the whole y bit-identical
+    _tile(layer)
+    del ws
+    y1, _, _ = _run(layer, x, ids, wts)
+    assert _same_bits(y, y1)
 
 
 @pytest.mark.parametrize("name", ["prefill_mxfp4", "prefill_fp8"])
