@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <utility>
 
 #include "fp4_device.h"
@@ -1372,6 +1373,20 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
     }
 }
 
+// Raises a kernel's dynamic-LDS limit on the current device the first time
+// it launches there; `raised` holds one bit per device, so concurrent callers
+// at worst set the attribute twice.
+static int raise_dyn_lds(const void* kernel, int bytes, std::atomic<uint64_t>& raised) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(FP4_ERR_HIP, "hipGetDevice failed");
+  const uint64_t bit = 1ull << (dev & 63);
+  if (raised.load(std::memory_order_acquire) & bit) return FP4_OK;
+  if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+    return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
+  raised.fetch_or(bit, std::memory_order_acq_rel);
+  return FP4_OK;
+}
+
 template <int EPI, int NSUB, int KS, bool WT>
 static int launch_gemm_nv2_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   using C = Nv2Cfg<EPI, NSUB, KS>;
@@ -1383,13 +1398,9 @@ static int launch_gemm_nv2_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream
   const size_t lds = a.dense_rows > 0 ? 0 : sizeof(int) * ((size_t)a.E + 1);
   constexpr size_t fixed = (size_t)C::RS * C::RAW + 2 * (size_t)C::DEC + 512;
   if (fixed + lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_nv2_kernel<EPI, NSUB, KS, WT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(160 * 1024 - fixed)) != hipSuccess)
-      return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_raised{0};
+  FP4_CHECK(raise_dyn_lds(reinterpret_cast<const void*>(&grouped_gemm_nv2_kernel<EPI, NSUB, KS, WT>),
+                            (int)(160 * 1024 - fixed), lds_raised));
   hipLaunchKernelGGL((grouped_gemm_nv2_kernel<EPI, NSUB, KS, WT>), dim3((unsigned)G), dim3(256), lds, st, a);
   return check_launch("grouped_gemm_nv2");
 }
@@ -1486,13 +1497,9 @@ static int launch_gemm_n_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t
   constexpr size_t dyn_max = 160 * 1024 - 256;
   const size_t lds = 2 * C::STAGE + (a.dense_rows > 0 ? 0 : sizeof(int) * ((size_t)a.E + 1));
   if (lds > dyn_max) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs %zu bytes of LDS", lds);
-  static bool attr_set = false;  // raise the dynamic-LDS limit once per kernel instance
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_kernel<GK, EPI, NSUB, WFP8, WT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn_max) != hipSuccess)
-      return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_raised{0};
+  FP4_CHECK(raise_dyn_lds(reinterpret_cast<const void*>(&grouped_gemm_kernel<GK, EPI, NSUB, WFP8, WT>),
+                            (int)dyn_max, lds_raised));
   hipLaunchKernelGGL((grouped_gemm_kernel<GK, EPI, NSUB, WFP8, WT>), dim3((unsigned)G), dim3(256), lds, st, a);
   return check_launch("grouped_gemm");
 }
@@ -1518,13 +1525,9 @@ static int launch_gemm_mx2_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream
   const size_t lds = a.dense_rows > 0 ? 0 : sizeof(int) * ((size_t)a.E + 1);
   constexpr size_t fixed = (size_t)C::RS * C::STAGE + 1024;
   if (fixed + lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS, WT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)(160 * 1024 - fixed)) != hipSuccess)
-      return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_raised{0};
+  FP4_CHECK(raise_dyn_lds(reinterpret_cast<const void*>(&grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS, WT>),
+                            (int)(160 * 1024 - fixed), lds_raised));
   hipLaunchKernelGGL((grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS, WT>), dim3((unsigned)G), dim3(256), lds, st, a);
   return check_launch("grouped_gemm_mx2");
 }
@@ -1546,14 +1549,9 @@ static int launch_gemm_mx_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream_
   const size_t lds = a.dense_rows > 0 ? 0 : sizeof(int) * ((size_t)a.E + 1);
   if (3 * (size_t)C::STAGE + 256 + lds > 160 * 1024)
     return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&grouped_gemm_mx_kernel<EPI, NSUB, WT>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)(160 * 1024 - 3 * C::STAGE - 256)) != hipSuccess)
-      return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_raised{0};
+  FP4_CHECK(raise_dyn_lds(reinterpret_cast<const void*>(&grouped_gemm_mx_kernel<EPI, NSUB, WT>),
+                            (int)(160 * 1024 - 3 * C::STAGE - 256), lds_raised));
   hipLaunchKernelGGL((grouped_gemm_mx_kernel<EPI, NSUB, WT>), dim3((unsigned)G), dim3(256), lds, st, a);
   return check_launch("grouped_gemm_mx");
 }
