@@ -1453,14 +1453,6 @@ static int64_t gemm_grid(int64_t tiles_m_bound, int N, int BN) {
   return (tiles_m_bound * (N / BN) + 7) / 8 * 8;
 }
 
-// Zero rows [n_valid, P) of a [P, cols] f32 buffer (n_valid read on the device).
-__global__ void zero_rows_tail_kernel(float* __restrict__ buf, const int32_t* __restrict__ n_valid, int64_t P,
-                                      int cols) {
-  const int64_t begin = (int64_t)n_valid[0] * cols, end = P * cols;
-  for (int64_t i = begin + (int64_t)blockIdx.x * 256 + threadIdx.x; i < end; i += (int64_t)gridDim.x * 256)
-    buf[i] = 0.0f;
-}
-
 // sigmoid(x_t . gate) for every token (one wave per token), bf16 x and gate.
 __global__ void __launch_bounds__(256) shared_gate_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ gate, int64_t T, int H,
@@ -1673,11 +1665,13 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   else FP4_CHECK((launch_gemm<GK_FP8, EPI_GATEUP>(a, tiles_bound, st)));
   FP4_CHECK(mark(3));
   // 4. quantization of h (sorted rows; NVFP4 tensor scale over all of h).
-  //    Rows of skipped pairs (invalid expert ids) hold no h: zero them first.
+  //    Rows of skipped pairs (invalid expert ids, sorted last) hold no h and
+  //    are quantized as whatever they hold: their codes are never read (a
+  //    tile row past its expert's end reads the expert's first row), the
+  //    FP8 / MX scales are per row and per block, and S_h comes from the
+  //    gate_up workgroups' maxima over the rows they stored.
   float* h_ts = static_h ? const_cast<float*>(L->inter_scale) : w.h_ts;
   if (!h_in_epilogue) {
-    hipLaunchKernelGGL(zero_rows_tail_kernel, dim3(64), dim3(256), 0, st, w.h, w.offsets + E, P, I);
-    FP4_CHECK(check_launch("zero_rows_tail"));
     if (h_parts) FP4_CHECK(nv_tensor_scale_from_parts(w.h_amax_part, a.amax_nparts, h_ts, st));
     FP4_CHECK(fp4_quantize(L->a_fmt, FP4_RULE_RTN, (static_h || h_parts) ? FP4_TS_STATIC : FP4_TS_DYNAMIC, w.h,
                            FP4_DT_F32, 1, P, I, w.hq_codes, w.hq_scales, h_ts, nullptr, st));

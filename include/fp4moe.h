@@ -186,7 +186,8 @@ typedef struct {
   size_t row_of_pair;    /* int32 [T*k] sorted row of each pair                     */
   size_t x_tensor_scale; /* f32: S_x (NVFP4 activations)                            */
   size_t h_tensor_scale; /* f32: S_h (NVFP4 activations)                            */
-  size_t h;              /* f32 [T*k, I]  SiLU(gate)*up in sorted row order          */
+  size_t h;              /* f32 [T*k, I]  SiLU(gate)*up in sorted row order (rows of
+                            skipped pairs, sorted last, unspecified)             */
   size_t hq_codes;       /* quantized h codes (layout of a_fmt), sorted row order    */
   size_t hq_scales;      /* quantized h scales                                       */
   size_t o;              /* f32 [T*k, H]  down projection per sorted row (unweighted) */
