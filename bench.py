@@ -412,24 +412,25 @@ def bench_stream_quant(args, torch, pkg, rule="4over6"):
             wr += q["codes"].numel() + q["scales"].numel() + q["tensor_scale"].numel() * 4
         if want:
             for w, q, names in ((w13, q13, ("gate", "up")), (w2, q2, ("down",))):
-                xh = pkg.dequantize(q, "nvfp4", w.shape, torch.float32)
-                src = w.float()
+                # squared error of every block from the library (fp4_block_error)
+                be = pkg.block_error(w, q, "nvfp4").double()
+                src = w.double()
                 parts = [(n, sl) for n, sl in zip(names, (slice(0, I), slice(I, 2 * I)))] if len(names) == 2 \
                     else [("down", slice(0, H))]
-                x46 = None
+                be46 = None
                 if rule != "4over6":  # the same tensors under 4/6, for comparison (untimed)
-                    x46 = pkg.dequantize(pkg.quantize(w, "nvfp4", "4over6"), "nvfp4", w.shape, torch.float32)
+                    be46 = pkg.block_error(w, pkg.quantize(w, "nvfp4", "4over6"), "nvfp4").double()
                 for n, sl in parts:
-                    d = (xh[:, sl] - src[:, sl]).pow(2).sum(dim=(1, 2))
+                    d = be[:, sl].sum(dim=(1, 2))
                     nrm = src[:, sl].pow(2).sum(dim=(1, 2))
                     rel = (d / nrm).sqrt()
                     rel46 = None
-                    if x46 is not None:
-                        rel46 = float(((x46[:, sl] - src[:, sl]).pow(2).sum(dim=(1, 2)) / nrm).sqrt().mean())
+                    if be46 is not None:
+                        rel46 = float((be46[:, sl].sum(dim=(1, 2)) / nrm).sqrt().mean())
                     stats.append((n, float(rel.mean()), float(rel.max()),
                                   float((q["m4"][:, sl] > 0).float().mean()), float(d.sum()), float(nrm.sum()),
                                   rel46))
-                del xh, src, x46
+                del be, src, be46
         del w13, w2, q13, q2
     ms_layer = total_ms / layers
     bytes_layer = (rd + wr) / layers

@@ -22,7 +22,7 @@ DT_BF16, DT_F32 = 0, 1
 STATUS = {0: "FP4_OK", -1: "FP4_ERR_INVALID_ARG", -2: "FP4_ERR_SHAPE",
           -3: "FP4_ERR_UNSUPPORTED", -4: "FP4_ERR_WORKSPACE", -5: "FP4_ERR_HIP"}
 
-EXPORTED = ["fp4_quantize", "fp4_dequantize", "moe_fp4_workspace_layout",
+EXPORTED = ["fp4_quantize", "fp4_dequantize", "fp4_block_error", "moe_fp4_workspace_layout",
             "moe_fp4_workspace_size", "moe_fp4_forward", "moe_fp4_forward_profiled",
             "moe_fp4_route", "moe_fp4_tile_weights", "fp4_status_string", "fp4_last_error"]
 STAGES = ["permute", "x_quant", "gate_up", "h_quant", "down", "shared", "combine"]
@@ -73,6 +73,8 @@ def lib():
         L.fp4_quantize.restype = i32
         L.fp4_dequantize.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp, i32, vp]
         L.fp4_dequantize.restype = i32
+        L.fp4_block_error.argtypes = [i32, vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.fp4_block_error.restype = i32
         L.moe_fp4_workspace_layout.argtypes = [ctypes.POINTER(LayerStruct), i64, ctypes.POINTER(WsLayoutStruct)]
         L.moe_fp4_workspace_layout.restype = i32
         L.moe_fp4_workspace_size.argtypes = [ctypes.POINTER(LayerStruct), i64, ctypes.POINTER(sz)]
@@ -171,6 +173,18 @@ def route(logits: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None):
     w = torch.empty(T, k, dtype=torch.float32, device=logits.device)
     _check(lib().moe_fp4_route(_ptr(logits), _ptr(bias), T, E, k, _ptr(ids), _ptr(w), _stream()))
     return ids, w
+
+
+def block_error(x: torch.Tensor, q: dict, fmt: str) -> torch.Tensor:
+    """fp4_block_error: f32 squared error of every block of x's quantization
+    q (a record from quantize(), NVFP4 or MXFP4), shape x.shape[:-1] +
+    (cols / block,)."""
+    bs = 16 if fmt == "nvfp4" else 32
+    b, r, c = (int(v) for v in _dims(x))
+    err = torch.empty(*x.shape[:-1], x.shape[-1] // bs, dtype=torch.float32, device=x.device)
+    _check(lib().fp4_block_error(FMT[fmt], _ptr(x), _dtype_code(x), b, r, c, _ptr(q["codes"]), _ptr(q["scales"]),
+                                 _ptr(q.get("tensor_scale")), _ptr(err), _stream()))
+    return err
 
 
 def tile_weights(codes: torch.Tensor, scales: Optional[torch.Tensor], fmt: str = "mxfp4"):

@@ -743,6 +743,45 @@ __global__ void __launch_bounds__(256) quant_mxfp8_deq_kernel(const T* __restric
 }
 
 // fmt: 0 NVFP4, 1 MXFP4, 2 MXFP8, 3 FP8_BLOCK, 4 FP8_ROW.  One thread per 8 values.
+// Squared quantization error of each NVFP4 (FMT 0, 16 values) or MXFP4 (FMT 1,
+// 32 values) block: err[g] = sum over the block of (x - xhat)^2, xhat the
+// dequantized value exactly as dequant_kernel produces it, each difference,
+// square and sum rounded to f32.  One lane per block.
+template <int FMT, typename T>
+__global__ void __launch_bounds__(256) block_err_kernel(const T* __restrict__ x, const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ scales,
+                                                        const float* __restrict__ tensor_scale, int64_t per,
+                                                        int64_t nblocks, float* __restrict__ err) {
+  constexpr int BS = FMT == 0 ? 16 : 32;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= nblocks) return;
+  const int64_t e0 = g * BS;
+  float v[BS];
+  load_vals<BS>(x + e0, v);
+  float sb = 0.0f, S = 0.0f;
+  int e = 0;
+  if (FMT == 0) {
+    sb = e4m3_to_f32(scales[g]);
+    S = tensor_scale[e0 / per];
+  } else {
+    e = (int)scales[g] - 127;
+  }
+  const uint32_t* cw = reinterpret_cast<const uint32_t*>(codes + e0 / 2);
+  float acc = 0.0f;
+#pragma unroll
+  for (int w = 0; w < BS / 8; ++w) {
+    const uint32_t d = cw[w];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t c = (d >> (4 * j)) & 15u;
+      const float mag = FMT == 0 ? (e2m1_mag_to_f32(c & 7u) * sb) * S : ldexpf(e2m1_mag_to_f32(c & 7u), e);
+      const float diff = v[8 * w + j] - ((c & 8u) ? -mag : mag);
+      acc = fmaf(diff, diff, acc);
+    }
+  }
+  err[g] = acc;
+}
+
 template <int FMT, typename OutT>
 __global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const void* __restrict__ scales,
@@ -1071,6 +1110,41 @@ int fp4_dequantize(int fmt, const uint8_t* codes, const void* scales, const floa
   }
 #undef FP4_DQ
   return check_launch("dequant");
+}
+
+int fp4_block_error(int fmt, const void* x, int x_dtype, int64_t batch, int64_t rows, int64_t cols,
+                    const uint8_t* codes, const void* scales, const float* tensor_scale, float* err,
+                    void* stream) {
+  using namespace fp4;
+  if (fmt != FP4_FMT_NVFP4 && fmt != FP4_FMT_MXFP4)
+    return fail(FP4_ERR_UNSUPPORTED, "fp4_block_error: NVFP4 or MXFP4 only (got %d)", fmt);
+  if (x_dtype != FP4_DT_BF16 && x_dtype != FP4_DT_F32)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_block_error: unknown dtype %d", x_dtype);
+  if (batch < 0 || rows < 0 || cols < 0) return fail(FP4_ERR_SHAPE, "fp4_block_error: negative dimension");
+  const int bs = fmt == FP4_FMT_NVFP4 ? 16 : 32;
+  if (cols % bs) return fail(FP4_ERR_SHAPE, "fp4_block_error: cols %lld not a multiple of %d", (long long)cols, bs);
+  if (batch == 0 || rows == 0 || cols == 0) return FP4_OK;
+  if (!x || !codes || !scales || !err || (fmt == FP4_FMT_NVFP4 && !tensor_scale))
+    return fail(FP4_ERR_INVALID_ARG, "fp4_block_error: null pointer");
+  if (reinterpret_cast<uintptr_t>(x) % 16 || reinterpret_cast<uintptr_t>(codes) % 4)
+    return fail(FP4_ERR_INVALID_ARG, "fp4_block_error: x needs 16-byte and codes 4-byte alignment");
+  const int64_t per = rows * cols, nb = batch * per / bs;
+  const dim3 grid(grid_1d(nb, 256));
+  hipStream_t st = as_stream(stream);
+  const uint8_t* sc = reinterpret_cast<const uint8_t*>(scales);
+  if (fmt == FP4_FMT_NVFP4 && x_dtype == FP4_DT_BF16)
+    hipLaunchKernelGGL((block_err_kernel<0, uint16_t>), grid, dim3(256), 0, st,
+                       reinterpret_cast<const uint16_t*>(x), codes, sc, tensor_scale, per, nb, err);
+  else if (fmt == FP4_FMT_NVFP4)
+    hipLaunchKernelGGL((block_err_kernel<0, float>), grid, dim3(256), 0, st, reinterpret_cast<const float*>(x),
+                       codes, sc, tensor_scale, per, nb, err);
+  else if (x_dtype == FP4_DT_BF16)
+    hipLaunchKernelGGL((block_err_kernel<1, uint16_t>), grid, dim3(256), 0, st,
+                       reinterpret_cast<const uint16_t*>(x), codes, sc, tensor_scale, per, nb, err);
+  else
+    hipLaunchKernelGGL((block_err_kernel<1, float>), grid, dim3(256), 0, st, reinterpret_cast<const float*>(x),
+                       codes, sc, tensor_scale, per, nb, err);
+  return check_launch("block_err");
 }
 
 }  // extern "C"

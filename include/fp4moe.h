@@ -119,6 +119,23 @@ int fp4_dequantize(int fmt, const uint8_t* codes, const void* scales,
                    int64_t cols, void* out, int out_dtype, void* stream);
 
 /*
+ * fp4_block_error - the squared quantization error of every block, the
+ * quantity the 4/6 rule compares between its two candidate scales
+ * ("dabsLabs NVFP4", section "What makes this build different"):
+ *   err[g] = sum over block g of (x - xhat)^2,
+ * x [batch][rows][cols] (bf16 or f32, 16-byte aligned) and its NVFP4 (blocks
+ * of 16) or MXFP4 (blocks of 32) quantization (codes, scales, tensor_scale
+ * as fp4_quantize wrote them), xhat the f32 value fp4_dequantize gives; each
+ * difference, square and sum rounded to f32.  err: f32 [batch][rows][cols /
+ * block], device memory, caller-owned.  Errors: other formats ->
+ * FP4_ERR_UNSUPPORTED; cols % block -> FP4_ERR_SHAPE; null or misaligned
+ * pointer -> FP4_ERR_INVALID_ARG.  Stream-ordered, asynchronous.
+ */
+int fp4_block_error(int fmt, const void* x, int x_dtype, int64_t batch, int64_t rows,
+                    int64_t cols, const uint8_t* codes, const void* scales,
+                    const float* tensor_scale, float* err, void* stream);
+
+/*
  * One routed-expert MoE layer.  E experts, hidden H, expert intermediate I,
  * top-k routing.  Expert weights are stacked: fused gate_up W13 [E, 2I, H]
  * (rows [0, I) gate, [I, 2I) up) and down W2 [E, H, I], in the layouts of

@@ -336,6 +336,9 @@ def dequantize_fp8_rows(codes, scales, group: int = FP8_TILE) -> np.ndarray:
 
 
 def block_sq_error(x, xhat, size) -> np.ndarray:
-    """Per-block squared reconstruction error (float64), for statistics."""
+    """Per-block squared reconstruction error sum_i (x_i - xhat_i)^2 in
+    float64, blocks of `size` consecutive values along the last dimension:
+    the quantity the 4/6 rule compares ("dabsLabs NVFP4", section "What makes
+    this build different"), reported per block."""
     d = (np.asarray(x, np.float64) - np.asarray(xhat, np.float64)).reshape(-1, size)
     return np.sum(d * d, axis=1)

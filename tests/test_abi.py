@@ -64,6 +64,15 @@ def test_host_validation_errors(L):
     # FP8 block weights need rows % 128
     assert L.fp4_quantize(3, 0, 0, fake, 0, 1, 64, 128, fake, fake, None, None, None) == -2
     assert L.fp4_dequantize(0, fake, fake, None, 1, 4, 32, fake, 1, None) == -1
+    # block errors: NVFP4 / MXFP4 only, cols % block, null and misaligned pointers, empty is a no-op
+    odd = ctypes.c_void_p(0x1004)
+    assert L.fp4_block_error(2, fake, 0, 1, 4, 64, fake, fake, None, fake, None) == -3
+    assert L.fp4_block_error(0, fake, 0, 1, 4, 40, fake, fake, fake, fake, None) == -2
+    assert L.fp4_block_error(1, fake, 0, 1, 4, 48, fake, fake, None, fake, None) == -2
+    assert L.fp4_block_error(0, fake, 0, 1, 4, 64, fake, fake, None, fake, None) == -1  # NVFP4 needs S
+    assert L.fp4_block_error(1, odd, 0, 1, 4, 64, fake, fake, None, fake, None) == -1
+    assert L.fp4_block_error(1, fake, 7, 1, 4, 64, fake, fake, None, fake, None) == -1
+    assert L.fp4_block_error(1, None, 0, 0, 4, 64, None, None, None, None, None) == 0
     # routing: k outside [1, min(E, 32)], too many experts, empty batch, null outputs
     assert L.moe_fp4_route(fake, None, 4, 8, 0, fake, fake, None) == -1
     assert L.moe_fp4_route(fake, None, 4, 8, 9, fake, fake, None) == -1

@@ -270,3 +270,31 @@ def test_nvfp4_large_batch_chunked_amax(rule):
         o = Q.quantize_nvfp4(F.bf16_to_f64(bits[b, rows]), rule, tensor_scale=want_ts[b])
         np.testing.assert_array_equal(codes[b, rows], F.pack_nibbles(o["codes"]), err_msg=f"oracle rows {b}")
         np.testing.assert_array_equal(scales[b, rows], o["scales"], err_msg=f"oracle scales {b}")
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_block_error_matches_oracle(fmt, dtype):
+    """fp4_block_error on three tensors (several 256-wide tiles of blocks)
+    against the oracle's float64 block errors of its own 4/6 quantization of
+    the same values; the GPU sums in f32 (each difference, square and sum
+    rounded once), within 1e-5 relative per block."""
+    m = _lib()
+    print_case(f"block error {fmt} {dtype}")
+    rng = np.random.default_rng(21)
+    x32 = (rng.standard_t(4, size=(3, 40, 256)) * 0.02).astype(np.float32)
+    if dtype == "bf16":
+        bits = F.bf16_bits_from_f32(x32)
+        xt, x64 = dev_bf16(bits), F.bf16_to_f64(bits)
+    else:
+        xt, x64 = dev(x32), x32.astype(np.float64)
+    q = m.quantize(xt, fmt, "4over6")
+    err = host(m.block_error(xt, q, fmt))
+    bs = 16 if fmt == "nvfp4" else 32
+    assert err.shape == (3, 40, 256 // bs)
+    for b in range(3):
+        qo = _oracle_q(fmt, x64[b], "4over6")
+        xh = (Q.dequantize_nvfp4(qo["codes"], qo["scales"], qo["tensor_scale"]) if fmt == "nvfp4"
+              else Q.dequantize_mxfp4(qo["codes"], qo["scales"]))
+        ref = Q.block_sq_error(x64[b], xh, bs).reshape(40, 256 // bs)
+        assert np.all(np.abs(err[b] - ref) <= 1e-5 * ref + 1e-30), f"tensor {b}"

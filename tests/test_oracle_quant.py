@@ -534,3 +534,45 @@ def test_mx_sweep_equals_four_over_six():
         a, b = Q.quantize_mxfp4(x, "sweep"), Q.quantize_mxfp4(x, "4over6")
         for k in ("codes", "scales", "m4"):
             np.testing.assert_array_equal(a[k], b[k])
+
+
+# ------------------------------------------------------------- block errors
+
+def test_block_error_hand_example_mx():
+    """MXFP4 block [1.0, 0.7, 0, ...]: amax 1 gives e = -2 (6 * 2^-2 >= 1 >
+    6 * 2^-3) under both plans, unit 0.25; 1.0 -> code 4 exactly, 0.7 / 0.25
+    = 2.8 -> nearest E2M1 3 -> 0.75; error (0.7 - 0.75)^2."""
+    x = np.zeros((1, 32))
+    x[0, 0], x[0, 1] = 1.0, 0.7
+    for rule in ("rtn", "4over6"):
+        q = Q.quantize_mxfp4(x, rule)
+        assert q["scales"][0, 0] == 127 - 2
+        err = Q.block_sq_error(x, Q.dequantize_mxfp4(q["codes"], q["scales"]), 32)
+        assert err.shape == (1,) and abs(err[0] - (0.7 - 0.75) ** 2) < 1e-15
+
+
+def test_block_error_four_over_six_never_worse_per_block():
+    """The 4/6 rule keeps, block by block, the plan with the smaller error, so
+    its block errors never exceed those of the block-max-to-6 plan (RTN), and
+    are strictly smaller exactly where it took the block-max-to-4 plan."""
+    rng = np.random.default_rng(5)
+    x = rng.standard_t(4, size=(6, 128)) * 0.02
+    q6 = Q.quantize_nvfp4(x, "rtn")
+    q46 = Q.quantize_nvfp4(x, "4over6")
+    e6 = Q.block_sq_error(x, Q.dequantize_nvfp4(q6["codes"], q6["scales"], q6["tensor_scale"]), 16)
+    e46 = Q.block_sq_error(x, Q.dequantize_nvfp4(q46["codes"], q46["scales"], q46["tensor_scale"]), 16)
+    m4 = np.asarray(q46["m4"]).reshape(-1).astype(bool)
+    assert e6.shape == e46.shape == (6 * 128 // 16,)
+    assert np.all(e46 <= e6 * (1 + 1e-12))
+    assert np.all(e46[m4] < e6[m4]) and np.array_equal(e46[~m4], e6[~m4]) and m4.any() and (~m4).any()
+
+
+def test_block_error_zero_on_the_grid():
+    """Values that are already dequantized MXFP4 values of one block scale
+    quantize to themselves: every block error is 0."""
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((4, 64))
+    q = Q.quantize_mxfp4(x, "rtn")
+    grid = Q.dequantize_mxfp4(q["codes"], q["scales"])
+    q2 = Q.quantize_mxfp4(grid, "rtn")
+    assert np.all(Q.block_sq_error(grid, Q.dequantize_mxfp4(q2["codes"], q2["scales"]), 32) == 0.0)
