@@ -26,7 +26,8 @@
  *    device, one helper stream with two events (created by the first forward
  *    of a layer with a shared expert; the shared expert runs on it,
  *    overlapped with the routed experts, forked from and joined back into
- *    the caller's stream).
+ *    the caller's stream), the device's compute-unit count, and one bit per
+ *    GEMM kernel recording that its dynamic-LDS limit has been raised.
  *  - `stream` is a hipStream_t (NULL = default stream).  Calls only enqueue
  *    work and return; a launch failure returns FP4_ERR_HIP, asynchronous faults
  *    surface at the caller's next synchronisation.
