@@ -526,6 +526,40 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
   }
 }
 
+// h of an MX gate_up tile straight to MXFP8.  With 128-output tiles a wave's
+// 32 outputs of a row are one block of 32 (two 16-column subtiles), so the
+// block amax is a max over the lane's two values and its 15 partner lanes;
+// exponent and codes as the standalone MXFP8 quantizer takes them (the max
+// is exact in any order, and the power-of-two scaling makes each convert
+// exact).  acc[i][j] holds gate and acc[i][2 + j] up of subtile j for rows
+// row0 + 16 i + 4 lg + r (r the accumulator element), column 16 j + lr of
+// the block; blk is the block's index within the row.
+__device__ __forceinline__ void store_h_mxfp8(const GemmArgs& g, const floatx4 (&acc)[4][4], int blk, int row0,
+                                              int n_rows, int64_t r_begin, int lg, int lr) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) v[j] = silu_f32(acc[i][j][r]) * acc[i][2 + j][r];
+      float amax = fmaxf(fabsf(v[0]), fabsf(v[1]));
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
+      const int ex = mx_exponent(amax, kE4M3Max);
+      const int rr = row0 + 16 * i + 4 * lg + r;
+      if (rr >= n_rows) continue;
+      const int64_t R = r_begin + rr;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t c = e4m3_hw(fminf(ldexpf(fabsf(v[j]), -ex), kE4M3Max)) |
+                           ((__float_as_uint(v[j]) >> 24) & 0x80u);
+        g.q_codes[R * g.N + 32 * blk + 16 * j + lr] = (uint8_t)c;
+      }
+      if (lr == 0) g.q_scales[R * (g.N / 32) + blk] = (uint8_t)(ex + 127);
+    }
+}
+
 // ------------------------------------------- MX path with LDS-DMA staging
 //
 // MXFP4 weights x MXFP8 activations.  Same tile as above (64 rows x 64*NSUB
@@ -754,34 +788,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx_kernel(GemmArgs g) {
   // ---- epilogue
   if constexpr (EPI == EPI_GATEUP && NSUB == 2) {
     if (g.q_codes) {
-      // h straight to MXFP8: a wave's 32 outputs of a row are one block of
-      // 32 (two subtiles of 16 lanes each), so the block amax is a max over
-      // the lane's two values and its 15 partner lanes; exponent and codes
-      // as the standalone MXFP8 quantizer takes them (the max is exact in
-      // any order, and the power-of-two scaling makes each convert exact)
-      const int blk = (nt * BN) / 32 + wave;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v[2];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) v[j] = silu_f32(acc[i][j][r]) * acc[i][2 + j][r];
-          float amax = fmaxf(fabsf(v[0]), fabsf(v[1]));
-#pragma unroll
-          for (int off = 8; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 16));
-          const int ex = mx_exponent(amax, kE4M3Max);
-          const int rr = mt * BM + 16 * i + 4 * lg + r;
-          if (rr >= n_rows) continue;
-          const int64_t R = r_begin + rr;
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const uint32_t c = e4m3_hw(fminf(ldexpf(fabsf(v[j]), -ex), kE4M3Max)) |
-                               ((__float_as_uint(v[j]) >> 24) & 0x80u);
-            g.q_codes[R * g.N + 32 * blk + 16 * j + lr] = (uint8_t)c;
-          }
-          if (lr == 0) g.q_scales[R * (g.N / 32) + blk] = (uint8_t)(ex + 127);
-        }
+      store_h_mxfp8(g, acc, (nt * BN) / 32 + wave, mt * BM, n_rows, r_begin, lg, lr);
       return;
     }
   }
@@ -824,7 +831,9 @@ struct Mx2Cfg {
   static constexpr int NU = EPI == EPI_GATEUP ? 2 : 1;
   static constexpr int NS = NU * NSUB;          // 16-column weight subtiles per wave
   static constexpr int RS = KS < 8 ? KS : 8;    // activation stages in the LDS ring
-  static constexpr int D = KS < 3 ? KS : 3;     // steps of weight fragments in flight per wave
+  // steps of weight fragments in flight per wave (2 for the MX gate_up, whose
+  // 4 weight subtiles per wave would otherwise spill)
+  static constexpr int D = KS < 3 ? KS : (GK == GK_MX && NS >= 4 ? 2 : 3);
   static constexpr int A_BYTES = BM * 128;
   // per row and step one scale dword: 4 UE8M0 block scales (MX) or the f32
   // scale of the 128-block (FP8); either way K/32 bytes per row
@@ -1092,6 +1101,12 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   // registers through every step)
   int z0;
   asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+  if constexpr (GK == GK_MX && EPI == EPI_GATEUP && NSUB == 2) {
+    if (g.q_codes) {
+      store_h_mxfp8(g, acc, (nt * BN) / 32 + wave, mt * BM + z0, n_rows, r_begin, lg, lr);
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1446,6 +1461,10 @@ __global__ void __launch_bounds__(256) tile_weights_kernel(const uint8_t* __rest
 // inter of 640, and the block-FP8 gate_up over its hidden of 2560.
 static bool mx_down_on_mx2(int N, int K) { return N % 128 == 0 && K == 640; }
 static bool fp8_gateup_on_mx2(int N, int K) { return N % 64 == 0 && K == 2560; }
+// the MX gate_up over the model's hidden of 2560 on 128-output tiles, when
+// its weights are tiled (then faster than the all-DMA kernel; on row-major
+// weights the all-DMA kernel is the faster one)
+static bool mx_gateup_on_mx2(int N, int K) { return N % 128 == 0 && K == 2560; }
 
 // Workgroups of a grouped GEMM launch: M-tile bound x output tiles, rounded
 // up to a multiple of the 8 XCDs (the tile remapping needs whole rounds).
@@ -1596,6 +1615,7 @@ static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st)
     if (mx_down_on_mx2(a.N, a.K)) return launch_gemm_mx2<GK_MX, EPI, 2, 5>(a, tiles_m_bound, st);
   }
   if constexpr (EPI == EPI_GATEUP) {
+    if (a.w_tiled && mx_gateup_on_mx2(a.N, a.K)) return launch_gemm_mx2<GK_MX, EPI, 2, 20>(a, tiles_m_bound, st);
     if (a.N % 128 == 0) return launch_gemm_mx<EPI, 2>(a, tiles_m_bound, st);
     if (a.q_codes) return fail(FP4_ERR_UNSUPPORTED, "MXFP8 h epilogue needs 128-output gate_up tiles");
     if (a.N % 64 == 0) return launch_gemm_mx<EPI, 1>(a, tiles_m_bound, st);
