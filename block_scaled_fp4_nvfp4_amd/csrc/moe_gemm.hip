@@ -1225,7 +1225,10 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
     __syncthreads();
     nt = L % NT;
     const int mg = L / NT;
-    if (mg >= s_toff[g.E]) return;
+    if (mg >= s_toff[g.E]) {
+      if (EPI == EPI_GATEUP && g.amax_part && threadIdx.x == 0) g.amax_part[L] = 0.0f;
+      return;
+    }
     int lo = 0, hi = g.E;
     while (hi - lo > 1) {
       int mid = (lo + hi) >> 1;
@@ -1366,6 +1369,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
   int z0;
   asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
   const float scale = g.a_tensor_scale[0] * g.w_tensor_scale[e];
+  float vmax = 0.0f;  // max |h| stored by this lane (gate_up)
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1379,6 +1383,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
         float v;
         if (EPI == EPI_GATEUP) {
           v = silu_f32(acc[i][j][r] * scale) * (acc[i][NSUB + j][r] * scale);
+          vmax = fmaxf(vmax, fabsf(v));
         } else {
           v = acc[i][j][r] * scale;
           if (g.row_scale) v *= g.row_scale[R];
@@ -1386,6 +1391,22 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
         g.out[R * g.N + n] = v;
       }
     }
+  if constexpr (EPI == EPI_GATEUP) {
+    if (g.amax_part) {  // as in the register-staged kernel: max |h| of the workgroup
+      __shared__ float red[4];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+      if (lane == 0) red[wave] = vmax;
+      __syncthreads();
+      if (tid == 0) g.amax_part[L] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    }
+  }
+}
+
+// Workgroups of a grouped GEMM launch: M-tile bound x output tiles, rounded
+// up to a multiple of the 8 XCDs (the tile remapping needs whole rounds).
+static int64_t gemm_grid(int64_t tiles_m_bound, int N, int BN) {
+  return (tiles_m_bound * (N / BN) + 7) / 8 * 8;
 }
 
 // Raises a kernel's dynamic-LDS limit on the current device the first time
@@ -1405,13 +1426,16 @@ static int raise_dyn_lds(const void* kernel, int bytes, std::atomic<uint64_t>& r
 template <int EPI, int NSUB, int KS, bool WT>
 static int launch_gemm_nv2_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   using C = Nv2Cfg<EPI, NSUB, KS>;
-  const int NT = a.N / C::BN;
-  int64_t G = tiles_m_bound * NT;
-  G = (G + 7) / 8 * 8;
+  const int64_t G = gemm_grid(tiles_m_bound, a.N, C::BN);
+  if (a.amax_part && G != a.amax_nparts)
+    return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM: %lld partial maxima expected, %lld workgroups",
+                (long long)a.amax_nparts, (long long)G);
   if (G <= 0) return FP4_OK;
   if (G > INT32_MAX) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM grid too large");
   const size_t lds = a.dense_rows > 0 ? 0 : sizeof(int) * ((size_t)a.E + 1);
-  constexpr size_t fixed = (size_t)C::RS * C::RAW + 2 * (size_t)C::DEC + 512;
+  // static LDS: the raw and decoded stages, 512 bytes of other arrays and 64
+  // for the gate_up epilogue's reduction
+  constexpr size_t fixed = (size_t)C::RS * C::RAW + 2 * (size_t)C::DEC + 512 + 64;
   if (fixed + lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
   static std::atomic<uint64_t> lds_raised{0};
   FP4_CHECK(raise_dyn_lds(reinterpret_cast<const void*>(&grouped_gemm_nv2_kernel<EPI, NSUB, KS, WT>),
@@ -1465,12 +1489,6 @@ static bool fp8_gateup_on_mx2(int N, int K) { return N % 64 == 0 && K == 2560; }
 // its weights are tiled (then faster than the all-DMA kernel; on row-major
 // weights the all-DMA kernel is the faster one)
 static bool mx_gateup_on_mx2(int N, int K) { return N % 128 == 0 && K == 2560; }
-
-// Workgroups of a grouped GEMM launch: M-tile bound x output tiles, rounded
-// up to a multiple of the 8 XCDs (the tile remapping needs whole rounds).
-static int64_t gemm_grid(int64_t tiles_m_bound, int N, int BN) {
-  return (tiles_m_bound * (N / BN) + 7) / 8 * 8;
-}
 
 // sigmoid(x_t . gate) for every token (one wave per token), bf16 x and gate.
 __global__ void __launch_bounds__(256) shared_gate_kernel(const uint16_t* __restrict__ x,
@@ -1588,6 +1606,10 @@ static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st)
     // faster there; over K = 2560 the register-staged kernel is faster)
     if constexpr (EPI == EPI_DOWN) {
       if (a.N % 128 == 0 && a.K == 640) return launch_gemm_nv2<EPI, 2, 5>(a, tiles_m_bound, st);
+    } else {
+      // gate_up over the model's hidden of 2560 on tiled weights: the
+      // register-fed kernel (on row-major weights the register-staged one)
+      if (a.w_tiled && a.N % 128 == 0 && a.K == 2560) return launch_gemm_nv2<EPI, 2, 20>(a, tiles_m_bound, st);
     }
     return launch_gemm_w<GK, EPI, false>(a, tiles_m_bound, st);
   }
