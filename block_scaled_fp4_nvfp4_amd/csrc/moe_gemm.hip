@@ -831,9 +831,9 @@ struct Mx2Cfg {
   static constexpr int NU = EPI == EPI_GATEUP ? 2 : 1;
   static constexpr int NS = NU * NSUB;          // 16-column weight subtiles per wave
   static constexpr int RS = KS < 8 ? KS : 8;    // activation stages in the LDS ring
-  // steps of weight fragments in flight per wave (2 for the MX gate_up, whose
-  // 4 weight subtiles per wave would otherwise spill)
-  static constexpr int D = KS < 3 ? KS : (GK == GK_MX && NS >= 4 ? 2 : 3);
+  // steps of weight fragments in flight per wave (2 for the 128-output
+  // gate_up tiles, whose 4 weight subtiles per wave would spill more)
+  static constexpr int D = KS < 3 ? KS : (NS >= 4 ? 2 : 3);
   static constexpr int A_BYTES = BM * 128;
   // per row and step one scale dword: 4 UE8M0 block scales (MX) or the f32
   // scale of the 128-block (FP8); either way K/32 bytes per row
@@ -1619,6 +1619,11 @@ static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st)
     if constexpr (EPI == EPI_DOWN) {
       if (mx_down_on_mx2(a.N, a.K)) return launch_gemm_mx2<GK_FP8, EPI, 2, 5>(a, tiles_m_bound, st);
     } else {
+      // 128-output tiles on tiled weights when they still give every CU 16
+      // workgroups (8192 tokens: 686 against 750 us); decode batches, whose
+      // grid the wider tiles would halve, and row-major weights keep 64
+      if (a.w_tiled && a.N % 128 == 0 && a.K == 2560 && tiles_m_bound * (a.N / 128) >= 16LL * device_cu_count())
+        return launch_gemm_mx2<GK_FP8, EPI, 2, 20>(a, tiles_m_bound, st);
       if (fp8_gateup_on_mx2(a.N, a.K)) return launch_gemm_mx2<GK_FP8, EPI, 1, 20>(a, tiles_m_bound, st);
     }
     if (a.w_tiled) return fail(FP4_ERR_UNSUPPORTED, "tiled weights on a GEMM kernel that reads rows");
