@@ -91,11 +91,6 @@ def e2m1_encode(x) -> np.ndarray:
     return (mag | (np.signbit(x).astype(np.int64) << 3)).astype(np.uint8)
 
 
-def f32_round(v) -> np.ndarray:
-    """Round float64 value(s) to float32 (IEEE round-to-nearest-even)."""
-    return np.asarray(v, dtype=np.float64).astype(np.float32)
-
-
 def bf16_bits_from_f32(a) -> np.ndarray:
     """float32 -> bfloat16 bit patterns, round-to-nearest-even (finite inputs)."""
     u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
@@ -104,6 +99,8 @@ def bf16_bits_from_f32(a) -> np.ndarray:
 
 
 def bf16_to_f64(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> float64: a bf16 value is the float32 whose
+    upper 16 bits are its pattern and whose lower 16 bits are zero."""
     return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 

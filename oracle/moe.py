@@ -80,10 +80,14 @@ def route(logits, bias, k: int):
 
 
 def silu(v):
+    """SiLU(v) = v * sigmoid(v), the gate activation of the SwiGLU experts
+    (FP4-Local AZ card, "The shared expert": silu(0) * 0 = 0)."""
     return v / (1.0 + np.exp(-v))
 
 
 def sigmoid(v):
+    """Logistic sigmoid 1 / (1 + e^-v): the shared expert's per-token gate
+    (FP4-Local AZ card, "The shared expert")."""
     return 1.0 / (1.0 + np.exp(-v))
 
 

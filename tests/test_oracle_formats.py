@@ -109,3 +109,31 @@ def test_bf16_rne():
     ref = torch.from_numpy(np.random.default_rng(4).standard_normal(10000).astype(np.float32))
     np.testing.assert_array_equal(F.bf16_bits_from_f32(ref.numpy()),
                                   ref.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+def _bf16_decoder_pins_hold(dec):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns
+        ours = dec(bits)
+    finite = np.isfinite(ref)
+    ok = np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok &= np.array_equal(ours[finite], ref[finite]) and np.array_equal(ours[np.isinf(ref)], ref[np.isinf(ref)])
+    # landmarks of the format: 1, -2, the largest finite value, the smallest subnormal, -0
+    ok &= dec(np.uint16(0x3F80)) == 1.0 and dec(np.uint16(0xC000)) == -2.0
+    ok &= dec(np.uint16(0x7F7F)) == (2.0 - 2.0 ** -7) * 2.0 ** 127
+    ok &= dec(np.uint16(0x0001)) == 2.0 ** -133
+    ok &= bool(np.signbit(dec(np.uint16(0x8000))))
+    return bool(ok)
+
+
+def test_bf16_decode_all_patterns():
+    """bf16_to_f64 against torch's bfloat16 -> float64 conversion on all 65,536
+    bit patterns (NaN patterns only checked to decode as NaN)."""
+    assert _bf16_decoder_pins_hold(F.bf16_to_f64)
+    # planted mistakes each fail: a wrong shift, the pattern's bytes swapped
+    assert not _bf16_decoder_pins_hold(
+        lambda b: (np.asarray(b, np.uint16).astype(np.uint32) << 15).view(np.float32).astype(np.float64))
+    assert not _bf16_decoder_pins_hold(
+        lambda b: (np.asarray(b, np.uint16).byteswap().astype(np.uint32) << 16).view(np.float32)
+        .astype(np.float64))

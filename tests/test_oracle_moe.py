@@ -159,6 +159,50 @@ def test_shared_expert_gate_and_band():
     np.testing.assert_allclose(g0 / out, (0.5 / gate)[:, None] * np.ones_like(out), rtol=1e-12)
 
 
+# ------------------------------------------------ activation functions
+# The shared expert's gate is a sigmoid and every expert's gate activation is
+# SiLU (FP4-Local AZ card, "The shared expert").  Pinned by identities and
+# closed-form values of the functions, not by restating their formulas.
+
+def _sigmoid_pins_hold(f):
+    v = np.linspace(-30.0, 30.0, 601)
+    ok = np.allclose(f(v) + f(-v), 1.0, rtol=0, atol=1e-15)          # symmetry
+    ok &= abs(f(np.float64(math.log(3.0))) - 0.75) < 1e-15           # e^-ln3 = 1/3 -> 1/(1+1/3)
+    ok &= f(np.float64(0.0)) == 0.5
+    ok &= bool(np.all(np.diff(f(v)) > 0))                            # increasing
+    ok &= 0.0 < f(np.float64(-40.0)) < 1e-17                         # ~ e^-40 = 4.25e-18
+    ok &= f(np.float64(40.0)) == 1.0
+    return bool(ok)
+
+
+def _silu_pins_hold(f):
+    v = np.linspace(-30.0, 30.0, 601)
+    ok = np.allclose(f(v) - f(-v), v, rtol=0, atol=1e-13)             # silu(v) - silu(-v) = v
+    ok &= abs(f(np.float64(math.log(3.0))) - 0.75 * math.log(3.0)) < 1e-15
+    ok &= f(np.float64(0.0)) == 0.0
+    ok &= -1e-15 < f(np.float64(-40.0)) < 0.0                        # ~ -40 e^-40
+    ok &= f(np.float64(40.0)) == 40.0
+    # minimum near v = -1.2785 (root of 1 + v (1 - sigmoid(v)) = 0), value -0.27846
+    ok &= abs(float(np.min(f(np.linspace(-3, 0, 30001)))) + 0.278464542761074) < 1e-9
+    return bool(ok)
+
+
+def test_sigmoid_closed_forms():
+    assert _sigmoid_pins_hold(moe.sigmoid)
+    # planted mistakes each fail: sign flip, the complement, a doubled slope
+    assert not _sigmoid_pins_hold(lambda v: 1.0 / (1.0 + np.exp(v)))
+    assert not _sigmoid_pins_hold(lambda v: np.exp(-v) / (1.0 + np.exp(-v)))
+    assert not _sigmoid_pins_hold(lambda v: 1.0 / (1.0 + np.exp(-2.0 * v)))
+
+
+def test_silu_closed_forms():
+    assert _silu_pins_hold(moe.silu)
+    assert not _silu_pins_hold(lambda v: v / (1.0 + np.exp(v)))           # sign flip
+    assert not _silu_pins_hold(lambda v: v / (1.0 + np.exp(-2.0 * v)))    # doubled slope
+    assert not _silu_pins_hold(lambda v: 1.0 / (1.0 + np.exp(-v)))        # the sigmoid alone
+    assert not _silu_pins_hold(lambda v: np.maximum(v, 0.0))              # ReLU
+
+
 # ----------------------------------------------------------------- routing
 
 def test_route_hand_example_and_ties():
