@@ -29,6 +29,13 @@ Readings where the cards are silent (each is listed in the design notes):
     the M=6 plan's to the M=4 plan's inclusive and keeps the first with the
     smallest exact post-rounding squared error; it contains both 4/6 plans,
     so its error never exceeds 4/6's;
+  * the Hessian-weighted search (the "local_hessian" / H-Scale search the
+    Local-Hessian card names in "What is different about it" and "Results",
+    without defining it): the sweep's candidates, each block's error weighted
+    by the 16 x 16 diagonal block H_b of the expert's input Hessian,
+    err = d^T H_b d with d = x - xhat (signed), the first candidate with the
+    smallest exact error kept; tensor scale amax/2688 unchanged; experts with
+    fewer than 64 calibration rows take plain max (the amax/6 plan);
   * MXFP4 plan M: e_M = min{e : M * 2^e >= amax_b}, clamped to [-127, 127]
     (the no-clip ceiling rule, as in the MXFP8 rule of the AZ card);
   * block FP8: one fp32 scale sigma = fp32(amax / 448) per 128 x 128 weight
@@ -174,6 +181,113 @@ def quantize_nvfp4(x, rule: str = "4over6", tensor_scale=None):
         "tensor_scale": np.float32(S),
         "m4": choose4.reshape(x.shape[:-1] + (x.shape[-1] // NV_BLOCK,)),
     }
+
+
+HESSIAN_MIN_ROWS = 64  # "experts with a full Hessian (>= 64 routed rows)"
+
+
+def _exact_weighted_error(x_row, q_row, H) -> Fraction:
+    """sum_ij H_ij d_i d_j with d = x - q, in exact rational arithmetic."""
+    d = [Fraction(float(a)) - Fraction(float(b)) for a, b in zip(x_row, q_row)]
+    Hf = [[Fraction(float(v)) for v in row] for row in H]
+    return sum(Hf[i][j] * d[i] * d[j] for i in range(len(d)) for j in range(len(d)))
+
+
+def quantize_nvfp4_hessian(x, hessian, calib_rows: int, tensor_scale=None):
+    """NVFP4 quantization of one expert matrix x [rows, cols] (cols % 16 == 0)
+    with block scales chosen by a Hessian-weighted search.
+
+    Local-Hessian NVFP4 card, "What is different about it": the per-group
+    weight scales come from a Hessian-weighted search ("local_hessian",
+    H-Scale) instead of the plain amax/MSE sweep, and only the weight_scale
+    values differ (same format, same tensor scale); "Results": experts with a
+    full Hessian have >= 64 routed calibration rows, thinner ones (including
+    none) keep plain max.  The search itself is not defined on the pages.
+    Reading:
+      * hessian [cols/16, 16, 16]: H_b, the diagonal 16 x 16 block of the
+        expert's input Hessian (1/n) sum_t a_t a_t^T for the columns of block b
+        (the output error of a block of row r over the calibration rows is
+        d^T H_b d, cross-block terms left out: "local");
+      * candidates: every E4M3 scale code from the amax/6 plan's to the
+        block-max-to-4 plan's, in increasing order (the sweep's window),
+        codes by E2M1 round-to-nearest-even of x / (s * S);
+      * err = sum_ij H_b[i, j] d_i d_j with d = x - xhat signed; the first
+        candidate with the smallest exact err is kept;
+      * calib_rows < 64: the amax/6 plan (plain max) for every block.
+    The float64 errors decide unless two are within 2^-40 of the sum of
+    sum_ij |H_ij| |d_i| |d_j| of both (their rounding error is below 2^-47 of
+    it); those are decided in exact rational arithmetic.
+    Returns dict: codes (nibbles [rows, cols]), scales (uint8 [rows, cols/16]),
+    tensor_scale (float32), choice (uint8 [rows, cols/16]: chosen code minus
+    the amax/6 plan's)."""
+    x = np.asarray(x, dtype=np.float64)
+    R, C = x.shape
+    if C % NV_BLOCK:
+        raise ValueError("cols must be a multiple of 16")
+    if calib_rows < HESSIAN_MIN_ROWS:
+        q = quantize_nvfp4(x, "rtn", tensor_scale)
+        q["choice"] = np.zeros(q["scales"].shape, np.uint8)
+        return q
+    H = np.asarray(hessian, dtype=np.float64)
+    nb = C // NV_BLOCK
+    if H.shape != (nb, NV_BLOCK, NV_BLOCK):
+        raise ValueError("hessian must be [cols/16, 16, 16]")
+    blk = x.reshape(-1, NV_BLOCK)
+    absx = np.abs(blk)
+    sgn = np.where(np.signbit(blk), -1.0, 1.0)
+    Hb = np.broadcast_to(H[None], (R, nb, NV_BLOCK, NV_BLOCK)).reshape(-1, NV_BLOCK, NV_BLOCK)
+    absH = np.abs(Hb)
+    if tensor_scale is None:
+        tensor_scale = nvfp4_tensor_scale(np.max(absx) if absx.size else 0.0)
+    S = np.float64(np.float32(tensor_scale))
+    amax_b = np.max(absx, axis=1)
+
+    def plan_scale(M):
+        if S == 0.0:
+            return np.zeros(len(amax_b), np.int64)
+        return e4m3_encode(amax_b / (M * S)).astype(np.int64)
+
+    def candidate(code):
+        unit = e4m3_decode(code) * S
+        safe = np.where(unit > 0, unit, 1.0)[:, None]
+        mag = np.where(unit[:, None] > 0, round_to_grid(absx, safe, E2M1_GRID), 0)
+        q = sgn * E2M1_GRID[mag] * unit[:, None]          # exact (<= 31 significant bits)
+        d = blk - q                                       # exact (see the design notes)
+        err = np.einsum("ni,nij,nj->n", d, Hb, d)
+        bound = np.einsum("ni,nij,nj->n", np.abs(d), absH, np.abs(d))
+        return mag, q, err, bound
+
+    s6, s4 = plan_scale(6.0), plan_scale(4.0)
+    best_code = s6.copy()
+    best_mag, best_q, best_err, best_bound = candidate(s6)
+    width = s4 - s6
+    for off in range(1, int(width.max(initial=0)) + 1):
+        live = off <= width
+        code = np.where(live, s6 + off, s6)
+        mag, q, err, bound = candidate(code)
+        take = err < best_err
+        close = np.abs(err - best_err) <= 2.0 ** -40 * (bound + best_bound)
+        for b in np.nonzero(close & live)[0]:
+            hb = H[b % nb]
+            take[b] = _exact_weighted_error(blk[b], q[b], hb) < _exact_weighted_error(blk[b], best_q[b], hb)
+        take &= live
+        best_code = np.where(take, code, best_code)
+        best_mag = np.where(take[:, None], mag, best_mag)
+        best_q = np.where(take[:, None], q, best_q)
+        best_err = np.where(take, err, best_err)
+        best_bound = np.where(take, bound, best_bound)
+    codes = (best_mag | (np.signbit(blk).astype(np.int64) << 3)).astype(np.uint8)
+    return {"codes": codes.reshape(R, C), "scales": best_code.astype(np.uint8).reshape(R, nb),
+            "tensor_scale": np.float32(S), "choice": (best_code - s6).astype(np.uint8).reshape(R, nb)}
+
+
+def hessian_weighted_error(x, codes, scales, tensor_scale, hessian) -> np.ndarray:
+    """Per-block d^T H_b d (float64) of a quantization of x [rows, cols]: the
+    quantity the Hessian-weighted search minimizes, for reporting."""
+    x = np.asarray(x, np.float64)
+    R, C = x.shape
+    d = (x - dequantize_nvfp4(codes, scales, tensor_scale)).reshape(R, C // NV_BLOCK, NV_BLOCK)
+    return np.einsum("rbi,bij,rbj->rb", d, np.asarray(hessian, np.float64), d)
 
 
 def dequantize_nvfp4(codes, scales, tensor_scale) -> np.ndarray:

@@ -18,7 +18,8 @@ Seeding: numpy PCG64 seeded by SeedSequence(entropy=<seed>, spawn_key=<key>),
 with key = (stream, ...).  Streams: 0 routed weights (layer, expert, proj
 with 0 gate / 1 up / 2 down), 1 activations, 2 router logits, 3 router bias,
 4 shared-expert weights (proj 0 gate / 1 up / 2 down), 5 shared-expert gate
-vector, 6 outlier rows of the streaming workload.  Values are drawn in
+vector, 6 outlier rows of the streaming workload, 7 calibration activations,
+8 calibration row counts.  Values are drawn in
 float32 and rounded to bfloat16 by round-to-nearest-even.
 """
 from __future__ import annotations
@@ -33,11 +34,11 @@ __all__ = [
     "MoEConfig", "CONFIGS", "FP8_ROUTED_LAYERS", "stack_configs", "rng", "f32_to_bf16_bits", "bf16_bits_to_f32",
     "normal_bf16", "expert_weights", "layer_weights", "activations",
     "router_logits", "router_bias", "route", "routing", "shared_expert",
-    "streaming_expert",
+    "streaming_expert", "calibration_hessian", "calibration_rows",
 ]
 
 STREAM_WEIGHTS, STREAM_X, STREAM_LOGITS, STREAM_BIAS, STREAM_SHARED, \
-    STREAM_SHARED_GATE, STREAM_OUTLIERS = range(7)
+    STREAM_SHARED_GATE, STREAM_OUTLIERS, STREAM_CALIB, STREAM_CALIB_ROWS = range(9)
 WEIGHT_STD = 0.02
 
 
@@ -224,3 +225,37 @@ def streaming_expert(layer: int, e: int, hidden: int = 2560, inter: int = 640,
         v[rows] *= np.float32(8.0)
         outs.append(f32_to_bf16_bits(v))
     return np.concatenate(outs[:2], axis=0), outs[2]
+
+
+def calibration_rows(seed: int, num_experts: int) -> np.ndarray:
+    """Calibration rows routed to each expert (int32 [E]): log-normal around
+    the median of 5,007 rows per expert that the Local-Hessian card reports
+    ("Calibration data"), at least 64, except one expert with no rows and one
+    with 30 (the card's thin experts, which keep plain-max scales)."""
+    g = rng(seed, STREAM_CALIB_ROWS)
+    n = np.maximum(64, np.round(5007.0 * np.exp(0.8 * g.standard_normal(num_experts)))).astype(np.int32)
+    if num_experts >= 4:
+        n[1] = 0
+        n[2] = 30
+    return n
+
+
+def calibration_hessian(seed: int, expert: int, in_dim: int, n_rows: int, proj: int = 0) -> np.ndarray:
+    """Synthetic local Hessian blocks of one expert matrix's input: n_rows
+    calibration activation rows a_t (bf16 values; per-channel scales
+    log-normal with sigma 0.5; within each 16-column block a shared
+    component of weight c_b ~ U(0, 1), so the blocks are correlated), and
+    H_b = (1/n) sum_t a_t,b a_t,b^T over the 16 columns of block b, summed in
+    float64 and rounded to float32.  Returns float32 [in_dim/16, 16, 16];
+    zeros when n_rows == 0."""
+    nb = in_dim // 16
+    if n_rows == 0:
+        return np.zeros((nb, 16, 16), np.float32)
+    g = rng(seed, STREAM_CALIB, expert, proj)
+    scale = np.exp(0.5 * g.standard_normal(in_dim)).astype(np.float32)
+    c = g.uniform(0.0, 1.0, nb).astype(np.float32)
+    z = g.standard_normal((n_rows, in_dim), dtype=np.float32)
+    sh = g.standard_normal((n_rows, nb), dtype=np.float32)
+    a = (z + np.repeat(c[None, :] * sh, 16, axis=1)) * scale[None, :]
+    a = bf16_bits_to_f32(f32_to_bf16_bits(a)).astype(np.float64).reshape(n_rows, nb, 16)
+    return (np.einsum("tbi,tbj->bij", a, a) / n_rows).astype(np.float32)
