@@ -24,7 +24,9 @@ STATUS = {0: "FP4_OK", -1: "FP4_ERR_INVALID_ARG", -2: "FP4_ERR_SHAPE",
 
 EXPORTED = ["fp4_quantize", "fp4_dequantize", "fp4_block_error", "moe_fp4_workspace_layout",
             "moe_fp4_workspace_size", "moe_fp4_forward", "moe_fp4_forward_profiled",
-            "moe_fp4_route", "moe_fp4_tile_weights", "fp4_status_string", "fp4_last_error"]
+            "moe_fp4_route", "moe_fp4_tile_weights", "moe_fp4_forward_noalloc", "fp4_status_string",
+            "fp4_last_error"]
+NOALLOC_SCRATCH_BYTES = 64 << 20  # FP4_NOALLOC_SCRATCH_BYTES
 STAGES = ["permute", "x_quant", "gate_up", "h_quant", "down", "shared", "combine"]
 
 
@@ -84,6 +86,8 @@ def lib():
         L.moe_fp4_forward_profiled.argtypes = [ctypes.POINTER(LayerStruct), vp, i64, vp, vp, vp, vp, sz, vp,
                                                ctypes.POINTER(vp), i32]
         L.moe_fp4_forward_profiled.restype = i32
+        L.moe_fp4_forward_noalloc.argtypes = [ctypes.POINTER(LayerStruct), vp, i64, vp, vp, vp, vp]
+        L.moe_fp4_forward_noalloc.restype = i32
         L.moe_fp4_route.argtypes = [vp, vp, i64, i32, i32, vp, vp, vp]
         L.moe_fp4_route.restype = i32
         L.moe_fp4_tile_weights.argtypes = [i32, vp, vp, i64, i64, i64, vp, vp, vp]
@@ -279,6 +283,20 @@ def moe_forward(layer: MoELayer, x: torch.Tensor, topk_ids: torch.Tensor,
     s = layer.struct()
     _check(lib().moe_fp4_forward(ctypes.byref(s), _ptr(x), T, _ptr(topk_ids), _ptr(topk_weights),
                                  _ptr(y), _ptr(workspace), workspace.numel(), _stream()))
+    return y
+
+
+def moe_forward_noalloc(layer: MoELayer, x: torch.Tensor, topk_ids: torch.Tensor,
+                        topk_weights: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """moe_fp4_forward_noalloc: moe_forward with the library's per-device
+    scratch as the workspace (nothing allocated by the call; y is allocated
+    here only when not given)."""
+    T = int(x.shape[0])
+    if y is None:
+        y = torch.empty(T, layer.hidden, dtype=torch.float32, device=x.device)
+    s = layer.struct()
+    _check(lib().moe_fp4_forward_noalloc(ctypes.byref(s), _ptr(x), T, _ptr(topk_ids), _ptr(topk_weights),
+                                         _ptr(y), _stream()))
     return y
 
 

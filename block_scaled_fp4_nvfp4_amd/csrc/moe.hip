@@ -965,9 +965,29 @@ static int side_stream(SideStream** out) {
   return FP4_OK;
 }
 
+// Joins the shared-expert helper stream back into the caller's stream on
+// every exit after the fork: an error return then still leaves no work of
+// the call running unjoined (and a captured graph with no dangling fork).
+struct SideJoin {
+  SideStream* side = nullptr;
+  hipStream_t st = nullptr;
+  bool joined = false;
+  int join() {
+    joined = true;
+    if (hipEventRecord(side->join, side->s) != hipSuccess || hipStreamWaitEvent(st, side->join, 0) != hipSuccess)
+      return fail(FP4_ERR_HIP, "join of the shared-expert stream failed");
+    return FP4_OK;
+  }
+  ~SideJoin() {
+    if (side && !joined) (void)join();
+  }
+};
+
+// inline_shared: the shared expert runs on the caller's stream ahead of the
+// routed experts (no helper stream, no fork / join events)
 static int forward_impl(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const int32_t* topk_ids,
                         const float* topk_weights, float* y, void* workspace, size_t workspace_bytes,
-                        void* stream, void* const* events) {
+                        void* stream, void* const* events, bool inline_shared = false) {
   FP4_CHECK(validate_layer(L, T));
   if (T == 0) return FP4_OK;
   if (!x || !topk_ids || !topk_weights || !y) return fail(FP4_ERR_INVALID_ARG, "null tensor pointer");
@@ -994,15 +1014,19 @@ static int forward_impl(const moe_fp4_layer* L, const uint16_t* x, int64_t T, co
   // concurrent callers apart.
   const float* extra = nullptr;
   std::unique_lock<std::mutex> side_lock;
-  SideStream* side = nullptr;
-  if (L->shared_inter > 0) {
+  SideJoin sj;
+  if (L->shared_inter > 0 && inline_shared) {
+    FP4_CHECK(launch_shared_expert(L, x, T, w, st));
+    extra = w.s_out;
+  } else if (L->shared_inter > 0) {
     side_lock = std::unique_lock<std::mutex>(g_side_mu);
+    SideStream* side = nullptr;
     FP4_CHECK(side_stream(&side));
     if (hipEventRecord(side->fork, st) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
       return fail(FP4_ERR_HIP, "fork to the shared-expert stream failed");
+    sj.side = side;
+    sj.st = st;
     FP4_CHECK(launch_shared_expert(L, x, T, w, side->s));
-    if (hipEventRecord(side->join, side->s) != hipSuccess)
-      return fail(FP4_ERR_HIP, "shared-expert completion event failed");
     extra = w.s_out;
   }
   FP4_CHECK(launch_permute(topk_ids, P, L->num_experts, kGemmTileM, w, st));
@@ -1020,18 +1044,60 @@ static int forward_impl(const moe_fp4_layer* L, const uint16_t* x, int64_t T, co
   } else {
     FP4_CHECK(launch_grouped(L, x, T, w, max_active, st, mark));
   }
-  if (side && hipStreamWaitEvent(st, side->join, 0) != hipSuccess)
-    return fail(FP4_ERR_HIP, "join of the shared-expert stream failed");
+  if (sj.side) FP4_CHECK(sj.join());
   FP4_CHECK(mark(6));  // the "shared" stage is the part of the shared expert not hidden by the routed path
   launch_combine(w.o, w.row_of_pair, topk_weights, T, L->hidden, L->top_k, extra, y, st);
   FP4_CHECK(check_launch("combine"));
   return mark(7);
 }
 
+// ------------------------------------------------- allocation-free forward
+
+// Scratch of moe_fp4_forward_noalloc: one array per device, held by the
+// loaded code object until the process ends.  Host code never uses the
+// array's name as an address (on the host it is only a stand-in for the
+// symbol): each device's address comes from hipGetSymbolAddress, taken once
+// per device with that device current.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[FP4_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+static int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(FP4_ERR_HIP, "no current HIP device");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(FP4_ERR_HIP, "hipGetSymbolAddress of the scratch array failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FP4_OK;
+}
+
 int moe_fp4_forward(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const int32_t* topk_ids,
                     const float* topk_weights, float* y, void* workspace, size_t workspace_bytes,
                     void* stream) {
   return forward_impl(L, x, T, topk_ids, topk_weights, y, workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_fp4_forward_noalloc(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const int32_t* topk_ids,
+                            const float* topk_weights, float* y, void* stream) {
+  FP4_CHECK(validate_layer(L, T));
+  if (T == 0) return FP4_OK;
+  WsPlan p;
+  FP4_CHECK(plan_workspace(L, T, &p));
+  if (p.total > FP4_NOALLOC_SCRATCH_BYTES)
+    return fail(FP4_ERR_WORKSPACE, "allocation-free forward: %lld tokens need %zu bytes of scratch, at most %zu held",
+                (long long)T, p.total, (size_t)FP4_NOALLOC_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  FP4_CHECK(scratch_address(&ptr));
+  return forward_impl(L, x, T, topk_ids, topk_weights, y, ptr, FP4_NOALLOC_SCRATCH_BYTES, stream, nullptr,
+                      /*inline_shared=*/true);
 }
 
 int moe_fp4_route(const float* logits, const float* bias, int64_t tokens, int num_experts, int top_k,

@@ -26,8 +26,10 @@
  *    device, one helper stream with two events (created by the first forward
  *    of a layer with a shared expert; the shared expert runs on it,
  *    overlapped with the routed experts, forked from and joined back into
- *    the caller's stream), the device's compute-unit count, and one bit per
- *    GEMM kernel recording that its dynamic-LDS limit has been raised.
+ *    the caller's stream), the device's compute-unit count, one bit per
+ *    GEMM kernel recording that its dynamic-LDS limit has been raised, and
+ *    the address of the device's scratch array of moe_fp4_forward_noalloc
+ *    (the array itself is part of the loaded code object).
  *  - `stream` is a hipStream_t (NULL = default stream).  Calls only enqueue
  *    work and return; a launch failure returns FP4_ERR_HIP, asynchronous faults
  *    surface at the caller's next synchronisation.
@@ -290,6 +292,32 @@ int moe_fp4_forward_profiled(const moe_fp4_layer* layer, const uint16_t* x, int6
                              const int32_t* topk_ids, const float* topk_weights, float* y,
                              void* workspace, size_t workspace_bytes, void* stream,
                              void* const* events, int n_events);
+
+/*
+ * moe_fp4_forward_noalloc - moe_fp4_forward for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  The same kernels in the same order, with the
+ * workspace taken from a scratch array that the library holds on each device
+ * (FP4_NOALLOC_SCRATCH_BYTES, kept until the process ends) and the shared
+ * expert run on the caller's stream ahead of the routed experts.  The caller
+ * still passes x, the routing and y, as for moe_fp4_forward.
+ *  - Allocates nothing: no device memory, streams or events are created
+ *    (the first call on a device looks up that device's scratch address).
+ *  - A layer and token count whose workspace (moe_fp4_workspace_size)
+ *    exceeds FP4_NOALLOC_SCRATCH_BYTES returns FP4_ERR_WORKSPACE before any
+ *    launch; at 512 experts, hidden 2560, inter 640 and top-10 that is above
+ *    about 500 tokens.
+ *  - Every call on a device shares that device's scratch, which keeps the
+ *    last call's contents; no call reads what an earlier one left (every
+ *    buffer is written before it is read).  Calls on one stream are ordered;
+ *    calls that overlap on one device (several streams or host threads)
+ *    race on the scratch and give undefined results.
+ *  - The out-of-range-id flag of the workspace is not readable here: ids
+ *    must lie in [0, E).
+ */
+#define FP4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_fp4_forward_noalloc(const moe_fp4_layer* layer, const uint16_t* x, int64_t tokens,
+                            const int32_t* topk_ids, const float* topk_weights, float* y, void* stream);
 
 const char* fp4_status_string(int status);
 const char* fp4_last_error(void);

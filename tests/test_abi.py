@@ -110,6 +110,19 @@ def test_moe_validation_and_workspace(L):
     assert L.moe_fp4_forward(ctypes.byref(s), fake, 64, fake, fake, fake, fake, 16, None) == -4
     # T == 0 is a no-op
     assert L.moe_fp4_forward(ctypes.byref(s), None, 0, None, None, None, None, 0, None) == 0
+    # the allocation-free forward validates the layer, then refuses (before any HIP call) a
+    # problem whose workspace exceeds its scratch; T == 0 is a no-op
+    from block_scaled_fp4_nvfp4_amd import _lib
+    big = _layer(num_experts=512, hidden=2560, inter=640, top_k=10)
+    assert L.moe_fp4_workspace_size(ctypes.byref(big), 8192, ctypes.byref(sz)) == 0
+    assert sz.value > _lib.NOALLOC_SCRATCH_BYTES
+    assert L.moe_fp4_forward_noalloc(ctypes.byref(big), fake, 8192, fake, fake, fake, None) == -4
+    assert b"scratch" in L.fp4_last_error()
+    assert L.moe_fp4_forward_noalloc(ctypes.byref(_layer(top_k=0)), fake, 64, fake, fake, fake, None) == -1
+    assert L.moe_fp4_forward_noalloc(ctypes.byref(s), None, 0, None, None, None, None) == 0
+    # the header's limit and the binding's agree
+    hdr = open(HEADER).read()
+    assert "#define FP4_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in hdr and _lib.NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
 def test_tile_weights_and_tiled_layer_validation(L):
