@@ -22,7 +22,7 @@ DT_BF16, DT_F32 = 0, 1
 STATUS = {0: "FP4_OK", -1: "FP4_ERR_INVALID_ARG", -2: "FP4_ERR_SHAPE",
           -3: "FP4_ERR_UNSUPPORTED", -4: "FP4_ERR_WORKSPACE", -5: "FP4_ERR_HIP"}
 
-EXPORTED = ["fp4_quantize", "fp4_dequantize", "fp4_block_error", "moe_fp4_workspace_layout",
+EXPORTED = ["fp4_quantize", "fp4_quantize_hessian", "fp4_dequantize", "fp4_block_error", "moe_fp4_workspace_layout",
             "moe_fp4_workspace_size", "moe_fp4_forward", "moe_fp4_forward_profiled",
             "moe_fp4_route", "moe_fp4_tile_weights", "moe_fp4_forward_noalloc", "fp4_status_string",
             "fp4_last_error"]
@@ -73,6 +73,8 @@ def lib():
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
         L.fp4_quantize.argtypes = [i32, i32, i32, vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
         L.fp4_quantize.restype = i32
+        L.fp4_quantize_hessian.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        L.fp4_quantize_hessian.restype = i32
         L.fp4_dequantize.argtypes = [i32, vp, vp, vp, i64, i64, i64, vp, i32, vp]
         L.fp4_dequantize.restype = i32
         L.fp4_block_error.argtypes = [i32, vp, i32, i64, i64, i64, vp, vp, vp, vp, vp]
@@ -163,6 +165,28 @@ def quantize(x: torch.Tensor, fmt: str, rule: str = "4over6",
     _check(lib().fp4_quantize(f, RULE[rule], ts_mode, _ptr(x), _dtype_code(x), b, r, c,
                               _ptr(codes), _ptr(scales), _ptr(ts), _ptr(m4), _stream()))
     return {"codes": codes, "scales": scales, "tensor_scale": ts, "m4": m4}
+
+
+def quantize_hessian(x: torch.Tensor, hessian: torch.Tensor, calib_rows: torch.Tensor,
+                     want_choice: bool = False):
+    """fp4_quantize_hessian.  x: contiguous bf16/f32 device tensor [E, rows,
+    cols] (or [rows, cols] for one expert); hessian: f32 [E, cols/16, 16, 16];
+    calib_rows: int32 [E].  Returns dict(codes, scales, tensor_scale, choice)
+    in the NVFP4 layout of quantize()."""
+    assert x.is_cuda and x.is_contiguous()
+    b, r, c = (int(v) for v in _dims(x))
+    dev = x.device
+    hessian = hessian.to(device=dev, dtype=torch.float32).contiguous()
+    calib_rows = calib_rows.to(device=dev, dtype=torch.int32).contiguous()
+    assert hessian.numel() == b * (c // 16) * 256 and calib_rows.numel() == b
+    lead = x.shape[:-1]
+    codes = torch.empty(*lead, c // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(*lead, c // 16, dtype=torch.uint8, device=dev)
+    ts = torch.empty(b, dtype=torch.float32, device=dev)
+    choice = torch.empty(*lead, c // 16, dtype=torch.uint8, device=dev) if want_choice else None
+    _check(lib().fp4_quantize_hessian(_ptr(x), _dtype_code(x), b, r, c, _ptr(hessian), _ptr(calib_rows),
+                                      _ptr(codes), _ptr(scales), _ptr(ts), _ptr(choice), _stream()))
+    return {"codes": codes, "scales": scales, "tensor_scale": ts, "choice": choice}
 
 
 def route(logits: torch.Tensor, k: int, bias: Optional[torch.Tensor] = None):

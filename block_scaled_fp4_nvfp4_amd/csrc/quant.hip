@@ -992,6 +992,22 @@ int quantize_typed(int fmt, int rule, int ts_mode, const T* x, int64_t batch, in
   return fail(FP4_ERR_INVALID_ARG, "unknown format %d", fmt);
 }
 
+template <typename T>
+int tensor_scales_typed(const T* x, int64_t batch, int64_t per, float* tensor_scale, hipStream_t st) {
+  FP4_CHECK(launch_fill(reinterpret_cast<uint32_t*>(tensor_scale), 0u, batch, st));
+  const int64_t chunks = (per / 8 + 255) / 256;
+  for (int64_t b0 = 0; b0 < batch; b0 += 65535) {
+    const int64_t nb = std::min<int64_t>(65535, batch - b0);
+    const int64_t target = 4LL * device_cu_count() / nb;
+    const unsigned gx = (unsigned)std::max<int64_t>(1, std::min<int64_t>(chunks, std::max<int64_t>(target, 1)));
+    hipLaunchKernelGGL(tensor_amax_kernel<T>, dim3(gx, (unsigned)nb), dim3(256), 0, st, x + b0 * per, per,
+                       reinterpret_cast<uint32_t*>(tensor_scale) + b0);
+    FP4_CHECK(check_launch("tensor_amax"));
+  }
+  hipLaunchKernelGGL(nv_tensor_scale_kernel, dim3(grid_1d(batch, 256)), dim3(256), 0, st, tensor_scale, batch);
+  return check_launch("tensor_scale");
+}
+
 int block_of(int fmt) {
   switch (fmt) {
     case FP4_FMT_NVFP4: return 16;
@@ -1021,6 +1037,14 @@ int mxfp8_quantize_dequant(const void* x, int x_dtype, int64_t rows, int64_t col
   else
     return fail(FP4_ERR_UNSUPPORTED, "MXFP8 quantize-dequantize: bf16->bf16 or f32->f32 only");
   return check_launch("quant_mxfp8_deq");
+}
+
+int nv_tensor_scales(const void* x, int x_dtype, int64_t batch, int64_t per, float* tensor_scale,
+                     hipStream_t st) {
+  if (batch <= 0) return FP4_OK;
+  if (x_dtype == FP4_DT_BF16)
+    return tensor_scales_typed(reinterpret_cast<const uint16_t*>(x), batch, per, tensor_scale, st);
+  return tensor_scales_typed(reinterpret_cast<const float*>(x), batch, per, tensor_scale, st);
 }
 
 int nv_tensor_scale_from_parts(const float* part, int64_t nparts, float* s, hipStream_t st) {

@@ -112,6 +112,38 @@ int fp4_quantize(int fmt, int rule, int ts_mode, const void* x, int x_dtype,
                  void* stream);
 
 /*
+ * fp4_quantize_hessian - NVFP4 quantization of `experts` expert matrices
+ * x[experts][rows][cols] with block scales chosen by a Hessian-weighted search
+ * ("Local-Hessian NVFP4 experts", section "What is different about it": the
+ * per-group weight scales come from a Hessian-weighted search instead of the
+ * plain amax / MSE sweep, and only weight_scale values differ; section
+ * "Results": experts with fewer than 64 routed calibration rows keep plain
+ * max).  The search is named, not defined, there; the reading taken:
+ *   candidates  every E4M3 scale code from the amax/6 plan's to the
+ *               block-max-to-4 plan's, codes E2M1 round-to-nearest-even;
+ *   error       d^T H_b d per 16-value block, d = x - xhat (signed), H_b the
+ *               16 x 16 diagonal block of the expert's input Hessian for the
+ *               block's columns; the first candidate with the smallest exact
+ *               error is kept (exact: float64 with a proven error bound, and
+ *               exact fixed-point arithmetic where the bound cannot decide).
+ *  x            bf16 or f32 (`x_dtype`), finite, 16-byte aligned.
+ *  hessian      f32 [experts][cols/16][16][16], H_b of every column block
+ *               (finite; the search uses sum_ij H_b[i][j] d_i d_j as given).
+ *  calib_rows   int32 [experts]: calibration rows behind each expert's
+ *               Hessian; fewer than 64 -> the amax/6 plan for all its blocks.
+ *  codes, scales, tensor_scale  out, as fp4_quantize NVFP4 with
+ *               FP4_TS_DYNAMIC (tensor scale amax/2688 per expert, unchanged
+ *               by the search); codes 8-byte aligned.
+ *  choice       optional out (may be NULL), one byte per block: the chosen
+ *               scale code minus the amax/6 plan's.
+ * Errors: cols % 16 -> FP4_ERR_SHAPE; bad dtype, null or misaligned pointer
+ * -> FP4_ERR_INVALID_ARG.  Stream-ordered, asynchronous.
+ */
+int fp4_quantize_hessian(const void* x, int x_dtype, int64_t experts, int64_t rows, int64_t cols,
+                         const float* hessian, const int32_t* calib_rows, uint8_t* codes,
+                         uint8_t* scales, float* tensor_scale, uint8_t* choice, void* stream);
+
+/*
  * fp4_dequantize - decode codes/scales (layouts as fp4_quantize) to
  * out[batch][rows][cols] in `out_dtype`.  f32 output is the correctly rounded
  * value g * s * S (NVFP4), g * 2^e (MX) or v * sigma (FP8_*); bf16 output is

@@ -73,6 +73,14 @@ def test_host_validation_errors(L):
     assert L.fp4_block_error(1, odd, 0, 1, 4, 64, fake, fake, None, fake, None) == -1
     assert L.fp4_block_error(1, fake, 7, 1, 4, 64, fake, fake, None, fake, None) == -1
     assert L.fp4_block_error(1, None, 0, 0, 4, 64, None, None, None, None, None) == 0
+    # Hessian-weighted search: cols % 16, dtype, null and misaligned pointers; empty is a no-op
+    assert L.fp4_quantize_hessian(fake, 0, 2, 4, 24, fake, fake, fake, fake, fake, None, None) == -2
+    assert L.fp4_quantize_hessian(fake, 3, 2, 4, 32, fake, fake, fake, fake, fake, None, None) == -1
+    assert L.fp4_quantize_hessian(fake, 0, 2, 4, 32, None, fake, fake, fake, fake, None, None) == -1
+    assert L.fp4_quantize_hessian(fake, 0, 2, 4, 32, fake, None, fake, fake, fake, None, None) == -1
+    assert L.fp4_quantize_hessian(odd, 0, 2, 4, 32, fake, fake, fake, fake, fake, None, None) == -1
+    assert L.fp4_quantize_hessian(fake, 0, 2, 4, 32, fake, fake, odd, fake, fake, None, None) == -1
+    assert L.fp4_quantize_hessian(None, 0, 0, 4, 32, None, None, None, None, None, None, None) == 0
     # routing: k outside [1, min(E, 32)], too many experts, empty batch, null outputs
     assert L.moe_fp4_route(fake, None, 4, 8, 0, fake, fake, None) == -1
     assert L.moe_fp4_route(fake, None, 4, 8, 9, fake, fake, None) == -1
