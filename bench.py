@@ -36,6 +36,97 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+class StepEvents:
+    """n HIP events recorded on the current stream between steps, created
+    without the system-scope fence (a default event's release writes back the
+    L2 at every record, several microseconds on a decode step), for per-step
+    times: median and p10 / p90."""
+
+    def __init__(self, n):
+        import ctypes
+
+        from block_scaled_fp4_nvfp4_amd import _lib
+        self._ct = ctypes
+        self._hip = _lib._hip_runtime()
+        if self._hip is None:
+            raise RuntimeError("HIP runtime library not found")
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self._hip.hipEventCreateWithFlags(ctypes.byref(e), _lib._HIP_EVENT_DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e.value)
+
+    def record(self, i, torch):
+        st = self._ct.c_void_p(torch.cuda.current_stream().cuda_stream)
+        if self._hip.hipEventRecord(self._ct.c_void_p(self.ev[i]), st) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, i, j):
+        out = self._ct.c_float()
+        if self._hip.hipEventElapsedTime(self._ct.byref(out), self._ct.c_void_p(self.ev[i]),
+                                         self._ct.c_void_p(self.ev[j])) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def __del__(self):
+        for e in getattr(self, "ev", []):
+            self._hip.hipEventDestroy(self._ct.c_void_p(e))
+
+
+def step_distribution(torch, step, steps):
+    """Times each of `steps` calls of step(i) between events; returns the
+    median, p10 and p90 in ms (event records add well under a microsecond)."""
+    import numpy as np
+    ev = StepEvents(steps + 1)
+    torch.cuda.synchronize()
+    ev.record(0, torch)
+    for i in range(steps):
+        step(i)
+        ev.record(i + 1, torch)
+    torch.cuda.synchronize()
+    t = np.array([ev.ms(i, i + 1) for i in range(steps)])
+    return {"median_ms": float(np.median(t)), "p10_ms": float(np.percentile(t, 10)),
+            "p90_ms": float(np.percentile(t, 90)), "steps": steps}
+
+
+def timed_oracle(fn, budget_s):
+    """fn() repeated for about budget_s seconds, once with the BLAS thread
+    pool at its default size (all host cores) and once limited to one
+    thread; returns (all-cores (reps, seconds), one-core (reps, seconds),
+    threads of the first)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    out = []
+    for limit in (None, 1):
+        with threadpool_limits(limits=limit):
+            t0 = time.perf_counter()
+            reps = 0
+            while True:
+                fn()
+                reps += 1
+                el = time.perf_counter() - t0
+                if el >= budget_s or reps >= 50:
+                    break
+        out.append((reps, el))
+    return out[0], out[1], threads
+
+
+def _oracle_quantize_task(task):
+    """Worker of the streaming workload's oracle leg: the oracle's NVFP4
+    quantization of one expert's gate_up and down bf16 tensors."""
+    w13_bits, w2_bits, rule = task
+    sys.path.insert(0, ROOT)
+    from oracle import quant
+    from oracle.formats import bf16_to_f64, pack_nibbles
+    out = []
+    for w in (w13_bits, w2_bits):
+        q = quant.quantize_nvfp4(bf16_to_f64(w), rule)
+        out.append((pack_nibbles(q["codes"]), q["scales"], float(q["tensor_scale"]),
+                    quant.dequantize_nvfp4(q["codes"], q["scales"], q["tensor_scale"])))
+    return out
+
+
 def expert_bytes(cfg):
     """Bytes of one expert's gate_up and down weights in the layer's format."""
     H, I = cfg.hidden, cfg.inter
@@ -121,20 +212,14 @@ def cpu_baseline(cfg, ids, wts, x_bits, budget_s=20.0):
         layer["shared"] = dict(w13=moe.quantize_expert_weight(s13, "mxfp8"),
                                w2=moe.quantize_expert_weight(s2, "mxfp8"), gate_bits=gate)
     ids_s, wts_s, x_s = ids[:n], wts[:n], x_bits[:n]
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        moe.moe_forward(layer, x_s, ids_s, wts_s)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 50:
-            break
-    tok_s = reps * n / el
-    return {"value": tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "threads_env": os.environ.get("OMP_NUM_THREADS"),
-            "sample": f"{n} token(s) x {reps} repeat(s) of the {cfg.name} layer forward "
-                      f"(dequantize-then-matmul in float64, weights pre-quantized by the oracle), "
-                      f"{el:.1f} s"}
+    (reps, el), (reps1, el1), threads = timed_oracle(lambda: moe.moe_forward(layer, x_s, ids_s, wts_s),
+                                                     budget_s / 2)
+    sample = (f"{n} token(s) of the {cfg.name} layer forward (dequantize-then-matmul in float64, weights "
+              f"pre-quantized by the oracle)")
+    return {"value": reps * n / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cores": cores, "sample": f"{sample}: {reps} repeat(s), {el:.1f} s",
+            "single_core": {"value": reps1 * n / el1, "unit": "tokens/s", "cores": 1, "blas_threads": 1,
+                            "sample": f"{sample}: {reps1} repeat(s), {el1:.1f} s"}}
 
 
 def time_route(cfg, torch, pkg, reps=50):
@@ -200,6 +285,8 @@ def bench_decode(args, torch, pkg):
         for k, v in timer.durations().items():
             acc[k] += v
     stages = {k: v / args.steps for k, v in acc.items()}
+    dist = step_distribution(torch, lambda i: pkg.moe_forward(layers[i % len(layers)], x, tid, tw, ws, y),
+                             args.steps)
 
     touched = len(np.unique(ids))
     b13, b2 = expert_bytes(cfg)
@@ -208,14 +295,18 @@ def bench_decode(args, torch, pkg):
     down_bytes = touched * b2 + P * cfg.inter * 4 + P * cfg.hidden * 4
     step_bytes = touched * (b13 + b2) + T * cfg.hidden * 2 + T * cfg.hidden * 4
     gu_ms = stages["gate_up"]
-    tr = measured_traffic("gemv_gateup_kernel", "decode")
-    roof = {"bound": "hbm", "kernel": "gemv_gateup_kernel",
+    tr = measured_traffic("gemv_gateup_kernel", "gate_up", "decode")
+    roof = {"bound": "hbm", "kernel": "gemv_gateup_kernel<NVFP4, 5>", "scope": "the gate_up GEMV kernel alone",
             "achieved": gateup_bytes / (gu_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "traffic": tr["bytes_per_launch"] if tr else None,
             "bytes_per_launch": gateup_bytes,
             "unit_of_work": f"{touched} touched experts x {b13} B of NVFP4 gate_up weights"
                             f" + x {T * cfg.hidden * 2} B + h {P * cfg.inter * 4} B"}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    # the whole layer step (every kernel of moe_fp4_forward) against the same peak
+    roof["layer"] = {"bytes": step_bytes, "achieved": step_bytes / (ms * 1e-3) / 1e9,
+                     "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "unit_of_work": f"{touched} touched experts x {b13 + b2} B + x + y"}
     out = {
         "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -228,6 +319,7 @@ def bench_decode(args, torch, pkg):
         "step_hbm": {"bytes": step_bytes, "GBps": step_bytes / (ms * 1e-3) / 1e9,
                      "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
         "stages_ms": stages,
+        "step_distribution": dist,
         "down": {"bytes_per_launch": down_bytes,
                  "GBps": down_bytes / (stages["down"] * 1e-3) / 1e9 if stages["down"] > 0 else None},
         "route": time_route(cfg, torch, pkg),
@@ -249,6 +341,7 @@ def time_steps(pkg, torch, layers, x, tid, tw, ws, y, steps, warmup):
     stop.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(stop) / steps
+    dist = step_distribution(torch, lambda i: pkg.moe_forward(layers[i % len(layers)], x, tid, tw, ws, y), steps)
     timer = pkg.StageTimer()
     acc = {s_: 0.0 for s_ in pkg.STAGES}
     for i in range(steps):
@@ -256,7 +349,7 @@ def time_steps(pkg, torch, layers, x, tid, tw, ws, y, steps, warmup):
         torch.cuda.synchronize()
         for k_, v in timer.durations().items():
             acc[k_] += v
-    return ms, {k_: v / steps for k_, v in acc.items()}
+    return ms, {k_: v / steps for k_, v in acc.items()}, dist
 
 
 def bench_prefill(name, args, torch, pkg):
@@ -282,7 +375,7 @@ def bench_prefill(name, args, torch, pkg):
     tid, tw = torch.from_numpy(ids).cuda(), torch.from_numpy(wts).cuda()
     ws = torch.empty(pkg.workspace_size(layers[0], T), dtype=torch.uint8, device="cuda")
     y = torch.empty(T, H, dtype=torch.float32, device="cuda")
-    ms, stages = time_steps(pkg, torch, layers, x, tid, tw, ws, y, args.prefill_steps, 2)
+    ms, stages, dist = time_steps(pkg, torch, layers, x, tid, tw, ws, y, args.prefill_steps, 2)
     flops_gu = 4.0 * P * H * I
     flops_down = 2.0 * P * H * I
     flops_shared = 6.0 * T * H * cfg.shared_inter
@@ -293,11 +386,13 @@ def bench_prefill(name, args, torch, pkg):
     peak_key = "bf16" if cfg.a_fmt == "nvfp4" else "fp8"
     peak = MFMA_PEAK_TFLOPS[peak_key]
     gu_ms = stages["gate_up"]
-    roof = {"bound": "mfma", "kernel": "grouped_gemm_kernel (gate_up)", "mfma_dtype":
+    gk = {"nvfp4": "grouped_gemm_nv2_kernel<0, 2, 20, WT>", "mxfp4": "grouped_gemm_mx2_kernel<1, 0, 2, 20, WT>",
+          "fp8_block": "grouped_gemm_mx2_kernel<2, 0, 2, 20, WT>"}[cfg.w_fmt].replace("WT", str(tiled).lower())
+    roof = {"bound": "mfma", "kernel": gk + " (gate_up)", "mfma_dtype":
             {"bf16": "fp16 (exact NVFP4 decode)", "fp8": "fp8 x fp4" if cfg.w_fmt == "mxfp4" else "fp8"}[peak_key],
             "achieved": flops_gu / (gu_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
             "traffic": (lambda t: t["bytes_per_launch"] if t else None)(
-                measured_traffic("grouped_gemm_kernel_gateup", name)),
+                measured_traffic(gk.split("<")[0], "gate_up", name)),
             "flops_per_launch": flops_gu,
             "unit_of_work": f"{P} (token, expert) rows x 2 x {2 * I} x {H} FLOPs"}
     roof["frac"] = roof["achieved"] / peak
@@ -308,7 +403,7 @@ def bench_prefill(name, args, torch, pkg):
                        + (", W13 and W2 tiled for the GEMMs" if tiled else ""),
            "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "steps": args.prefill_steps,
            "dtype": {"nvfp4": "fp16", "mxfp8": "fp8", "fp8_row": "fp8"}[cfg.a_fmt],
-           "roofline": roof, "stages_ms": stages,
+           "roofline": roof, "stages_ms": stages, "step_distribution": dist,
            "step_mfma": {"flops": total_flops, "TFLOPs": total_flops / (ms * 1e-3) / 1e12,
                          "frac_of_peak": total_flops / (ms * 1e-3) / 1e12 / peak},
            "step_hbm": {"weight_bytes": weight_bytes, "touched_experts": touched,
@@ -328,7 +423,7 @@ def file_sha(rel):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel, workload):
+def measured_traffic(kernel, stage, workload):
     """HBM bytes per launch of `kernel` in `workload` from the committed
     rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE, scaled by what the
     same counters read for a plain copy of known size), or None when the
@@ -340,7 +435,7 @@ def measured_traffic(kernel, workload):
         if line.startswith("#") or "=" not in line:
             continue
         kv = dict(t.split("=", 1) for t in line.split())
-        if kv.get("kernel") != kernel or kv.get("workload") != workload:
+        if kv.get("kernel") != kernel or kv.get("stage") != stage or kv.get("workload") != workload:
             continue
         if file_sha(kv["source"]) != kv["source_sha"]:
             return None
@@ -369,6 +464,93 @@ def bench_copy(args, torch):
     ms = start.elapsed_time(stop) / args.steps
     return {"metric": "plain copy GB/s", "value": 2 * n * 4 / (ms * 1e-3) / 1e9, "unit": "GB/s",
             "bytes_read": n * 4, "bytes_written": n * 4, "ms_per_launch": ms, "steps": args.steps}
+
+
+def bench_ceilings(args, torch, pkg):
+    """Measured device ceilings (include/fp4moe_probe.h): a streaming read
+    over 4 GiB (larger than the 256 MB Infinity Cache) at several grid sizes,
+    the issue rate of each MFMA operand type the kernels use, and the
+    routing-weighted combine as a store of o plus a combine pass against fp32
+    atomics into y, at the prefill and decode shapes."""
+    import ctypes
+
+    import numpy as np
+    L = pkg.lib()
+    vp = ctypes.c_void_p
+    L.fp4_probe_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, vp, vp]
+    L.fp4_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    L.fp4_probe_combine.argtypes = [ctypes.c_int, vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
+    stream = lambda: vp(torch.cuda.current_stream().cuda_stream)
+
+    def timeit(fn, reps=10):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def ok(st):
+        if st != 0:
+            raise RuntimeError(L.fp4_last_error().decode())
+
+    out = {"metric": "measured device ceilings", "unit": "GB/s and TFLOP/s"}
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    reads = {}
+    for grid in (1024, 2048, 4096, 8192, 16384, 32768, 65536):
+        ms = timeit(lambda: ok(L.fp4_probe_read(vp(buf.data_ptr()), nbytes, grid, vp(sink.data_ptr()), stream())))
+        reads[grid] = nbytes / (ms * 1e-3) / 1e9
+    out["stream_read_GBps"] = {"by_grid": reads, "best": max(reads.values()), "bytes": nbytes,
+                               "peak_spec": HBM_PEAK_GBS, "frac_of_spec": max(reads.values()) / HBM_PEAK_GBS}
+    del buf
+    grid, iters = 2048, 2000
+    acc = torch.empty(grid * 256 * 4, dtype=torch.float32, device="cuda")
+    kinds = {"f16": (0, 16384, 2500.0), "bf16": (1, 16384, 2500.0), "fp8_x_fp8": (2, 65536, 5000.0),
+             "fp8_x_fp4": (3, 65536, 5000.0), "fp4_x_fp4": (4, 65536, 10100.0),
+             "f16_32x32x16": (5, 32768, 2500.0), "fp8_x_fp8_32x32x64": (6, 131072, 5000.0),
+             "fp4_x_fp4_32x32x64": (7, 131072, 10100.0)}
+    mf = {}
+    for name, (kind, flops, peak) in kinds.items():
+        ms = timeit(lambda: ok(L.fp4_probe_mfma(kind, iters, grid, vp(acc.data_ptr()), stream())), reps=5)
+        tf = grid * 4 * iters * 8 * flops / (ms * 1e-3) / 1e12
+        mf[name] = {"TFLOPs": tf, "peak_spec": peak, "frac_of_spec": tf / peak}
+    out["mfma_TFLOPs"] = mf
+    rng = np.random.default_rng(1)
+    comb = {}
+    for T, k in ((8192, 10), (8192, 5), (16, 10)):
+        E, H = 512, 2560
+        ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+        por = np.argsort(ids.reshape(-1), kind="stable").astype(np.int32)
+        rop = np.empty_like(por)
+        rop[por] = np.arange(T * k, dtype=np.int32)
+        w = np.full(T * k, 0.1, np.float32)
+        d_por, d_rop, d_w = (torch.from_numpy(a).cuda() for a in (por, rop, w))
+        o = torch.empty(T * k, H, dtype=torch.float32, device="cuda")
+        y = torch.zeros(T, H, dtype=torch.float32, device="cuda")
+        args_ = lambda mode: (mode, vp(d_por.data_ptr()), vp(d_rop.data_ptr()), vp(d_w.data_ptr()), T, k, H,
+                              vp(o.data_ptr()), vp(y.data_ptr()), stream())
+        t_store = timeit(lambda: ok(L.fp4_probe_combine(*args_(0))))
+        t_comb = timeit(lambda: ok(L.fp4_probe_combine(*args_(1))))
+        t_zero = timeit(lambda: y.zero_())
+        t_atom = timeit(lambda: ok(L.fp4_probe_combine(*args_(2))))
+        y.zero_()
+        ok(L.fp4_probe_combine(*args_(2)))
+        ya = y.clone()
+        ok(L.fp4_probe_combine(*args_(0)))
+        ok(L.fp4_probe_combine(*args_(1)))
+        torch.cuda.synchronize()
+        comb[f"T{T}_k{k}"] = {"store_o_us": t_store * 1e3, "combine_us": t_comb * 1e3,
+                              "store_plus_combine_us": (t_store + t_comb) * 1e3,
+                              "zero_y_us": t_zero * 1e3, "atomic_into_y_us": t_atom * 1e3,
+                              "max_abs_diff": float((ya - y).abs().max())}
+    out["combine_experiment"] = comb
+    return out
 
 
 def bench_stream_quant(args, torch, pkg, rule="4over6"):
@@ -410,6 +592,17 @@ def bench_stream_quant(args, torch, pkg, rule="4over6"):
         for w, q in ((w13, q13), (w2, q2)):
             rd += w.numel() * 2
             wr += q["codes"].numel() + q["scales"].numel() + q["tensor_scale"].numel() * 4
+        if layer == 0 and not args.no_cpu_baseline:
+            # the oracle leg below quantizes these very tensors (the first
+            # experts of layer 0) and compares with the GPU's bytes
+            ne = args.oracle_experts
+            kept = {"w13": w13[:ne].view(torch.int16).cpu().numpy().view(np.uint16),
+                    "w2": w2[:ne].view(torch.int16).cpu().numpy().view(np.uint16)}
+            for nm, q, w in (("q13", q13, w13), ("q2", q2, w2)):
+                sub = {k: q[k][:ne] for k in ("codes", "scales", "tensor_scale")}
+                be = pkg.block_error(w[:ne], sub, "nvfp4").double().sum(dim=(1, 2))
+                kept[nm] = {k: v.cpu().numpy() for k, v in sub.items()}
+                kept[nm]["sq_err"] = be.cpu().numpy()
         if want:
             for w, q, names in ((w13, q13, ("gate", "up")), (w2, q2, ("down",))):
                 # squared error of every block from the library (fp4_block_error)
@@ -443,7 +636,7 @@ def bench_stream_quant(args, torch, pkg, rule="4over6"):
            "roofline": {"bound": "hbm", "kernel": "quant_fp4_kernel (fused with the next chunk's amax) + tensor_amax_kernel (first chunk)",
                         "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
                         "traffic": (lambda t: t["bytes_per_launch"] if t else None)(
-                            measured_traffic("quant_fp4_kernel", "stream_quant" if rule == "4over6" else "sweep_quant")),
+                            measured_traffic("quant_fp4_kernel", "quantize", "stream_quant" if rule == "4over6" else "sweep_quant")),
                         "bytes_per_layer": bytes_layer,
                         "unit_of_work": "2 B read + 0.5625 B written per value (+4 B per tensor)"},
            "quality": {"per_tensor_rel_err": {n: {"mean": m, "max": mx} for n, m, mx, *_ in stats},
@@ -453,25 +646,183 @@ def bench_stream_quant(args, torch, pkg, rule="4over6"):
         out["quality"]["note"] = ("m4_fraction: blocks whose scale is not the amax/6 plan's; "
                                   "first and last layer")
     if not args.no_cpu_baseline:
-        log(f"timing the CPU oracle on streaming quantization ({rule})")
-        import synth
+        log(f"timing the CPU oracle on streaming quantization ({rule}) and checking the GPU's bytes")
+        import multiprocessing as mp
+        ne = kept["w13"].shape[0]
+        tasks = [(kept["w13"][e], kept["w2"][e], rule) for e in range(ne)]
+        cores = len(os.sched_getaffinity(0))
+        procs = max(1, min(16, cores, ne))
+        t0 = time.perf_counter()
+        with mp.get_context("spawn").Pool(procs) as pool:
+            res = pool.map(_oracle_quantize_task, tasks)
+        el = time.perf_counter() - t0
+        n1 = max(1, min(ne, 2))
+        t1 = time.perf_counter()
+        for t in tasks[:n1]:
+            _oracle_quantize_task(t)
+        el1 = time.perf_counter() - t1
+        vals_e = 3 * H * I
+        ok_codes = ok_scales = ok_ts = True
+        rel_gpu, rel_orc = [], []
+        for e in range(ne):
+            for j, (nm, wk) in enumerate((("q13", "w13"), ("q2", "w2"))):
+                codes, scales, ts, deq = res[e][j]
+                g = kept[nm]
+                ok_codes &= bool(np.array_equal(codes, g["codes"][e]))
+                ok_scales &= bool(np.array_equal(scales, g["scales"][e]))
+                ok_ts &= bool(np.float32(ts) == g["tensor_scale"][e])
+                src = (kept[wk][e].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+                nrm = float((src * src).sum())
+                rel_orc.append(float(np.sqrt(((src - deq) ** 2).sum() / nrm)))
+                rel_gpu.append(float(np.sqrt(g["sq_err"][e] / nrm)))
+        out["oracle_check"] = {
+            "tensors": f"gate_up and down of experts 0..{ne - 1} of layer 0, copied back from the device "
+                       f"after the timed quantization",
+            "codes_equal": ok_codes, "scales_equal": ok_scales, "tensor_scales_equal": ok_ts,
+            "rel_err_gpu_mean": float(np.mean(rel_gpu)), "rel_err_oracle_mean": float(np.mean(rel_orc)),
+            "rel_err_max_abs_diff": float(np.max(np.abs(np.array(rel_gpu) - np.array(rel_orc))))}
+        out["cpu_baseline"] = {"value": ne * vals_e * 2.5625 / el / 1e9, "unit": "GB/s",
+                               "values_per_s": ne * vals_e / el, "cores": procs, "kind": "oracle",
+                               "sample": f"{ne} experts of layer 0 (the device tensors above, gate_up + down), "
+                                         f"one expert per process of a {procs}-process pool, {el:.1f} s "
+                                         f"(process start included)",
+                               "single_core": {"value": n1 * vals_e * 2.5625 / el1 / 1e9, "unit": "GB/s",
+                                               "cores": 1, "sample": f"{n1} of those experts in this process, "
+                                                                     f"{el1:.1f} s"}}
+    return out
+
+
+def bench_hessian_quant(args, torch, pkg):
+    """One layer of 512 experts (fused gate_up 1280 x 2560, down 2560 x 640;
+    bf16 Student-t(4) source with 1% outlier rows x8, as the streaming
+    workload) quantized to NVFP4 by the Hessian-weighted scale search, with
+    synthetic calibration covariances drawn on the device per expert (the
+    recipe of synth.calibration_hessian, estimated from 256 sampled rows)
+    and calibration row counts from synth.calibration_rows (two thin
+    experts keep plain max)."""
+    import numpy as np
+
+    import synth
+    E, H, I = 512, 2560, 640
+    gen = torch.Generator(device="cuda")
+    tdist = torch.distributions.StudentT(torch.tensor(4.0, device="cuda"))
+
+    def source(rows, cols, seed):
+        gen.manual_seed(seed)
+        torch.manual_seed(seed + 1)
+        v = tdist.sample((E, rows, cols)) * (0.02 / 2 ** 0.5)
+        n_out = int(round(0.01 * rows))
+        idx = torch.argsort(torch.rand(E, rows, device="cuda", generator=gen), dim=1)[:, :n_out]
+        v.scatter_(1, idx[:, :, None].expand(E, n_out, cols), v.gather(1, idx[:, :, None].expand(E, n_out, cols)) * 8)
+        return v.to(torch.bfloat16)
+
+    def hessians(cols, n_rows, seed, sample=256):
+        nb = cols // 16
+        out = torch.empty(E, nb, 16, 16, dtype=torch.float32, device="cuda")
+        gen.manual_seed(seed)
+        for e0 in range(0, E, 32):
+            ne = min(32, E - e0)
+            scale = torch.exp(0.5 * torch.randn(ne, 1, cols, device="cuda", generator=gen))
+            c = torch.rand(ne, 1, nb, device="cuda", generator=gen)
+            z = torch.randn(ne, sample, cols, device="cuda", generator=gen)
+            sh = torch.randn(ne, sample, nb, device="cuda", generator=gen)
+            a = ((z + (c * sh).repeat_interleave(16, dim=2)) * scale).to(torch.bfloat16).double()
+            a = a.view(ne, sample, nb, 16)
+            out[e0:e0 + ne] = (torch.einsum("etbi,etbj->ebij", a, a) / sample).float()
+        out[torch.from_numpy(n_rows == 0).cuda()] = 0.0
+        return out
+
+    n_rows = synth.calibration_rows(11, E)
+    rows_dev = torch.from_numpy(n_rows).cuda()
+    w13, w2 = source(2 * I, H, 3000), source(H, I, 3100)
+    h13, h2 = hessians(H, n_rows, 3200), hessians(I, n_rows, 3300)
+    torch.cuda.synchronize()
+    for _ in range(1):
+        pkg.quantize_hessian(w13, h13, rows_dev)
+        pkg.quantize_hessian(w2, h2, rows_dev)
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = args.hessian_reps
+    start.record()
+    for _ in range(reps):
+        q13 = pkg.quantize_hessian(w13, h13, rows_dev, want_choice=True)
+        q2 = pkg.quantize_hessian(w2, h2, rows_dev, want_choice=True)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / reps
+    vals = E * 3 * H * I
+    hbytes = h13.numel() * 4 + h2.numel() * 4
+    alg_bytes = vals * 2.5625 + hbytes + E * 8 + E * 4 * 2
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+
+    # fp64 FMAs the search spends: 16 x 17 per candidate of every block whose
+    # window holds more than one code (the amax/6 and block-max-to-4 plans'
+    # codes, from the block maxima and the tensor scales; thin experts none)
+    def fmas(w, q, full):
+        amax_b = w.float().abs().view(E, -1, 16).amax(dim=2)
+        S = q["tensor_scale"].view(E, 1)
+        c6 = torch.clamp(amax_b / (6 * S), max=448.0).to(torch.float8_e4m3fn).view(torch.uint8).int()
+        c4 = torch.clamp(amax_b / (4 * S), max=448.0).to(torch.float8_e4m3fn).view(torch.uint8).int()
+        width = torch.where(full.view(E, 1), c4 - c6 + 1, torch.ones_like(c4))
+        return float(torch.where(width > 1, width, torch.zeros_like(width)).sum()) * 16 * 17
+
+    full = torch.from_numpy(n_rows >= 64).cuda()
+    n_fma = fmas(w13, q13, full) + fmas(w2, q2, full)
+    tflops = 2 * n_fma / (ms * 1e-3) / 1e12
+    # quality on the first experts: relative plain and H-weighted error of the
+    # Hessian search, the plain sweep, 4/6 and plain max on the same tensors
+    qual = {}
+    ne = 8
+    for name, w, hh in (("gate_up", w13[:ne].contiguous(), h13[:ne]), ("down", w2[:ne].contiguous(), h2[:ne])):
+        x = w.double()
+        xv = x.view(ne, x.shape[1], -1, 16)
+        hx = torch.einsum("erbi,ebij,erbj->e", xv, hh.double(), xv)
+        res = {}
+        cand = {"hessian": pkg.quantize_hessian(w, hh, rows_dev[:ne])}
+        for rule in ("sweep", "4over6", "rtn"):
+            cand[rule] = pkg.quantize(w, "nvfp4", rule)
+        for rule, q in cand.items():
+            d = (x - pkg.dequantize(q, "nvfp4", tuple(w.shape)).double()).view(ne, x.shape[1], -1, 16)
+            hd = torch.einsum("erbi,ebij,erbj->e", d, hh.double(), d)
+            full_e = full[:ne]
+            res[rule] = {"rel_err": float((d.pow(2).sum(dim=(1, 2, 3)) / x.pow(2).sum(dim=(1, 2))).sqrt()[full_e].mean()),
+                         "rel_weighted_err": float((hd / hx).sqrt()[full_e].mean())}
+        qual[name] = res
+    out = {"workload": f"Hessian-weighted NVFP4 quantization of one layer: {E} experts x (gate_up {2 * I}x{H}, "
+                       f"down {H}x{I}), bf16 Student-t(4) source with 1% outlier rows x8, synthetic per-expert "
+                       f"calibration covariances (16x16 diagonal blocks of the input Hessian)",
+           "value": gbs, "unit": "GB/s", "ms_per_layer": ms, "reps": reps, "dtype": "f64",
+           "roofline": {"bound": "alu", "kernel": "hessian_quant_kernel",
+                        "achieved": tflops, "peak": 78.6, "unit": "TFLOP/s", "frac": tflops / 78.6,
+                        "traffic": None, "flops_per_layer": 2 * n_fma,
+                        "unit_of_work": "2 x 16 x 17 fp64 FLOPs per candidate scale of each block whose "
+                                        "window holds more than one code"},
+           "bytes_per_layer": alg_bytes,
+           "thin_experts": int((n_rows < 64).sum()),
+           "quality_first_experts": qual}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the Hessian-weighted search")
         from oracle import quant
         from oracle.formats import bf16_to_f64
         t0 = time.perf_counter()
         n_vals = 0
         e = 0
-        budget = args.cpu_budget if rule == "4over6" else args.cpu_budget / 2
-        while time.perf_counter() - t0 < budget and e < 64:
-            w13, w2 = synth.streaming_expert(0, e)
-            for w in (w13, w2):
-                quant.quantize_nvfp4(bf16_to_f64(w), rule)
+        while time.perf_counter() - t0 < args.cpu_budget and e < 8:
+            w13h, w2h = synth.streaming_expert(0, e)
+            for w, cols in ((w2h, I), (w13h, H)):
+                hh = synth.calibration_hessian(11, e, cols, 256)
+                quant.quantize_nvfp4_hessian(bf16_to_f64(w), hh, 256)
                 n_vals += w.size
+                if time.perf_counter() - t0 >= args.cpu_budget:
+                    break
             e += 1
         el = time.perf_counter() - t0
         out["cpu_baseline"] = {"value": n_vals * 2.5625 / el / 1e9, "unit": "GB/s", "values_per_s": n_vals / el,
                                "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
-                               "sample": f"{e} expert(s) of layer 0 (gate_up + down), source drawn on the host, "
-                                         f"{el:.1f} s"}
+                               "sample": f"{n_vals} values of layer-0 experts (down then gate_up), source and "
+                                         f"covariances drawn on the host, {el:.1f} s"}
+    del w13, w2, h13, h2
+    torch.cuda.empty_cache()
     return out
 
 
@@ -613,7 +964,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
                     choices=["all", "decode", "prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant",
-                             "sweep_quant", "stack_decode", "copy"],
+                             "sweep_quant", "hessian_quant", "stack_decode", "copy", "ceilings"],
                     help="'all': the decode headline plus every other workload under 'workloads'; "
                          "'copy': a plain 1 GiB device copy that calibrates the HBM byte counters")
     ap.add_argument("--prefill-steps", type=int, default=10)
@@ -627,6 +978,10 @@ def main():
     ap.add_argument("--stack-steps", type=int, default=20)
     ap.add_argument("--sweep-layers", type=int, default=16,
                     help="layers of the streaming workload under the scale-sweep rule")
+    ap.add_argument("--oracle-experts", type=int, default=16,
+                    help="streaming workloads: experts of layer 0 copied back and checked against the oracle")
+    ap.add_argument("--hessian-reps", type=int, default=3,
+                    help="timed repetitions of the Hessian-weighted quantization of one layer")
     ap.add_argument("--copies", type=int, default=8,
                     help="resident copies of the quantized layer rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -650,12 +1005,16 @@ def main():
     if args.workload == "copy":
         print(json.dumps(bench_copy(args, torch)), flush=True)
         return
+    if args.workload == "ceilings":
+        print(json.dumps(bench_ceilings(args, torch, pkg)), flush=True)
+        return
     if args.workload in ("all", "decode"):
         dargs = argparse.Namespace(**vars(args))
         dargs.workload = "decode"
         out = bench_decode(dargs, torch, pkg)
         torch.cuda.empty_cache()
-        others = (["prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant", "sweep_quant", "stack_decode"]
+        others = (["prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant", "sweep_quant", "hessian_quant",
+                   "stack_decode"]
                   if args.workload == "all" else [])
     else:
         out = None
@@ -667,6 +1026,8 @@ def main():
             extra[name] = bench_stream_quant(args, torch, pkg)
         elif name == "sweep_quant":
             extra[name] = bench_stream_quant(args, torch, pkg, rule="sweep")
+        elif name == "hessian_quant":
+            extra[name] = bench_hessian_quant(args, torch, pkg)
         elif name == "stack_decode":
             extra[name] = bench_stack(args, torch, pkg)
         else:

@@ -134,14 +134,20 @@ __device__ __forceinline__ void candidate_residuals(const float (&v)[16], double
 
 // d^T H d by fma chains (H rows from LDS, broadcast reads) and the bound
 // (sum |d|)^2 * max |H| of its rounding error's scale.
+// The LDS offset passes through an empty asm statement on every call, so the
+// 256 reads of H stay inside the candidate loop (hoisted out of it, they
+// would hold 512 registers).
 __device__ __forceinline__ void weighted_error(const double (&d)[16], const double* H, double hmax, double& err,
                                                double& bound) {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  const double* Hz = H + z;
   double e = 0.0, s = 0.0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     double t = 0.0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) t = fma(H[16 * i + j], d[j], t);
+    for (int j = 0; j < 16; ++j) t = fma(Hz[16 * i + j], d[j], t);
     e = fma(d[i], t, e);
     s += fabs(d[i]);
   }

@@ -31,6 +31,19 @@ inline int check_launch(const char* what) {
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// While alive, this thread's stream-capture mode is relaxed, so the one-time
+// per-device set-up calls (raising a kernel's dynamic-LDS limit, creating
+// the shared expert's helper stream and events) are allowed even when the
+// first forward on a device is issued inside a graph capture.
+struct RelaxedCapture {
+  hipStreamCaptureMode mode = hipStreamCaptureModeRelaxed;
+  bool ok;
+  RelaxedCapture() { ok = hipThreadExchangeStreamCaptureMode(&mode) == hipSuccess; }
+  ~RelaxedCapture() {
+    if (ok) (void)hipThreadExchangeStreamCaptureMode(&mode);
+  }
+};
+
 inline unsigned grid_1d(int64_t n, int threads) {
   return (unsigned)((n + threads - 1) / threads);
 }

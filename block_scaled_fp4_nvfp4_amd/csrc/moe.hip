@@ -956,6 +956,7 @@ static int side_stream(SideStream** out) {
     return fail(FP4_ERR_HIP, "no current HIP device");
   SideStream& ss = g_side[dev];
   if (!ss.s) {
+    RelaxedCapture relaxed;
     if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
         hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)

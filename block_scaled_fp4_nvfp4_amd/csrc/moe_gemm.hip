@@ -1417,6 +1417,7 @@ static int raise_dyn_lds(const void* kernel, int bytes, std::atomic<uint64_t>& r
   if (hipGetDevice(&dev) != hipSuccess) return fail(FP4_ERR_HIP, "hipGetDevice failed");
   const uint64_t bit = 1ull << (dev & 63);
   if (raised.load(std::memory_order_acquire) & bit) return FP4_OK;
+  RelaxedCapture relaxed;
   if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
     return fail(FP4_ERR_HIP, "hipFuncSetAttribute failed");
   raised.fetch_or(bit, std::memory_order_acq_rel);

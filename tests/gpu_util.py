@@ -78,12 +78,40 @@ class OracleLayer:
             self.shared = dict(w13=moe.quantize_expert_weight(s13, "mxfp8"),
                                w2=moe.quantize_expert_weight(s2, "mxfp8"), gate_bits=gate)
 
-    @functools.lru_cache(maxsize=None)
+    _done = None
+
+    def prefetch(self, experts, processes=16):
+        """Quantize these experts now, in a pool of processes (the oracle is
+        plain single-threaded numpy; a whole decode layer's touched experts
+        take minutes on one core)."""
+        import concurrent.futures as cf
+        import multiprocessing as mp
+
+        from oracle_pool import quantize_expert_pair
+        if self._done is None:
+            self._done = {}
+        todo = [int(e) for e in experts if int(e) not in self._done]
+        tasks = [(self.w13_bits[e], self.w2_bits[e], self.cfg.w_fmt, self.rule) for e in todo]
+        with cf.ProcessPoolExecutor(max(1, min(processes, len(todo))), mp.get_context("spawn")) as ex:
+            for e, r in zip(todo, ex.map(quantize_expert_pair, tasks)):
+                self._done[e] = r
+
     def w13(self, e):
+        if self._done is not None and e in self._done:
+            return self._done[e][0]
+        return self._w13(e)
+
+    def w2(self, e):
+        if self._done is not None and e in self._done:
+            return self._done[e][1]
+        return self._w2(e)
+
+    @functools.lru_cache(maxsize=None)
+    def _w13(self, e):
         return self._moe.quantize_expert_weight(self.w13_bits[e], self.cfg.w_fmt, self.rule)
 
     @functools.lru_cache(maxsize=None)
-    def w2(self, e):
+    def _w2(self, e):
         return self._moe.quantize_expert_weight(self.w2_bits[e], self.cfg.w_fmt, self.rule)
 
     def as_dict(self):

@@ -11,8 +11,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fp4moe.h")
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER):
+    with open(header) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
 
@@ -31,8 +32,14 @@ def test_header_declares_the_entry_points():
 
 
 def test_library_exports_every_declared_symbol(L):
-    for n in _declared_functions():
-        assert hasattr(L, n), n
+    import glob
+    headers = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+    assert HEADER in headers and len(headers) == 2  # the library ABI and its ceiling probes
+    for h in headers:
+        for n in _declared_functions(h):
+            assert hasattr(L, n), (h, n)
+    assert _declared_functions(os.path.join(ROOT, "include", "fp4moe_probe.h")) == \
+        ["fp4_probe_combine", "fp4_probe_mfma", "fp4_probe_read"]
     from block_scaled_fp4_nvfp4_amd import _lib
     assert sorted(_lib.EXPORTED) == _declared_functions()
 

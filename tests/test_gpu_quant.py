@@ -272,6 +272,44 @@ def test_nvfp4_large_batch_chunked_amax(rule):
         np.testing.assert_array_equal(scales[b, rows], o["scales"], err_msg=f"oracle scales {b}")
 
 
+def test_nvfp4_eight_chunks_with_a_short_last_chunk():
+    """67 bf16 tensors of 1024 x 1024: the batch is cut into 8 chunks of 9
+    tensors (the last holds 4), each chunk's tensor amaxes taken inside the
+    previous chunk's quantization launch (the streaming workload's path at
+    512 experts).  Every tensor scale is the oracle's amax / 2688 bit for bit;
+    codes and scales of the first and last tensor of every chunk equal
+    one-tensor calls; two tensors' sampled rows equal the oracle."""
+    print_case("nvfp4/4over6 67 x 1024 x 1024, 8 chunks")
+    m = _lib()
+    B, R, C = 67, 1024, 1024
+    rng = np.random.default_rng(67)
+    x = rng.standard_normal((B, R * C), dtype=np.float32)
+    for b in range(B):
+        x[b] *= np.float32(2.0 ** ((b % 23) - 11) * (1 + 0.01 * b))
+        x[b, (b * 7919 + 13) % (R * C)] = np.float32(9.0 * 2.0 ** ((b % 23) - 11))
+    bits = F.bf16_bits_from_f32(x).reshape(B, R, C)
+    del x
+    t = dev_bf16(bits)
+    q = m.quantize(t, "nvfp4", "4over6")
+    torch.cuda.synchronize()
+    ts = host(q["tensor_scale"])
+    want_ts = np.array([Q.nvfp4_tensor_scale(np.max(np.abs(F.bf16_to_f64(bits[b])))) for b in range(B)], np.float32)
+    np.testing.assert_array_equal(ts.view(np.uint32), want_ts.view(np.uint32))
+    codes, scales = host(q["codes"]), host(q["scales"])
+    edges = sorted({b for c0 in range(0, B, 9) for b in (c0, min(c0 + 8, B - 1))})
+    assert 63 in edges and 66 in edges
+    for b in edges:
+        one = m.quantize(t[b:b + 1], "nvfp4", "4over6")
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(codes[b], host(one["codes"])[0], err_msg=f"codes, tensor {b}")
+        np.testing.assert_array_equal(scales[b], host(one["scales"])[0], err_msg=f"scales, tensor {b}")
+    for b in (8, 64):
+        rows = slice(128, 192)
+        o = Q.quantize_nvfp4(F.bf16_to_f64(bits[b, rows]), "4over6", tensor_scale=want_ts[b])
+        np.testing.assert_array_equal(codes[b, rows], F.pack_nibbles(o["codes"]), err_msg=f"oracle rows {b}")
+        np.testing.assert_array_equal(scales[b, rows], o["scales"], err_msg=f"oracle scales {b}")
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp4"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_block_error_matches_oracle(fmt, dtype):
