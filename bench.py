@@ -478,7 +478,7 @@ def bench_ceilings(args, torch, pkg):
     L = pkg.lib()
     vp = ctypes.c_void_p
     L.fp4_probe_read.argtypes = [vp, ctypes.c_size_t, ctypes.c_int, vp, vp]
-    L.fp4_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp]
+    L.fp4_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     L.fp4_probe_combine.argtypes = [ctypes.c_int, vp, vp, vp, ctypes.c_int64, ctypes.c_int, ctypes.c_int, vp, vp, vp]
     stream = lambda: vp(torch.cuda.current_stream().cuda_stream)
 
@@ -511,15 +511,22 @@ def bench_ceilings(args, torch, pkg):
     del buf
     grid, iters = 2048, 2000
     acc = torch.empty(grid * 256 * 4, dtype=torch.float32, device="cuda")
+    clk = torch.zeros(128, dtype=torch.int64, device="cuda")
     kinds = {"f16": (0, 16384, 2500.0), "bf16": (1, 16384, 2500.0), "fp8_x_fp8": (2, 65536, 5000.0),
              "fp8_x_fp4": (3, 65536, 5000.0), "fp4_x_fp4": (4, 65536, 10100.0),
              "f16_32x32x16": (5, 32768, 2500.0), "fp8_x_fp8_32x32x64": (6, 131072, 5000.0),
              "fp4_x_fp4_32x32x64": (7, 131072, 10100.0)}
     mf = {}
     for name, (kind, flops, peak) in kinds.items():
-        ms = timeit(lambda: ok(L.fp4_probe_mfma(kind, iters, grid, vp(acc.data_ptr()), stream())), reps=5)
+        ms = timeit(lambda: ok(L.fp4_probe_mfma(kind, iters, grid, vp(acc.data_ptr()), vp(clk.data_ptr()),
+                                                stream())), reps=5)
         tf = grid * 4 * iters * 8 * flops / (ms * 1e-3) / 1e12
-        mf[name] = {"TFLOPs": tf, "peak_spec": peak, "frac_of_spec": tf / peak}
+        c = clk.cpu().numpy().reshape(64, 2).astype(np.float64)
+        ghz = 0.1 * c[:, 0].sum() / c[:, 1].sum()  # shader cycles per 100 MHz tick, last launch
+        # cycles one SIMD spends per instruction at that clock (256 CUs x 4 SIMDs)
+        cyc = flops * 1024 * ghz * 1e9 / (tf * 1e12)
+        mf[name] = {"TFLOPs": tf, "peak_spec": peak, "frac_of_spec": tf / peak, "clock_GHz": ghz,
+                    "simd_cycles_per_instruction": cyc}
     out["mfma_TFLOPs"] = mf
     rng = np.random.default_rng(1)
     comb = {}
@@ -957,7 +964,63 @@ def bench_stack(args, torch, pkg):
     return out
 
 
+def pmc_summary(dirs, num_xcd=8, num_cu=256, simd_per_cu=4):
+    """Per-kernel table from rocprofv3 --pmc counter CSVs (a directory per
+    pass; averages over a kernel's dispatches).  The normalisations are those
+    of rocprofv3's own derived metrics: the CSV's GRBM_GUI_ACTIVE is summed over
+    the XCDs, so per XCD it is / num_xcd; MFMA busy = sum of
+    SQ_VALU_MFMA_BUSY_CYCLES / (GUI x SIMDs) (MfmaUtil); VALU busy = sum of
+    SQ_ACTIVE_INST_VALU / (GUI x CUs) (VALUBusy); LDS bank conflicts per access
+    = conflict / (active - conflict) cycles (LdsBankConflict); L2 hit = hits /
+    (hits + misses); waits are fractions of SQ_WAVE_CYCLES.  MFMA FLOPs per
+    operand type = SQ_INSTS_VALU_MFMA_MOPS_<type> x 512."""
+    import csv
+    import glob
+    from collections import defaultdict
+    per = defaultdict(lambda: defaultdict(list))
+    for d in dirs:
+        for path in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    k = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("fp4::", "")
+                    per[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    rows = []
+    for k, cs in per.items():
+        a = {c: sum(v) / len(v) for c, v in cs.items()}
+        if "SQ_INSTS_MFMA" in a and a["SQ_INSTS_MFMA"] == 0:
+            continue
+        gui = a.get("GRBM_GUI_ACTIVE", 0.0) / num_xcd
+        row = {"kernel": k, "dispatches": min(len(v) for v in cs.values()), "gui_cycles": gui}
+        if gui and "SQ_VALU_MFMA_BUSY_CYCLES" in a:
+            row["mfma_busy"] = a["SQ_VALU_MFMA_BUSY_CYCLES"] / (gui * num_cu * simd_per_cu)
+        if gui and "SQ_ACTIVE_INST_VALU" in a:
+            row["valu_busy"] = a["SQ_ACTIVE_INST_VALU"] / (gui * num_cu)
+        if gui and "SQ_BUSY_CU_CYCLES" in a:
+            row["cu_busy"] = a["SQ_BUSY_CU_CYCLES"] / (gui * num_cu)
+        if "SQ_WAVE_CYCLES" in a:
+            for c, n in (("SQ_WAIT_INST_ANY", "wait_any"), ("SQ_WAIT_INST_LDS", "wait_lds")):
+                if c in a:
+                    row[n] = a[c] / a["SQ_WAVE_CYCLES"]
+        if "SQ_LDS_BANK_CONFLICT" in a and "SQ_LDS_IDX_ACTIVE" in a:
+            row["lds_conflicts_per_access"] = a["SQ_LDS_BANK_CONFLICT"] / max(
+                a["SQ_LDS_IDX_ACTIVE"] - a["SQ_LDS_BANK_CONFLICT"], 1.0)
+        if "TCC_HIT_sum" in a and "TCC_MISS_sum" in a:
+            row["l2_hit"] = a["TCC_HIT_sum"] / max(a["TCC_HIT_sum"] + a["TCC_MISS_sum"], 1.0)
+        for t in ("F8", "F6F4", "F16", "BF16"):
+            c = "SQ_INSTS_VALU_MFMA_MOPS_" + t
+            if c in a:
+                row["mfma_gflop_" + t.lower()] = a[c] * 512 / 1e9
+        if "SQ_INSTS_MFMA" in a:
+            row["mfma_insts"] = a["SQ_INSTS_MFMA"]
+        rows.append(row)
+    return rows
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
+        for row in pmc_summary(sys.argv[2:]):
+            print(json.dumps(row))
+        return
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)

@@ -16,6 +16,7 @@ typedef _Float16 p_half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 p_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float p_floatx4 __attribute__((ext_vector_type(4)));
 typedef int p_intx8 __attribute__((ext_vector_type(8)));
+typedef int p_intx4 __attribute__((ext_vector_type(4)));
 
 // Every thread reads 16-byte chunks, four per iteration, grid-stride; the
 // XOR of everything read is kept and stored only when it equals a constant
@@ -36,15 +37,36 @@ __global__ void __launch_bounds__(256) probe_read_kernel(const uint4* __restrict
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
+// Shader-clock cycles and 100 MHz constant-clock ticks that wave 0 of
+// workgroups 0..63 spent in its MFMA loop (their ratio gives the shader clock
+// under that load): clk[2 b] and clk[2 b + 1] for workgroup b.
+__device__ __forceinline__ void store_clocks(uint64_t* clk, uint64_t t0, uint64_t r0) {
+  const uint64_t t1 = __builtin_readcyclecounter();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  if (clk && threadIdx.x == 0 && blockIdx.x < 64) {
+    clk[2 * blockIdx.x] = t1 - t0;
+    clk[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 // Eight independent accumulator chains per wave (enough to keep one SIMD's
 // matrix unit issuing back to back), `iters` rounds; operands are register
-// values that never change, accumulators are stored at the end.
+// values that never change, accumulators are stored at the end.  The 16 x 16
+// MFMAs are written as inline asm on AGPR accumulators tied to their own
+// source: from the builtins the register allocator assigns each loop-carried
+// accumulator a destination two registers off its source and rotates them
+// back with about 50 AGPR copies per round of 8 MFMAs, which wait on the
+// MFMA results and halve the measured rate.  The s_nops cover the MFMA
+// hazards the compiler cannot see inside the asm (a VALU write of an
+// accumulator before its first MFMA, the MFMA results read after the loop);
+// a missed hazard could only change the values, not the timing.
 template <int KIND>
-__global__ void __launch_bounds__(256) probe_mfma_kernel(int iters, float* __restrict__ out) {
+__global__ void __launch_bounds__(256) probe_mfma_kernel(int iters, float* __restrict__ out, uint64_t* __restrict__ clk) {
   const int lane = threadIdx.x & 63;
   p_floatx4 acc[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) acc[c] = p_floatx4{0.f, 0.f, 0.f, 0.f};
+  uint64_t t0, r0;
   if constexpr (KIND == FP4_PROBE_MFMA_F16 || KIND == FP4_PROBE_MFMA_BF16) {
     p_half8 a, b;
     p_bf16x8 ab, bb;
@@ -55,41 +77,64 @@ __global__ void __launch_bounds__(256) probe_mfma_kernel(int iters, float* __res
       ab[i] = (__bf16)(0.001f * (lane + i));
       bb[i] = (__bf16)(0.002f * (lane - i));
     }
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+    t0 = __builtin_readcyclecounter();
+    r0 = __builtin_amdgcn_s_memrealtime();
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         if constexpr (KIND == FP4_PROBE_MFMA_F16)
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[c], 0, 0, 0);
+          asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc[c]) : "v"(a), "v"(b));
         else
-          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ab, bb, acc[c], 0, 0, 0);
+          asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[c]) : "v"(ab), "v"(bb));
       }
     }
   } else {
-    // block-scaled f8f6f4 MFMA; format codes 0 = E4M3, 4 = E2M1 (FP4 uses
-    // the first four dwords of each operand)
-    constexpr int FA = KIND == FP4_PROBE_MFMA_FP4_FP4 ? 4 : 0;
-    constexpr int FB = KIND == FP4_PROBE_MFMA_FP8_FP8 ? 0 : 4;
+    // block-scaled f8f6f4 MFMA, both scales 127 (2^0); E2M1 operands take
+    // four dwords (cbsz / blgp 4), E4M3 eight
+    const int one = 127;
     p_intx8 a, b;
+    p_intx4 a4, b4;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       a[i] = 0x38383838 ^ (lane + i);
       b[i] = 0x22222222 ^ (lane * 3 + i);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a4[i] = a[i];
+      b4[i] = b[i];
+    }
+    asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+    t0 = __builtin_readcyclecounter();
+    r0 = __builtin_amdgcn_s_memrealtime();
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        acc[c] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc[c], FA, FB, 0, 127, 0, 127);
+      for (int c = 0; c < 8; ++c) {
+        if constexpr (KIND == FP4_PROBE_MFMA_FP8_FP8)
+          asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                       : "+a"(acc[c]) : "v"(a), "v"(b), "v"(one));
+        else if constexpr (KIND == FP4_PROBE_MFMA_FP8_FP4)
+          asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] blgp:4"
+                       : "+a"(acc[c]) : "v"(a), "v"(b4), "v"(one));
+        else
+          asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                       : "+a"(acc[c]) : "v"(a4), "v"(b4), "v"(one));
+      }
     }
   }
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  store_clocks(clk, t0, r0);
   p_floatx4 s = acc[0];
 #pragma unroll
   for (int c = 1; c < 8; ++c) s += acc[c];
   reinterpret_cast<p_floatx4*>(out)[(size_t)blockIdx.x * 256 + threadIdx.x] = s;
 }
 
-// The 32 x 32 shapes: eight chains of 16-register accumulators.
+// The 32 x 32 shapes: eight chains of 16-register accumulators (from the
+// builtins these loops compile to MFMAs only).
 template <int KIND>
-__global__ void __launch_bounds__(256) probe_mfma32_kernel(int iters, float* __restrict__ out) {
+__global__ void __launch_bounds__(256) probe_mfma32_kernel(int iters, float* __restrict__ out, uint64_t* __restrict__ clk) {
   typedef float floatx16 __attribute__((ext_vector_type(16)));
   const int lane = threadIdx.x & 63;
   floatx16 acc[8];
@@ -97,31 +142,39 @@ __global__ void __launch_bounds__(256) probe_mfma32_kernel(int iters, float* __r
   for (int c = 0; c < 8; ++c)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[c][r] = 0.0f;
+  uint64_t t0, r0;
   if constexpr (KIND == FP4_PROBE_MFMA_F16_32) {
-    p_half8 a, b;
+    p_half8 a[8], b;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      a[i] = (_Float16)(0.001f * (lane + i));
+#pragma unroll
+      for (int c = 0; c < 8; ++c) a[c][i] = (_Float16)(0.001f * (lane + i + 3 * c));
       b[i] = (_Float16)(0.002f * (lane - i));
     }
+    t0 = __builtin_readcyclecounter();
+    r0 = __builtin_amdgcn_s_memrealtime();
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, acc[c], 0, 0, 0);
+      for (int c = 0; c < 8; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[c], b, acc[c], 0, 0, 0);
     }
   } else {
     constexpr int F = KIND == FP4_PROBE_MFMA_FP4_32 ? 4 : 0;
-    p_intx8 a, b;
+    p_intx8 a[8], b;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      a[i] = 0x38383838 ^ (lane + i);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) a[c][i] = 0x38383838 ^ (lane + i + 8 * c);
       b[i] = 0x22222222 ^ (lane * 3 + i);
     }
+    t0 = __builtin_readcyclecounter();
+    r0 = __builtin_amdgcn_s_memrealtime();
     for (int it = 0; it < iters; ++it) {
 #pragma unroll
       for (int c = 0; c < 8; ++c)
-        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, acc[c], F, F, 0, 127, 0, 127);
+        acc[c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[c], b, acc[c], F, F, 0, 127, 0, 127);
     }
   }
+  store_clocks(clk, t0, r0);
   p_floatx4 s = p_floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int c = 0; c < 8; ++c)
@@ -199,30 +252,30 @@ int fp4_probe_read(const void* src, size_t bytes, int grid, uint32_t* sink, void
   return check_launch("probe_read");
 }
 
-int fp4_probe_mfma(int kind, int iters, int grid, float* out, void* stream) {
+int fp4_probe_mfma(int kind, int iters, int grid, float* out, uint64_t* clocks, void* stream) {
   if (!out || grid < 1 || iters < 1) return fail(FP4_ERR_INVALID_ARG, "probe_mfma: bad arguments");
   const dim3 g((unsigned)grid), b(256);
   hipStream_t st = as_stream(stream);
   switch (kind) {
-    case FP4_PROBE_MFMA_F16: hipLaunchKernelGGL(probe_mfma_kernel<FP4_PROBE_MFMA_F16>, g, b, 0, st, iters, out); break;
-    case FP4_PROBE_MFMA_BF16: hipLaunchKernelGGL(probe_mfma_kernel<FP4_PROBE_MFMA_BF16>, g, b, 0, st, iters, out); break;
+    case FP4_PROBE_MFMA_F16: hipLaunchKernelGGL(probe_mfma_kernel<FP4_PROBE_MFMA_F16>, g, b, 0, st, iters, out, clocks); break;
+    case FP4_PROBE_MFMA_BF16: hipLaunchKernelGGL(probe_mfma_kernel<FP4_PROBE_MFMA_BF16>, g, b, 0, st, iters, out, clocks); break;
     case FP4_PROBE_MFMA_FP8_FP8:
-      hipLaunchKernelGGL(probe_mfma_kernel<FP4_PROBE_MFMA_FP8_FP8>, g, b, 0, st, iters, out);
+      hipLaunchKernelGGL(probe_mfma_kernel<FP4_PROBE_MFMA_FP8_FP8>, g, b, 0, st, iters, out, clocks);
       break;
     case FP4_PROBE_MFMA_FP8_FP4:
-      hipLaunchKernelGGL(probe_mfma_kernel<FP4_PROBE_MFMA_FP8_FP4>, g, b, 0, st, iters, out);
+      hipLaunchKernelGGL(probe_mfma_kernel<FP4_PROBE_MFMA_FP8_FP4>, g, b, 0, st, iters, out, clocks);
       break;
     case FP4_PROBE_MFMA_FP4_FP4:
-      hipLaunchKernelGGL(probe_mfma_kernel<FP4_PROBE_MFMA_FP4_FP4>, g, b, 0, st, iters, out);
+      hipLaunchKernelGGL(probe_mfma_kernel<FP4_PROBE_MFMA_FP4_FP4>, g, b, 0, st, iters, out, clocks);
       break;
     case FP4_PROBE_MFMA_F16_32:
-      hipLaunchKernelGGL(probe_mfma32_kernel<FP4_PROBE_MFMA_F16_32>, g, b, 0, st, iters, out);
+      hipLaunchKernelGGL(probe_mfma32_kernel<FP4_PROBE_MFMA_F16_32>, g, b, 0, st, iters, out, clocks);
       break;
     case FP4_PROBE_MFMA_FP8_32:
-      hipLaunchKernelGGL(probe_mfma32_kernel<FP4_PROBE_MFMA_FP8_32>, g, b, 0, st, iters, out);
+      hipLaunchKernelGGL(probe_mfma32_kernel<FP4_PROBE_MFMA_FP8_32>, g, b, 0, st, iters, out, clocks);
       break;
     case FP4_PROBE_MFMA_FP4_32:
-      hipLaunchKernelGGL(probe_mfma32_kernel<FP4_PROBE_MFMA_FP4_32>, g, b, 0, st, iters, out);
+      hipLaunchKernelGGL(probe_mfma32_kernel<FP4_PROBE_MFMA_FP4_32>, g, b, 0, st, iters, out, clocks);
       break;
     default: return fail(FP4_ERR_INVALID_ARG, "probe_mfma: unknown kind %d", kind);
   }

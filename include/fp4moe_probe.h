@@ -37,8 +37,12 @@ enum {
 
 /* MFMA issue rate: `grid` workgroups of 4 waves, each wave `iters` rounds of
  * 8 independent MFMAs of `kind`; out: f32 [grid * 256 * 4] (the accumulators,
- * so the work is kept).  FLOPs = grid * 4 * iters * 8 * (FLOPs per instruction). */
-int fp4_probe_mfma(int kind, int iters, int grid, float* out, void* stream);
+ * so the work is kept).  FLOPs = grid * 4 * iters * 8 * (FLOPs per instruction).
+ * clocks: null, or uint64 [128] receiving, for workgroups b < min(grid, 64),
+ * the shader-clock cycles (clocks[2 b]) and 100 MHz constant-clock ticks
+ * (clocks[2 b + 1]) that the workgroup's first wave spent in its MFMA loop;
+ * 0.1 GHz * cycles / ticks is the shader clock under that load. */
+int fp4_probe_mfma(int kind, int iters, int grid, float* out, uint64_t* clocks, void* stream);
 
 enum {
   FP4_PROBE_STORE_O = 0,  /* the down GEMM's epilogue stores o [T*k, H] (f32)                   */

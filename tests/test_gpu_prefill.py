@@ -227,6 +227,32 @@ def test_tiny_shared_expert(tiny):
     assert rel_fro(y, y0) > 0.05
 
 
+def test_shared_expert_at_model_width():
+    """The MXFP8 shared expert at the model's widths (hidden 2560, shared
+    1280; the tiny-layer test covers 256 and 128) over 200 tokens (three full
+    64-row tiles and a ragged one), next to four NVFP4 routed experts: y
+    against the oracle, and the shared part alone (y with it minus y without
+    it) against the oracle's."""
+    print_case("shared expert at hidden 2560, width 1280, 200 tokens")
+    cfg = synth.CONFIGS["prefill_nvfp4"].replace(num_experts=4, top_k=2, tokens=200, input_seed=11)
+    assert cfg.shared_inter == 1280 and cfg.hidden == 2560
+    w13, w2 = synth.layer_weights(cfg)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    shared = synth.shared_expert(cfg)
+    y, _, _ = _run(gpu_layer(cfg, w13, w2, shared=shared), x, ids, wts)
+    y0, _, _ = _run(gpu_layer(cfg.replace(shared_inter=0), w13, w2), x, ids, wts)
+    ref = OracleLayer(cfg, w13, w2, shared=shared)
+    y_ref = moe.moe_forward(ref.as_dict(), x, ids, wts)
+    ref0 = ref.as_dict()
+    del ref0["shared"]
+    y0_ref = moe.moe_forward(ref0, x, ids, wts)
+    err, err_s = rel_fro(y, y_ref), rel_fro(y.astype(np.float64) - y0, y_ref - y0_ref)
+    print(f"relative Frobenius error: y {err:.3e}, shared part {err_s:.3e}")
+    assert err <= TOL and err_s <= TOL
+    assert rel_fro(y, y0) > 0.05
+
+
 def test_tiny_invalid_ids_w4a4(tiny):
     print_case("tiny W4A4 invalid ids")
     cfg, w13, w2, x, ids, wts = tiny
