@@ -780,7 +780,8 @@ def bench_hessian_quant(args, torch, pkg):
     # Hessian search, the plain sweep, 4/6 and plain max on the same tensors
     qual = {}
     ne = 8
-    for name, w, hh in (("gate_up", w13[:ne].contiguous(), h13[:ne]), ("down", w2[:ne].contiguous(), h2[:ne])):
+    for name, w, hh in () if args.no_quality else (("gate_up", w13[:ne].contiguous(), h13[:ne]),
+                                                    ("down", w2[:ne].contiguous(), h2[:ne])):
         x = w.double()
         xv = x.view(ne, x.shape[1], -1, 16)
         hx = torch.einsum("erbi,ebij,erbj->e", xv, hh.double(), xv)
@@ -801,7 +802,9 @@ def bench_hessian_quant(args, torch, pkg):
            "value": gbs, "unit": "GB/s", "ms_per_layer": ms, "reps": reps, "dtype": "f64",
            "roofline": {"bound": "alu", "kernel": "hessian_quant_kernel",
                         "achieved": tflops, "peak": 78.6, "unit": "TFLOP/s", "frac": tflops / 78.6,
-                        "traffic": None, "flops_per_layer": 2 * n_fma,
+                        "traffic": (lambda t: t["bytes_per_launch"] if t else None)(
+                            measured_traffic("hessian_quant_kernel", "quantize", "hessian_quant")),
+                        "traffic_unit": "HBM bytes per layer", "flops_per_layer": 2 * n_fma,
                         "unit_of_work": "2 x 16 x 17 fp64 FLOPs per candidate scale of each block whose "
                                         "window holds more than one code"},
            "bytes_per_layer": alg_bytes,
@@ -1012,14 +1015,89 @@ def pmc_summary(dirs, num_xcd=8, num_cu=256, simd_per_cu=4):
                 row["mfma_gflop_" + t.lower()] = a[c] * 512 / 1e9
         if "SQ_INSTS_MFMA" in a:
             row["mfma_insts"] = a["SQ_INSTS_MFMA"]
+        if "SQ_INSTS_VALU" in a and a.get("SQ_WAVES"):
+            row["valu_insts_per_wave"] = a["SQ_INSTS_VALU"] / a["SQ_WAVES"]
+            row["valu_insts"] = a["SQ_INSTS_VALU"]
         rows.append(row)
     return rows
+
+
+# kernels whose HBM traffic profiles/hbm_traffic.txt records, per workload:
+# (kernel, demangled-name prefixes, stage, source file, per): per "launch" is
+# the average over the matching dispatches, per "layer" the sum over the run
+# divided by the layers run (the quantizer's amax, scale and code kernels)
+_QUANT_KERNELS = ("quant_fp4_kernel<", "tensor_amax_kernel<", "amax_parts_kernel<", "nv_scale_from_parts_kernel",
+                  "nv_tensor_scale_kernel", "fill_u32_kernel")
+TRAFFIC_KERNELS = {
+    "decode": [("gemv_gateup_kernel", ("gemv_gateup_kernel<",), "gate_up", "moe.hip", "launch"),
+               ("gemv_down_kernel", ("gemv_down_kernel<",), "down", "moe.hip", "launch"),
+               ("perm_small_kernel", ("perm_small_kernel",), "permute", "moe.hip", "launch"),
+               ("combine_kernel", ("combine_kernel<",), "combine", "moe.hip", "launch")],
+    "prefill_nvfp4": [("grouped_gemm_nv2_kernel", ("grouped_gemm_nv2_kernel<0,",), "gate_up", "moe_gemm.hip", "launch"),
+                      ("grouped_gemm_nv2_kernel", ("grouped_gemm_nv2_kernel<1,",), "down", "moe_gemm.hip", "launch"),
+                      ("combine_kernel", ("combine_kernel<",), "combine", "moe.hip", "launch")],
+    "prefill_mxfp4": [("grouped_gemm_mx2_kernel", ("grouped_gemm_mx2_kernel<1, 0,",), "gate_up", "moe_gemm.hip", "launch"),
+                      ("grouped_gemm_mx2_kernel", ("grouped_gemm_mx2_kernel<1, 1,",), "down", "moe_gemm.hip", "launch"),
+                      ("combine_kernel", ("combine_kernel<",), "combine", "moe.hip", "launch")],
+    "prefill_fp8": [("grouped_gemm_mx2_kernel", ("grouped_gemm_mx2_kernel<2, 0,",), "gate_up", "moe_gemm.hip", "launch"),
+                    ("grouped_gemm_mx2_kernel", ("grouped_gemm_mx2_kernel<2, 1,",), "down", "moe_gemm.hip", "launch"),
+                    ("combine_kernel", ("combine_kernel<",), "combine", "moe.hip", "launch")],
+    "stream_quant": [("quant_fp4_kernel", _QUANT_KERNELS, "quantize", "quant.hip", "layer")],
+    "sweep_quant": [("quant_fp4_kernel", _QUANT_KERNELS, "quantize", "quant.hip", "layer")],
+    "hessian_quant": [("hessian_quant_kernel", ("hessian_quant_kernel<",), "quantize", "hessian.hip", "layer")],
+}
+
+
+def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, layers=1):
+    """hbm_traffic.txt lines from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs
+    (one counter per run, KiB per dispatch summed over the XCDs' L2s) of the
+    workload and of `bench.py --workload copy` (2^28 float32 read and written
+    per launch), which calibrates each counter to bytes."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        out = {}
+        for path in glob.glob(os.path.join(d, "*counter_collection.csv")):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r["Counter_Name"] == counter:
+                        k = r["Kernel_Name"].replace("void ", "").replace("fp4::", "")
+                        out.setdefault(k, []).append(float(r["Counter_Value"]))
+        return out
+
+    def calib(d, counter):
+        vals = [v for k, vs in per_kernel(d, counter).items() if "neg" in k for v in vs]
+        return (1 << 30) / (1024.0 * sum(vals) / len(vals))
+
+    fs, ws = calib(copy_fetch_dir, "FETCH_SIZE"), calib(copy_write_dir, "WRITE_SIZE")
+    fk, wk = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    lines = []
+    for kernel, prefixes, stage, src, per in TRAFFIC_KERNELS[workload]:
+        def pick(m):
+            v = [x for k, xs in m.items() if k.startswith(prefixes) for x in xs]
+            if not v:
+                return None
+            return (sum(v) / len(v) if per == "launch" else sum(v) / layers) * 1024.0
+        f, w = pick(fk), pick(wk)
+        if f is None or w is None:
+            continue
+        rel = "block_scaled_fp4_nvfp4_amd/csrc/" + src
+        lines.append(f"kernel={kernel} stage={stage} workload={workload} fetch_bytes={f * fs:.0f} "
+                     f"write_bytes={w * ws:.0f} bytes_per_launch={f * fs + w * ws:.0f} copy_scale={fs:.4f} "
+                     f"write_scale={ws:.4f} per={per} source={rel} source_sha={file_sha(rel)}")
+    return lines
 
 
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
         for row in pmc_summary(sys.argv[2:]):
             print(json.dumps(row))
+        return
+    if len(sys.argv) > 1 and sys.argv[1] == "--traffic-summary":
+        a = sys.argv[2:]
+        for line in traffic_summary(a[0], a[1], a[2], a[3], a[4], int(a[5]) if len(a) > 5 else 1):
+            print(line)
         return
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -1049,8 +1127,8 @@ def main():
                     help="resident copies of the quantized layer rotated across steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-quality", action="store_true",
-                    help="streaming workloads: skip the error statistics (for counter runs that must see "
-                         "only the timed kernels)")
+                    help="streaming and Hessian workloads: skip the error statistics (for counter runs that "
+                         "must see only the timed kernels)")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
     args = ap.parse_args()
     if args.gpus != 1:
