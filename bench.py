@@ -762,7 +762,8 @@ def bench_hessian_quant(args, torch, pkg):
     alg_bytes = vals * 2.5625 + hbytes + E * 8 + E * 4 * 2
     gbs = alg_bytes / (ms * 1e-3) / 1e9
 
-    # fp64 FMAs the search spends: 16 x 17 per candidate of every block whose
+    # fp64 FMAs the search spends: 152 per candidate (136 for t = T d over the
+    # upper triangle T of H + H^T, 16 for d . t) of every block whose
     # window holds more than one code (the amax/6 and block-max-to-4 plans'
     # codes, from the block maxima and the tensor scales; thin experts none)
     def fmas(w, q, full):
@@ -771,7 +772,7 @@ def bench_hessian_quant(args, torch, pkg):
         c6 = torch.clamp(amax_b / (6 * S), max=448.0).to(torch.float8_e4m3fn).view(torch.uint8).int()
         c4 = torch.clamp(amax_b / (4 * S), max=448.0).to(torch.float8_e4m3fn).view(torch.uint8).int()
         width = torch.where(full.view(E, 1), c4 - c6 + 1, torch.ones_like(c4))
-        return float(torch.where(width > 1, width, torch.zeros_like(width)).sum()) * 16 * 17
+        return float(torch.where(width > 1, width, torch.zeros_like(width)).sum()) * 152
 
     full = torch.from_numpy(n_rows >= 64).cuda()
     n_fma = fmas(w13, q13, full) + fmas(w2, q2, full)
@@ -805,7 +806,7 @@ def bench_hessian_quant(args, torch, pkg):
                         "traffic": (lambda t: t["bytes_per_launch"] if t else None)(
                             measured_traffic("hessian_quant_kernel", "quantize", "hessian_quant")),
                         "traffic_unit": "HBM bytes per layer", "flops_per_layer": 2 * n_fma,
-                        "unit_of_work": "2 x 16 x 17 fp64 FLOPs per candidate scale of each block whose "
+                        "unit_of_work": "2 x 152 fp64 FLOPs per candidate scale of each block whose "
                                         "window holds more than one code"},
            "bytes_per_layer": alg_bytes,
            "thin_experts": int((n_rows < 64).sum()),

@@ -14,9 +14,12 @@
 //
 // Exactness.  d is exact in double (x has at most 24 significant bits,
 // xhat = g s S at most 31, and where g > 0 the two lie within a factor of a
-// few of each other; where g = 0, d = x).  err is evaluated in double with
-// fma chains, t_i = sum_j H_ij d_j then sum_i d_i t_i, whose rounding error
-// is below 2 * 16 * 2^-53 * M with M = sum_ij |H_ij| |d_i| |d_j|; M is bounded
+// few of each other; where g = 0, d = x).  err is evaluated in double from
+// the upper triangle T of H + H^T (T_ii = H_ii, T_ij = H_ij + H_ji for j > i,
+// exact in double from f32 H) with fma chains, t_i = sum_{j>=i} T_ij d_j then
+// sum_i d_i t_i (d^T H d equals d^T T d for any H; 152 fmas against 272 for
+// the full product), whose rounding error is below 2 * 16 * 2^-53 * M with
+// M = sum_ij |T_ij| |d_i| |d_j| <= sum_ij |H_ij| |d_i| |d_j|; M is bounded
 // by B = (sum_i |d_i|)^2 max |H|.  Two candidates whose double errors differ
 // by more than 2^-46 (B_a + B_b) are therefore ordered correctly; closer
 // ones are compared exactly: every term H_ij d_i d_j is split into four
@@ -132,22 +135,26 @@ __device__ __forceinline__ void candidate_residuals(const float (&v)[16], double
   }
 }
 
-// d^T H d by fma chains (H rows from LDS, broadcast reads) and the bound
+// Row i of the packed upper triangle starts at tri_row(i) (16 - i entries).
+constexpr int kTriSize = 136;
+__host__ __device__ constexpr int tri_row(int i) { return 16 * i - i * (i - 1) / 2; }
+
+// d^T T d by fma chains (T rows from LDS, broadcast reads) and the bound
 // (sum |d|)^2 * max |H| of its rounding error's scale.
 // The LDS offset passes through an empty asm statement on every call, so the
-// 256 reads of H stay inside the candidate loop (hoisted out of it, they
-// would hold 512 registers).
-__device__ __forceinline__ void weighted_error(const double (&d)[16], const double* H, double hmax, double& err,
+// 136 reads of T stay inside the candidate loop (hoisted out of it, they
+// would hold 272 registers).
+__device__ __forceinline__ void weighted_error(const double (&d)[16], const double* T, double hmax, double& err,
                                                double& bound) {
   int z;
   asm volatile("v_mov_b32 %0, 0" : "=v"(z));
-  const double* Hz = H + z;
+  const double* Tz = T + z;
   double e = 0.0, s = 0.0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     double t = 0.0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) t = fma(Hz[16 * i + j], d[j], t);
+    for (int j = i; j < 16; ++j) t = fma(Tz[tri_row(i) + j - i], d[j], t);
     e = fma(d[i], t, e);
     s += fabs(d[i]);
   }
@@ -190,7 +197,8 @@ __global__ void __launch_bounds__(256) hessian_quant_kernel(const T* __restrict_
                                                             const float* __restrict__ tensor_scale,
                                                             uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                             uint8_t* __restrict__ choice) {
-  __shared__ double Hs[256];
+  __shared__ double Hs[256];        // H_b, for the exact comparison
+  __shared__ double Ts[kTriSize];   // upper triangle of H_b + H_b^T, for the double errors
   __shared__ float red[4];
   const int64_t e = blockIdx.z;
   const int b = blockIdx.y;
@@ -207,6 +215,9 @@ __global__ void __launch_bounds__(256) hessian_quant_kernel(const T* __restrict_
     if ((tid & 63) == 0) red[tid >> 6] = m;
     __syncthreads();
     hmax = (double)fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const int i = tid >> 4, j = tid & 15;
+    if (j >= i) Ts[tri_row(i) + j - i] = j == i ? Hs[tid] : Hs[16 * i + j] + Hs[16 * j + i];
+    __syncthreads();
   }
   const int64_t r = (int64_t)blockIdx.x * 256 + tid;
   if (r >= rows) return;
@@ -231,13 +242,13 @@ __global__ void __launch_bounds__(256) hessian_quant_kernel(const T* __restrict_
   candidate_residuals(v, (double)e4m3_to_f32(c6) * Sd, best_mags, d);
   if (c4 > c6) {
     double best_err, best_bound;
-    weighted_error(d, Hs, hmax, best_err, best_bound);
+    weighted_error(d, Ts, hmax, best_err, best_bound);
     for (uint32_t c = c6 + 1; c <= c4; ++c) {
       uint64_t mags;
       double dc[16];
       candidate_residuals(v, (double)e4m3_to_f32(c) * Sd, mags, dc);
       double err, bound;
-      weighted_error(dc, Hs, hmax, err, bound);
+      weighted_error(dc, Ts, hmax, err, bound);
       const double margin = 0x1p-46 * (bound + best_bound);
       bool take;
       if (fabs(err - best_err) > margin) {
@@ -245,10 +256,15 @@ __global__ void __launch_bounds__(256) hessian_quant_kernel(const T* __restrict_
       } else if (bound + best_bound == 0.0) {
         take = false;  // both residuals zero: equal errors, the first stays
       } else {
-        double db[16];
+        // the exact comparison takes its residuals through memory: copies
+        // made here, so that dc (written for every candidate) stays in
+        // registers instead of living in scratch for the whole loop
+        double da[16], db[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) da[i] = dc[i];
         uint64_t bm;
         candidate_residuals(v, (double)e4m3_to_f32(best) * Sd, bm, db);
-        take = exact_less(dc, db, Hs);
+        take = exact_less(da, db, Hs);
       }
       if (take) {
         best = c;

@@ -50,6 +50,10 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 constexpr int vmcnt_only(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 constexpr int vmcnt_lgkm0(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
 
-__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+// SiLU(g) = g / (1 + e^-g), as g times the hardware reciprocal (about 1 ulp)
+// of 1 + e^-g: two VALU instructions where the IEEE divide takes about ten,
+// in epilogues that evaluate it 32 times per lane.  g very negative gives
+// 1 + e^-g = inf and a signed zero, as the divide does.
+__device__ __forceinline__ float silu_f32(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 }  // namespace fp4
