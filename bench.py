@@ -1090,7 +1090,51 @@ def traffic_summary(workload, fetch_dir, write_dir, copy_fetch_dir, copy_write_d
     return lines
 
 
+def trace_summary(workload, stats_csv, bench_log, extra=""):
+    """profiles/kernels_<workload>.txt from a rocprofv3 --kernel-trace --stats
+    run of bench.py: the bench line of the same run and the library's
+    kernels by total time (torch's own kernels, which set up the inputs,
+    are left out)."""
+    import csv
+    line = None
+    with open(bench_log) as f:
+        for ln in f:
+            if ln.startswith("{"):
+                line = json.loads(ln)
+    out = [f"# rocprofv3 kernel trace of the {workload} workload (bench.py defaults for it{extra and ', ' + extra})",
+           f"# command: cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats --output-format csv -d <out> -o "
+           f"{workload} -- python3 /root/repo/bench.py --workload {workload}{extra and ' ' + extra} --no-cpu-baseline",
+           f"# table: python3 /root/repo/bench.py --trace-summary {workload} <out>/{workload}_kernel_stats.csv "
+           f"<bench stdout>{extra and ' ' + repr(extra)}"]
+    if line:
+        w = line.get("workloads", {}).get(workload, line)
+        r = w.get("roofline", {})
+        ms = w.get("ms_per_step", w.get("ms_per_layer"))
+        out.append(f"# bench line of the same run (timed under the profiler): value {w.get('value'):.6g} {w.get('unit')}, ms per "
+                   f"{'step' if 'ms_per_step' in w else 'layer'} {ms:.6g}, roofline achieved "
+                   f"{r.get('achieved', float('nan')):.6g} {r.get('unit')} (frac {r.get('frac', float('nan')):.4f})")
+        out.append(f"# stage times from HIP events in that run (ms): "
+                   f"{json.dumps({k: round(v, 4) for k, v in (w.get('stages_ms') or {}).items()})}")
+    out.append("#")
+    out.append(f"{'kernel':64s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_%':>8s}")
+    rows = []
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Name"].replace("void ", "")
+            if not name.startswith("fp4::"):
+                continue
+            rows.append((name[5:].split("(")[0], int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    for k, c, a, lo, hi, pc in sorted(rows, key=lambda x: -x[1] * x[2]):
+        out.append(f"{k[:64]:64s} {c:6d} {a:10.2f} {lo:10.2f} {hi:10.2f} {pc:8.2f}")
+    return out
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--trace-summary":
+        a = sys.argv[2:]
+        print("\n".join(trace_summary(a[0], a[1], a[2], a[3] if len(a) > 3 else "")))
+        return
     if len(sys.argv) > 1 and sys.argv[1] == "--pmc-summary":
         for row in pmc_summary(sys.argv[2:]):
             print(json.dumps(row))
