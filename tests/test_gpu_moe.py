@@ -101,6 +101,36 @@ def test_tiny_invalid_ids_flagged_and_skipped(tiny):
     assert rel_fro(y, y_ref) < 1e-5
 
 
+def test_tiny_all_ids_invalid_gives_zero(tiny):
+    """No pair valid: no expert is active, y is the combine of no rows (zero),
+    and the flag counts every pair."""
+    print_case("tiny all ids invalid")
+    cfg, w13, w2, x, ids, wts = tiny
+    bad = np.full_like(ids, cfg.num_experts)
+    y, ws, lay = _run(gpu_layer(cfg, w13, w2), x, bad, wts)
+    assert _ws_i32(ws, lay["error_flag"], 1)[0] == bad.size
+    assert np.all(y == 0.0)
+
+
+@pytest.mark.parametrize("w_fmt,a_fmt", [("nvfp4", "none"), ("mxfp4", "none"), ("mxfp4", "mxfp8")])
+def test_gemv_path_batch_invariant(tiny, w_fmt, a_fmt):
+    """The same 16 tokens alone and as the first rows of a 65-token batch give
+    bit-identical y: every stage of the GEMV path is per row (per-token MXFP8
+    blocks, per-pair dot products in a fixed lane order) and the combine adds
+    each token's slots in order, so neither the other tokens nor the grid
+    shape reach a token's output."""
+    print_case(f"GEMV path batch invariance {w_fmt} x {a_fmt}")
+    cfg, w13, w2, _, _, _ = tiny
+    c = cfg.replace(w_fmt=w_fmt, a_fmt=a_fmt, tokens=65, input_seed=31)
+    x, ids, wts = synth.activations(c), *synth.routing(c)
+    layer = gpu_layer(c, w13, w2)
+    y65, _, _ = _run(layer, x, ids, wts)
+    y16, _, _ = _run(layer, x[:16], ids[:16], wts[:16])
+    np.testing.assert_array_equal(y16.view(np.uint32), y65[:16].view(np.uint32))
+    y_ref = moe.moe_forward(OracleLayer(c, w13, w2).as_dict(), x, ids, wts)
+    assert rel_fro(y65, y_ref) <= TOL
+
+
 def test_single_expert_top1_reduces_to_dense(tiny):
     print_case("tiny E=1 k=1")
     cfg, w13, w2, x, _, _ = tiny
