@@ -30,7 +30,9 @@
 // tile of one expert (for gate_up: 64 gate and the matching 64 up rows).  The
 // permutation kernel provides each expert's first tile; workgroups are
 // remapped so that consecutive tiles (same expert) run on the same XCD and
-// share its L2.
+// share its L2.  The register-fed down projections of large batches give a
+// workgroup several consecutive output tiles of its rows: their activation
+// tile (K = inter, short) is loaded into LDS once for all of them.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -849,29 +851,31 @@ struct Mx2Cfg {
 // issues W(0..D-1) then A(0..RS-2); step j issues A(j+RS-1) after its barrier
 // and W(j+D) after its MFMAs.  The wait covers both, so the compiler never
 // adds its own (it would wait for every load in flight).
-template <int KS, int RS, int D, int OA, int OW>
+// VS >= KS: steps that load weight fragments (a workgroup looping over
+// several output tiles keeps loading weights after its KS activation stages).
+template <int KS, int RS, int D, int OA, int OW, int VS = KS>
 constexpr int mx2_ops_between_steps(int j0, int ks) {  // steps j0+1 .. ks-1
   int n = 0;
   for (int j = j0 + 1; j < ks; ++j) {
     if (j + RS - 1 < KS) n += OA;
-    if (j + D < KS) n += OW;
+    if (j + D < VS) n += OW;
   }
   return n;
 }
-template <int KS, int RS, int D, int OA, int OW>
+template <int KS, int RS, int D, int OA, int OW, int VS = KS>
 constexpr int mx2_wait_count(int ks) {
   const int last = (KS < RS - 1 ? KS : RS - 1) - 1;  // last stage of the prologue
   int na = 0, nw = 0;
   if (ks <= RS - 2) {
-    na = (last - ks) * OA + mx2_ops_between_steps<KS, RS, D, OA, OW>(-1, ks);
+    na = (last - ks) * OA + mx2_ops_between_steps<KS, RS, D, OA, OW, VS>(-1, ks);
   } else {
     const int j0 = ks - RS + 1;
-    na = (j0 + D < KS ? OW : 0) + mx2_ops_between_steps<KS, RS, D, OA, OW>(j0, ks);
+    na = (j0 + D < VS ? OW : 0) + mx2_ops_between_steps<KS, RS, D, OA, OW, VS>(j0, ks);
   }
   if (ks < D) {
-    nw = (D - 1 - ks) * OW + (last + 1) * OA + mx2_ops_between_steps<KS, RS, D, OA, OW>(-1, ks);
+    nw = (D - 1 - ks) * OW + (last + 1) * OA + mx2_ops_between_steps<KS, RS, D, OA, OW, VS>(-1, ks);
   } else {
-    nw = mx2_ops_between_steps<KS, RS, D, OA, OW>(ks - D, ks);
+    nw = mx2_ops_between_steps<KS, RS, D, OA, OW, VS>(ks - D, ks);
   }
   const int n = na < nw ? na : nw;
   return n < 63 ? n : 63;  // 63 outstanding is the counter's limit
@@ -892,12 +896,20 @@ __device__ __forceinline__ void wait_vm_lgkm0() {
   __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(N));
 }
 
-template <int GK, int EPI, int NSUB, int KS, bool WT>
+// NTW > 1 (down projection): a workgroup computes NTW consecutive output
+// tiles of its rows.  Its activation tile stays in the LDS ring (RS = KS
+// stages, loaded once); the weight fragments of the next tile load under the
+// current tile's last steps (the lead of D steps runs on across tiles); each
+// tile's o rows are stored as soon as its KS steps are done.
+template <int GK, int EPI, int NSUB, int KS, bool WT, int NTW = 1>
 __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   static_assert(GK == GK_MX || GK == GK_FP8, "MX or block-FP8 operands");
   using C = Mx2Cfg<GK, EPI, NSUB, KS>;
   constexpr int BM = C::BM, BN = C::BN, NU = C::NU, NS = C::NS, RS = C::RS, D = C::D;
   static_assert(RS <= 8, "ring of at most 8 stages");
+  static_assert(NTW == 1 || (EPI == EPI_DOWN && RS == KS), "several tiles per workgroup: down, resident activations");
+  static_assert(NTW == 1 || GK == GK_MX || BN % 128 == 0, "block-FP8 weight scales per 128 outputs");
+  constexpr int VS = KS * NTW;  // steps of the workgroup
   // one array per stage: the compiler then sees that reading a stage does
   // not alias the DMAs into the others (one array would make it wait for
   // every DMA in flight before each read)
@@ -919,7 +931,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   int* s_toff = reinterpret_cast<int*>(lds_dyn);
 
-  const int NT = g.N / BN;
+  const int NT = g.N / (BN * NTW);  // groups of NTW output tiles
   const int G = gridDim.x;
   const int per_xcd = G / 8;
   const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -927,7 +939,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   int e, mt, nt, r_begin, n_rows;
   if (g.dense_rows > 0) {
     e = 0;
-    nt = L % NT;
+    nt = (L % NT) * NTW;
     mt = L / NT;
     if (mt * BM >= g.dense_rows) return;
     r_begin = 0;
@@ -935,7 +947,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   } else {
     for (int i = threadIdx.x; i <= g.E; i += 256) s_toff[i] = g.tile_offsets[i];
     __syncthreads();
-    nt = L % NT;
+    nt = (L % NT) * NTW;
     const int mg = L / NT;
     if (mg >= s_toff[g.E]) return;
     int lo = 0, hi = g.E;
@@ -1010,12 +1022,20 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   };
   u32x4 wq[D][NS][C::W_LD];
   int wsq[D][NS];
-  auto load_w = [&](int ks, u32x4 (&q)[NS][C::W_LD], int (&sc)[NS]) __attribute__((always_inline)) {
+  // step v = (tile v / KS of the workgroup, K step v % KS); the next output
+  // tile is BN weight rows further: whole 16-row groups when tiled, whole
+  // 128 x 128 scale blocks for block FP8 (BN % 128 == 0)
+  constexpr int64_t W_NT = WT ? (int64_t)(BN / 16) * KS * PH * 1024 : (int64_t)BN * W_ROW;
+  constexpr int64_t WS_NT = GK == GK_MX ? (WT ? (int64_t)(BN / 16) * KS * 64 : (int64_t)BN * SKB)
+                                        : (int64_t)(BN / 128) * KS * 4;
+  auto load_w = [&](int v, u32x4 (&q)[NS][C::W_LD], int (&sc)[NS]) __attribute__((always_inline)) {
+    const int nv = v / KS, ks = v % KS;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      q[s][0] = ld16(w_src[s] + W_STEP * ks);
-      if constexpr (GK == GK_FP8) q[s][C::W_LD - 1] = ld16(w_src[s] + W_STEP * ks + W_HALF);
-      sc[s] = (int)*reinterpret_cast<const uint32_t*>(ws_src[s] + WS_STEP * ks);  // MX: byte lg is this lane's
+      const uint8_t* wp = w_src[s] + W_NT * nv + W_STEP * ks;
+      q[s][0] = ld16(wp);
+      if constexpr (GK == GK_FP8) q[s][C::W_LD - 1] = ld16(wp + W_HALF);
+      sc[s] = (int)*reinterpret_cast<const uint32_t*>(ws_src[s] + WS_NT * nv + WS_STEP * ks);  // MX: byte lg is this lane's
     }
   };
 
@@ -1034,16 +1054,51 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   });
   __builtin_amdgcn_sched_barrier(0);
 
-  static_for<KS>([&](auto kc) __attribute__((always_inline)) {
-    constexpr int ks = decltype(kc)::value;
-    // own DMAs of stage ks done (later ones may stay in flight); own LDS
-    // reads of the previous step done; then everyone's
-    wait_vm_lgkm0<mx2_wait_count<KS, RS, D, C::OPS_A, C::OPS_W>(ks)>();
-    asm volatile("s_barrier" ::: "memory");
-    if constexpr (ks + RS - 1 < KS) dma_a(ks + RS - 1, stage(std::integral_constant<int, (ks + RS - 1) % RS>{}));
+  // epilogue of one output tile (its index arithmetic starts from an opaque
+  // zero so that none of it is hoisted into the unrolled K loop, where it
+  // would hold registers through every step)
+  auto store_tile = [&](int ntile) __attribute__((always_inline)) {
+    int z0;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NSUB; ++j) {
+        const int n = ntile * BN + wave * 16 * NSUB + j * 16 + lr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = mt * BM + 16 * i + 4 * lg + r + z0;
+          if (rr >= n_rows) continue;
+          const int64_t R = r_begin + rr;
+          float v;
+          if (EPI == EPI_GATEUP) {
+            v = silu_f32(acc[i][j][r]) * acc[i][NSUB + j][r];
+          } else {
+            v = acc[i][j][r];
+            if (g.row_scale) v *= g.row_scale[R];
+          }
+          g.out[R * g.N + n] = v;
+        }
+      }
+  };
+
+  static_for<VS>([&](auto vc) __attribute__((always_inline)) {
+    constexpr int v = decltype(vc)::value, ks = v % KS;
+    if constexpr (v < KS) {
+      // own DMAs of stage ks done (later ones may stay in flight); own LDS
+      // reads of the previous step done; then everyone's.  Later tiles read
+      // the same stages, which no DMA overwrites.
+      wait_vm_lgkm0<mx2_wait_count<KS, RS, D, C::OPS_A, C::OPS_W, VS>(ks)>();
+      asm volatile("s_barrier" ::: "memory");
+      if constexpr (ks + RS - 1 < KS) dma_a(ks + RS - 1, stage(std::integral_constant<int, (ks + RS - 1) % RS>{}));
+    }
     __builtin_amdgcn_sched_barrier(0);
     {
-      const uint8_t* s_a = stage(std::integral_constant<int, ks % RS>{});
+      // with several tiles, an opaque zero keeps the compiler from holding
+      // every stage's fragments in registers from one tile to the next
+      int zo = 0;
+      if constexpr (NTW > 1) asm volatile("s_mov_b32 %0, 0" : "=s"(zo));
+      const uint8_t* s_a = stage(std::integral_constant<int, ks % RS>{}) + zo;
       const uint8_t* s_as = s_a + C::A_BYTES;
       intx8 af[4];
       int asc[4];
@@ -1064,18 +1119,18 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         if constexpr (GK == GK_MX) {
-          const u32x4 c = wq[ks % D][s][0];
+          const u32x4 c = wq[v % D][s][0];
           const intx8 bv = intx8{(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
-          const int bsc = (int)(((uint32_t)wsq[ks % D][s] >> (8 * lg)) & 0xFFu);
+          const int bsc = (int)(((uint32_t)wsq[v % D][s] >> (8 * lg)) & 0xFFu);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             acc[i][s] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bv, acc[i][s], 0, 4, 0, asc[i], 0, bsc);
         } else {
           // unit-scale E4M3 products of the 128-block, then the block's
           // activation-row and weight scales in f32
-          const u32x4 lo = wq[ks % D][s][0], hi = wq[ks % D][s][C::W_LD - 1];
+          const u32x4 lo = wq[v % D][s][0], hi = wq[v % D][s][C::W_LD - 1];
           const intx8 bv = intx8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-          const float ws = __uint_as_float((uint32_t)wsq[ks % D][s]);
+          const float ws = __uint_as_float((uint32_t)wsq[v % D][s]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const floatx4 pp = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
@@ -1093,40 +1148,27 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(acc[i][s]));
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ks + D < KS) load_w(ks + D, wq[ks % D], wsq[ks % D]);
+    if constexpr (v + D < VS) load_w(v + D, wq[v % D], wsq[v % D]);
+    if constexpr (NTW > 1 && ks == KS - 1) {
+      store_tile(nt + v / KS);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[i][s] = floatx4{0.f, 0.f, 0.f, 0.f};
+      __builtin_amdgcn_sched_barrier(0);
+    }
   });
+  if constexpr (NTW > 1) return;
 
-  // ---- epilogue (its index arithmetic starts from an opaque zero so that
-  // none of it is hoisted into the unrolled K loop, where it would hold
-  // registers through every step)
-  int z0;
-  asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
   if constexpr (GK == GK_MX && EPI == EPI_GATEUP && NSUB == 2) {
     if (g.q_codes) {
+      int z0;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
       store_h_mxfp8(g, acc, (nt * BN) / 32 + wave, mt * BM + z0, n_rows, r_begin, lg, lr);
       return;
     }
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < NSUB; ++j) {
-      const int n = nt * BN + wave * 16 * NSUB + j * 16 + lr;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int rr = mt * BM + 16 * i + 4 * lg + r + z0;
-        if (rr >= n_rows) continue;
-        const int64_t R = r_begin + rr;
-        float v;
-        if (EPI == EPI_GATEUP) {
-          v = silu_f32(acc[i][j][r]) * acc[i][NSUB + j][r];
-        } else {
-          v = acc[i][j][r];
-          if (g.row_scale) v *= g.row_scale[R];
-        }
-        g.out[R * g.N + n] = v;
-      }
-    }
+  store_tile(nt);
 }
 
 // NVFP4 x NVFP4 on the same plan: each wave's weight fragments (E2M1 codes
@@ -1154,40 +1196,49 @@ struct Nv2Cfg {
 // a step's weight loads) and the wait at the top of step ks.  Prologue:
 // W(0..D-1), raw(0..RS-2); step j: raw(j+RS-1) after the barrier, W(j+D)
 // after the MFMAs.
-template <int KS, int RS, int D, int OA, int OW>
+// VS >= KS: steps that load weight fragments (several output tiles per
+// workgroup); raw stages are loaded during the first KS steps only.
+template <int KS, int RS, int D, int OA, int OW, int VS = KS>
 constexpr int nv2_ops_steps(int j0, int ks) {  // ops of steps j0+1 .. ks-1
   int n = 0;
   for (int j = j0 + 1; j < ks; ++j) {
     if (j + RS - 1 < KS) n += OA;
-    if (j + D < KS) n += OW;
+    if (j + D < VS) n += OW;
   }
   return n;
 }
-template <int KS, int RS, int D, int OA, int OW>
+template <int KS, int RS, int D, int OA, int OW, int VS = KS>
 constexpr int nv2_after_raw(int s, int ks) {  // raw stage s, wait of step ks
   const int last = (KS < RS - 1 ? KS : RS - 1) - 1;
-  if (s <= RS - 2) return (last - s) * OA + nv2_ops_steps<KS, RS, D, OA, OW>(-1, ks);
+  if (s <= RS - 2) return (last - s) * OA + nv2_ops_steps<KS, RS, D, OA, OW, VS>(-1, ks);
   const int j0 = s - RS + 1;
-  return (j0 + D < KS ? OW : 0) + nv2_ops_steps<KS, RS, D, OA, OW>(j0, ks);
+  return (j0 + D < VS ? OW : 0) + nv2_ops_steps<KS, RS, D, OA, OW, VS>(j0, ks);
 }
-template <int KS, int RS, int D, int OA, int OW>
+template <int KS, int RS, int D, int OA, int OW, int VS = KS>
 constexpr int nv2_wait_count(int ks) {  // raw(ks+1) and W(ks) done
   const int last = (KS < RS - 1 ? KS : RS - 1) - 1;
-  const int nw = ks < D ? (D - 1 - ks) * OW + (last + 1) * OA + nv2_ops_steps<KS, RS, D, OA, OW>(-1, ks)
-                        : nv2_ops_steps<KS, RS, D, OA, OW>(ks - D, ks);
+  const int nw = ks < D ? (D - 1 - ks) * OW + (last + 1) * OA + nv2_ops_steps<KS, RS, D, OA, OW, VS>(-1, ks)
+                        : nv2_ops_steps<KS, RS, D, OA, OW, VS>(ks - D, ks);
   int n = nw;
   if (ks + 1 < KS) {
-    const int na = nv2_after_raw<KS, RS, D, OA, OW>(ks + 1, ks);
+    const int na = nv2_after_raw<KS, RS, D, OA, OW, VS>(ks + 1, ks);
     n = na < n ? na : n;
   }
   return n < 63 ? n : 63;
 }
 
-template <int EPI, int NSUB, int KS, bool WT>
+// NTW > 1 (down projection): a workgroup computes NTW consecutive output
+// tiles of its rows.  The raw activation stages stay in LDS (RS = KS, loaded
+// once) and every tile decodes them again, one step ahead as in the first;
+// the weight lead of D steps runs on across tiles; each tile's o rows are
+// stored as soon as its KS steps are done.
+template <int EPI, int NSUB, int KS, bool WT, int NTW = 1>
 __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
   using C = Nv2Cfg<EPI, NSUB, KS>;
   constexpr int BM = C::BM, BN = C::BN, NU = C::NU, NS = C::NS, RS = C::RS, D = C::D;
   static_assert(RS <= 6, "ring of at most 6 raw stages");
+  static_assert(NTW == 1 || (EPI == EPI_DOWN && RS == KS), "several tiles per workgroup: down, resident activations");
+  constexpr int VS = KS * NTW;  // steps of the workgroup
   __shared__ __attribute__((aligned(16))) uint8_t q0[C::RAW], q1[RS > 1 ? C::RAW : 16], q2[RS > 2 ? C::RAW : 16],
       q3[RS > 3 ? C::RAW : 16], q4[RS > 4 ? C::RAW : 16], q5[RS > 5 ? C::RAW : 16];
   __shared__ __attribute__((aligned(16))) uint8_t d0[C::DEC], d1[C::DEC];
@@ -1208,14 +1259,14 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   int* s_toff = reinterpret_cast<int*>(lds_dyn);
 
-  const int NT = g.N / BN;
+  const int NT = g.N / (BN * NTW);  // groups of NTW output tiles
   const int G = gridDim.x;
   const int per_xcd = G / 8;
   const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   int e, mt, nt, r_begin, n_rows;
   if (g.dense_rows > 0) {
     e = 0;
-    nt = L % NT;
+    nt = (L % NT) * NTW;
     mt = L / NT;
     if (mt * BM >= g.dense_rows) return;
     r_begin = 0;
@@ -1223,7 +1274,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
   } else {
     for (int i = threadIdx.x; i <= g.E; i += 256) s_toff[i] = g.tile_offsets[i];
     __syncthreads();
-    nt = L % NT;
+    nt = (L % NT) * NTW;
     const int mg = L / NT;
     if (mg >= s_toff[g.E]) {
       if (EPI == EPI_GATEUP && g.amax_part && threadIdx.x == 0) g.amax_part[L] = 0.0f;
@@ -1296,11 +1347,16 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
   }
   u32x4 wq[D][NS];
   u32x2 wsq[D][NS];
-  auto load_w = [&](int ks, u32x4 (&q)[NS], u32x2 (&sc)[NS]) __attribute__((always_inline)) {
+  // step v = (tile v / KS of the workgroup, K step v % KS); the next output
+  // tile is BN weight rows further (whole 16-row groups when tiled)
+  constexpr int64_t W_NT = WT ? (int64_t)(BN / 16) * KS * 1024 : (int64_t)BN * (K / 2);
+  constexpr int64_t WS_NT = WT ? (int64_t)(BN / 16) * KS * 128 : (int64_t)BN * (K / 16);
+  auto load_w = [&](int v, u32x4 (&q)[NS], u32x2 (&sc)[NS]) __attribute__((always_inline)) {
+    const int nv = v / KS, ks = v % KS;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      q[s] = ld16(w_src[s] + W_STEP * ks);
-      sc[s] = *reinterpret_cast<const u32x2*>(ws_src[s] + WS_STEP * ks);  // the row's 8 scales of the step
+      q[s] = ld16(w_src[s] + W_NT * nv + W_STEP * ks);
+      sc[s] = *reinterpret_cast<const u32x2*>(ws_src[s] + WS_NT * nv + WS_STEP * ks);  // the row's 8 scales of the step
     }
   };
 
@@ -1323,17 +1379,45 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
   decode_raw(raw(std::integral_constant<int, 0>{}), dec(std::integral_constant<int, 0>{}));
   __builtin_amdgcn_sched_barrier(0);
 
-  static_for<KS>([&](auto kc) __attribute__((always_inline)) {
-    constexpr int ks = decltype(kc)::value;
-    wait_vm_lgkm0<nv2_wait_count<KS, RS, D, C::OPS_A, C::OPS_W>(ks)>();
+  // epilogue of one down tile (index arithmetic from an opaque zero: not
+  // hoisted into the K loop)
+  auto store_down_tile = [&](int ntile) __attribute__((always_inline)) {
+    int z0;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+    const float scale = g.a_tensor_scale[0] * g.w_tensor_scale[e];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < NSUB; ++j) {
+        const int n = ntile * BN + wave * 16 * NSUB + j * 16 + lr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int rr = mt * BM + 16 * i + 4 * lg + r + z0;
+          if (rr >= n_rows) continue;
+          const int64_t R = r_begin + rr;
+          float v = acc[i][j][r] * scale;
+          if (g.row_scale) v *= g.row_scale[R];
+          g.out[R * g.N + n] = v;
+        }
+      }
+  };
+
+  static_for<VS>([&](auto vc) __attribute__((always_inline)) {
+    constexpr int v = decltype(vc)::value, ks = v % KS;
+    if constexpr (v < KS) {
+      wait_vm_lgkm0<nv2_wait_count<KS, RS, D, C::OPS_A, C::OPS_W, VS>(ks)>();
+    } else {
+      wait_vm_lgkm0<63>();  // this thread's decode of the step done (the raw stages all arrived in the first tile)
+    }
     asm volatile("s_barrier" ::: "memory");
-    if constexpr (ks + RS - 1 < KS) dma_raw(ks + RS - 1, raw(std::integral_constant<int, (ks + RS - 1) % RS>{}));
+    if constexpr (ks + RS - 1 < KS && v < KS)
+      dma_raw(ks + RS - 1, raw(std::integral_constant<int, (ks + RS - 1) % RS>{}));
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ks + 1 < KS)
-      decode_raw(raw(std::integral_constant<int, (ks + 1) % RS>{}), dec(std::integral_constant<int, (ks + 1) % 2>{}));
+    if constexpr (v + 1 < VS)
+      decode_raw(raw(std::integral_constant<int, (v + 1) % KS % RS>{}), dec(std::integral_constant<int, (v + 1) % 2>{}));
     __builtin_amdgcn_sched_barrier(0);
     {
-      const uint8_t* s_a = dec(std::integral_constant<int, ks % 2>{});
+      const uint8_t* s_a = dec(std::integral_constant<int, v % 2>{});
       uint32_t af[4][16];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -1344,8 +1428,8 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
         }
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        const u32x4 c = wq[ks % D][s];
-        const u32x2 sc = wsq[ks % D][s];
+        const u32x4 c = wq[v % D][s];
+        const u32x2 sc = wsq[v % D][s];
         const uint32_t s2 = ((lg < 2 ? sc.x : sc.y) >> (16 * (lg & 1))) & 0xFFFFu;
         uint32_t wd[16];
         nv_decode32(make_uint4(c.x, c.y, c.z, c.w), s2, wd);
@@ -1362,8 +1446,17 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
 #pragma unroll
       for (int s = 0; s < NS; ++s) asm volatile("" ::"v"(acc[i][s]));
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ks + D < KS) load_w(ks + D, wq[ks % D], wsq[ks % D]);
+    if constexpr (v + D < VS) load_w(v + D, wq[v % D], wsq[v % D]);
+    if constexpr (NTW > 1 && ks == KS - 1) {
+      store_down_tile(nt + v / KS);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[i][s] = floatx4{0.f, 0.f, 0.f, 0.f};
+      __builtin_amdgcn_sched_barrier(0);
+    }
   });
+  if constexpr (NTW > 1) return;
 
   // ---- epilogue (index arithmetic from an opaque zero: not hoisted into the K loop)
   int z0;
@@ -1403,6 +1496,20 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
   }
 }
 
+// Output tiles per workgroup of the register-fed down GEMMs (nt tiles of
+// output per row block, tiles_m_bound row blocks): 4, else 2, as long as the
+// grid keeps 16 workgroups per CU, else 1.  At 8192 tokens x top-10 (1,792
+// row blocks, 20 output tiles) 4 measured 345 / 351 / 461 us for the NVFP4 /
+// MX / block-FP8 down GEMMs against 404 / 421 / 520 us with one tile (10:
+// 355 / 361 / 467); a 16-token batch (163 row blocks) keeps one tile, whose
+// grid is then 12.7 workgroups per CU.
+static int down_tiles_per_wg(int64_t tiles_m_bound, int nt) {
+  const int64_t want = 16LL * device_cu_count();
+  if (nt % 4 == 0 && tiles_m_bound * (nt / 4) >= want) return 4;
+  if (nt % 2 == 0 && tiles_m_bound * (nt / 2) >= want) return 2;
+  return 1;
+}
+
 // Workgroups of a grouped GEMM launch: M-tile bound x output tiles, rounded
 // up to a multiple of the 8 XCDs (the tile remapping needs whole rounds).
 static int64_t gemm_grid(int64_t tiles_m_bound, int N, int BN) {
@@ -1424,10 +1531,11 @@ static int raise_dyn_lds(const void* kernel, int bytes, std::atomic<uint64_t>& r
   return FP4_OK;
 }
 
-template <int EPI, int NSUB, int KS, bool WT>
+template <int EPI, int NSUB, int KS, bool WT, int NTW = 1>
 static int launch_gemm_nv2_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   using C = Nv2Cfg<EPI, NSUB, KS>;
-  const int64_t G = gemm_grid(tiles_m_bound, a.N, C::BN);
+  if (a.N % (C::BN * NTW)) return fail(FP4_ERR_SHAPE, "grouped GEMM: %d outputs are not whole groups of tiles", a.N);
+  const int64_t G = gemm_grid(tiles_m_bound, a.N, C::BN * NTW);
   if (a.amax_part && G != a.amax_nparts)
     return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM: %lld partial maxima expected, %lld workgroups",
                 (long long)a.amax_nparts, (long long)G);
@@ -1439,16 +1547,24 @@ static int launch_gemm_nv2_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream
   constexpr size_t fixed = (size_t)C::RS * C::RAW + 2 * (size_t)C::DEC + 512 + 64;
   if (fixed + lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
   static std::atomic<uint64_t> lds_raised{0};
-  FP4_CHECK(raise_dyn_lds(reinterpret_cast<const void*>(&grouped_gemm_nv2_kernel<EPI, NSUB, KS, WT>),
+  FP4_CHECK(raise_dyn_lds(reinterpret_cast<const void*>(&grouped_gemm_nv2_kernel<EPI, NSUB, KS, WT, NTW>),
                             (int)(160 * 1024 - fixed), lds_raised));
-  hipLaunchKernelGGL((grouped_gemm_nv2_kernel<EPI, NSUB, KS, WT>), dim3((unsigned)G), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((grouped_gemm_nv2_kernel<EPI, NSUB, KS, WT, NTW>), dim3((unsigned)G), dim3(256), lds, st, a);
   return check_launch("grouped_gemm_nv2");
 }
 
-template <int EPI, int NSUB, int KS>
+template <int EPI, int NSUB, int KS, int NTW = 1>
 static int launch_gemm_nv2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
-  return a.w_tiled ? launch_gemm_nv2_t<EPI, NSUB, KS, true>(a, tiles_m_bound, st)
-                   : launch_gemm_nv2_t<EPI, NSUB, KS, false>(a, tiles_m_bound, st);
+  return a.w_tiled ? launch_gemm_nv2_t<EPI, NSUB, KS, true, NTW>(a, tiles_m_bound, st)
+                   : launch_gemm_nv2_t<EPI, NSUB, KS, false, NTW>(a, tiles_m_bound, st);
+}
+template <int EPI, int NSUB, int KS>
+static int launch_gemm_nv2_down(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+  switch (down_tiles_per_wg(tiles_m_bound, a.N / (64 * NSUB))) {
+    case 4: return launch_gemm_nv2<EPI, NSUB, KS, 4>(a, tiles_m_bound, st);
+    case 2: return launch_gemm_nv2<EPI, NSUB, KS, 2>(a, tiles_m_bound, st);
+    default: return launch_gemm_nv2<EPI, NSUB, KS>(a, tiles_m_bound, st);
+  }
 }
 
 // Tiled order of moe_fp4_tile_weights.  The E stacked [rows, cols] tensors
@@ -1544,10 +1660,11 @@ static int launch_gemm_n(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t s
   return launch_gemm_n_t<GK, EPI, NSUB, WFP8, false>(a, tiles_m_bound, st);
 }
 
-template <int GK, int EPI, int NSUB, int KS, bool WT>
+template <int GK, int EPI, int NSUB, int KS, bool WT, int NTW = 1>
 static int launch_gemm_mx2_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
   using C = Mx2Cfg<GK, EPI, NSUB, KS>;
-  const int NT = a.N / C::BN;
+  if (a.N % (C::BN * NTW)) return fail(FP4_ERR_SHAPE, "grouped GEMM: %d outputs are not whole groups of tiles", a.N);
+  const int NT = a.N / (C::BN * NTW);
   int64_t G = tiles_m_bound * NT;
   G = (G + 7) / 8 * 8;
   if (G <= 0) return FP4_OK;
@@ -1556,16 +1673,25 @@ static int launch_gemm_mx2_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream
   constexpr size_t fixed = (size_t)C::RS * C::STAGE + 1024;
   if (fixed + lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
   static std::atomic<uint64_t> lds_raised{0};
-  FP4_CHECK(raise_dyn_lds(reinterpret_cast<const void*>(&grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS, WT>),
+  FP4_CHECK(raise_dyn_lds(reinterpret_cast<const void*>(&grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS, WT, NTW>),
                             (int)(160 * 1024 - fixed), lds_raised));
-  hipLaunchKernelGGL((grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS, WT>), dim3((unsigned)G), dim3(256), lds, st, a);
+  hipLaunchKernelGGL((grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS, WT, NTW>), dim3((unsigned)G), dim3(256), lds, st, a);
   return check_launch("grouped_gemm_mx2");
 }
 
-template <int GK, int EPI, int NSUB, int KS>
+template <int GK, int EPI, int NSUB, int KS, int NTW = 1>
 static int launch_gemm_mx2(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
-  return a.w_tiled ? launch_gemm_mx2_t<GK, EPI, NSUB, KS, true>(a, tiles_m_bound, st)
-                   : launch_gemm_mx2_t<GK, EPI, NSUB, KS, false>(a, tiles_m_bound, st);
+  return a.w_tiled ? launch_gemm_mx2_t<GK, EPI, NSUB, KS, true, NTW>(a, tiles_m_bound, st)
+                   : launch_gemm_mx2_t<GK, EPI, NSUB, KS, false, NTW>(a, tiles_m_bound, st);
+}
+
+template <int GK, int EPI, int NSUB, int KS>
+static int launch_gemm_mx2_down(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st) {
+  switch (down_tiles_per_wg(tiles_m_bound, a.N / (64 * NSUB))) {
+    case 4: return launch_gemm_mx2<GK, EPI, NSUB, KS, 4>(a, tiles_m_bound, st);
+    case 2: return launch_gemm_mx2<GK, EPI, NSUB, KS, 2>(a, tiles_m_bound, st);
+    default: return launch_gemm_mx2<GK, EPI, NSUB, KS>(a, tiles_m_bound, st);
+  }
 }
 
 template <int EPI, int NSUB, bool WT>
@@ -1606,7 +1732,7 @@ static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st)
     // down over the model's inter 640 on the register-fed kernel (measured
     // faster there; over K = 2560 the register-staged kernel is faster)
     if constexpr (EPI == EPI_DOWN) {
-      if (a.N % 128 == 0 && a.K == 640) return launch_gemm_nv2<EPI, 2, 5>(a, tiles_m_bound, st);
+      if (a.N % 128 == 0 && a.K == 640) return launch_gemm_nv2_down<EPI, 2, 5>(a, tiles_m_bound, st);
     } else {
       // gate_up over the model's hidden of 2560 on tiled weights: the
       // register-fed kernel (on row-major weights the register-staged one)
@@ -1618,7 +1744,7 @@ static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st)
     // the model's reduction sizes on the register-fed kernel (gate_up with
     // 64-output tiles: 128-output ones spill)
     if constexpr (EPI == EPI_DOWN) {
-      if (mx_down_on_mx2(a.N, a.K)) return launch_gemm_mx2<GK_FP8, EPI, 2, 5>(a, tiles_m_bound, st);
+      if (mx_down_on_mx2(a.N, a.K)) return launch_gemm_mx2_down<GK_FP8, EPI, 2, 5>(a, tiles_m_bound, st);
     } else {
       // 128-output tiles on tiled weights when they still give every CU 16
       // workgroups (8192 tokens: 686 against 750 us); decode batches, whose
@@ -1640,7 +1766,7 @@ static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st)
   // its K loop unrolled (measured faster than either staging kernel there;
   // over K = 2560 the all-DMA kernel is faster)
   if constexpr (EPI == EPI_DOWN) {
-    if (mx_down_on_mx2(a.N, a.K)) return launch_gemm_mx2<GK_MX, EPI, 2, 5>(a, tiles_m_bound, st);
+    if (mx_down_on_mx2(a.N, a.K)) return launch_gemm_mx2_down<GK_MX, EPI, 2, 5>(a, tiles_m_bound, st);
   }
   if constexpr (EPI == EPI_GATEUP) {
     if (a.w_tiled && mx_gateup_on_mx2(a.N, a.K)) return launch_gemm_mx2<GK_MX, EPI, 2, 20>(a, tiles_m_bound, st);
