@@ -98,15 +98,29 @@ struct GemmArgs {
   // scales [rows][N/32]) and `out` is not written
   uint8_t* q_codes;
   uint8_t* q_scales;
-  // NVFP4 gate_up on the register-staged kernel only: when set, workgroup L
-  // of the amax_nparts launched writes max |h| over the h values it stores to
-  // amax_part[L] (0 if it has no tile), for the tensor scale of h
+  // NVFP4 gate_up: when set, workgroup i of the amax_nparts launched writes
+  // max |h| over the h values it stores to amax_part[i] (0 if it has no
+  // tile), for the tensor scale of h
   float* amax_part;
   int64_t amax_nparts;
   // MX gate_up (grouped_gemm_mx_kernel): w_codes / w_scales are in the tiled
   // order of moe_fp4_tile_weights
   int w_tiled;
 };
+
+// Tile of this workgroup among n_tiles real (row block, output group) tiles.
+// Workgroups are dispatched to the 8 XCDs in turn (workgroup i to XCD i % 8);
+// XCD x takes the contiguous range [x per, (x + 1) per), per = ceil(n_tiles /
+// 8), so an expert's consecutive tiles share that XCD's L2, and the
+// workgroups beyond the real tiles (the grid is sized by a bound on the tile
+// count) are spread over all XCDs instead of leaving the last ones idle.
+// -1: no tile.
+__device__ __forceinline__ int xcd_tile(int n_tiles) {
+  const int per = (n_tiles + 7) / 8;
+  const int k = blockIdx.x / 8;
+  const int L = (blockIdx.x % 8) * per + k;
+  return k < per && L < n_tiles ? L : -1;
+}
 
 // ---------------------------------------------------------------- operands
 
@@ -178,27 +192,26 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
   int* s_toff = reinterpret_cast<int*>(lds + 2 * stage);
 
   const int NT = g.N / BN;
-  const int G = gridDim.x;
-  const int per_xcd = G / 8;
-  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 
-  int e, mt, nt, r_begin, n_rows;
+  int L, e, mt, nt, r_begin, n_rows;
   if (g.dense_rows > 0) {
     e = 0;
+    L = xcd_tile((g.dense_rows + BM - 1) / BM * NT);
+    if (L < 0) return;
     nt = L % NT;
     mt = L / NT;
-    if (mt * BM >= g.dense_rows) return;
     r_begin = 0;
     n_rows = g.dense_rows;
   } else {
     for (int i = threadIdx.x; i <= g.E; i += 256) s_toff[i] = g.tile_offsets[i];
     __syncthreads();
-    nt = L % NT;
-    const int mg = L / NT;
-    if (mg >= s_toff[g.E]) {
-      if (GK == GK_NV && EPI == EPI_GATEUP && g.amax_part && threadIdx.x == 0) g.amax_part[L] = 0.0f;
+    L = xcd_tile(s_toff[g.E] * NT);
+    if (L < 0) {
+      if (GK == GK_NV && EPI == EPI_GATEUP && g.amax_part && threadIdx.x == 0) g.amax_part[blockIdx.x] = 0.0f;
       return;
     }
+    nt = L % NT;
+    const int mg = L / NT;
     int lo = 0, hi = g.E;
     while (hi - lo > 1) {
       int mid = (lo + hi) >> 1;
@@ -523,7 +536,7 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
       for (int off = 32; off > 0; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
       if (lane == 0) red[wave] = vmax;
       __syncthreads();
-      if (tid == 0) g.amax_part[L] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      if (tid == 0) g.amax_part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     }
   }
 }
@@ -620,24 +633,23 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx_kernel(GemmArgs g) {
   int* s_toff = reinterpret_cast<int*>(lds_dyn);
 
   const int NT = g.N / BN;
-  const int G = gridDim.x;
-  const int per_xcd = G / 8;
-  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 
-  int e, mt, nt, r_begin, n_rows;
+  int L, e, mt, nt, r_begin, n_rows;
   if (g.dense_rows > 0) {
     e = 0;
+    L = xcd_tile((g.dense_rows + BM - 1) / BM * NT);
+    if (L < 0) return;
     nt = L % NT;
     mt = L / NT;
-    if (mt * BM >= g.dense_rows) return;
     r_begin = 0;
     n_rows = g.dense_rows;
   } else {
     for (int i = threadIdx.x; i <= g.E; i += 256) s_toff[i] = g.tile_offsets[i];
     __syncthreads();
+    L = xcd_tile(s_toff[g.E] * NT);
+    if (L < 0) return;
     nt = L % NT;
     const int mg = L / NT;
-    if (mg >= s_toff[g.E]) return;
     int lo = 0, hi = g.E;
     while (hi - lo > 1) {
       int mid = (lo + hi) >> 1;
@@ -932,24 +944,23 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   int* s_toff = reinterpret_cast<int*>(lds_dyn);
 
   const int NT = g.N / (BN * NTW);  // groups of NTW output tiles
-  const int G = gridDim.x;
-  const int per_xcd = G / 8;
-  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
 
-  int e, mt, nt, r_begin, n_rows;
+  int L, e, mt, nt, r_begin, n_rows;
   if (g.dense_rows > 0) {
     e = 0;
+    L = xcd_tile((g.dense_rows + BM - 1) / BM * NT);
+    if (L < 0) return;
     nt = (L % NT) * NTW;
     mt = L / NT;
-    if (mt * BM >= g.dense_rows) return;
     r_begin = 0;
     n_rows = g.dense_rows;
   } else {
     for (int i = threadIdx.x; i <= g.E; i += 256) s_toff[i] = g.tile_offsets[i];
     __syncthreads();
+    L = xcd_tile(s_toff[g.E] * NT);
+    if (L < 0) return;
     nt = (L % NT) * NTW;
     const int mg = L / NT;
-    if (mg >= s_toff[g.E]) return;
     int lo = 0, hi = g.E;
     while (hi - lo > 1) {
       int mid = (lo + hi) >> 1;
@@ -1260,26 +1271,25 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
   int* s_toff = reinterpret_cast<int*>(lds_dyn);
 
   const int NT = g.N / (BN * NTW);  // groups of NTW output tiles
-  const int G = gridDim.x;
-  const int per_xcd = G / 8;
-  const int L = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  int e, mt, nt, r_begin, n_rows;
+  int L, e, mt, nt, r_begin, n_rows;
   if (g.dense_rows > 0) {
     e = 0;
+    L = xcd_tile((g.dense_rows + BM - 1) / BM * NT);
+    if (L < 0) return;
     nt = (L % NT) * NTW;
     mt = L / NT;
-    if (mt * BM >= g.dense_rows) return;
     r_begin = 0;
     n_rows = g.dense_rows;
   } else {
     for (int i = threadIdx.x; i <= g.E; i += 256) s_toff[i] = g.tile_offsets[i];
     __syncthreads();
-    nt = (L % NT) * NTW;
-    const int mg = L / NT;
-    if (mg >= s_toff[g.E]) {
-      if (EPI == EPI_GATEUP && g.amax_part && threadIdx.x == 0) g.amax_part[L] = 0.0f;
+    L = xcd_tile(s_toff[g.E] * NT);
+    if (L < 0) {
+      if (EPI == EPI_GATEUP && g.amax_part && threadIdx.x == 0) g.amax_part[blockIdx.x] = 0.0f;
       return;
     }
+    nt = (L % NT) * NTW;
+    const int mg = L / NT;
     int lo = 0, hi = g.E;
     while (hi - lo > 1) {
       int mid = (lo + hi) >> 1;
@@ -1491,7 +1501,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
       for (int off = 32; off > 0; off >>= 1) vmax = fmaxf(vmax, __shfl_xor(vmax, off));
       if (lane == 0) red[wave] = vmax;
       __syncthreads();
-      if (tid == 0) g.amax_part[L] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      if (tid == 0) g.amax_part[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     }
   }
 }
