@@ -386,8 +386,10 @@ def bench_prefill(name, args, torch, pkg):
     peak_key = "bf16" if cfg.a_fmt == "nvfp4" else "fp8"
     peak = MFMA_PEAK_TFLOPS[peak_key]
     gu_ms = stages["gate_up"]
-    gk = {"nvfp4": "grouped_gemm_nv2_kernel<0, 2, 20, WT>", "mxfp4": "grouped_gemm_mx2_kernel<1, 0, 2, 20, WT>",
-          "fp8_block": "grouped_gemm_mx2_kernel<2, 0, 2, 20, WT>"}[cfg.w_fmt].replace("WT", str(tiled).lower())
+    # the gate_up kernel as the kernel trace names it (last parameter: output
+    # tiles per workgroup, 1 for gate_up)
+    gk = {"nvfp4": "grouped_gemm_nv2_kernel<0, 2, 20, WT, 1>", "mxfp4": "grouped_gemm_mx2_kernel<1, 0, 2, 20, WT, 1>",
+          "fp8_block": "grouped_gemm_mx2_kernel<2, 0, 2, 20, WT, 1>"}[cfg.w_fmt].replace("WT", str(tiled).lower())
     roof = {"bound": "mfma", "kernel": gk + " (gate_up)", "mfma_dtype":
             {"bf16": "fp16 (exact NVFP4 decode)", "fp8": "fp8 x fp4" if cfg.w_fmt == "mxfp4" else "fp8"}[peak_key],
             "achieved": flops_gu / (gu_ms * 1e-3) / 1e12, "peak": peak, "unit": "TFLOP/s",
