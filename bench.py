@@ -274,7 +274,23 @@ def bench_decode(args, torch, pkg):
         pkg.moe_forward(layers[i % len(layers)], x, tid, tw, ws, y)
     stop.record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    eager_ms = start.elapsed_time(stop) / args.steps
+    # the timed steps: the same K forwards (layer copies in turn) captured as
+    # one HIP graph and replayed, as a serving runtime runs decode (the
+    # MXFP4-FP8-R12 card's deployment table: decode CUDA graphs); eager
+    # launches leave the GPU idle for a few microseconds at each call
+    from block_scaled_fp4_nvfp4_amd.stack import LayerStack
+    n = args.steps
+    gstack = LayerStack([layers[i % len(layers)] for i in range(n)], [x] * n, [tid] * n, [tw] * n)
+    gstack.capture()
+    gstack.replay()
+    torch.cuda.synchronize()
+    start.record()
+    gstack.replay()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / n
+    del gstack
 
     # per-stage durations (events recorded by the library between its launches)
     timer = pkg.StageTimer()
@@ -314,7 +330,9 @@ def bench_decode(args, torch, pkg):
         "config": {"workload": f"{cfg.name}: {cfg.num_experts} experts, top-{cfg.top_k}, hidden "
                                f"{cfg.hidden}, inter {cfg.inter}, {T} tokens, {cfg.w_fmt} "
                                f"({cfg.rule}) weights x bf16 activations",
-                   "tokens": T, "touched_experts": int(touched), "layer_copies": len(layers)},
+                   "tokens": T, "touched_experts": int(touched), "layer_copies": len(layers),
+                   "timing": "the K steps captured as one HIP graph: one untimed replay, then the timed one"},
+        "eager_ms_per_step": eager_ms,
         "roofline": roof,
         "step_hbm": {"bytes": step_bytes, "GBps": step_bytes / (ms * 1e-3) / 1e9,
                      "frac": step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
@@ -1148,7 +1166,7 @@ def main():
         return
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="all",
                     choices=["all", "decode", "prefill_nvfp4", "prefill_mxfp4", "prefill_fp8", "stream_quant",
