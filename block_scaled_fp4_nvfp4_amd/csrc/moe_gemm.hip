@@ -849,11 +849,13 @@ struct Mx2Cfg {
   // gate_up tiles, whose 4 weight subtiles per wave would spill more)
   static constexpr int D = KS < 3 ? KS : (NS >= 4 ? 2 : 3);
   static constexpr int A_BYTES = BM * 128;
+  static constexpr int STAGE = A_BYTES;
   // per row and step one scale dword: 4 UE8M0 block scales (MX) or the f32
-  // scale of the 128-block (FP8); either way K/32 bytes per row
-  static constexpr int STAGE = A_BYTES + BM * 4;
+  // scale of the 128-block (FP8); either way K/32 bytes per row.  The tile's
+  // scales of all KS steps sit in one LDS table [step][row], copied once.
+  static constexpr int TAB = KS * BM * 4;
   static constexpr int A_INS = A_BYTES / 4096;    // 16-byte DMA instructions per thread and stage
-  static constexpr int OPS_A = A_INS + 1;         // + one 4-byte DMA of the scales
+  static constexpr int OPS_A = A_INS;
   static constexpr int W_LD = GK == GK_FP8 ? 2 : 1;  // 16-byte code loads per subtile and step
   static constexpr int OPS_W = (W_LD + 1) * NS;   // + one scale dword per subtile
 };
@@ -939,7 +941,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
     else if constexpr (S == 6) return r6;
     else return r7;
   };
-  __shared__ __attribute__((aligned(16))) uint8_t dummy[1024];  // target of the unused scale DMA lanes
+  __shared__ __attribute__((aligned(16))) uint8_t s_tab[C::TAB];  // activation scales [step][row]
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   int* s_toff = reinterpret_cast<int*>(lds_dyn);
 
@@ -1005,8 +1007,8 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
     const int chunk = slot ^ ((row ^ (row >> 3)) & 7);  // inverse of swz<128>
     a_src[q] = g.a_codes + a_row_of(row) * K + 16 * chunk;
   }
-  const uint8_t* as_src = reinterpret_cast<const uint8_t*>(g.a_scales) + a_row_of(tid < BM ? tid : 0) * SKB;
-  uint8_t* as_dst_base = tid < BM ? nullptr : dummy;  // resolved per stage below
+  // this lane's row of the scale table (row = lane; each wave copies steps w, w + 4, ...)
+  const uint8_t* as_src = reinterpret_cast<const uint8_t*>(g.a_scales) + a_row_of(lane) * SKB;
   // this lane's weight rows: column lr of subtile s, K block lg of each step
   const uint8_t* w_src[NS];
   const uint8_t* ws_src[NS];
@@ -1029,7 +1031,6 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
   auto dma_a = [&](int ks, uint8_t* st) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < C::A_INS; ++q) dma16_to_lds(a_src[q] + ks * 128, st + (q * 4 + wave) * 1024);
-    dma4_to_lds(as_src + ks * 4, as_dst_base ? as_dst_base : st + C::A_BYTES);
   };
   u32x4 wq[D][NS][C::W_LD];
   int wsq[D][NS];
@@ -1056,7 +1057,9 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) acc[i][s] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // prologue: weights of steps 0..D-1, then activation stages 0..RS-2
+  // prologue: the scale table (older than every later load, so the waits
+  // below cover it), weights of steps 0..D-1, then activation stages 0..RS-2
+  for (int ks = __builtin_amdgcn_readfirstlane(wave); ks < KS; ks += 4) dma4_to_lds(as_src + 4 * ks, s_tab + ks * BM * 4);
 #pragma unroll
   for (int j = 0; j < D; ++j) load_w(j, wq[j], wsq[j]);
   static_for<RS - 1>([&](auto jc) __attribute__((always_inline)) {
@@ -1110,7 +1113,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
       int zo = 0;
       if constexpr (NTW > 1) asm volatile("s_mov_b32 %0, 0" : "=s"(zo));
       const uint8_t* s_a = stage(std::integral_constant<int, ks % RS>{}) + zo;
-      const uint8_t* s_as = s_a + C::A_BYTES;
+      const uint8_t* s_as = s_tab + ks * BM * 4 + zo;
       intx8 af[4];
       int asc[4];
       float afs[4][4];
@@ -1688,7 +1691,7 @@ static int launch_gemm_mx2_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream
   if (G <= 0) return FP4_OK;
   if (G > INT32_MAX) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM grid too large");
   const size_t lds = a.dense_rows > 0 ? 0 : sizeof(int) * ((size_t)a.E + 1);
-  constexpr size_t fixed = (size_t)C::RS * C::STAGE + 1024;
+  constexpr size_t fixed = (size_t)C::RS * C::STAGE + C::TAB;
   if (fixed + lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
   static std::atomic<uint64_t> lds_raised{0};
   FP4_CHECK(raise_dyn_lds(reinterpret_cast<const void*>(&grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS, WT, NTW>),
