@@ -575,6 +575,63 @@ __device__ __forceinline__ void store_h_mxfp8(const GemmArgs& g, const floatx4 (
     }
 }
 
+// h of a block-FP8 gate_up tile (128 outputs: 4 waves x 2 subtiles x 16)
+// straight to FP8 with one f32 scale per (row, 128 outputs), as
+// quant_fp8_row_kernel takes them from the f32 h: the row's amax over the
+// tile's 128 values (16-lane shuffles within a wave, then the four waves
+// through LDS; max is exact in any order), sigma = fp32(amax / 448), the
+// exact E4M3 code of |v| / sigma and the sign of v (sigma 0: signed zeros).
+// acc[i][j] holds gate and acc[i][2 + j] up of subtile j for rows
+// row0 + 16 i + 4 lg + r, column 16 j + lr of the wave's 32; nt is the tile's
+// 128-output block.
+__device__ __forceinline__ void store_h_fp8row(const GemmArgs& g, const floatx4 (&acc)[4][4], int nt, int row0,
+                                               int n_rows, int64_t r_begin, int wave, int lg, int lr) {
+  __shared__ float s_amax[4][64];
+  float v[4][4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) v[i][r][j] = silu_f32(acc[i][j][r]) * acc[i][2 + j][r];
+      float m = fmaxf(fabsf(v[i][r][0]), fabsf(v[i][r][1]));
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+      if (lr == 0) s_amax[wave][16 * i + 4 * lg + r] = m;
+    }
+  __syncthreads();
+  const int64_t N = g.N;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 16 * i + 4 * lg + r;
+      const float amax = fmaxf(fmaxf(s_amax[0][row], s_amax[1][row]), fmaxf(s_amax[2][row], s_amax[3][row]));
+      const float sigma = (float)((double)amax / 448.0);
+      const float sg = sigma > 0.0f ? sigma : 1.0f;
+      const int rr = row0 + row;
+      if (rr >= n_rows) continue;
+      const int64_t R = r_begin + rr;
+      // codes of |v| r (1 -/+ 2^-20) with r ~ 1/sigma within 2^-23 bracket
+      // the code of the exact quotient; where they agree it is that code,
+      // else the exact quotient decides (as in the standalone quantizer)
+      // (sigma below 2^-120, where 1/sigma nears the float range, always exact)
+      const bool rok = sg >= 0x1p-120f;
+      const float r0 = rok ? __builtin_amdgcn_rcpf(sg) : 0.0f;
+      const float rc = fmaf(r0, fmaf(-sg, r0, 1.0f), r0);
+      const float rl = rc * 0x1.ffffe0p-1f, rh = rc * 0x1.000010p+0f;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const float a = fabsf(v[i][r][j]);
+        uint32_t c = e4m3_hw(fminf(a * rl, kE4M3Max));
+        if (!rok || c != e4m3_hw(fminf(a * rh, kE4M3Max))) c = e4m3_exact_quotient(a, sg);
+        c = (sigma > 0.0f ? c : 0u) | ((__float_as_uint(v[i][r][j]) >> 24) & 0x80u);
+        g.q_codes[R * N + 128 * nt + 32 * wave + 16 * j + lr] = (uint8_t)c;
+      }
+      if (wave == 0 && lr == 0) reinterpret_cast<float*>(g.q_scales)[R * (N / 128) + nt] = sigma;
+    }
+}
+
 // ------------------------------------------- MX path with LDS-DMA staging
 //
 // MXFP4 weights x MXFP8 activations.  Same tile as above (64 rows x 64*NSUB
@@ -1182,6 +1239,14 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
       return;
     }
   }
+  if constexpr (GK == GK_FP8 && EPI == EPI_GATEUP && NSUB == 2) {
+    if (g.q_codes) {
+      int z0;
+      asm volatile("v_mov_b32 %0, 0" : "=v"(z0));
+      store_h_fp8row(g, acc, nt, mt * BM + z0, n_rows, r_begin, wave, lg, lr);
+      return;
+    }
+  }
   store_tile(nt);
 }
 
@@ -1623,6 +1688,13 @@ __global__ void __launch_bounds__(256) tile_weights_kernel(const uint8_t* __rest
 // inter of 640, and the block-FP8 gate_up over its hidden of 2560.
 static bool mx_down_on_mx2(int N, int K) { return N % 128 == 0 && K == 640; }
 static bool fp8_gateup_on_mx2(int N, int K) { return N % 64 == 0 && K == 2560; }
+// Block-FP8 gate_up on 128-output tiles (tiled weights, and a grid that
+// keeps 16 workgroups per CU; decode-size grids, which the wider tiles would
+// halve, keep 64): 8192 tokens 750 -> 686 us.  Its epilogue can then hold a
+// (row, 128) block of h whole and write h quantized.
+static bool fp8_gateup_128(int w_tiled, int N, int K, int64_t tiles_m_bound) {
+  return w_tiled && N % 128 == 0 && K == 2560 && tiles_m_bound * (N / 128) >= 16LL * device_cu_count();
+}
 // the MX gate_up over the model's hidden of 2560 on 128-output tiles, when
 // its weights are tiled (then faster than the all-DMA kernel; on row-major
 // weights the all-DMA kernel is the faster one)
@@ -1691,7 +1763,8 @@ static int launch_gemm_mx2_t(const GemmArgs& a, int64_t tiles_m_bound, hipStream
   if (G <= 0) return FP4_OK;
   if (G > INT32_MAX) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM grid too large");
   const size_t lds = a.dense_rows > 0 ? 0 : sizeof(int) * ((size_t)a.E + 1);
-  constexpr size_t fixed = (size_t)C::RS * C::STAGE + C::TAB;
+  // static LDS: the ring, the scale table and 1 KB for the FP8 h epilogue's row maxima
+  constexpr size_t fixed = (size_t)C::RS * C::STAGE + C::TAB + 1024;
   if (fixed + lds > 160 * 1024) return fail(FP4_ERR_UNSUPPORTED, "grouped GEMM tile needs too much LDS");
   static std::atomic<uint64_t> lds_raised{0};
   FP4_CHECK(raise_dyn_lds(reinterpret_cast<const void*>(&grouped_gemm_mx2_kernel<GK, EPI, NSUB, KS, WT, NTW>),
@@ -1770,8 +1843,8 @@ static int launch_gemm(const GemmArgs& a, int64_t tiles_m_bound, hipStream_t st)
       // 128-output tiles on tiled weights when they still give every CU 16
       // workgroups (8192 tokens: 686 against 750 us); decode batches, whose
       // grid the wider tiles would halve, and row-major weights keep 64
-      if (a.w_tiled && a.N % 128 == 0 && a.K == 2560 && tiles_m_bound * (a.N / 128) >= 16LL * device_cu_count())
-        return launch_gemm_mx2<GK_FP8, EPI, 2, 20>(a, tiles_m_bound, st);
+      if (fp8_gateup_128(a.w_tiled, a.N, a.K, tiles_m_bound)) return launch_gemm_mx2<GK_FP8, EPI, 2, 20>(a, tiles_m_bound, st);
+      if (a.q_codes) return fail(FP4_ERR_UNSUPPORTED, "FP8 h epilogue needs 128-output gate_up tiles");
       if (fp8_gateup_on_mx2(a.N, a.K)) return launch_gemm_mx2<GK_FP8, EPI, 1, 20>(a, tiles_m_bound, st);
     }
     if (a.w_tiled) return fail(FP4_ERR_UNSUPPORTED, "tiled weights on a GEMM kernel that reads rows");
@@ -1844,8 +1917,10 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   a.out = w.h;
   a.row_scale = nullptr;
   // MXFP8 h has one scale per 32 outputs, which the MX gate_up kernel's
-  // 128-output tiles hold whole: its epilogue writes h quantized (no f32 h)
-  const bool h_in_epilogue = gk == GK_MX && I % 128 == 0;
+  // 128-output tiles hold whole: its epilogue writes h quantized (no f32 h);
+  // likewise FP8 h (one scale per 128 outputs) on the block-FP8 kernel's
+  // 128-output tiles
+  const bool h_in_epilogue = (gk == GK_MX && I % 128 == 0) || (gk == GK_FP8 && fp8_gateup_128(a.w_tiled, I, H, tiles_bound));
   a.q_codes = h_in_epilogue ? w.hq_codes : nullptr;
   a.q_scales = h_in_epilogue ? static_cast<uint8_t*>(w.hq_scales) : nullptr;
   // NVFP4 h with a dynamic tensor scale: the gate_up workgroups (register-

@@ -554,30 +554,6 @@ __global__ void __launch_bounds__(256) quant_mxfp8_kernel(const T* __restrict__ 
   (void)mxfp8_block<T>(x, g, codes, scales, out);
 }
 
-// Exact E4M3 code (saturating) of a / sigma for a >= 0, sigma > 0 floats.
-// The float quotient q = RN(a / sigma) rounds to the same code as the exact
-// quotient unless q lands exactly on an E4M3 midpoint (RN is monotone and
-// every midpoint is a float); only then is a compared with midpoint * sigma,
-// exactly in double (5 + 24 significant bits), to pick the side.
-__device__ __forceinline__ bool e4m3_is_midpoint(float q) {
-  const bool normal_mid = (__float_as_uint(q) & 0x000FFFFFu) == 0x00080000u;  // half of the 3-bit ulp
-  const float t = q * 1024.0f;  // subnormal quantum 2^-9: midpoints are odd multiples of 2^-10
-  const bool sub_mid = (t == rintf(t)) & (((int)t & 1) != 0);
-  return q >= 0.015625f ? normal_mid : sub_mid;
-}
-__device__ __forceinline__ uint32_t e4m3_fix_midpoint(uint32_t c, float q, float a, float sigma) {
-  const double A = (double)a, M = (double)q * (double)sigma;
-  const float vc = __builtin_amdgcn_cvt_f32_fp8((int)c, 0);
-  if (A > M && vc < q) return c + 1;
-  if (A < M && vc > q) return c - 1;
-  return c;
-}
-__device__ __forceinline__ uint32_t e4m3_exact_quotient(float a, float sigma) {
-  const float q = fminf(a / sigma, kE4M3Max);
-  const uint32_t c = e4m3_hw(q);
-  return e4m3_is_midpoint(q) ? e4m3_fix_midpoint(c, q, a, sigma) : c;
-}
-
 // FP8 with one fp32 scale per (row, 128 columns): 4 lanes per group of 128.
 template <typename T>
 __global__ void __launch_bounds__(256) quant_fp8_row_kernel(const T* __restrict__ x, int64_t ngroups,
