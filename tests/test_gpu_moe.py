@@ -131,6 +131,39 @@ def test_gemv_path_batch_invariant(tiny, w_fmt, a_fmt):
     assert rel_fro(y65, y_ref) <= TOL
 
 
+@pytest.mark.parametrize("w_fmt", ["nvfp4", "mxfp4"])
+@pytest.mark.parametrize("with_shared", [False, True])
+def test_gemv_path_permutations_agree(tiny, w_fmt, with_shared):
+    """512 tokens at top-2 (1024 pairs: the one-workgroup permutation) and the
+    same tokens as the head of a 513-token batch (the multi-pass one) give
+    bit-identical y on the bf16-activation GEMV path, with pairs out of range
+    (token 3 has no valid pair, so its y is the shared expert's output alone,
+    or zero) and with the MXFP8 shared expert added on a second stream; y also
+    against the oracle."""
+    print_case(f"GEMV path, both permutations {w_fmt}, shared={with_shared}")
+    cfg, w13, w2, _, _, _ = tiny
+    c = cfg.replace(w_fmt=w_fmt, tokens=513, input_seed=41, shared_inter=128 if with_shared else 0)
+    x = synth.activations(c)
+    ids, wts = synth.routing(c)
+    ids = ids.copy()
+    ids[3, :] = c.num_experts
+    ids[7, 1] = -1
+    ids[400, 0] = c.num_experts + 5
+    shared = synth.shared_expert(c) if with_shared else None
+    layer = gpu_layer(c, w13, w2, shared=shared)
+    y513, _, _ = _run(layer, x, ids, wts)
+    y512, ws, lay = _run(layer, x[:512], ids[:512], wts[:512])
+    assert _ws_i32(ws, lay["error_flag"], 1)[0] == c.top_k + 2
+    np.testing.assert_array_equal(y512.view(np.uint32), y513[:512].view(np.uint32))
+    if not with_shared:
+        assert np.all(y512[3] == 0.0)
+    fixed, wz = ids.copy(), wts.copy()
+    bad = (ids < 0) | (ids >= c.num_experts)
+    fixed[bad], wz[bad] = 0, 0.0
+    y_ref = moe.moe_forward(OracleLayer(c, w13, w2, shared=shared).as_dict(), x[:512], fixed[:512], wz[:512])
+    assert rel_fro(y512, y_ref) <= TOL
+
+
 def test_single_expert_top1_reduces_to_dense(tiny):
     print_case("tiny E=1 k=1")
     cfg, w13, w2, x, _, _ = tiny
