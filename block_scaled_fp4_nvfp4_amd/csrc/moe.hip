@@ -254,12 +254,14 @@ __global__ void __launch_bounds__(1024) perm_small_kernel(const int32_t* __restr
 __global__ void __launch_bounds__(kPermBlock) perm_count_kernel(const int32_t* __restrict__ ids, int64_t P,
                                                                 int E, int32_t* __restrict__ rank,
                                                                 int32_t* __restrict__ block_counts,
-                                                                int32_t* __restrict__ block_invalid) {
+                                                                int32_t* __restrict__ block_invalid,
+                                                                int32_t* __restrict__ scan_done) {
   extern __shared__ int smem[];
   int* s_ids = smem;              // kPermBlock
   int* s_hist = smem + kPermBlock;  // E
   int tid = threadIdx.x;
   int64_t p = (int64_t)blockIdx.x * kPermBlock + tid;
+  if ((blockIdx.x | tid) == 0) *scan_done = 0;  // arrivals of the next pass's workgroups
   for (int e = tid; e < E; e += kPermBlock) s_hist[e] = 0;
   int my = -1;
   if (p < P) {
@@ -292,43 +294,80 @@ __global__ void __launch_bounds__(kPermBlock) perm_count_kernel(const int32_t* _
   }
 }
 
-// Pass 2 (one workgroup of 1024): per-expert running sums over blocks
-// (turning block_counts into block bases), totals, offsets, active list,
-// tile offsets and the error flag.
+// Pass 2 (grid = ceil(E/64) workgroups of 1024): per-expert running sums
+// over blocks, turning block_counts into block bases.  Lane l of every wave
+// takes expert 64 x + l (coalesced rows of block_counts), wave w the w-th
+// sixteenth of the blocks; a workgroup adds up its waves' parts in LDS, then
+// rewrites its columns.  Each workgroup stores its experts' totals at device
+// scope (written through to memory), waits for them, and counts itself in
+// scan_done (zeroed by pass 1); the last to arrive reads every total back at
+// device scope and writes the offsets, the active list, the tile offsets and
+// the error flag.  No workgroup waits for another.
 __global__ void __launch_bounds__(1024) perm_scan_kernel(int nb, int E, int tile_m,
                                                          int32_t* __restrict__ block_counts,
                                                          const int32_t* __restrict__ block_invalid,
                                                          int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ active,
                                                          int32_t* __restrict__ tile_offsets,
-                                                         int32_t* __restrict__ error_flag) {
+                                                         int32_t* __restrict__ error_flag,
+                                                         int32_t* __restrict__ scan_done) {
+  extern __shared__ int s_cnt[];  // E: the last workgroup's copy of the totals
   __shared__ int tmp[64];
-  for (int e = threadIdx.x; e < E; e += 1024) {
-    int run = 0, b = 0;
-    for (; b + 16 <= nb; b += 16) {  // 16 independent loads in flight
-      int c[16];
+  __shared__ int s_part[16][64];
+  __shared__ int s_last;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 64 + lane;
+  const int per = (nb + 15) / 16;
+  const int b0 = min(nb, wave * per), b1 = min(nb, b0 + per);
+  int32_t* col = block_counts + e;
+  int sum = 0;
+  if (e < E) {
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {  // 8 independent loads in flight
+      int c[8];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) c[u] = block_counts[(int64_t)(b + u) * E + e];
+      for (int u = 0; u < 8; ++u) c[u] = col[(int64_t)(b + u) * E];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        block_counts[(int64_t)(b + u) * E + e] = run;
+      for (int u = 0; u < 8; ++u) sum += c[u];
+    }
+    for (; b < b1; ++b) sum += col[(int64_t)b * E];
+  }
+  s_part[wave][lane] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int w = 0; w < wave; ++w) run += s_part[w][lane];
+  if (e < E) {
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = col[(int64_t)(b + u) * E];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        col[(int64_t)(b + u) * E] = run;
         run += c[u];
       }
     }
-    for (; b < nb; ++b) {
-      int c = block_counts[(int64_t)b * E + e];
-      block_counts[(int64_t)b * E + e] = run;
+    for (; b < b1; ++b) {
+      const int c = col[(int64_t)b * E];
+      col[(int64_t)b * E] = run;
       run += c;
     }
-    counts[e] = run;
+    if (wave == 15) __hip_atomic_store(counts + e, run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // wave 15 ends at nb
   }
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's stores acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0)
+    s_last = __hip_atomic_fetch_add(scan_done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1;
+  __syncthreads();
+  if (!s_last) return;
+  for (int i = threadIdx.x; i < E; i += 1024) s_cnt[i] = __hip_atomic_load(counts + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int bad[1] = {0}, bad_tot[1];
   for (int b = threadIdx.x; b < nb; b += 1024) bad[0] += block_invalid[b];
   block_scan_1024<1>(bad, tmp, bad_tot);
   const int tot_bad = bad_tot[0];
-  __threadfence_block();
   __syncthreads();
-  finish_offsets(counts, E, tile_m, offsets, active, tile_offsets, tmp);
+  finish_offsets(s_cnt, E, tile_m, offsets, active, tile_offsets, tmp);
   if (threadIdx.x == 0) error_flag[0] = tot_bad;
 }
 
@@ -361,11 +400,13 @@ int launch_permute(const int32_t* ids, int64_t P, int E, int tile_m, const WsPtr
   int64_t nb = (P + kPermBlock - 1) / kPermBlock;
   if (nb == 0) nb = 1;  // still writes counts/offsets for P == 0
   size_t lds = sizeof(int) * (kPermBlock + E);
+  int32_t* scan_done = w.error_flag + 1;
   hipLaunchKernelGGL(perm_count_kernel, dim3((unsigned)nb), dim3(kPermBlock), lds, st, ids, P, E,
-                     w.row_of_pair, w.block_counts, w.block_invalid);
+                     w.row_of_pair, w.block_counts, w.block_invalid, scan_done);
   FP4_CHECK(check_launch("perm_count"));
-  hipLaunchKernelGGL(perm_scan_kernel, dim3(1), dim3(1024), 0, st, (int)nb, E, tile_m, w.block_counts,
-                     w.block_invalid, w.counts, w.offsets, w.active, w.tile_offsets, w.error_flag);
+  hipLaunchKernelGGL(perm_scan_kernel, dim3((unsigned)((E + 63) / 64)), dim3(1024), sizeof(int) * (size_t)E, st,
+                     (int)nb, E, tile_m, w.block_counts, w.block_invalid, w.counts, w.offsets, w.active,
+                     w.tile_offsets, w.error_flag, scan_done);
   FP4_CHECK(check_launch("perm_scan"));
   if (P > 0) {
     hipLaunchKernelGGL(perm_scatter_kernel, dim3((unsigned)nb), dim3(kPermBlock), 0, st, ids, P, E,

@@ -233,7 +233,8 @@ typedef struct {
  * quantized and only hq_codes / hq_scales hold it). */
 typedef struct {
   size_t total;          /* required workspace bytes                              */
-  size_t error_flag;     /* int32: nonzero if a topk id was out of range           */
+  size_t error_flag;     /* int32: nonzero if a topk id was out of range (the next
+                            int32 is the permutation's own arrival counter)      */
   size_t counts;         /* int32 [E]   pairs per expert                           */
   size_t offsets;        /* int32 [E+1] first sorted row of each expert            */
   size_t pair_of_row;    /* int32 [T*k] pair (t*k + j) held by each sorted row      */
