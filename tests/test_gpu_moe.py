@@ -211,6 +211,40 @@ def test_decode_layer_all_tokens(decode_layer):
     assert np.all(np.isfinite(y)) and np.linalg.norm(y) > 0
 
 
+def test_decode_layer_graph_replay_bit_identical(decode_layer):
+    """The decode layer as the benchmark times it: several forwards of the
+    full-size layer (16 tokens, 512 experts, top-10) captured as one HIP graph
+    and replayed; every replay's y equals the eager forward bit for bit, with
+    other forwards (other routing, the same workspace) and synchronisations
+    between the replays."""
+    print_case("decode layer, graph replay vs eager")
+    from block_scaled_fp4_nvfp4_amd.stack import LayerStack
+    m = _lib()
+    cfg, w13, w2 = decode_layer
+    x = dev_bf16(synth.activations(cfg))
+    ids, wts = synth.routing(cfg)
+    layer = gpu_layer(cfg, w13, w2)
+    n = 4
+    st = LayerStack([layer] * n, [x] * n, [dev(ids)] * n, [dev(wts)] * n)
+    st.eager()
+    torch.cuda.synchronize()
+    eager = host(st.ys[0]).copy()
+    for y in st.ys[1:]:
+        np.testing.assert_array_equal(host(y).view(np.uint32), eager.view(np.uint32))
+    st.capture()
+    ids2, wts2 = synth.routing(cfg.replace(input_seed=cfg.input_seed + 7))
+    for rep in range(3):
+        for y in st.ys:
+            y.fill_(float("nan"))
+        m.moe_forward(layer, x, dev(ids2), dev(wts2), st.workspace)  # other work in the shared workspace
+        torch.cuda.synchronize()
+        st.replay()
+        torch.cuda.synchronize()
+        for i, y in enumerate(st.ys):
+            np.testing.assert_array_equal(host(y).view(np.uint32), eager.view(np.uint32),
+                                          err_msg=f"replay {rep}, forward {i}")
+
+
 def test_many_tokens_uses_multipass_permutation(tiny):
     """1200 pairs (> 1024) go through the three-pass permutation."""
     print_case("tiny layer, 600 tokens")
