@@ -827,13 +827,72 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
   reinterpret_cast<float4*>(y + t * H)[c4] = acc;
 }
 
-static void launch_combine(const float* o, const int32_t* row_of_pair, const float* topk_w, int64_t T, int H,
-                           int k, const float* extra, float* y, hipStream_t st) {
+// The same combine over o in fp16 (the grouped path's down GEMMs leave it
+// so): eight outputs per thread, one 16-byte load of o per slot, the sum in
+// f32 in the same slot order.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+template <int CW>
+__global__ void __launch_bounds__(256) combine_f16_kernel(const _Float16* __restrict__ o,
+                                                          const int32_t* __restrict__ row_of_pair,
+                                                          const float* __restrict__ topk_w, int64_t T, int H,
+                                                          int k, const float* __restrict__ extra,
+                                                          float* __restrict__ y) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // eight consecutive floats of y
+  int64_t per_row = H / 8;
+  if (i >= T * per_row) return;
+  int64_t t = i / per_row, c8 = i - t * per_row;
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+  for (int j0 = 0; j0 < k; j0 += CW) {
+    int rows[CW];
+    float w[CW];
+#pragma unroll
+    for (int u = 0; u < CW; ++u)
+      if (j0 + u < k) {
+        rows[u] = row_of_pair[t * k + j0 + u];
+        w[u] = topk_w[t * k + j0 + u];
+      }
+    half8_t v[CW];
+#pragma unroll
+    for (int u = 0; u < CW; ++u)
+      if (j0 + u < k && rows[u] >= 0) v[u] = reinterpret_cast<const half8_t*>(o + (int64_t)rows[u] * H)[c8];
+#pragma unroll
+    for (int u = 0; u < CW; ++u)
+      if (j0 + u < k && rows[u] >= 0) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = fmaf(w[u], (float)v[u][q], acc[q]);
+      }
+  }
+  if (extra) {
+    const float4* e = reinterpret_cast<const float4*>(extra + t * H) + 2 * c8;
+    const float4 e0 = e[0], e1 = e[1];
+    acc[0] += e0.x; acc[1] += e0.y; acc[2] += e0.z; acc[3] += e0.w;
+    acc[4] += e1.x; acc[5] += e1.y; acc[6] += e1.z; acc[7] += e1.w;
+  }
+  float4* yo = reinterpret_cast<float4*>(y + t * H) + 2 * c8;
+  yo[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+  yo[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+static void launch_combine(const void* o, bool o_f16, const int32_t* row_of_pair, const float* topk_w, int64_t T,
+                           int H, int k, const float* extra, float* y, hipStream_t st) {
+  if (o_f16) {
+    const _Float16* oh = static_cast<const _Float16*>(o);
+    const dim3 grid(grid_1d(T * H / 8, 256)), block(256);
+    if (k <= 4) hipLaunchKernelGGL(combine_f16_kernel<4>, grid, block, 0, st, oh, row_of_pair, topk_w, T, H, k, extra, y);
+    else if (k <= 8) hipLaunchKernelGGL(combine_f16_kernel<8>, grid, block, 0, st, oh, row_of_pair, topk_w, T, H, k, extra, y);
+    else if (k <= 12) hipLaunchKernelGGL(combine_f16_kernel<12>, grid, block, 0, st, oh, row_of_pair, topk_w, T, H, k, extra, y);
+    else hipLaunchKernelGGL(combine_f16_kernel<16>, grid, block, 0, st, oh, row_of_pair, topk_w, T, H, k, extra, y);
+    return;
+  }
+  const float* of = static_cast<const float*>(o);
   const dim3 grid(grid_1d(T * H / 4, 256)), block(256);
-  if (k <= 4) hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, st, o, row_of_pair, topk_w, T, H, k, extra, y);
-  else if (k <= 8) hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, st, o, row_of_pair, topk_w, T, H, k, extra, y);
-  else if (k <= 12) hipLaunchKernelGGL(combine_kernel<12>, grid, block, 0, st, o, row_of_pair, topk_w, T, H, k, extra, y);
-  else hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, st, o, row_of_pair, topk_w, T, H, k, extra, y);
+  if (k <= 4) hipLaunchKernelGGL(combine_kernel<4>, grid, block, 0, st, of, row_of_pair, topk_w, T, H, k, extra, y);
+  else if (k <= 8) hipLaunchKernelGGL(combine_kernel<8>, grid, block, 0, st, of, row_of_pair, topk_w, T, H, k, extra, y);
+  else if (k <= 12) hipLaunchKernelGGL(combine_kernel<12>, grid, block, 0, st, of, row_of_pair, topk_w, T, H, k, extra, y);
+  else hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, st, of, row_of_pair, topk_w, T, H, k, extra, y);
 }
 
 // ---------------------------------------------------------- GEMV dispatch
@@ -1073,6 +1132,7 @@ static int forward_impl(const moe_fp4_layer* L, const uint16_t* x, int64_t T, co
   }
   FP4_CHECK(launch_permute(topk_ids, P, L->num_experts, kGemmTileM, w, st));
   FP4_CHECK(mark(1));
+  bool grouped = false;  // the grouped GEMMs leave o in fp16, the GEMVs in f32
   if (L->a_fmt == FP4_FMT_NONE) {
     FP4_CHECK(mark(2));
     if (L->w_fmt == FP4_FMT_NVFP4) FP4_CHECK(launch_gemv<FP4_FMT_NVFP4>(x, w, L, P, max_active, st, mark));
@@ -1084,11 +1144,12 @@ static int forward_impl(const moe_fp4_layer* L, const uint16_t* x, int64_t T, co
     FP4_CHECK(mark(2));
     FP4_CHECK(launch_gemv<FP4_FMT_MXFP4>(w.x_deq, w, L, P, max_active, st, mark, true));
   } else {
+    grouped = true;
     FP4_CHECK(launch_grouped(L, x, T, w, max_active, st, mark));
   }
   if (sj.side) FP4_CHECK(sj.join());
   FP4_CHECK(mark(6));  // the "shared" stage is the part of the shared expert not hidden by the routed path
-  launch_combine(w.o, w.row_of_pair, topk_weights, T, L->hidden, L->top_k, extra, y, st);
+  launch_combine(w.o, grouped, w.row_of_pair, topk_weights, T, L->hidden, L->top_k, extra, y, st);
   FP4_CHECK(check_launch("combine"));
   return mark(7);
 }

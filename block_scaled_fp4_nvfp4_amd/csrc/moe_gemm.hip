@@ -92,6 +92,9 @@ struct GemmArgs {
   int E, k, dense_rows;         // dense_rows > 0: one expert with that many rows, no routing
   int K, N;                     // reduction size; outputs (gate_up: I; down: H)
   float* out;                   // gate_up: h [rows][N]; down: o [rows][N]
+  // down: when set, o leaves the epilogue here as fp16 (rounded to nearest
+  // even from the f32 accumulator) and `out` is not written
+  _Float16* out_f16;
   const float* row_scale;       // down epilogue: per-row multiplier (shared-expert gate), may be null
   // MX gate_up on 128-output tiles only (grouped_gemm_mx_kernel<EPI_GATEUP, 2>):
   // when set, h leaves the epilogue as MXFP8 (E4M3 codes [rows][N], UE8M0
@@ -107,6 +110,14 @@ struct GemmArgs {
   // order of moe_fp4_tile_weights
   int w_tiled;
 };
+
+// One value of an epilogue: h or o in f32, or o in fp16 where the caller
+// asked for it.
+template <int EPI>
+__device__ __forceinline__ void store_out(const GemmArgs& g, int64_t idx, float v) {
+  if (EPI == EPI_DOWN && g.out_f16) g.out_f16[idx] = (_Float16)v;
+  else g.out[idx] = v;
+}
 
 // Tile of this workgroup among n_tiles real (row block, output group) tiles.
 // Workgroups are dispatched to the 8 XCDs in turn (workgroup i to XCD i % 8);
@@ -524,7 +535,7 @@ __global__ void __launch_bounds__(256) grouped_gemm_kernel(GemmArgs g) {
           v = acc[i][j][r] * scale;
           if (g.row_scale) v *= g.row_scale[R];
         }
-        g.out[R * g.N + n] = v;
+        store_out<EPI>(g, R * g.N + n, v);
       }
     }
   if constexpr (GK == GK_NV && EPI == EPI_GATEUP) {
@@ -880,7 +891,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx_kernel(GemmArgs g) {
           v = acc[i][j][r];
           if (g.row_scale) v *= g.row_scale[R];
         }
-        g.out[R * g.N + n] = v;
+        store_out<EPI>(g, R * g.N + n, v);
       }
     }
 }
@@ -1148,7 +1159,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_mx2_kernel(GemmArgs g) {
             v = acc[i][j][r];
             if (g.row_scale) v *= g.row_scale[R];
           }
-          g.out[R * g.N + n] = v;
+          store_out<EPI>(g, R * g.N + n, v);
         }
       }
   };
@@ -1479,7 +1490,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
           const int64_t R = r_begin + rr;
           float v = acc[i][j][r] * scale;
           if (g.row_scale) v *= g.row_scale[R];
-          g.out[R * g.N + n] = v;
+          store_out<EPI>(g, R * g.N + n, v);
         }
       }
   };
@@ -1567,7 +1578,7 @@ __global__ void __launch_bounds__(256, 2) grouped_gemm_nv2_kernel(GemmArgs g) {
           v = acc[i][j][r] * scale;
           if (g.row_scale) v *= g.row_scale[R];
         }
-        g.out[R * g.N + n] = v;
+        store_out<EPI>(g, R * g.N + n, v);
       }
     }
   if constexpr (EPI == EPI_GATEUP) {
@@ -1965,7 +1976,8 @@ int launch_grouped(const moe_fp4_layer* L, const uint16_t* x, int64_t T, const W
   d.w_tensor_scale = L->w2_scale_2;
   d.K = I;
   d.N = H;
-  d.out = w.o;
+  d.out = nullptr;
+  d.out_f16 = reinterpret_cast<_Float16*>(w.o);  // o in fp16: half the bytes the combine reads back
   if (gk == GK_NV) FP4_CHECK((launch_gemm<GK_NV, EPI_DOWN>(d, tiles_bound, st)));
   else if (gk == GK_MX) FP4_CHECK((launch_gemm<GK_MX, EPI_DOWN>(d, tiles_bound, st)));
   else FP4_CHECK((launch_gemm<GK_FP8, EPI_DOWN>(d, tiles_bound, st)));

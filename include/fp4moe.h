@@ -245,7 +245,11 @@ typedef struct {
                             skipped pairs, sorted last, unspecified)             */
   size_t hq_codes;       /* quantized h codes (layout of a_fmt), sorted row order    */
   size_t hq_scales;      /* quantized h scales                                       */
-  size_t o;              /* f32 [T*k, H]  down projection per sorted row (unweighted) */
+  size_t o;              /* [T*k, H] down projection per sorted row (unweighted):
+                            f32 on the GEMV paths (bf16 or MXFP8 activations at
+                            decode sizes); fp16, rounded to nearest even from the
+                            f32 accumulator, in the first half of this region on
+                            the grouped MFMA path                                */
 } moe_fp4_ws_layout;
 
 int moe_fp4_workspace_layout(const moe_fp4_layer* layer, int64_t tokens,
