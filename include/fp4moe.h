@@ -265,6 +265,10 @@ int moe_fp4_workspace_size(const moe_fp4_layer* layer, int64_t tokens,
  *  topk_weights f32 [T, k], routing weights, applied after the down projection.
  *  workspace    >= moe_fp4_workspace_size bytes of device memory.
  * Routing (softmax / top-k) is done by the caller.
+ * Precision: f32 accumulation throughout.  With quantized activations (the
+ * grouped MFMA path) each pair's unweighted down output is held in fp16
+ * between the down GEMM and the combine: a layer whose |o| can exceed 65504
+ * gets inf in y there.
  * Shape errors (FP4_ERR_SHAPE): hidden or inter not a multiple of 32 (128 for
  * the quantized-activation pairs and block FP8; shared width a multiple of
  * 128).  FP4_ERR_UNSUPPORTED: k > 32, E > 8192, or, for weight-only layers,
