@@ -1056,13 +1056,13 @@ TRAFFIC_KERNELS = {
                ("combine_kernel", ("combine_kernel<",), "combine", "moe.hip", "launch")],
     "prefill_nvfp4": [("grouped_gemm_nv2_kernel", ("grouped_gemm_nv2_kernel<0,",), "gate_up", "moe_gemm.hip", "launch"),
                       ("grouped_gemm_nv2_kernel", ("grouped_gemm_nv2_kernel<1,",), "down", "moe_gemm.hip", "launch"),
-                      ("combine_kernel", ("combine_kernel<",), "combine", "moe.hip", "launch")],
+                      ("combine_f16_kernel", ("combine_f16_kernel<",), "combine", "moe.hip", "launch")],
     "prefill_mxfp4": [("grouped_gemm_mx2_kernel", ("grouped_gemm_mx2_kernel<1, 0,",), "gate_up", "moe_gemm.hip", "launch"),
                       ("grouped_gemm_mx2_kernel", ("grouped_gemm_mx2_kernel<1, 1,",), "down", "moe_gemm.hip", "launch"),
-                      ("combine_kernel", ("combine_kernel<",), "combine", "moe.hip", "launch")],
+                      ("combine_f16_kernel", ("combine_f16_kernel<",), "combine", "moe.hip", "launch")],
     "prefill_fp8": [("grouped_gemm_mx2_kernel", ("grouped_gemm_mx2_kernel<2, 0,",), "gate_up", "moe_gemm.hip", "launch"),
                     ("grouped_gemm_mx2_kernel", ("grouped_gemm_mx2_kernel<2, 1,",), "down", "moe_gemm.hip", "launch"),
-                    ("combine_kernel", ("combine_kernel<",), "combine", "moe.hip", "launch")],
+                    ("combine_f16_kernel", ("combine_f16_kernel<",), "combine", "moe.hip", "launch")],
     "stream_quant": [("quant_fp4_kernel", _QUANT_KERNELS, "quantize", "quant.hip", "layer")],
     "sweep_quant": [("quant_fp4_kernel", _QUANT_KERNELS, "quantize", "quant.hip", "layer")],
     "hessian_quant": [("hessian_quant_kernel", ("hessian_quant_kernel<",), "quantize", "hessian.hip", "layer")],
