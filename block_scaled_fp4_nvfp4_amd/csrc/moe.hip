@@ -828,12 +828,13 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
 }
 
 // The same combine over o in fp16 (the grouped path's down GEMMs leave it
-// so): eight outputs per thread, one 16-byte load of o per slot, the sum in
-// f32 in the same slot order.
+// so; passed as its bit patterns, which keeps the kernel's name readable in
+// profiler output): eight outputs per thread, one 16-byte load of o per
+// slot, the sum in f32 in the same slot order.
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
 template <int CW>
-__global__ void __launch_bounds__(256) combine_f16_kernel(const _Float16* __restrict__ o,
+__global__ void __launch_bounds__(256) combine_f16_kernel(const uint16_t* __restrict__ o,
                                                           const int32_t* __restrict__ row_of_pair,
                                                           const float* __restrict__ topk_w, int64_t T, int H,
                                                           int k, const float* __restrict__ extra,
@@ -879,7 +880,7 @@ __global__ void __launch_bounds__(256) combine_f16_kernel(const _Float16* __rest
 static void launch_combine(const void* o, bool o_f16, const int32_t* row_of_pair, const float* topk_w, int64_t T,
                            int H, int k, const float* extra, float* y, hipStream_t st) {
   if (o_f16) {
-    const _Float16* oh = static_cast<const _Float16*>(o);
+    const uint16_t* oh = static_cast<const uint16_t*>(o);
     const dim3 grid(grid_1d(T * H / 8, 256)), block(256);
     if (k <= 4) hipLaunchKernelGGL(combine_f16_kernel<4>, grid, block, 0, st, oh, row_of_pair, topk_w, T, H, k, extra, y);
     else if (k <= 8) hipLaunchKernelGGL(combine_f16_kernel<8>, grid, block, 0, st, oh, row_of_pair, topk_w, T, H, k, extra, y);
