@@ -102,6 +102,64 @@ def test_tiny_quantized_activations(tiny, w_fmt, a_fmt):
         _check_h_tensor_scale(ws, lay, h)
 
 
+def _ulp16(v):
+    """Spacing of fp16 values at |v| (the subnormal spacing 2^-24 below 2^-14)."""
+    a = np.abs(np.asarray(v, np.float64))
+    e = np.floor(np.log2(np.where(a >= 2.0 ** -14, a, 1.0)))
+    return np.where(a >= 2.0 ** -14, 2.0 ** (e - 10), 2.0 ** -24)
+
+
+@pytest.mark.parametrize("w_fmt,a_fmt", MODES)
+def test_tiny_o_is_the_fp16_rounding_of_the_down_product(tiny, w_fmt, a_fmt):
+    """The grouped path holds each pair's unweighted down output o in fp16:
+    every o value lies within half an fp16 spacing (plus the f32
+    accumulation's rounding) of the float64 product of the GPU's own
+    quantized h, dequantized by the oracle, with the oracle's W2 of the
+    row's expert.  This isolates the down GEMM and its fp16 store from the
+    stages before it.  520 tokens at top-2 (1040 pairs) keep MXFP4 x MXFP8
+    off the GEMV path, which takes up to 1024 pairs and keeps o in f32."""
+    from oracle import quant as Q
+    from oracle.formats import unpack_nibbles
+    print_case(f"tiny {w_fmt} x {a_fmt}: o in fp16")
+    cfg, w13, w2, _, _, _ = tiny
+    cfg = cfg.replace(w_fmt=w_fmt, a_fmt=a_fmt, tokens=520, input_seed=53)
+    x = synth.activations(cfg)
+    ids, wts = synth.routing(cfg)
+    _, ws, lay = _run(gpu_layer(cfg, w13, w2), x, ids, wts)
+    P, I, H = cfg.pairs, cfg.inter, cfg.hidden
+    assert P > 1024
+    offsets, _, _ = moe.permute(ids, cfg.num_experts)
+    codes = host(ws[lay["hq_codes"]:lay["hq_codes"] + P * I])
+    if a_fmt == "nvfp4":
+        sc = host(ws[lay["hq_scales"]:lay["hq_scales"] + P * I // 16]).reshape(P, I // 16)
+        sh = host(ws[lay["h_tensor_scale"]:lay["h_tensor_scale"] + 4].view(torch.float32))[0]
+        hq = Q.dequantize_nvfp4(unpack_nibbles(codes[:P * I // 2].reshape(P, I // 2)), sc, sh)
+    elif a_fmt == "mxfp8":
+        sc = host(ws[lay["hq_scales"]:lay["hq_scales"] + P * I // 32]).reshape(P, I // 32)
+        hq = Q.dequantize_mxfp8(codes.reshape(P, I), sc)
+    else:
+        sc = host(ws[lay["hq_scales"]:lay["hq_scales"] + 4 * P * I // 128].view(torch.float32))
+        hq = Q.dequantize_fp8_rows(codes.reshape(P, I), sc.reshape(P, I // 128))
+    o = host(ws[lay["o"]:lay["o"] + 2 * P * H].view(torch.float16)).astype(np.float64).reshape(P, H)
+    ol = OracleLayer(cfg, w13, w2)
+    o_ref = np.zeros((P, H))
+    for e in range(cfg.num_experts):
+        r0, r1 = offsets[e], offsets[e + 1]
+        if r1 > r0:
+            o_ref[r0:r1] = hq[r0:r1] @ moe.dequantize_weight(ol.w2(e), w_fmt).T
+    assert np.all(np.isfinite(o))
+    # the MFMA's accumulation: fp16 MFMA on exactly decoded values sums exact
+    # products in f32 (within 1e-5 of the row's largest value here); the
+    # block-scaled FP8 MFMA's sum is less exact (the h stage above allows
+    # 1e-4; measured up to about 4e-5 of the row's largest value per element
+    # in the MXFP4 x MXFP8 down GEMM)
+    slack = (2e-5 if a_fmt == "nvfp4" else 1e-4) * np.abs(o_ref).max(axis=1, keepdims=True)
+    bound = 0.5 * _ulp16(np.maximum(np.abs(o_ref), np.abs(o))) + slack
+    worst = np.max(np.abs(o - o_ref) / bound)
+    print(f"largest |o - o_ref| / bound {worst:.3f}; relative Frobenius {rel_fro(o, o_ref):.3e}")
+    assert worst <= 1.0
+
+
 def _check_h_tensor_scale(ws, lay, h):
     """S_h = fp32(amax / 2688) over the GPU's own f32 h, exactly (the amax
     comes from partial maxima left by the gate_up workgroups)."""
